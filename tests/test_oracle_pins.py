@@ -1,0 +1,454 @@
+"""Pins for the fp64 oracle, each against something other than the oracle.
+
+CPU only.  Every check here is fixed by the pages or by mathematics:
+  * the three worked examples printed on "Gated DeltaNet State Update";
+  * invariants the recurrence implies (beta=0/gamma=1 identity, gamma=0 reset,
+    unit-key overwrite, linearity in (V, S0));
+  * a brute-force product of explicit Dk x Dk per-step matrices, as the page's
+    hints suggest (identity matrix, batched matmul, broadcast outer products),
+    and a tree reduction of the per-step affine maps;
+  * a closed form: one-hot keys turn every state row into a scalar EMA;
+  * contract identities from the ONNX card and the FlashInfer page (ragged ==
+    separate calls, cu_seqlens clamping, empty-request copy, GVA == explicit
+    head repeat, split/resume, decode == prefill, Householder sub-steps ==
+    expanded tokens, slot skip / scatter / disable rules);
+  * library routines for the gate (torch softplus with threshold 20, sigmoid).
+A plausible slip in the oracle (dropped term, wrong sign, transposed operand,
+wrong head map, readout before the update, decay applied per sub-step) fails
+at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+def _bsd_to_tokens(x):
+    """(B, S, D) -> (B*S, 1, D): one head, requests packed back to back."""
+    x = np.asarray(x, dtype=np.float64)
+    return x.reshape(x.shape[0] * x.shape[1], 1, x.shape[2])
+
+
+# ----------------------------------------------------------------------------
+# worked examples ("Gated DeltaNet State Update", Examples)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("idx", [0, 1, 2])
+def test_worked_examples(idx):
+    ex = json.load(open(GOLDEN))["examples"][idx]
+    q = _bsd_to_tokens(ex["q"])
+    k = _bsd_to_tokens(ex["k"])
+    v = _bsd_to_tokens(ex["v"])
+    B, S = len(ex["q"]), len(ex["q"][0])
+    gam = np.asarray(ex["gamma"], dtype=np.float64).reshape(B * S, 1)
+    beta = np.asarray(ex["beta"], dtype=np.float64).reshape(B * S, 1)
+    out, fin = oracle.prefill(q, k, v, gam, beta, decay_is_gamma=True, n_seqs=B, seq_len=S,
+                              scale=1.0)
+    want_out = np.asarray(ex["outputs"], dtype=np.float64)
+    want_fin = np.asarray(ex["final_state"], dtype=np.float64)  # (B, Dk, Dv) K-major
+    np.testing.assert_array_equal(out.reshape(want_out.shape), want_out)
+    # oracle final state is V-major (B, H, Dv, Dk)
+    np.testing.assert_array_equal(fin[:, 0].transpose(0, 2, 1), want_fin)
+
+
+# ----------------------------------------------------------------------------
+# brute force with explicit per-step matrices
+# ----------------------------------------------------------------------------
+
+def _bruteforce(q, k, v, gam, beta, S0, scale):
+    """S_t = M_t S_{t-1} + beta_t k_t v_t^T with M_t = gamma_t (I - beta_t k_t k_t^T),
+    y_t = scale * q_t^T S_t; single head, K-major state."""
+    dk = q.shape[1]
+    S = S0.copy()
+    ys = []
+    I = np.eye(dk)
+    for t in range(q.shape[0]):
+        M = gam[t] * (I - beta[t] * np.outer(k[t], k[t]))
+        S = M @ S + beta[t] * np.outer(k[t], v[t])
+        ys.append(scale * (q[t] @ S))
+    return np.array(ys), S
+
+
+def _affine_tree(k, v, gam, beta, S0):
+    """Final state via a balanced tree reduction of the affine maps S -> M S + B."""
+    dk = k.shape[1]
+    maps = [(gam[t] * (np.eye(dk) - beta[t] * np.outer(k[t], k[t])), beta[t] * np.outer(k[t], v[t]))
+            for t in range(k.shape[0])]
+    while len(maps) > 1:
+        nxt = []
+        for i in range(0, len(maps) - 1, 2):
+            (M1, B1), (M2, B2) = maps[i], maps[i + 1]  # apply 1, then 2
+            nxt.append((M2 @ M1, M2 @ B1 + B2))
+        if len(maps) % 2:
+            nxt.append(maps[-1])
+        maps = nxt
+    M, Bm = maps[0]
+    return M @ S0 + Bm
+
+
+@pytest.mark.parametrize("seed,dk,dv,S", [(0, 2, 3, 5), (1, 4, 4, 17), (2, 8, 5, 32), (3, 7, 8, 9)])
+def test_bruteforce_explicit_matrices(seed, dk, dv, S):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((S, dk))
+    k = rng.standard_normal((S, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.standard_normal((S, dv))
+    gam = rng.uniform(0.0, 1.0, S)
+    beta = rng.uniform(0.0, 1.0, S)
+    S0 = rng.standard_normal((dk, dv))
+    scale = 0.7
+    y_bf, S_bf = _bruteforce(q, k, v, gam, beta, S0, scale)
+    out, fin = oracle.prefill(q[:, None], k[:, None], v[:, None], gam[:, None], beta[:, None],
+                              decay_is_gamma=True, n_seqs=1, seq_len=S,
+                              initial_state=S0.T[None, None], scale=scale)
+    np.testing.assert_allclose(out[:, 0], y_bf, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(fin[0, 0].T, S_bf, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(fin[0, 0].T, _affine_tree(k, v, gam, beta, S0), rtol=1e-11, atol=1e-11)
+
+
+# ----------------------------------------------------------------------------
+# invariants
+# ----------------------------------------------------------------------------
+
+def test_beta0_gamma1_leaves_state_unchanged():
+    rng = np.random.default_rng(5)
+    dk, dv, S = 6, 5, 11
+    q = rng.standard_normal((S, 1, dk))
+    k = rng.standard_normal((S, 1, dk))
+    v = rng.standard_normal((S, 1, dv))
+    S0 = rng.standard_normal((1, 1, dv, dk))
+    out, fin = oracle.prefill(q, k, v, np.ones((S, 1)), np.zeros((S, 1)), decay_is_gamma=True,
+                              n_seqs=1, seq_len=S, initial_state=S0, scale=2.0)
+    np.testing.assert_array_equal(fin, S0)
+    np.testing.assert_allclose(out[:, 0], 2.0 * q[:, 0] @ S0[0, 0].T, rtol=1e-13)
+
+
+def test_gamma0_gives_rank_one_state():
+    rng = np.random.default_rng(6)
+    dk, dv, S = 5, 7, 9
+    q = rng.standard_normal((S, 1, dk))
+    k = rng.standard_normal((S, 1, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((S, 1, dv))
+    gam = rng.uniform(0.2, 1.0, (S, 1))
+    gam[-1] = 0.0
+    beta = rng.uniform(0.0, 1.0, (S, 1))
+    S0 = rng.standard_normal((1, 1, dv, dk))
+    _, fin = oracle.prefill(q, k, v, gam, beta, decay_is_gamma=True, n_seqs=1, seq_len=S,
+                            initial_state=S0)
+    want = beta[-1, 0] * np.outer(k[-1, 0], v[-1, 0])  # K-major
+    np.testing.assert_allclose(fin[0, 0].T, want, rtol=1e-14, atol=1e-15)
+    # the same reset through the log-space input (log 0 = -inf)
+    with np.errstate(divide="ignore"):
+        logd = np.log(gam)
+    _, fin2 = oracle.prefill(q, k, v, logd, beta, n_seqs=1, seq_len=S, initial_state=S0)
+    np.testing.assert_array_equal(fin2, fin)
+
+
+def test_unit_key_beta1_overwrites_its_direction():
+    rng = np.random.default_rng(7)
+    dk, dv = 8, 6
+    S0 = rng.standard_normal((dk, dv))
+    k = rng.standard_normal(dk)
+    k /= np.linalg.norm(k)
+    v = rng.standard_normal(dv)
+    g = 0.6
+    out, fin = oracle.prefill(np.zeros((1, 1, dk)), k[None, None], v[None, None],
+                              np.array([[g]]), np.array([[1.0]]), decay_is_gamma=True,
+                              n_seqs=1, seq_len=1, initial_state=S0.T[None, None])
+    S1 = fin[0, 0].T
+    np.testing.assert_allclose(S1.T @ k, v, rtol=1e-13, atol=1e-13)  # retrieves exactly v
+    P = np.eye(dk) - np.outer(k, k)
+    np.testing.assert_allclose(P @ S1, g * (P @ S0), rtol=1e-13, atol=1e-13)  # rest only decays
+
+
+def test_linear_in_values_and_initial_state():
+    rng = np.random.default_rng(8)
+    T, dk, dv = 40, 6, 5
+    q = rng.standard_normal((T, 1, dk))
+    k = rng.standard_normal((T, 1, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    gam = rng.uniform(0.5, 1.0, (T, 1))
+    beta = rng.uniform(0.0, 1.0, (T, 1))
+    v1, v2 = rng.standard_normal((2, T, 1, dv))
+    s1, s2 = rng.standard_normal((2, 1, 1, dv, dk))
+    a, b = 1.7, -0.4
+    run = lambda v, s: oracle.prefill(q, k, v, gam, beta, decay_is_gamma=True, n_seqs=1,
+                                      seq_len=T, initial_state=s)
+    o1, f1 = run(v1, s1)
+    o2, f2 = run(v2, s2)
+    o3, f3 = run(a * v1 + b * v2, a * s1 + b * s2)
+    np.testing.assert_allclose(o3, a * o1 + b * o2, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(f3, a * f1 + b * f2, rtol=1e-11, atol=1e-11)
+
+
+def test_onehot_keys_closed_form():
+    """k_t = e_{i_t}: row i_t follows S <- gamma (1 - beta) S + beta v, every
+    other row S <- gamma S; outputs read row i of the state through q."""
+    rng = np.random.default_rng(9)
+    T, dk, dv = 300, 32, 24
+    idx = rng.integers(0, dk, T)
+    k = np.zeros((T, 1, dk))
+    k[np.arange(T), 0, idx] = 1.0
+    q = rng.standard_normal((T, 1, dk))
+    v = rng.standard_normal((T, 1, dv))
+    gam = rng.uniform(0.8, 1.0, (T, 1))
+    beta = rng.uniform(0.0, 1.0, (T, 1))
+    S0 = rng.standard_normal((dk, dv))
+    out, fin = oracle.prefill(q, k, v, gam, beta, decay_is_gamma=True, n_seqs=1, seq_len=T,
+                              initial_state=S0.T[None, None], scale=0.5)
+    S = S0.copy()
+    for t in range(T):
+        i = idx[t]
+        S *= gam[t, 0]                                              # every row decays
+        S[i] = (1.0 - beta[t, 0]) * S[i] + beta[t, 0] * v[t, 0]     # addressed row: EMA
+        np.testing.assert_allclose(out[t, 0], 0.5 * q[t, 0] @ S, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(fin[0, 0].T, S, rtol=1e-10, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# contract identities: ragged / empty / clamped / GVA / split-resume
+# ----------------------------------------------------------------------------
+
+def _small(seed, lengths, hq=2, hv=4, dk=8, dv=6, init=True, gate="gamma"):
+    return synth.prefill_inputs(seed, lengths=lengths, hq=hq, hv=hv, dk=dk, dv=dv,
+                                dtype="f32", gate=gate, gamma_range=(0.5, 1.0),
+                                init_std=0.3 if init else None)
+
+
+def _run(x, **kw):
+    dec = x.get("gamma", x.get("log_decay"))
+    args = dict(decay_is_gamma="gamma" in x, cu_seqlens=x["cu_seqlens"],
+                initial_state=x["initial_state"], scale=x["scale"])
+    args.update(kw)
+    return oracle.prefill(x["q"], x["k"], x["v"], dec, x["beta"], **args)
+
+
+def test_ragged_equals_separate_requests():
+    lengths = [5, 0, 13, 1, 9]
+    x = _small(11, lengths)
+    out, fin = _run(x)
+    cu = x["cu_seqlens"].tolist()
+    for r, L in enumerate(lengths):
+        s, e = cu[r], cu[r + 1]
+        dec = x["gamma"][s:e]
+        o_r, f_r = oracle.prefill(x["q"][s:e], x["k"][s:e], x["v"][s:e], dec, x["beta"][s:e],
+                                  decay_is_gamma=True, n_seqs=1, seq_len=L,
+                                  initial_state=x["initial_state"][r:r + 1], scale=x["scale"])
+        np.testing.assert_array_equal(out[s:e], o_r)
+        np.testing.assert_array_equal(fin[r], f_r[0])
+    # the empty request copies its incoming state bit for bit
+    np.testing.assert_array_equal(fin[1], x["initial_state"][1].double().numpy())
+
+
+def test_empty_request_without_initial_state_is_zero():
+    x = _small(12, [4, 0, 3], init=False)
+    _, fin = _run(x)
+    assert np.all(fin[1] == 0.0)
+
+
+def test_cu_seqlens_clamped_and_decreasing():
+    x = _small(13, [6, 6, 6])
+    T = x["T"]
+    cu = torch.tensor([0, 6, 3, T + 50], dtype=torch.int32)  # decreasing, then past the end
+    out, fin = _run(x, cu_seqlens=cu)
+    # request 1 is [6, 3) -> empty: copies its state
+    np.testing.assert_array_equal(fin[1], x["initial_state"][1].double().numpy())
+    # request 2 is clamped to [3, T)
+    ref_o, ref_f = oracle.prefill(x["q"][3:], x["k"][3:], x["v"][3:], x["gamma"][3:],
+                                  x["beta"][3:], decay_is_gamma=True, n_seqs=1, seq_len=T - 3,
+                                  initial_state=x["initial_state"][2:3], scale=x["scale"])
+    np.testing.assert_array_equal(fin[2], ref_f[0])
+    np.testing.assert_array_equal(out[3:], ref_o)
+
+
+def test_gva_equals_explicit_head_repeat():
+    x = _small(14, [7, 12], hq=2, hv=6)
+    out, fin = _run(x)
+    rep = 6 // 2
+    q = x["q"].repeat_interleave(rep, dim=1)
+    k = x["k"].repeat_interleave(rep, dim=1)
+    out2, fin2 = oracle.prefill(q, k, x["v"], x["gamma"], x["beta"], decay_is_gamma=True,
+                                cu_seqlens=x["cu_seqlens"], initial_state=x["initial_state"],
+                                scale=x["scale"])
+    np.testing.assert_array_equal(out, out2)
+    np.testing.assert_array_equal(fin, fin2)
+    # and value head h really reads q/k head h*hq/hv: swapping the q/k heads changes heads 0..2 only
+    q_sw = x["q"].flip(1)
+    out3, _ = oracle.prefill(q_sw, x["k"], x["v"], x["gamma"], x["beta"], decay_is_gamma=True,
+                             cu_seqlens=x["cu_seqlens"], initial_state=x["initial_state"],
+                             scale=x["scale"])
+    assert not np.allclose(out3[:, 0], out[:, 0])
+
+
+def test_split_resume():
+    x = _small(15, [40], hq=1, hv=2)
+    out, fin = _run(x)
+    n = 17
+    o1, f1 = oracle.prefill(x["q"][:n], x["k"][:n], x["v"][:n], x["gamma"][:n], x["beta"][:n],
+                            decay_is_gamma=True, n_seqs=1, seq_len=n,
+                            initial_state=x["initial_state"], scale=x["scale"])
+    o2, f2 = oracle.prefill(x["q"][n:], x["k"][n:], x["v"][n:], x["gamma"][n:], x["beta"][n:],
+                            decay_is_gamma=True, n_seqs=1, seq_len=40 - n, initial_state=f1,
+                            scale=x["scale"])
+    np.testing.assert_allclose(np.concatenate([o1, o2]), out, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(f2, fin, rtol=1e-12, atol=1e-13)
+
+
+def test_log_and_gamma_inputs_agree():
+    x = _small(16, [9, 4])
+    out, fin = _run(x)
+    out2, fin2 = oracle.prefill(x["q"], x["k"], x["v"], torch.log(x["gamma"].double()), x["beta"],
+                                cu_seqlens=x["cu_seqlens"], initial_state=x["initial_state"],
+                                scale=x["scale"])
+    np.testing.assert_allclose(out2, out, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(fin2, fin, rtol=1e-13, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# gate vs library routines
+# ----------------------------------------------------------------------------
+
+def test_gate_against_torch_routines():
+    rng = np.random.default_rng(17)
+    hv = 5
+    A_log = rng.uniform(-2.0, 3.0, hv)
+    dt_bias = rng.normal(0.0, 0.5, hv)
+    a = np.concatenate([rng.normal(0.0, 4.0, (40, hv)),
+                        np.array([[20.0, 20.0 + 1e-9, 19.999, 25.0, -30.0]]) - dt_bias])
+    b = rng.normal(0.0, 3.0, (41, hv))
+    g, gam, beta = oracle.gate(A_log, dt_bias, a, b)
+    x = torch.tensor(a + dt_bias, dtype=torch.float64)
+    sp = torch.nn.functional.softplus(x, beta=1.0, threshold=20.0).numpy()
+    want_g = -np.exp(A_log) * sp
+    np.testing.assert_allclose(g, want_g, rtol=1e-14, atol=0)
+    np.testing.assert_allclose(gam, np.exp(want_g), rtol=1e-14, atol=0)
+    np.testing.assert_allclose(beta, torch.sigmoid(torch.tensor(b)).numpy(), rtol=1e-15, atol=0)
+
+
+def test_gate_special_values():
+    g, gam, beta = oracle.gate([-math.inf, 0.0], [0.0, 0.0], [[3.0, 0.0]], [[0.0, 0.0]])
+    assert gam[0, 0] == 1.0                       # A_log = -inf: no decay
+    assert g[0, 1] == -math.log(2.0)              # softplus(0) = ln 2
+    assert beta[0, 0] == 0.5                      # sigmoid(0)
+    # threshold: identity strictly above 20, log1p(exp(x)) at and below
+    g2, _, _ = oracle.gate([0.0], [0.0], [[20.5], [20.0]], None)
+    assert g2[0, 0] == -20.5
+    assert g2[1, 0] == -math.log1p(math.exp(20.0))
+
+
+# ----------------------------------------------------------------------------
+# decode identities
+# ----------------------------------------------------------------------------
+
+def _dec(seed, **kw):
+    args = dict(pool_size=12, batch=3, T=3, n_hh=1, hq=2, hv=4, dk=8, dv=6, dtype="f32")
+    args.update(kw)
+    return synth.decode_inputs(seed, **args)
+
+
+def _run_dec(x, **kw):
+    args = dict(write_idx=x["write_idx"], scatter_idx=x["scatter_idx"], scale=x["scale"])
+    args.update(kw)
+    return oracle.decode(x["q"], x["k"], x["v"], x["A_log"], x["dt_bias"], x["a"], x["b"],
+                         x["pool"], x["read_idx"], **args)
+
+
+def test_decode_equals_prefill_with_slot_state():
+    x = _dec(21, T=5)
+    out, pool = _run_dec(x)
+    g, _, beta = oracle.gate(x["A_log"], x["dt_bias"], x["a"], x["b"][:, :, 0])
+    for b in range(x["batch"]):
+        rd, wr = int(x["read_idx"][b]), int(x["write_idx"][b])
+        o, f = oracle.prefill(x["q"][b], x["k"][b, :, 0], x["v"][b, :, 0], g[b], beta[b],
+                              n_seqs=1, seq_len=x["T"], initial_state=x["pool"][rd:rd + 1],
+                              scale=x["scale"])
+        np.testing.assert_allclose(out[b], o, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(pool[wr], f[0], rtol=1e-12, atol=1e-13)
+
+
+def test_householder_substeps_equal_expanded_tokens():
+    """n sub-steps per token == gated delta over T*n tokens whose decay is the
+    token's gamma on its first sub-step and 1 on the others, read out on the
+    last sub-step."""
+    x = _dec(22, T=3, n_hh=3)
+    out, pool = _run_dec(x)
+    T, n = x["T"], x["n_hh"]
+    g, _, _ = oracle.gate(x["A_log"], x["dt_bias"], x["a"], None)
+    _, _, beta = oracle.gate(x["A_log"], x["dt_bias"], None, x["b"])  # [B,T,n,hv]
+    for b in range(x["batch"]):
+        rd, wr = int(x["read_idx"][b]), int(x["write_idx"][b])
+        kk = x["k"][b].reshape(T * n, x["hq"], x["dk"])
+        vv = x["v"][b].reshape(T * n, x["hv"], x["dv"])
+        qq = x["q"][b].repeat_interleave(n, dim=0)  # same q on every sub-step
+        dec = np.zeros((T, n, x["hv"]))
+        dec[:, 0] = g[b]
+        bb = beta[b].reshape(T * n, x["hv"])
+        o, f = oracle.prefill(qq, kk, vv, dec.reshape(T * n, -1), bb, n_seqs=1, seq_len=T * n,
+                              initial_state=x["pool"][rd:rd + 1], scale=x["scale"])
+        o = o.reshape(T, n, x["hv"], x["dv"])[:, -1]
+        np.testing.assert_allclose(out[b], o, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(pool[wr], f[0], rtol=1e-12, atol=1e-13)
+
+
+def test_decode_skip_write_scatter_disable_rules():
+    x = _dec(23, batch=4, T=2, pool_size=20)
+    pool0 = x["pool"].double().numpy()
+    read = x["read_idx"].clone()
+    write = x["write_idx"].clone()
+    read[1] = -1          # skipped row
+    read[2] = 20          # out of range: skipped as well
+    write[3] = -5         # row 3 computes its output but writes nothing back
+    sentinel = np.full((4, 2, x["hv"], x["dv"]), 7.25)
+    out, pool = oracle.decode(x["q"], x["k"], x["v"], x["A_log"], x["dt_bias"], x["a"], x["b"],
+                              x["pool"], read, write_idx=write, scale=x["scale"], out_init=sentinel)
+    assert np.all(out[1] == 7.25) and np.all(out[2] == 7.25)
+    assert not np.any(out[3] == 7.25) and not np.any(out[0] == 7.25)
+    changed = {int(write[0])}
+    for s in range(20):
+        if s not in changed:
+            np.testing.assert_array_equal(pool[s], pool0[s])
+    assert not np.array_equal(pool[int(write[0])], pool0[int(write[0])])
+    # disable_state_update: outputs identical, pool untouched
+    out_d, pool_d = oracle.decode(x["q"], x["k"], x["v"], x["A_log"], x["dt_bias"], x["a"],
+                                  x["b"], x["pool"], read, write_idx=write, scale=x["scale"],
+                                  out_init=sentinel, disable_state_update=True)
+    np.testing.assert_array_equal(out_d, out)
+    np.testing.assert_array_equal(pool_d, pool0)
+    # scatter: state after each token to its slot, negative entries skipped, no end writeback
+    sc = torch.tensor([[10, 11], [12, 13], [14, 15], [-1, 16]], dtype=torch.int32)
+    out_s, pool_s = oracle.decode(x["q"], x["k"], x["v"], x["A_log"], x["dt_bias"], x["a"],
+                                  x["b"], x["pool"], read, write_idx=write, scatter_idx=sc,
+                                  scale=x["scale"], out_init=sentinel)
+    np.testing.assert_array_equal(out_s, out)
+    np.testing.assert_array_equal(pool_s[11], pool[int(write[0])])  # last token of row 0
+    for s in (12, 13, 14, 15):  # rows 1 and 2 are skipped entirely
+        np.testing.assert_array_equal(pool_s[s], pool0[s])
+    np.testing.assert_array_equal(pool_s[int(write[0])], pool0[int(write[0])])
+    with pytest.raises(ValueError):
+        oracle.decode(x["q"], x["k"], x["v"], x["A_log"], x["dt_bias"], x["a"], x["b"], x["pool"],
+                      read, scatter_idx=sc, disable_state_update=True)
+
+
+def test_decode_scatter_first_token_equals_one_token_call():
+    x = _dec(24, batch=2, T=2, pool_size=10, write_slots=False, scatter=True)
+    out, pool = _run_dec(x)
+    x1 = dict(x)
+    for key in ("q", "k", "v", "a", "b"):
+        x1[key] = x[key][:, :1]
+    sc1 = x["scatter_idx"][:, :1]
+    out1, pool1 = oracle.decode(x1["q"], x1["k"], x1["v"], x["A_log"], x["dt_bias"], x1["a"],
+                                x1["b"], x["pool"], x["read_idx"], scatter_idx=sc1,
+                                scale=x["scale"])
+    np.testing.assert_array_equal(out[:, 0], out1[:, 0])
+    for b in range(2):
+        s = int(sc1[b, 0])
+        np.testing.assert_array_equal(pool[s], pool1[s])
