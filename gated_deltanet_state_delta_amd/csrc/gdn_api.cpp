@@ -1,0 +1,141 @@
+// gdn_api.cpp -- the C ABI of libgdn: argument validation and dispatch.
+//
+// Everything checked here is host-visible metadata (pointers, sizes, strides,
+// dtypes).  No device memory is read and nothing is synchronised, so every
+// entry point can be captured in a HIP graph.  Data-dependent conditions
+// (cu_seqlens contents, slot indices) are handled on the device as the pages
+// prescribe: clamping and skipping, never faulting.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/libgdn.h"
+#include "gdn_kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gdn_status fail(gdn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+gdn_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return GDN_OK;
+  return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool head_size_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+size_t elem_size(int32_t dt) { return dt == GDN_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_last_error(void) { return g_err; }
+
+const char* gdn_version(void) { return "0.1.0"; }
+
+gdn_status gdn_gate(const float* A_log, const float* dt_bias, const void* a, const void* b,
+                    int32_t ab_dtype, int64_t n_tokens, int32_t hv, float* log_decay_out,
+                    float* gamma_out, float* beta_out, void* stream) {
+  g_err[0] = 0;
+  if (ab_dtype != GDN_F32 && ab_dtype != GDN_BF16) return fail(GDN_ERR_DTYPE, "gdn_gate: ab_dtype %d", ab_dtype);
+  if (n_tokens < 0 || hv <= 0) return fail(GDN_ERR_SHAPE, "gdn_gate: n_tokens=%lld hv=%d", (long long)n_tokens, hv);
+  if ((log_decay_out || gamma_out) && !a) return fail(GDN_ERR_NULL, "gdn_gate: decay output requested without a");
+  if (beta_out && !b) return fail(GDN_ERR_NULL, "gdn_gate: beta output requested without b");
+  if (a && (!A_log || !dt_bias)) return fail(GDN_ERR_NULL, "gdn_gate: a given without A_log / dt_bias");
+  if (n_tokens == 0) return GDN_OK;
+  // an input whose outputs are all absent is ignored
+  const void* ua = (log_decay_out || gamma_out) ? a : nullptr;
+  const void* ub = beta_out ? b : nullptr;
+  if (!ua && !ub) return GDN_OK;
+  return from_hip(gdn::launch_gate(A_log, dt_bias, ua, ub, ab_dtype, n_tokens, hv, log_decay_out,
+                                   gamma_out, beta_out, (hipStream_t)stream),
+                  "gdn_gate launch");
+}
+
+gdn_status gdn_prefill(const gdn_prefill_args* p, void* stream) {
+  g_err[0] = 0;
+  if (!p) return fail(GDN_ERR_NULL, "gdn_prefill: args is NULL");
+  const gdn_prefill_args& a = *p;
+  if (a.io_dtype != GDN_F32 && a.io_dtype != GDN_BF16) return fail(GDN_ERR_DTYPE, "gdn_prefill: io_dtype %d", a.io_dtype);
+  if (a.decay_kind != GDN_DECAY_LOG && a.decay_kind != GDN_DECAY_GAMMA)
+    return fail(GDN_ERR_DTYPE, "gdn_prefill: decay_kind %d", a.decay_kind);
+  if (a.n_seqs < 0 || a.total_tokens < 0 || a.hq <= 0 || a.hv <= 0 || a.dk <= 0 || a.dv <= 0)
+    return fail(GDN_ERR_SHAPE, "gdn_prefill: bad sizes n_seqs=%d T=%lld hq=%d hv=%d dk=%d dv=%d", a.n_seqs,
+                (long long)a.total_tokens, a.hq, a.hv, a.dk, a.dv);
+  if (a.hv % a.hq != 0) return fail(GDN_ERR_SHAPE, "gdn_prefill: hv=%d is not a multiple of hq=%d", a.hv, a.hq);
+  if (!head_size_ok(a.dk) || !head_size_ok(a.dv))
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill: dk=%d dv=%d (supported: 16, 32, 64, 128)", a.dk, a.dv);
+  if (a.chunk_size != 0 && a.chunk_size != 16 && a.chunk_size != 32 && a.chunk_size != 64)
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill: chunk_size=%d (supported: 0, 16, 32, 64)", a.chunk_size);
+  if (!a.cu_seqlens && (a.seq_len < 0 || (int64_t)a.n_seqs * a.seq_len != a.total_tokens))
+    return fail(GDN_ERR_SHAPE, "gdn_prefill: without cu_seqlens n_seqs*seq_len (%d*%d) must equal total_tokens %lld",
+                a.n_seqs, a.seq_len, (long long)a.total_tokens);
+  if (a.n_seqs == 0) return GDN_OK;
+  if (!a.final_state) return fail(GDN_ERR_NULL, "gdn_prefill: final_state is NULL");
+  if (a.total_tokens > 0 && (!a.q || !a.k || !a.v || !a.out || !a.decay || !a.beta))
+    return fail(GDN_ERR_NULL, "gdn_prefill: q, k, v, out, decay and beta are required");
+  const void* ptrs[] = {a.q, a.k, a.v, a.out, a.decay, a.beta, a.initial_state, a.final_state, a.cu_seqlens};
+  for (const void* q : ptrs)
+    if (q && !aligned(q, 16)) return fail(GDN_ERR_LAYOUT, "gdn_prefill: pointers must be 16-byte aligned");
+  const int64_t strides[] = {a.q_stride_token, a.q_stride_head, a.k_stride_token, a.k_stride_head,
+                             a.v_stride_token, a.v_stride_head, a.out_stride_token, a.out_stride_head};
+  for (int64_t s : strides)
+    if (s < 0 || s % 8 != 0) return fail(GDN_ERR_LAYOUT, "gdn_prefill: strides must be non-negative multiples of 8 elements");
+  if (a.total_tokens > 0) {
+    if (a.q_stride_head < a.dk || a.k_stride_head < a.dk || a.v_stride_head < a.dv || a.out_stride_head < a.dv ||
+        a.q_stride_token < (int64_t)a.hq * a.dk || a.k_stride_token < (int64_t)a.hq * a.dk ||
+        a.v_stride_token < (int64_t)a.hv * a.dv || a.out_stride_token < (int64_t)a.hv * a.dv)
+      return fail(GDN_ERR_LAYOUT, "gdn_prefill: strides smaller than the dense extents");
+  }
+  if (a.initial_state && a.initial_state != a.final_state) {
+    const char* i0 = (const char*)a.initial_state;
+    const char* f0 = (const char*)a.final_state;
+    const size_t bytes = (size_t)a.n_seqs * a.hv * a.dv * a.dk * sizeof(float);
+    if (i0 < f0 + bytes && f0 < i0 + bytes)
+      return fail(GDN_ERR_LAYOUT, "gdn_prefill: initial_state and final_state partially overlap");
+  }
+  return from_hip(gdn::launch_prefill(a, (hipStream_t)stream), "gdn_prefill launch");
+}
+
+gdn_status gdn_decode(const gdn_decode_args* p, void* stream) {
+  g_err[0] = 0;
+  if (!p) return fail(GDN_ERR_NULL, "gdn_decode: args is NULL");
+  const gdn_decode_args& a = *p;
+  if (a.io_dtype != GDN_F32 && a.io_dtype != GDN_BF16) return fail(GDN_ERR_DTYPE, "gdn_decode: io_dtype %d", a.io_dtype);
+  if (a.batch < 0 || a.T <= 0 || a.hq <= 0 || a.hv <= 0 || a.dk <= 0 || a.dv <= 0 || a.pool_size < 0)
+    return fail(GDN_ERR_SHAPE, "gdn_decode: bad sizes batch=%d T=%d hq=%d hv=%d dk=%d dv=%d pool_size=%d", a.batch,
+                a.T, a.hq, a.hv, a.dk, a.dv, a.pool_size);
+  if (a.T > 64) return fail(GDN_ERR_UNSUPPORTED, "gdn_decode: T=%d (supported 1..64)", a.T);
+  if (a.n_householder < 1 || a.n_householder > 4)
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_decode: n_householder=%d (supported 1..4)", a.n_householder);
+  if (a.hv % a.hq != 0) return fail(GDN_ERR_SHAPE, "gdn_decode: hv=%d is not a multiple of hq=%d", a.hv, a.hq);
+  if (!head_size_ok(a.dk) || !head_size_ok(a.dv))
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_decode: dk=%d dv=%d (supported: 16, 32, 64, 128)", a.dk, a.dv);
+  if (a.scatter_idx && a.disable_state_update)
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_decode: scatter_idx requires disable_state_update == 0");
+  if (a.batch == 0) return GDN_OK;
+  if (!a.q || !a.k || !a.v || !a.A_log || !a.dt_bias || !a.a || !a.b || !a.pool || !a.read_idx || !a.out)
+    return fail(GDN_ERR_NULL, "gdn_decode: q, k, v, A_log, dt_bias, a, b, pool, read_idx and out are required");
+  if (!aligned(a.pool, 16) || a.pool_slot_stride % 4 != 0 || a.pool_head_stride % 4 != 0 ||
+      a.pool_slot_stride < 0 || a.pool_head_stride < 0)
+    return fail(GDN_ERR_LAYOUT, "gdn_decode: pool must be 16-byte aligned with strides multiple of 4 elements");
+  if (a.pool_head_stride < (int64_t)a.dv * a.dk || a.pool_slot_stride < (int64_t)(a.hv - 1) * a.pool_head_stride + (int64_t)a.dv * a.dk)
+    return fail(GDN_ERR_LAYOUT, "gdn_decode: pool strides smaller than the dense extents");
+  const size_t es = elem_size(a.io_dtype);
+  const void* act[] = {a.q, a.k, a.v, a.out};
+  for (const void* q : act)
+    if (!aligned(q, es == 2 ? 8 : 16)) return fail(GDN_ERR_LAYOUT, "gdn_decode: q, k, v, out must be aligned to 4 elements");
+  return from_hip(gdn::launch_decode(a, (hipStream_t)stream), "gdn_decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,173 @@
+// gdn_decode.hip -- streaming decode / multi-token verification over a slot pool.
+//
+// Contract: "flashinfer.cake_gdp.cake_gated_delta_product_mtp" (parameters and
+// notes) -- per batch row and value head: read the state from the row's read
+// slot, per token decay it once by the fused gate, apply num_householder
+// delta sub-steps (own k, v, sigmoid beta), read out after the sub-steps,
+// scatter after each token or write back once after the last.
+//
+// Design (HBM-bound): the state of one head is a V-major [DV][DK] fp32 array;
+// every V-row evolves independently (the recurrence only couples a row with
+// itself through k).  A row is held by L = DK/16 lanes, 16 floats per lane
+// in four 16-byte segments, so each wave instruction touches whole 128-byte
+// lines.  The row is read once into VGPRs with non-temporal 16-byte loads,
+// updated in registers for every token and sub-step (dot products reduced
+// across the L lanes with DPP), and written once per required slot with
+// non-temporal 16-byte stores.  One workgroup covers ROWS rows of one
+// (batch row, head); skipped rows exit before touching memory.
+#include "gdn_device.hpp"
+#include "gdn_kernels.hpp"
+
+namespace gdn {
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* A_log;
+  const float* dt_bias;
+  const void* a;
+  const void* b;
+  float* pool;
+  int64_t slot_stride, head_stride;
+  const int32_t* read_idx;
+  const int32_t* write_idx;
+  const int32_t* scatter_idx;
+  void* out;
+  int batch, T, nhh, hq, hv, pool_size, disable;
+  float scale;
+};
+
+template <typename IO, int DK, int DV, int ROWS>
+__global__ void __launch_bounds__(ROWS * (DK / 16))
+decode_kernel(const DecodeParams p) {
+  constexpr int L = DK / 16;          // lanes per V-row
+  constexpr int NRB = DV / ROWS;      // row blocks per head
+  const int blk = blockIdx.x;
+  const int rb = blk % NRB;
+  const int h = (blk / NRB) % p.hv;
+  const int b = blk / (NRB * p.hv);
+  const int tid = threadIdx.x;
+  const int row = rb * ROWS + tid / L;
+  const int o = tid % L;
+
+  const int rd = p.read_idx[b];
+  if (rd < 0 || rd >= p.pool_size) return;  // skipped row: touch nothing
+  const int wr = p.write_idx ? p.write_idx[b] : rd;
+  const int qh = (int)(((int64_t)h * p.hq) / p.hv);
+
+  const IO* __restrict__ q = (const IO*)p.q;
+  const IO* __restrict__ k = (const IO*)p.k;
+  const IO* __restrict__ v = (const IO*)p.v;
+  const IO* __restrict__ ga = (const IO*)p.a;
+  const IO* __restrict__ gb = (const IO*)p.b;
+  IO* __restrict__ out = (IO*)p.out;
+
+  // column of element e of segment i held by this lane: i*4L + 4o + e
+  const int64_t head_off = (int64_t)h * p.head_stride + (int64_t)row * DK + 4 * o;
+  f4 x[4];
+  {
+    const float* src = p.pool + (int64_t)rd * p.slot_stride + head_off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = ld_nt(src + i * 4 * L);
+  }
+  const float A_log = p.A_log[h];
+  const float dt_bias = p.dt_bias[h];
+
+  for (int t = 0; t < p.T; ++t) {
+    const int64_t bt = (int64_t)b * p.T + t;
+    const float gamma = expf(gate_log_decay(A_log, dt_bias, to_f32(ga[bt * p.hv + h])));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] *= gamma;
+    for (int j = 0; j < p.nhh; ++j) {
+      const int64_t btj = bt * p.nhh + j;
+      const IO* kp = k + (btj * p.hq + qh) * DK + 4 * o;
+      f4 kf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kf[i] = load4(kp + i * 4 * L);
+      const float vj = to_f32(v[(btj * p.hv + h) * DV + row]);
+      const float beta = sigmoidf(to_f32(gb[btj * p.hv + h]));
+      float r = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        r += x[i][0] * kf[i][0] + x[i][1] * kf[i][1] + x[i][2] * kf[i][2] + x[i][3] * kf[i][3];
+      r = group_sum<L>(r);
+      const float u = beta * (vj - r);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] += u * kf[i];
+    }
+    const IO* qp = q + (bt * p.hq + qh) * DK + 4 * o;
+    float y = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f4 qf = load4(qp + i * 4 * L);
+      y += x[i][0] * qf[0] + x[i][1] * qf[1] + x[i][2] * qf[2] + x[i][3] * qf[3];
+    }
+    y = group_sum<L>(y);
+    if (o == 0) out[(bt * p.hv + h) * DV + row] = from_f32<IO>(p.scale * y);
+    if (p.scatter_idx) {
+      const int s = p.scatter_idx[bt];
+      if (s >= 0 && s < p.pool_size) {
+        float* dst = p.pool + (int64_t)s * p.slot_stride + head_off;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st_nt(dst + i * 4 * L, x[i]);
+      }
+    }
+  }
+  if (!p.scatter_idx && !p.disable && wr >= 0 && wr < p.pool_size) {
+    float* dst = p.pool + (int64_t)wr * p.slot_stride + head_off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st_nt(dst + i * 4 * L, x[i]);
+  }
+}
+
+template <typename IO, int DK, int DV>
+static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
+  constexpr int L = DK / 16;
+  constexpr int ROWS = (DV * L <= 256) ? DV : 256 / L;  // rows per workgroup
+  constexpr int NRB = DV / ROWS;
+  const int64_t nblk = (int64_t)p.batch * p.hv * NRB;
+  hipLaunchKernelGGL((decode_kernel<IO, DK, DV, ROWS>), dim3((unsigned)nblk), dim3(ROWS * L), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+template <typename IO, int DK>
+static hipError_t dispatch_dv(const DecodeParams& p, int dv, hipStream_t s) {
+  switch (dv) {
+    case 16: return launch_decode_t<IO, DK, 16>(p, s);
+    case 32: return launch_decode_t<IO, DK, 32>(p, s);
+    case 64: return launch_decode_t<IO, DK, 64>(p, s);
+    case 128: return launch_decode_t<IO, DK, 128>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename IO>
+static hipError_t dispatch_dk(const DecodeParams& p, int dk, int dv, hipStream_t s) {
+  switch (dk) {
+    case 16: return dispatch_dv<IO, 16>(p, dv, s);
+    case 32: return dispatch_dv<IO, 32>(p, dv, s);
+    case 64: return dispatch_dv<IO, 64>(p, dv, s);
+    case 128: return dispatch_dv<IO, 128>(p, dv, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const gdn_decode_args& a, hipStream_t stream) {
+  if (a.batch == 0) return hipSuccess;
+  DecodeParams p;
+  p.q = a.q; p.k = a.k; p.v = a.v;
+  p.A_log = a.A_log; p.dt_bias = a.dt_bias;
+  p.a = a.a; p.b = a.b;
+  p.pool = a.pool;
+  p.slot_stride = a.pool_slot_stride; p.head_stride = a.pool_head_stride;
+  p.read_idx = a.read_idx; p.write_idx = a.write_idx; p.scatter_idx = a.scatter_idx;
+  p.out = a.out;
+  p.batch = a.batch; p.T = a.T; p.nhh = a.n_householder; p.hq = a.hq; p.hv = a.hv;
+  p.pool_size = a.pool_size; p.disable = a.disable_state_update; p.scale = a.scale;
+  if (a.io_dtype == GDN_BF16) return dispatch_dk<__bf16>(p, a.dk, a.dv, stream);
+  return dispatch_dk<float>(p, a.dk, a.dv, stream);
+}
+
+}  // namespace gdn

@@ -1,0 +1,138 @@
+// gdn_device.hpp -- device helpers shared by the libgdn kernels (gfx950 only).
+//
+// Scalar conversions, the fused gate, 16-byte global accesses, DPP row
+// reductions and the 16x16 MFMA fragment helpers the prefill kernel is built
+// from.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef unsigned short us4 __attribute__((ext_vector_type(4)));
+
+// ----------------------------------------------------------------- scalars --
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// Input element -> fp32 (bf16 widening is exact).
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+// fp32 -> io element, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// Four consecutive io elements -> f4 (8-byte load for bf16, 16-byte for fp32).
+__device__ __forceinline__ f4 load4(const float* p) { return *reinterpret_cast<const f4*>(p); }
+__device__ __forceinline__ f4 load4(const __bf16* p) {
+  const bf4 v = *reinterpret_cast<const bf4*>(p);
+  return f4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+// ------------------------------------------------------------------- gate --
+// The "qwen" gate of the ONNX GatedDeltaNet card / the fused gate of the
+// FlashInfer decode page: g = -exp(A_log) * softplus(a + dt_bias), softplus
+// being the identity above 20.  Accurate libm forms: the gate is not hot.
+
+__device__ __forceinline__ float softplus20(float x) { return x > 20.0f ? x : log1pf(expf(x)); }
+
+__device__ __forceinline__ float gate_log_decay(float A_log, float dt_bias, float a) {
+  return -expf(A_log) * softplus20(a + dt_bias);
+}
+
+__device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// ------------------------------------------------------- 16-byte accesses --
+// Non-temporal loads/stores for data touched exactly once (state pools).
+
+__device__ __forceinline__ f4 ld_nt(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+}
+__device__ __forceinline__ void st_nt(float* p, f4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p));
+}
+
+// ----------------------------------------------------- DPP row reductions --
+// Sum over aligned groups of L lanes (L in {1, 2, 4, 8, 16}); every lane of
+// the group ends with the group's sum.  quad_perm swaps for 2 and 4,
+// row_half_mirror for 8, row_mirror for 16.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+template <int L>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (L >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  if constexpr (L >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (L >= 8) x += dpp<0x141>(x);  // row_half_mirror
+  if constexpr (L >= 16) x += dpp<0x140>(x); // row_mirror
+  return x;
+}
+
+// ------------------------------------------------------------ MFMA tiles --
+// All products are built from 16x16 output tiles.  A "K16 fragment" of an
+// operand is what one lane holds for 16 contraction indices: lane l
+// (x = l % 16, g = l / 16) holds the 4 values at contraction indices
+// 4g .. 4g+3 for row/column x.  This is exactly how a 16x16 fp32 accumulator
+// is spread (lane (col, g) holds rows 4g .. 4g+3), so an accumulator tile is
+// directly a B fragment for the next product, with the tile's rows as the
+// contraction index.  Because a product sums over the contraction index, any
+// assignment of contraction indices to (lane group, register) gives the same
+// result as long as A and B use the same one; the helpers below rely on that.
+
+// acc += A(16 x 16) * B(16 x 16) for io element type bf16 (1 MFMA) ...
+__device__ __forceinline__ f4 mma_k16(f4 acc, bf4 a, bf4 b) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a),
+                                                   __builtin_bit_cast(s4, b), acc, 0, 0, 0);
+}
+// ... and fp32 (4 MFMAs of K = 4; register s of every lane is one K step).
+__device__ __forceinline__ f4 mma_k16(f4 acc, f4 a, f4 b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+  return acc;
+}
+
+// acc += A(16 x 32) * B(32 x 16): two K16 fragments per operand.  bf16 uses
+// one 16x16x32 MFMA (register halves = the two K16 blocks).
+__device__ __forceinline__ f4 mma_k32(f4 acc, bf4 a0, bf4 a1, bf4 b0, bf4 b1) {
+  const bf8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+  const bf8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mma_k32(f4 acc, f4 a0, f4 a1, f4 b0, f4 b1) {
+  return mma_k16(mma_k16(acc, a0, b0), a1, b1);
+}
+
+// Fragment type for an operand element type.
+template <typename E> struct frag_of;
+template <> struct frag_of<__bf16> { typedef bf4 type; };
+template <> struct frag_of<float> { typedef f4 type; };
+
+// Accumulator (fp32) -> operand fragment.
+__device__ __forceinline__ void cvt_frag(f4 x, bf4& o) {
+  o = bf4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+}
+__device__ __forceinline__ void cvt_frag(f4 x, f4& o) { o = x; }
+
+// Four consecutive operand elements from LDS.
+__device__ __forceinline__ void lds_frag(const __bf16* p, bf4& o) {
+  o = *reinterpret_cast<const bf4*>(p);
+}
+__device__ __forceinline__ void lds_frag(const float* p, f4& o) {
+  o = *reinterpret_cast<const f4*>(p);
+}
+
+}  // namespace gdn

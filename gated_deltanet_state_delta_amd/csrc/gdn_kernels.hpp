@@ -1,0 +1,21 @@
+// gdn_kernels.hpp -- internal launch entry points behind the C ABI.
+//
+// The C ABI (gdn_api.cpp) validates arguments and then calls these; each
+// returns the hipError_t of its launch.  Arguments are already checked.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/libgdn.h"
+
+namespace gdn {
+
+hipError_t launch_gate(const float* A_log, const float* dt_bias, const void* a, const void* b,
+                       int ab_dtype, int64_t n_tokens, int hv, float* log_decay, float* gamma,
+                       float* beta, hipStream_t stream);
+
+hipError_t launch_decode(const gdn_decode_args& args, hipStream_t stream);
+
+hipError_t launch_prefill(const gdn_prefill_args& args, hipStream_t stream);
+
+}  // namespace gdn

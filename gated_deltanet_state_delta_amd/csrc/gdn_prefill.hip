@@ -1,0 +1,33 @@
+// gdn_prefill.hip -- host dispatch of the chunked prefill kernel.
+//
+// Picks the chunk (the ONNX card's chunk_size hint; 0 selects 64 for bf16 and
+// 32 for fp32 operands, the largest chunk whose working set fits the LDS of
+// one workgroup with a full 4-wave slice) and the (dk, dv) instantiation.
+#include "gdn_prefill.hpp"
+
+namespace gdn {
+
+hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream) {
+  PrefillParams p;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.out = a.out;
+  p.q_st = a.q_stride_token; p.q_sh = a.q_stride_head;
+  p.k_st = a.k_stride_token; p.k_sh = a.k_stride_head;
+  p.v_st = a.v_stride_token; p.v_sh = a.v_stride_head;
+  p.o_st = a.out_stride_token; p.o_sh = a.out_stride_head;
+  p.decay = a.decay; p.beta = a.beta; p.cu = a.cu_seqlens;
+  p.init = a.initial_state; p.fin = a.final_state;
+  p.T = a.total_tokens; p.n_seqs = a.n_seqs; p.seq_len = a.seq_len;
+  p.hq = a.hq; p.hv = a.hv; p.dv = a.dv; p.nsplit = 1;
+  p.decay_is_gamma = a.decay_kind == GDN_DECAY_GAMMA;
+  p.scale = a.scale;
+  const bool bf = a.io_dtype == GDN_BF16;
+  const int c = a.chunk_size != 0 ? a.chunk_size : (bf ? 64 : 32);
+  switch (c) {
+    case 16: return bf ? prefill_bf16_c16(p, a.dk, a.dv, stream) : prefill_f32_c16(p, a.dk, a.dv, stream);
+    case 32: return bf ? prefill_bf16_c32(p, a.dk, a.dv, stream) : prefill_f32_c32(p, a.dk, a.dv, stream);
+    case 64: return bf ? prefill_bf16_c64(p, a.dk, a.dv, stream) : prefill_f32_c64(p, a.dk, a.dv, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

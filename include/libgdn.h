@@ -1,0 +1,211 @@
+/*
+ * libgdn.h -- C ABI of the MI355X (gfx950) gated delta rule library.
+ *
+ * The method (statement of "Gated DeltaNet State Update", first display):
+ *     S_t = gamma_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+ *     y_t = scale * q_t^T S_t            (read out after the update)
+ * taken independently per value head; value head h reads query/key head
+ * h * hq / hv ("com.microsoft.GatedDeltaNet", Description).
+ *
+ * Conventions shared by every call
+ *  - All data pointers are DEVICE pointers (hipMalloc / torch CUDA memory) and
+ *    are owned by the caller.  The library never allocates, frees or keeps a
+ *    pointer after a call returns.  Inputs are never written.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *    is enqueued asynchronously; calls read no device memory on the host and
+ *    never synchronise, so every call is hipGraph-capturable.
+ *  - Recurrent states are fp32 and V-major: one head's state is a [dv][dk]
+ *    array, row j holding value index j across all dk keys (the ONNX card's
+ *    (batch, Hv, Dv, Dk) state; the FlashInfer pool's "K-last" layout).
+ *  - Argument errors visible on the host (NULL required pointer, bad sizes,
+ *    unsupported head sizes, misalignment, forbidden combinations) return a
+ *    status other than GDN_OK before anything is enqueued; gdn_last_error()
+ *    then returns a description (thread-local, valid until the next call on
+ *    that thread).  Data-dependent conditions are never errors: out-of-range
+ *    cu_seqlens become empty requests, out-of-range or negative slots mean
+ *    "skip" (see each call).
+ *  - Supported head sizes: dk and dv in {16, 32, 64, 128}.
+ *  - Calls that overlap on one device race only where they write the same
+ *    memory; two rows of one decode call that name the same pool slot (for
+ *    reading by one and writing by another) are undefined behaviour.
+ */
+#ifndef LIBGDN_H
+#define LIBGDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  GDN_ERR_SHAPE = 2,       /* a size is <= 0, inconsistent, or hv % hq != 0        */
+  GDN_ERR_DTYPE = 3,       /* unknown dtype or decay kind                          */
+  GDN_ERR_LAYOUT = 4,      /* misaligned pointer / stride, or a partial overlap    */
+  GDN_ERR_UNSUPPORTED = 5, /* valid request this build does not implement          */
+  GDN_ERR_HIP = 6          /* a HIP launch failed; gdn_last_error() has the text   */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Meaning of the prefill decay input. */
+typedef enum {
+  GDN_DECAY_LOG = 0,   /* log-space decay g, gamma = exp(g); -inf means gamma = 0 */
+  GDN_DECAY_GAMMA = 1  /* gamma itself, in [0, 1]                                 */
+} gdn_decay_kind;
+
+/* Text describing the last non-OK status returned on the calling thread. */
+const char* gdn_last_error(void);
+
+/* Library version as "major.minor.patch". */
+const char* gdn_version(void);
+
+/* ----------------------------------------------------------------------------
+ * gdn_gate -- fused gates, elementwise over n_tokens rows of hv heads.
+ *
+ * Follows the "qwen" gate_activation of "com.microsoft.GatedDeltaNet"
+ * (Attributes) and the fused gate of "flashinfer.cake_gdp.
+ * cake_gated_delta_product_mtp" (description; softplus threshold 20):
+ *     log_decay[i,h] = -exp(A_log[h]) * softplus(a[i,h] + dt_bias[h])
+ *     gamma[i,h]     = exp(log_decay[i,h])
+ *     beta[i,h]      = sigmoid(b[i,h])
+ * with softplus(x) = x for x > 20, log1p(exp(x)) otherwise.  Arithmetic fp32.
+ *
+ *   A_log, dt_bias   [hv] fp32                     (required when a != NULL)
+ *   a, b             [n_tokens, hv] dense, ab_dtype; either may be NULL
+ *   log_decay_out, gamma_out   [n_tokens, hv] fp32, nullable; need a
+ *   beta_out                   [n_tokens, hv] fp32, nullable; needs b
+ * n_tokens == 0 is a no-op.  An output requested without its input is
+ * GDN_ERR_NULL.
+ * ------------------------------------------------------------------------- */
+gdn_status gdn_gate(const float* A_log, const float* dt_bias,
+                    const void* a, const void* b, int32_t ab_dtype,
+                    int64_t n_tokens, int32_t hv,
+                    float* log_decay_out, float* gamma_out, float* beta_out,
+                    void* stream);
+
+/* ----------------------------------------------------------------------------
+ * gdn_prefill -- chunked prefill over packed or ragged requests.
+ *
+ * Contract of "com.microsoft.GatedDeltaNet" (Inputs, Outputs, Attributes) with
+ * update_rule gated_delta, gate_activation none and beta_activation none
+ * (gates come from gdn_gate or the caller), qk_l2_norm 0 (keys arrive
+ * normalised, as "Gated DeltaNet State Update" Constraints require):
+ *  - request r covers tokens [cu_seqlens[r], cu_seqlens[r+1]), both offsets
+ *    clamped to [0, total_tokens]; a decreasing pair is an empty request.
+ *    cu_seqlens == NULL means uniform packing, request r = [r*seq_len,
+ *    (r+1)*seq_len), and then n_seqs * seq_len must equal total_tokens.
+ *  - the state of (request r, value head h) starts from initial_state[r,h]
+ *    (zeros when initial_state == NULL) and ends in final_state[r,h]; an
+ *    empty request copies its incoming state.
+ *  - out[t,h,:] = scale * S_t^T q[t, h*hq/hv] for every token t of a request;
+ *    rows of tokens no request covers are not written.
+ *  - chunk_size is a scheduling hint (0 = 64; accepted 16, 32, 64): it never
+ *    changes which result is computed, only the rounding order.
+ *
+ * Layouts (strides in elements; the last dimension is always dense):
+ *   q, k   [total_tokens, hq, dk] io_dtype, strides {token, head}
+ *   v      [total_tokens, hv, dv] io_dtype, strides {token, head}
+ *   out    [total_tokens, hv, dv] io_dtype, strides {token, head}
+ *   decay  [total_tokens, hv] fp32 dense  (decay_kind says log or gamma)
+ *   beta   [total_tokens, hv] fp32 dense  (already activated)
+ *   cu_seqlens   [n_seqs + 1] int32, or NULL
+ *   initial_state, final_state  [n_seqs, hv, dv, dk] fp32 dense, V-major;
+ *                final_state may be the same buffer as initial_state (each
+ *                state slice is read completely before it is written) but
+ *                must not partially overlap it.
+ * Requirements: pointers 16-byte aligned; head and token strides multiples of
+ * 8 elements; io_dtype in {GDN_F32, GDN_BF16}.  total_tokens == 0 still
+ * writes final_state (copies / zeros).  n_seqs == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t n_seqs;
+  int32_t seq_len;         /* used iff cu_seqlens == NULL                     */
+  int64_t total_tokens;
+  int32_t hq, hv, dk, dv;
+  int32_t io_dtype;        /* gdn_dtype of q, k, v and out                     */
+  int32_t decay_kind;      /* gdn_decay_kind                                   */
+  int32_t chunk_size;      /* 0 = default 64                                   */
+  float scale;             /* applied as given                                 */
+  const void* q;  int64_t q_stride_token, q_stride_head;
+  const void* k;  int64_t k_stride_token, k_stride_head;
+  const void* v;  int64_t v_stride_token, v_stride_head;
+  void* out;      int64_t out_stride_token, out_stride_head;
+  const float* decay;
+  const float* beta;
+  const int32_t* cu_seqlens;
+  const float* initial_state;
+  float* final_state;
+} gdn_prefill_args;
+
+gdn_status gdn_prefill(const gdn_prefill_args* args, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * gdn_decode -- one fused launch over a slot-indexed fp32 state pool.
+ *
+ * Contract of "flashinfer.cake_gdp.cake_gated_delta_product_mtp" (parameters
+ * and notes), generalised to grouped value heads (hv a multiple of hq) and to
+ * dk, dv in {16, 32, 64, 128}; q/k arrive normalised (no in-kernel L2 norm).
+ * For every batch row b and value head h:
+ *  - rd = read_idx[b]; rd < 0 or rd >= pool_size skips the row entirely: no
+ *    pool read, no output store, no write-back, no scatter.
+ *  - S = pool[rd, h].  For each token t: gamma_t from the fused gate (as in
+ *    gdn_gate, on a[b,t,h]); S <- gamma_t S; then for each sub-step
+ *    j < n_householder: beta = sigmoid(b[b,t,j,h]) and
+ *    S <- (I - beta k k^T) S + beta k v^T with k = k[b,t,j,h*hq/hv],
+ *    v = v[b,t,j,h]; then out[b,t,h] = scale * S^T q[b,t,h*hq/hv].
+ *  - scatter_idx != NULL: after every token, S is stored to
+ *    pool[scatter_idx[b,t], h] unless that entry is < 0 or >= pool_size; no
+ *    end-of-row write-back happens.  Requires disable_state_update == 0.
+ *  - otherwise, unless disable_state_update != 0: after the last token S is
+ *    stored to pool[wr, h] with wr = write_idx ? write_idx[b] : rd, unless
+ *    wr < 0 or wr >= pool_size (the output is still stored).
+ *
+ * Layouts (dense, row-major):
+ *   q [batch, T, hq, dk]; k [batch, T, n_householder, hq, dk];
+ *   v [batch, T, n_householder, hv, dv]; a [batch, T, hv];
+ *   b [batch, T, n_householder, hv]  -- all io_dtype
+ *   A_log, dt_bias [hv] fp32
+ *   pool: slot s, head h starts at pool + s*pool_slot_stride +
+ *         h*pool_head_stride and holds a dense [dv][dk] fp32 array
+ *         (padding between heads or slots is allowed)
+ *   read_idx [batch] int32; write_idx [batch] int32 or NULL;
+ *   scatter_idx [batch, T] int32 or NULL
+ *   out [batch, T, hv, dv] io_dtype; rows of skipped batch rows keep their
+ *       previous contents
+ * Requirements: pool pointer 16-byte aligned and both pool strides multiples
+ * of 4 elements; q, k, v, out 8-byte aligned; 1 <= T <= 64;
+ * 1 <= n_householder <= 4; batch == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch, T, n_householder;
+  int32_t hq, hv, dk, dv;
+  int32_t io_dtype;
+  int32_t disable_state_update;
+  float scale;                     /* applied as given (0.0 included)          */
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* A_log;
+  const float* dt_bias;
+  const void* a;
+  const void* b;
+  float* pool;
+  int32_t pool_size;
+  int64_t pool_slot_stride, pool_head_stride;
+  const int32_t* read_idx;
+  const int32_t* write_idx;
+  const int32_t* scatter_idx;
+  void* out;
+} gdn_decode_args;
+
+gdn_status gdn_decode(const gdn_decode_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBGDN_H */

@@ -1,0 +1,151 @@
+"""The C ABI on the host (no GPU needed): exports and host-side validation.
+
+Every symbol include/libgdn.h declares must be exported by libgdn.so, and every
+argument error the header documents must be returned before anything is
+launched -- these calls never reach the device, so they run without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_state_delta_amd._lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libgdn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from gated_deltanet_state_delta_amd import build
+        build.build()
+    return L.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_exported_set(lib):
+    names = declared_functions()
+    assert names == sorted(L.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), "libgdn.so does not export %s" % n
+
+
+def test_version_and_error_text(lib):
+    assert re.match(r"^\d+\.\d+\.\d+$", lib.gdn_version().decode())
+    st = lib.gdn_gate(None, None, None, None, 9, 1, 1, None, None, None, None)
+    assert st == 3  # GDN_ERR_DTYPE
+    assert b"ab_dtype" in lib.gdn_last_error()
+
+
+FAKE = 0x10000  # a 16-byte-aligned address that is never dereferenced on the host
+
+
+def _prefill(**over):
+    a = L.PrefillArgs()
+    a.n_seqs, a.seq_len, a.total_tokens = 2, 8, 16
+    a.hq, a.hv, a.dk, a.dv = 2, 4, 64, 64
+    a.io_dtype, a.decay_kind, a.chunk_size, a.scale = L.GDN_BF16, L.GDN_DECAY_LOG, 0, 0.125
+    a.q, a.q_stride_token, a.q_stride_head = FAKE, 128, 64
+    a.k, a.k_stride_token, a.k_stride_head = FAKE * 2, 128, 64
+    a.v, a.v_stride_token, a.v_stride_head = FAKE * 3, 256, 64
+    a.out, a.out_stride_token, a.out_stride_head = FAKE * 4, 256, 64
+    a.decay, a.beta = FAKE * 5, FAKE * 6
+    a.cu_seqlens = None
+    a.initial_state = None
+    a.final_state = FAKE * 7
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def _decode(**over):
+    d = L.DecodeArgs()
+    d.batch, d.T, d.n_householder = 4, 2, 2
+    d.hq, d.hv, d.dk, d.dv = 2, 4, 128, 64
+    d.io_dtype, d.disable_state_update, d.scale = L.GDN_BF16, 0, 0.1
+    d.q, d.k, d.v, d.A_log, d.dt_bias, d.a, d.b = (FAKE * i for i in range(1, 8))
+    d.pool, d.pool_size, d.pool_slot_stride, d.pool_head_stride = FAKE * 8, 10, 4 * 64 * 128, 64 * 128
+    d.read_idx, d.write_idx, d.scatter_idx, d.out = FAKE * 9, None, None, FAKE * 10
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+PREFILL_ERRORS = [
+    (dict(io_dtype=5), 3),
+    (dict(decay_kind=2), 3),
+    (dict(hq=3), 2),                      # hv % hq != 0
+    (dict(dk=48), 5),
+    (dict(dv=256), 5),
+    (dict(chunk_size=8), 5),
+    (dict(seq_len=7), 2),                 # n_seqs * seq_len != total_tokens
+    (dict(final_state=None), 1),
+    (dict(q=None), 1),
+    (dict(beta=None), 1),
+    (dict(q=FAKE + 8), 4),                # misaligned pointer
+    (dict(v_stride_head=68), 4),          # stride not a multiple of 8
+    (dict(q_stride_token=64), 4),         # token stride smaller than heads * dk
+    (dict(initial_state=FAKE * 7 + 1024), 4),  # partial overlap with final_state
+    (dict(n_seqs=-1), 2),
+]
+
+
+@pytest.mark.parametrize("over,status", PREFILL_ERRORS)
+def test_prefill_rejects(lib, over, status):
+    a = _prefill(**over)
+    assert lib.gdn_prefill(ctypes.byref(a), None) == status
+    assert lib.gdn_last_error()
+
+
+def test_prefill_null_args_and_noop(lib):
+    assert lib.gdn_prefill(None, None) == 1
+    a = _prefill(n_seqs=0, seq_len=0, total_tokens=0)
+    assert lib.gdn_prefill(ctypes.byref(a), None) == 0  # nothing to do, nothing launched
+
+
+DECODE_ERRORS = [
+    (dict(io_dtype=2), 3),
+    (dict(T=0), 2),
+    (dict(T=65), 5),
+    (dict(n_householder=0), 5),
+    (dict(n_householder=5), 5),
+    (dict(hq=3), 2),
+    (dict(dk=96), 5),
+    (dict(scatter_idx=FAKE * 11, disable_state_update=1), 5),
+    (dict(pool=None), 1),
+    (dict(read_idx=None), 1),
+    (dict(pool=FAKE + 4), 4),
+    (dict(pool_head_stride=64 * 128 + 2), 4),
+    (dict(pool_slot_stride=64 * 128), 4),   # slots overlap the heads
+    (dict(q=FAKE + 2), 4),
+    (dict(pool_size=-1), 2),
+]
+
+
+@pytest.mark.parametrize("over,status", DECODE_ERRORS)
+def test_decode_rejects(lib, over, status):
+    d = _decode(**over)
+    assert lib.gdn_decode(ctypes.byref(d), None) == status
+    assert lib.gdn_last_error()
+
+
+def test_decode_null_args_and_noop(lib):
+    assert lib.gdn_decode(None, None) == 1
+    d = _decode(batch=0)
+    assert lib.gdn_decode(ctypes.byref(d), None) == 0
+
+
+def test_gate_rejects(lib):
+    assert lib.gdn_gate(None, None, None, None, 1, -1, 4, None, None, None, None) == 2
+    assert lib.gdn_gate(None, None, None, None, 1, 4, 0, None, None, None, None) == 2
+    assert lib.gdn_gate(None, None, None, FAKE, 1, 4, 4, FAKE, None, None, None) == 1  # decay w/o a
+    assert lib.gdn_gate(None, None, FAKE, None, 1, 4, 4, None, None, FAKE, None) == 1  # beta w/o b
+    assert lib.gdn_gate(None, None, FAKE, None, 1, 4, 4, FAKE, None, None, None) == 1  # a w/o A_log
+    assert lib.gdn_gate(None, None, None, None, 1, 0, 4, None, None, None, None) == 0  # n == 0
