@@ -1,0 +1,233 @@
+"""Benchmark of the gated delta rule hot path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input:
+  gdn_gate + gdn_prefill on the chunked-prefill workload
+      (B=4 x S=4096 packed, Hq=16, Hv=32, Dk=Dv=128, bf16, qwen gates), then
+  gdn_decode on the slot-pool decode workload
+      (pool [1024, 32, 128, 128] fp32, B=256 rows with 26 skipped, T=1, bf16).
+A 1 GiB buffer is written before the prefill and before the decode so that
+neither reads its inputs out of the 256 MB last-level cache.  Kernel times come
+from HIP events recorded on the launch stream; `value` is prefill tokens/s
+(16384 tokens over the gate + prefill time).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--only prefill|decode] [--copy-calib]
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+
+METRIC = "GDN prefill tokens/s (B4×S4096,Hv32,d128) + decode state HBM GB/s % of peak"
+
+
+def prefill_algorithmic(T, hq, hv, dk, dv, n_seqs, chunk, io_bytes=2):
+    """Bytes and flops one prefill launch must move / compute."""
+    per_token_bytes = (hq * dk * io_bytes * 2          # q, k
+                       + hv * dv * io_bytes * 2        # v, out
+                       + hv * 4 * 2)                   # log-decay, beta (fp32)
+    state_bytes = n_seqs * hv * dv * dk * 4            # final state (no initial state)
+    bytes_ = T * per_token_bytes + state_bytes
+    flops_per_token = hq * 4 * chunk * dk + hv * (6 * dk * dv + 4 * chunk * dv)
+    return bytes_, T * flops_per_token
+
+
+def decode_algorithmic(x):
+    """Bytes one decode launch must move: per active (row, head) its state read
+    once and written once per required slot, plus the row's activations."""
+    import torch
+    B, T, n = x["batch"], x["T"], x["n_hh"]
+    hq, hv, dk, dv = x["hq"], x["hv"], x["dk"], x["dv"]
+    active = int(((x["read_idx"] >= 0) & (x["read_idx"] < x["pool_size"])).sum())
+    st = dv * dk * 4
+    if x["scatter_idx"] is not None:
+        sc = x["scatter_idx"][(x["read_idx"] >= 0)]
+        writes = int(((sc >= 0) & (sc < x["pool_size"])).sum()) * hv * st
+    else:
+        wr = x["write_idx"][(x["read_idx"] >= 0)]
+        writes = int(((wr >= 0) & (wr < x["pool_size"])).sum()) * hv * st
+    reads = active * hv * st
+    e = 2 if x["dtype"] == "bf16" else 4
+    act = active * T * (hq * dk + n * hq * dk + n * hv * dv + hv + n * hv + hv * dv) * e
+    return reads + writes + act
+
+
+def cpu_baseline_prefill(x, budget_units=None):
+    """The fp64 oracle on the prefill workload (all of it unless budget_units)."""
+    import oracle
+    import torch
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    g, _, beta = oracle.gate(x["A_log"], x["dt_bias"], x["a"], x["b"])
+    T = x["T"]
+    if budget_units is None:
+        oracle.prefill(x["q"], x["k"], x["v"], g, beta, n_seqs=x["n_seqs"], seq_len=x["seq_len"],
+                       scale=x["scale"], nthreads=threads)
+        tokens = T
+        sample = "whole workload: gate + prefill of all 4 requests x 32 value heads"
+    else:
+        raise NotImplementedError
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_deltanet_state_delta_amd as gdn
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    do_prefill = args.only in (None, "prefill")
+    do_decode = args.only in (None, "decode")
+
+    # ---------------------------------------------------------------- inputs
+    px = synth.chunked_prefill_b4_s4096()
+    B, S = px["n_seqs"], px["seq_len"]
+    q = px["q"].to(dev).view(B, S, px["hq"], px["dk"])
+    k = px["k"].to(dev).view(B, S, px["hq"], px["dk"])
+    v = px["v"].to(dev).view(B, S, px["hv"], px["dv"])
+    A_log, dt_bias = px["A_log"].to(dev), px["dt_bias"].to(dev)
+    a, b = px["a"].to(dev), px["b"].to(dev)
+    out = torch.empty_like(v)
+    fin = torch.empty(B, px["hv"], px["dv"], px["dk"], dtype=torch.float32, device=dev)
+    g_buf = torch.empty(px["T"], px["hv"], dtype=torch.float32, device=dev)
+    b_buf = torch.empty_like(g_buf)
+
+    dx = synth.decode_pool_b256()
+    pool = dx["pool"].to(dev)
+    dq, dk_, dv_ = dx["q"].to(dev), dx["k"].to(dev), dx["v"].to(dev)
+    dA, ddt, da, db = dx["A_log"].to(dev), dx["dt_bias"].to(dev), dx["a"].to(dev), dx["b"].to(dev)
+    rd, wr = dx["read_idx"].to(dev), dx["write_idx"].to(dev)
+    dout = torch.zeros(dx["batch"], 1, dx["hv"], dx["dv"], dtype=torch.bfloat16, device=dev)
+
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    stream = torch.cuda.current_stream()
+
+    def run_gate():
+        gdn.gate(A_log, dt_bias, a, b, log_decay_out=g_buf, beta_out=b_buf)
+
+    def run_prefill():
+        gdn.prefill(q, k, v, g_buf.view(B, S, -1), b_buf.view(B, S, -1), scale=px["scale"],
+                    out=out, final_state=fin)
+
+    def run_decode():
+        gdn.decode(dq, dk_, dv_, dA, ddt, da, db, pool, rd, write_idx=wr, scale=dx["scale"],
+                   out=dout)
+
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    n_ev = args.warmup + args.steps
+    ev = [[E() for _ in range(5)] for _ in range(n_ev)]
+
+    def step(i):
+        e = ev[i]
+        if do_prefill:
+            flush.zero_()
+            e[0].record(stream)
+            run_gate()
+            e[1].record(stream)
+            run_prefill()
+            e[2].record(stream)
+        if do_decode:
+            flush.zero_()
+            e[3].record(stream)
+            run_decode()
+            e[4].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, n_ev):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    if args.copy_calib:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    timed = ev[args.warmup:]
+    res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "chunked_prefill_b4_s4096_hq16_hv32_d128_bf16 + "
+                                  "decode_pool1024_b256_t1_hq16_hv32_d128_bf16",
+                      "prefill_tokens": px["T"], "chunk": 64, "decode_rows": dx["batch"],
+                      "decode_active_rows": int((dx["read_idx"] >= 0).sum()),
+                      "device": props.name, "cus": props.multi_processor_count}}
+
+    if do_prefill:
+        gate_ms = [e[0].elapsed_time(e[1]) for e in timed]
+        pre_ms = [e[1].elapsed_time(e[2]) for e in timed]
+        tot = statistics.mean(g_ + p_ for g_, p_ in zip(gate_ms, pre_ms))
+        pb, pf = prefill_algorithmic(px["T"], px["hq"], px["hv"], px["dk"], px["dv"], B, 64)
+        pm = statistics.mean(pre_ms)
+        res["value"] = px["T"] / (tot * 1e-3)
+        res["unit"] = "tokens/s"
+        gbs = pb / (pm * 1e-3) / 1e9
+        tfl = pf / (pm * 1e-3) / 1e12
+        res["roofline"] = {"kernel": "prefill_kernel<bf16,128,64,64>", "bound": "hbm",
+                           "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                           "algorithmic_bytes": pb, "algorithmic_flops": pf,
+                           "mfma_tflops": tfl, "mfma_peak_tflops": BF16_PEAK_TFLOPS,
+                           "mfma_frac": tfl / BF16_PEAK_TFLOPS, "avg_ms": pm}
+        res["prefill"] = {"gate_ms": statistics.mean(gate_ms), "prefill_ms": pm,
+                          "prefill_ms_min": min(pre_ms), "tokens_per_s": res["value"]}
+    if do_decode:
+        dec_ms = [e[3].elapsed_time(e[4]) for e in timed]
+        dm = statistics.mean(dec_ms)
+        db_ = decode_algorithmic(dx)
+        gbs = db_ / (dm * 1e-3) / 1e9
+        res["decode"] = {"kernel": "decode_kernel<bf16,128,128,32>", "bound": "hbm",
+                         "ms": dm, "ms_min": min(dec_ms), "algorithmic_bytes": db_,
+                         "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS}
+        if not do_prefill:
+            res["value"] = gbs
+            res["unit"] = "GB/s"
+            res["roofline"] = dict(res["decode"], traffic=None)
+
+    if not args.no_cpu_baseline and do_prefill:
+        res["cpu_baseline"] = cpu_baseline_prefill(px)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

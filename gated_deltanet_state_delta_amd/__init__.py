@@ -4,7 +4,8 @@ Three calls with the names of the C ABI (include/libgdn.h).  This layer only
 marshals arguments (device pointers, strides, dtype codes, the current HIP
 stream); every step of the computation runs in libgdn's HIP kernels.  There
 is no other implementation: a missing libgdn.so or a non-GPU tensor is an
-error.
+error.  Every tensor's shape is checked against the call's contract here,
+because the kernels trust the sizes and strides they are given.
 
   gate(A_log, dt_bias, a, b)            -> (log_decay, gamma | None, beta)
   prefill(q, k, v, decay, beta, ...)    -> (out, final_state)
@@ -20,7 +21,8 @@ import torch
 from . import _lib
 from ._lib import GdnError
 
-__all__ = ["gate", "prefill", "decode", "version", "GdnError"]
+__all__ = ["gate", "prefill", "decode", "version", "GdnError",
+           "prefill_args", "decode_args"]
 
 _DT = {torch.float32: _lib.GDN_F32, torch.bfloat16: _lib.GDN_BF16}
 
@@ -50,27 +52,42 @@ def _io_dtype(t):
     return _DT[t.dtype]
 
 
-def _idx32(t):
+def _shape(t, name, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    return t
+
+
+def _idx32(t, name, shape):
     if t is None:
         return None
-    if t.dtype != torch.int32:
-        t = t.to(torch.int32)
-    return t.contiguous()
+    if t.dtype not in (torch.int32, torch.int64):
+        raise ValueError("%s must be int32 or int64" % name)
+    _shape(t, name, shape)
+    return t.to(torch.int32).contiguous()
 
 
-def _last_dense(t, name):
-    """Keep views whose last dim is dense with 8-aligned outer strides, copy others."""
+def _f32c(t, name, shape):
+    _shape(t, name, shape)
+    return t.to(torch.float32).contiguous()
+
+
+def _strided3(t):
+    """A [tokens, heads, dim] view the kernels can read in place: dense last dim,
+    outer strides multiples of 8 elements, 16-byte aligned base; else a copy."""
     if t.stride(-1) != 1 or any(s % 8 for s in t.stride()[:-1]) or t.data_ptr() % 16:
         t = t.contiguous()
     return t
 
 
-def gate(A_log, dt_bias, a=None, b=None, *, want_gamma=False, stream=None):
+def gate(A_log, dt_bias, a=None, b=None, *, want_gamma=False, log_decay_out=None,
+         beta_out=None, stream=None):
     """Fused gates: log_decay = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b).
 
     a, b: [..., hv] float32 or bfloat16 (either may be None).  Returns
     (log_decay, gamma, beta) as float32 tensors shaped like a / b; gamma only
-    when want_gamma.
+    when want_gamma.  log_decay_out / beta_out: optional preallocated
+    contiguous float32 outputs of a's / b's shape.
     """
     lib = _lib.load()
     ref = a if a is not None else b
@@ -80,19 +97,108 @@ def gate(A_log, dt_bias, a=None, b=None, *, want_gamma=False, stream=None):
     dt = _io_dtype(ref)
     a = None if a is None else _dev(a, "a").contiguous()
     b = None if b is None else _dev(b, "b").contiguous()
-    if a is not None and b is not None and a.dtype != b.dtype:
-        raise ValueError("a and b must share a dtype")
-    A_log = None if A_log is None else _dev(A_log, "A_log").float().contiguous()
-    dt_bias = None if dt_bias is None else _dev(dt_bias, "dt_bias").float().contiguous()
+    if a is not None and b is not None:
+        if a.dtype != b.dtype or b.shape[-1] != hv or b.numel() != a.numel():
+            raise ValueError("a and b must share dtype and element count")
+    if a is not None:
+        A_log = _f32c(_dev(A_log, "A_log"), "A_log", (hv,))
+        dt_bias = _f32c(_dev(dt_bias, "dt_bias"), "dt_bias", (hv,))
+    else:
+        A_log = dt_bias = None
     n = ref.numel() // hv
-    if a is not None and b is not None and b.numel() != a.numel():
-        raise ValueError("a and b must have the same number of elements")
-    g = torch.empty(a.shape, dtype=torch.float32, device=a.device) if a is not None else None
+    def _outbuf(t, ref_t, name):
+        if ref_t is None:
+            return None
+        if t is None:
+            return torch.empty(ref_t.shape, dtype=torch.float32, device=ref_t.device)
+        _dev(t, name)
+        if tuple(t.shape) != tuple(ref_t.shape) or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("%s must be contiguous float32 of shape %s" % (name, tuple(ref_t.shape)))
+        return t
+
+    g = _outbuf(log_decay_out, a, "log_decay_out")
     gam = torch.empty_like(g) if (a is not None and want_gamma) else None
-    bet = torch.empty(b.shape, dtype=torch.float32, device=b.device) if b is not None else None
+    bet = _outbuf(beta_out, b, "beta_out")
     _lib.check(lib.gdn_gate(_ptr(A_log), _ptr(dt_bias), _ptr(a), _ptr(b), dt, n, hv, _ptr(g),
                             _ptr(gam), _ptr(bet), _stream(stream)))
     return g, gam, bet
+
+
+def prefill_args(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None,
+                 initial_state=None, scale=None, chunk_size=0, out=None, final_state=None):
+    """Validate shapes and build the gdn_prefill_args struct (device-agnostic).
+
+    Returns (args, keep, out, final_state): `keep` holds every tensor whose
+    pointer is in args (converted copies included), `out` is the caller-shaped
+    output tensor.
+    """
+    batched = q.dim() == 4
+    if batched:
+        B, S = q.shape[0], q.shape[1]
+        if cu_seqlens is not None:
+            raise ValueError("cu_seqlens requires the [T, heads, dim] form")
+        _shape(k, "k", q.shape)
+        if v.dim() != 4 or tuple(v.shape[:2]) != (B, S):
+            raise ValueError("v must be [B, S, hv, dv] like q")
+        q3, k3, v3 = q.reshape(B * S, *q.shape[2:]), k.reshape(B * S, *k.shape[2:]), \
+            v.reshape(B * S, *v.shape[2:])
+    else:
+        if q.dim() != 3 or v.dim() != 3:
+            raise ValueError("q, k, v must be [T, heads, dim] (or [B, S, heads, dim])")
+        q3, k3, v3 = q, k, v
+    T, hq, dk = q3.shape
+    hv, dv = v3.shape[1], v3.shape[2]
+    _shape(k3, "k", (T, hq, dk))
+    _shape(v3, "v", (T, hv, dv))
+    if k3.dtype != q3.dtype or v3.dtype != q3.dtype:
+        raise ValueError("q, k and v must share a dtype")
+    dt = _io_dtype(q3)
+    q3, k3, v3 = _strided3(q3), _strided3(k3), _strided3(v3)
+    decay = _f32c(decay.reshape(-1, hv) if decay.dim() == 3 else decay, "decay", (T, hv))
+    beta = _f32c(beta.reshape(-1, hv) if beta.dim() == 3 else beta, "beta", (T, hv))
+    if cu_seqlens is not None:
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise ValueError("cu_seqlens must be [N + 1]")
+        cu = _idx32(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),))
+        n_seqs, seq_len = cu.numel() - 1, 0
+    else:
+        cu = None
+        n_seqs, seq_len = (B, S) if batched else (1, T)
+    if initial_state is not None:
+        _shape(initial_state, "initial_state", (n_seqs, hv, dv, dk))
+        if initial_state.dtype != torch.float32 or not initial_state.is_contiguous():
+            initial_state = initial_state.to(torch.float32).contiguous()
+    dev = q3.device
+    if out is None:
+        out = torch.empty((B, S, hv, dv) if batched else (T, hv, dv), dtype=q3.dtype, device=dev)
+    if out.dtype != q3.dtype:
+        raise ValueError("out must have q's dtype")
+    _shape(out, "out", (B, S, hv, dv) if (batched and out.dim() == 4) else (T, hv, dv))
+    out3 = out.view(T, hv, dv)  # a view, never a copy: the kernel writes through it
+    if out3.stride(-1) != 1 or any(s % 8 for s in out3.stride()[:-1]) or out3.data_ptr() % 16:
+        raise ValueError("out must have a dense last dim, 8-aligned strides and a 16-byte base")
+    if final_state is None:
+        final_state = torch.empty((n_seqs, hv, dv, dk), dtype=torch.float32, device=dev)
+    _shape(final_state, "final_state", (n_seqs, hv, dv, dk))
+    if final_state.dtype != torch.float32 or not final_state.is_contiguous():
+        raise ValueError("final_state must be contiguous float32")
+    a = _lib.PrefillArgs()
+    a.n_seqs, a.seq_len, a.total_tokens = n_seqs, seq_len, T
+    a.hq, a.hv, a.dk, a.dv = hq, hv, dk, dv
+    a.io_dtype = dt
+    a.decay_kind = _lib.GDN_DECAY_GAMMA if decay_kind == "gamma" else _lib.GDN_DECAY_LOG
+    a.chunk_size = int(chunk_size)
+    a.scale = (1.0 / math.sqrt(dk)) if scale is None else float(scale)
+    a.q, a.q_stride_token, a.q_stride_head = q3.data_ptr(), q3.stride(0), q3.stride(1)
+    a.k, a.k_stride_token, a.k_stride_head = k3.data_ptr(), k3.stride(0), k3.stride(1)
+    a.v, a.v_stride_token, a.v_stride_head = v3.data_ptr(), v3.stride(0), v3.stride(1)
+    a.out, a.out_stride_token, a.out_stride_head = out3.data_ptr(), out3.stride(0), out3.stride(1)
+    a.decay, a.beta = decay.data_ptr(), beta.data_ptr()
+    a.cu_seqlens = None if cu is None else cu.data_ptr()
+    a.initial_state = None if initial_state is None else initial_state.data_ptr()
+    a.final_state = final_state.data_ptr()
+    keep = (q3, k3, v3, decay, beta, cu, initial_state, out3, final_state)
+    return a, keep, out, final_state
 
 
 def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_state=None,
@@ -103,99 +209,55 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
     v: [T, hv, dv] (or [B, S, hv, dv]); decay, beta: [T, hv] float32 (decay is
     log-space for decay_kind="log", gamma for "gamma"); cu_seqlens: [N+1]
     int32/int64 or None; initial_state: [N, hv, dv, dk] float32 or None.
-    scale None means 1/sqrt(dk).  Returns (out [T, hv, dv] in q's dtype,
-    final_state [N, hv, dv, dk] float32).
+    scale None means 1/sqrt(dk).  Returns (out, final_state [N, hv, dv, dk]
+    float32); out is [T, hv, dv] (or [B, S, hv, dv]) in q's dtype.
     """
     lib = _lib.load()
-    for name, t in (("q", q), ("k", k), ("v", v), ("decay", decay), ("beta", beta)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("decay", decay), ("beta", beta),
+                    ("cu_seqlens", cu_seqlens), ("initial_state", initial_state),
+                    ("out", out), ("final_state", final_state)):
         _dev(t, name)
-    batched = q.dim() == 4
-    if batched:
-        B, S = q.shape[0], q.shape[1]
-        if cu_seqlens is not None:
-            raise ValueError("cu_seqlens requires the [T, heads, dim] form")
-        q = q.reshape(B * S, *q.shape[2:])
-        k = k.reshape(B * S, *k.shape[2:])
-        v = v.reshape(B * S, *v.shape[2:])
-        decay = decay.reshape(B * S, -1)
-        beta = beta.reshape(B * S, -1)
-    T, hq, dk = q.shape
-    hv, dv = v.shape[1], v.shape[2]
-    if k.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("k must match q in shape and dtype; v must share q's dtype")
-    dt = _io_dtype(q)
-    q, k, v = _last_dense(q, "q"), _last_dense(k, "k"), _last_dense(v, "v")
-    decay = decay.float().contiguous()
-    beta = beta.float().contiguous()
-    cu = _idx32(_dev(cu_seqlens, "cu_seqlens"))
-    if cu is not None:
-        n_seqs, seq_len = cu.numel() - 1, 0
-    elif batched:
-        n_seqs, seq_len = B, S
-    else:
-        n_seqs, seq_len = 1, T
-    if initial_state is not None:
-        initial_state = _dev(initial_state, "initial_state")
-        if initial_state.dtype != torch.float32 or not initial_state.is_contiguous():
-            initial_state = initial_state.float().contiguous()
-    if out is None:
-        out = torch.empty((T, hv, dv), dtype=q.dtype, device=q.device)
-    if final_state is None:
-        final_state = torch.empty((n_seqs, hv, dv, dk), dtype=torch.float32, device=q.device)
-    a = _lib.PrefillArgs()
-    a.n_seqs, a.seq_len, a.total_tokens = n_seqs, seq_len, T
-    a.hq, a.hv, a.dk, a.dv = hq, hv, dk, dv
-    a.io_dtype = dt
-    a.decay_kind = _lib.GDN_DECAY_GAMMA if decay_kind == "gamma" else _lib.GDN_DECAY_LOG
-    a.chunk_size = int(chunk_size)
-    a.scale = (1.0 / math.sqrt(dk)) if scale is None else float(scale)
-    a.q, a.q_stride_token, a.q_stride_head = q.data_ptr(), q.stride(0), q.stride(1)
-    a.k, a.k_stride_token, a.k_stride_head = k.data_ptr(), k.stride(0), k.stride(1)
-    a.v, a.v_stride_token, a.v_stride_head = v.data_ptr(), v.stride(0), v.stride(1)
-    a.out, a.out_stride_token, a.out_stride_head = out.data_ptr(), out.stride(0), out.stride(1)
-    a.decay, a.beta = decay.data_ptr(), beta.data_ptr()
-    a.cu_seqlens = None if cu is None else cu.data_ptr()
-    a.initial_state = None if initial_state is None else initial_state.data_ptr()
-    a.final_state = final_state.data_ptr()
+    a, keep, out, final_state = prefill_args(
+        q, k, v, decay, beta, decay_kind=decay_kind, cu_seqlens=cu_seqlens,
+        initial_state=initial_state, scale=scale, chunk_size=chunk_size, out=out,
+        final_state=final_state)
     _lib.check(lib.gdn_prefill(ctypes.byref(a), _stream(stream)))
-    if batched:
-        out = out.view(B, S, hv, dv)
+    del keep
     return out, final_state
 
 
-def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None, scatter_idx=None,
-           disable_state_update=False, scale=None, out=None, stream=None):
-    """Slot-pool decode with Householder sub-steps (one fused launch).
+def decode_args(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None,
+                scatter_idx=None, disable_state_update=False, scale=None, out=None):
+    """Validate shapes and build the gdn_decode_args struct (device-agnostic).
 
-    q [B, T, hq, dk]; k [B, T, n, hq, dk]; v [B, T, n, hv, dv]; A_log, dt_bias
-    [hv] float32; a [B, T, hv]; b [B, T, n, hv]; pool [P, hv, dv, dk] float32
-    (updated in place); read_idx [B]; write_idx [B] or None; scatter_idx [B, T]
-    or None.  scale None means 1/sqrt(dk).  Returns (out [B, T, hv, dv], pool);
-    rows of skipped batch rows keep out's previous contents (zeros when out is
-    None).
-    """
-    lib = _lib.load()
-    for name, t in (("q", q), ("k", k), ("v", v), ("a", a), ("b", b), ("pool", pool),
-                    ("read_idx", read_idx)):
-        _dev(t, name)
+    Returns (args, keep, out)."""
+    if q.dim() != 4 or k.dim() != 5 or v.dim() != 5:
+        raise ValueError("q [B,T,hq,dk], k [B,T,n,hq,dk], v [B,T,n,hv,dv] expected")
     B, T, hq, dk = q.shape
     n = k.shape[2]
     hv, dv = v.shape[3], v.shape[4]
+    _shape(k, "k", (B, T, n, hq, dk))
+    _shape(v, "v", (B, T, n, hv, dv))
+    _shape(a, "a", (B, T, hv))
+    _shape(b, "b", (B, T, n, hv))
     dt = _io_dtype(q)
-    q, k, v, a, b = (t.contiguous() for t in (q, k, v, a, b))
-    if a.dtype != q.dtype or b.dtype != q.dtype or k.dtype != q.dtype or v.dtype != q.dtype:
+    if any(t.dtype != q.dtype for t in (k, v, a, b)):
         raise ValueError("q, k, v, a and b must share one dtype")
-    A_log = _dev(A_log, "A_log").float().contiguous()
-    dt_bias = _dev(dt_bias, "dt_bias").float().contiguous()
+    q, k, v, a, b = (t.contiguous() for t in (q, k, v, a, b))
+    A_log = _f32c(A_log, "A_log", (hv,))
+    dt_bias = _f32c(dt_bias, "dt_bias", (hv,))
+    if pool.dim() != 4 or tuple(pool.shape[1:]) != (hv, dv, dk):
+        raise ValueError("pool must be [P, %d, %d, %d], got %s" % (hv, dv, dk, tuple(pool.shape)))
     if pool.dtype != torch.float32 or pool.stride(-1) != 1 or pool.stride(-2) != dk:
         raise ValueError("pool must be float32 with dense [dv][dk] rows")
     if out is None:
         out = torch.zeros((B, T, hv, dv), dtype=q.dtype, device=q.device)
-    elif not out.is_contiguous() or out.dtype != q.dtype:
+    _shape(out, "out", (B, T, hv, dv))
+    if not out.is_contiguous() or out.dtype != q.dtype:
         raise ValueError("out must be contiguous and of q's dtype")
-    read_idx = _idx32(read_idx)
-    write_idx = _idx32(write_idx)
-    scatter_idx = _idx32(scatter_idx)
+    read_idx = _idx32(read_idx, "read_idx", (B,))
+    write_idx = _idx32(write_idx, "write_idx", (B,))
+    scatter_idx = _idx32(scatter_idx, "scatter_idx", (B, T))
     d = _lib.DecodeArgs()
     d.batch, d.T, d.n_householder = B, T, n
     d.hq, d.hv, d.dk, d.dv = hq, hv, dk, dv
@@ -211,5 +273,29 @@ def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None, sca
     d.write_idx = None if write_idx is None else write_idx.data_ptr()
     d.scatter_idx = None if scatter_idx is None else scatter_idx.data_ptr()
     d.out = out.data_ptr()
+    keep = (q, k, v, a, b, A_log, dt_bias, read_idx, write_idx, scatter_idx)
+    return d, keep, out
+
+
+def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None, scatter_idx=None,
+           disable_state_update=False, scale=None, out=None, stream=None):
+    """Slot-pool decode with Householder sub-steps (one fused launch).
+
+    q [B, T, hq, dk]; k [B, T, n, hq, dk]; v [B, T, n, hv, dv]; A_log, dt_bias
+    [hv] float32; a [B, T, hv]; b [B, T, n, hv]; pool [P, hv, dv, dk] float32
+    (updated in place); read_idx [B]; write_idx [B] or None; scatter_idx [B, T]
+    or None.  scale None means 1/sqrt(dk).  Returns (out [B, T, hv, dv], pool);
+    rows of skipped batch rows keep out's previous contents (zeros when out is
+    None).
+    """
+    lib = _lib.load()
+    for name, t in (("q", q), ("k", k), ("v", v), ("A_log", A_log), ("dt_bias", dt_bias),
+                    ("a", a), ("b", b), ("pool", pool), ("read_idx", read_idx),
+                    ("write_idx", write_idx), ("scatter_idx", scatter_idx), ("out", out)):
+        _dev(t, name)
+    d, keep, out = decode_args(q, k, v, A_log, dt_bias, a, b, pool, read_idx,
+                               write_idx=write_idx, scatter_idx=scatter_idx,
+                               disable_state_update=disable_state_update, scale=scale, out=out)
     _lib.check(lib.gdn_decode(ctypes.byref(d), _stream(stream)))
+    del keep
     return out, pool

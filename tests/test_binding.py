@@ -1,0 +1,153 @@
+"""The Python binding's argument marshalling, on the CPU (no library call).
+
+The kernels trust the sizes and strides in the argument structs, so every
+struct the binding builds must describe memory inside the tensors it points
+at.  For each pointer we compute the furthest element the kernel can touch
+from the struct's sizes and strides and compare it with the tensor's storage.
+Includes the benchmark's exact shapes (a 4-D output buffer), which once
+reached the prefill kernel with batch/sequence strides in place of
+token/head strides.
+"""
+import pytest
+import torch
+
+import gated_deltanet_state_delta_amd as gdn
+
+
+def _span_ok(ptr, max_elem, t):
+    """ptr + max_elem (elements of t's dtype) lies inside t's storage."""
+    base = t.untyped_storage().data_ptr()
+    end = base + t.untyped_storage().nbytes()
+    last = ptr + (max_elem + 1) * t.element_size()
+    return base <= ptr and last <= end
+
+
+def _check_prefill(a, keep, T):
+    q3, k3, v3, decay, beta, cu, init, out3, fin = keep
+    last_q = (T - 1) * a.q_stride_token + (a.hq - 1) * a.q_stride_head + a.dk - 1
+    last_k = (T - 1) * a.k_stride_token + (a.hq - 1) * a.k_stride_head + a.dk - 1
+    last_v = (T - 1) * a.v_stride_token + (a.hv - 1) * a.v_stride_head + a.dv - 1
+    last_o = (T - 1) * a.out_stride_token + (a.hv - 1) * a.out_stride_head + a.dv - 1
+    assert _span_ok(a.q, last_q, q3)
+    assert _span_ok(a.k, last_k, k3)
+    assert _span_ok(a.v, last_v, v3)
+    assert _span_ok(a.out, last_o, out3)
+    assert _span_ok(a.decay, T * a.hv - 1, decay)
+    assert _span_ok(a.beta, T * a.hv - 1, beta)
+    assert _span_ok(a.final_state, a.n_seqs * a.hv * a.dv * a.dk - 1, fin)
+    if a.initial_state:
+        assert _span_ok(a.initial_state, a.n_seqs * a.hv * a.dv * a.dk - 1, init)
+    if a.cu_seqlens:
+        assert _span_ok(a.cu_seqlens, a.n_seqs, cu)
+    else:
+        assert a.n_seqs * a.seq_len == T
+
+
+def test_bench_prefill_shapes_with_4d_out():
+    B, S, hq, hv, d = 4, 4096, 16, 32, 128
+    q = torch.zeros(B, S, hq, d, dtype=torch.bfloat16)
+    k = torch.zeros_like(q)
+    v = torch.zeros(B, S, hv, d, dtype=torch.bfloat16)
+    g = torch.zeros(B * S, hv)
+    out = torch.empty_like(v)
+    fin = torch.empty(B, hv, d, d)
+    a, keep, o, f = gdn.prefill_args(q, k, v, g.view(B, S, hv), g.view(B, S, hv), out=out,
+                                     final_state=fin)
+    assert o is out and f is fin
+    assert (a.out_stride_token, a.out_stride_head) == (hv * d, d)
+    assert (a.q_stride_token, a.q_stride_head) == (hq * d, d)
+    assert (a.n_seqs, a.seq_len, a.total_tokens) == (B, S, B * S)
+    _check_prefill(a, keep, B * S)
+
+
+@pytest.mark.parametrize("form", ["packed3", "batched4", "ragged", "strided"])
+def test_prefill_struct_in_bounds(form):
+    T, hq, hv, dk, dv = 96, 2, 4, 64, 32
+    g = torch.zeros(T, hv)
+    kw = {}
+    if form == "batched4":
+        q = torch.zeros(3, 32, hq, dk)
+        v = torch.zeros(3, 32, hv, dv)
+    elif form == "strided":
+        q = torch.zeros(T, hq, dk + 32)[:, :, :dk]
+        v = torch.zeros(T, hv + 1, dv)[:, 1:]
+    else:
+        q = torch.zeros(T, hq, dk)
+        v = torch.zeros(T, hv, dv)
+    if form == "ragged":
+        kw["cu_seqlens"] = torch.tensor([0, 10, 10, 96])
+        kw["initial_state"] = torch.zeros(3, hv, dv, dk)
+    a, keep, o, f = gdn.prefill_args(q, q.clone() if form != "strided" else q, v, g, g, **kw)
+    _check_prefill(a, keep, T)
+    assert tuple(o.shape) == ((3, 32, hv, dv) if form == "batched4" else (T, hv, dv))
+
+
+BAD_PREFILL = [
+    dict(out=torch.empty(96, 4, 16)),                 # wrong dv
+    dict(out=torch.empty(2, 48, 4, 32)),              # 4-D out for a 3-D call
+    dict(final_state=torch.empty(1, 4, 32, 32)),      # wrong dk
+    dict(initial_state=torch.empty(2, 4, 32, 64)),    # wrong n_seqs
+    dict(decay=torch.zeros(95, 4)),
+    dict(beta=torch.zeros(96, 3)),
+    dict(out=torch.empty(96, 4, 32, dtype=torch.bfloat16)),  # dtype
+]
+
+
+@pytest.mark.parametrize("bad", BAD_PREFILL)
+def test_prefill_rejects_bad_shapes(bad):
+    T, hq, hv, dk, dv = 96, 2, 4, 64, 32
+    args = dict(q=torch.zeros(T, hq, dk), k=torch.zeros(T, hq, dk), v=torch.zeros(T, hv, dv),
+                decay=torch.zeros(T, hv), beta=torch.zeros(T, hv))
+    kw = {}
+    for key, val in bad.items():
+        (args if key in args else kw)[key] = val
+    with pytest.raises(ValueError):
+        gdn.prefill_args(args["q"], args["k"], args["v"], args["decay"], args["beta"], **kw)
+
+
+def _dec(B=8, T=2, n=2, hq=2, hv=4, dk=64, dv=32, P=20):
+    return dict(q=torch.zeros(B, T, hq, dk, dtype=torch.bfloat16),
+                k=torch.zeros(B, T, n, hq, dk, dtype=torch.bfloat16),
+                v=torch.zeros(B, T, n, hv, dv, dtype=torch.bfloat16),
+                A_log=torch.zeros(hv), dt_bias=torch.zeros(hv),
+                a=torch.zeros(B, T, hv, dtype=torch.bfloat16),
+                b=torch.zeros(B, T, n, hv, dtype=torch.bfloat16),
+                pool=torch.zeros(P, hv, dv, dk), read_idx=torch.zeros(B, dtype=torch.int64))
+
+
+def test_decode_struct_in_bounds_bench_shapes():
+    x = _dec(B=256, T=1, n=1, hq=16, hv=32, dk=128, dv=128, P=8)
+    out = torch.zeros(256, 1, 32, 128, dtype=torch.bfloat16)
+    d, keep, o = gdn.decode_args(x["q"], x["k"], x["v"], x["A_log"], x["dt_bias"], x["a"],
+                                 x["b"], x["pool"], x["read_idx"],
+                                 write_idx=torch.zeros(256, dtype=torch.int32), out=out)
+    assert o is out
+    P = x["pool"]
+    last = (d.pool_size - 1) * d.pool_slot_stride + (d.hv - 1) * d.pool_head_stride + d.dv * d.dk - 1
+    assert _span_ok(d.pool, last, P)
+    assert _span_ok(d.out, d.batch * d.T * d.hv * d.dv - 1, out)
+
+
+BAD_DECODE = [
+    ("out", torch.zeros(8, 2, 4, 16, dtype=torch.bfloat16)),
+    ("pool", torch.zeros(20, 4, 32, 32)),
+    ("a", torch.zeros(8, 2, 3, dtype=torch.bfloat16)),
+    ("b", torch.zeros(8, 2, 1, 4, dtype=torch.bfloat16)),
+    ("read_idx", torch.zeros(7, dtype=torch.int32)),
+    ("write_idx", torch.zeros(9, dtype=torch.int32)),
+    ("scatter_idx", torch.zeros(8, 3, dtype=torch.int32)),
+    ("A_log", torch.zeros(5)),
+]
+
+
+@pytest.mark.parametrize("key,val", BAD_DECODE)
+def test_decode_rejects_bad_shapes(key, val):
+    x = _dec()
+    kw = {}
+    if key in x:
+        x[key] = val
+    else:
+        kw[key] = val
+    with pytest.raises(ValueError):
+        gdn.decode_args(x["q"], x["k"], x["v"], x["A_log"], x["dt_bias"], x["a"], x["b"],
+                        x["pool"], x["read_idx"], **kw)
