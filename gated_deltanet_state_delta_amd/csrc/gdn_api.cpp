@@ -90,7 +90,8 @@ gdn_status gdn_prefill(const gdn_prefill_args* p, void* stream) {
   const int64_t strides[] = {a.q_stride_token, a.q_stride_head, a.k_stride_token, a.k_stride_head,
                              a.v_stride_token, a.v_stride_head, a.out_stride_token, a.out_stride_head};
   for (int64_t s : strides)
-    if (s < 0 || s % 8 != 0) return fail(GDN_ERR_LAYOUT, "gdn_prefill: strides must be non-negative multiples of 8 elements");
+    if (s < 0 || s % 8 != 0 || s >= (int64_t(1) << 25))
+      return fail(GDN_ERR_LAYOUT, "gdn_prefill: strides must be non-negative multiples of 8 elements below 2^25");
   if (a.total_tokens > 0) {
     if (a.q_stride_head < a.dk || a.k_stride_head < a.dk || a.v_stride_head < a.dv || a.out_stride_head < a.dv ||
         a.q_stride_token < (int64_t)a.hq * a.dk || a.k_stride_token < (int64_t)a.hq * a.dk ||

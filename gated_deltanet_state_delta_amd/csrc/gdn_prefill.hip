@@ -1,8 +1,9 @@
 // gdn_prefill.hip -- host dispatch of the chunked prefill kernel.
 //
-// Picks the chunk (the ONNX card's chunk_size hint; 0 selects 64 for bf16 and
-// 32 for fp32 operands, the largest chunk whose working set fits the LDS of
-// one workgroup with a full 4-wave slice) and the (dk, dv) instantiation.
+// Picks the chunk -- the ONNX card's chunk_size is a scheduling hint that
+// never changes the result: 0 means 64, and a hint is lowered to the largest
+// chunk whose double-buffered working set fits one workgroup's LDS (for fp32
+// operands with dk = 128 that is 32) -- and the (dk, dv) instantiation.
 #include "gdn_prefill.hpp"
 
 namespace gdn {
@@ -21,7 +22,9 @@ hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream) {
   p.decay_is_gamma = a.decay_kind == GDN_DECAY_GAMMA;
   p.scale = a.scale;
   const bool bf = a.io_dtype == GDN_BF16;
-  const int c = a.chunk_size != 0 ? a.chunk_size : (bf ? 64 : 32);
+  const int hint = a.chunk_size != 0 ? a.chunk_size : 64;
+  const int c = bf ? prefill_chunk_for<__bf16>(a.dk, a.dv, hint)
+                   : prefill_chunk_for<float>(a.dk, a.dv, hint);
   switch (c) {
     case 16: return bf ? prefill_bf16_c16(p, a.dk, a.dv, stream) : prefill_f32_c16(p, a.dk, a.dv, stream);
     case 32: return bf ? prefill_bf16_c32(p, a.dk, a.dv, stream) : prefill_f32_c32(p, a.dk, a.dv, stream);

@@ -21,27 +21,30 @@
 // exactly by tracking the last zero index z_t inside the chunk:
 // D(t,s) = 0 when z_t > s.
 //
-// Mapping onto gfx950.  One workgroup (4 waves) owns one (request, value
-// head, slice of DVS value columns); it walks the request's chunks in order
-// and keeps its state slice in MFMA accumulators for the whole request.  Per
-// chunk:
-//   1. load   Q, K (and a transposed copy of K), the V slice, decay, beta
-//             into LDS; padded tokens get gamma = 1, beta = 0, k = q = v = 0;
-//   2. scan   (wave 0) prefix sums of log2 gamma, last-zero index, and the
-//             factors Gam_t, D(C-1,t);
-//   3. gram   lower-triangular 16x16 tiles of K K^T and Q K^T on MFMA, masked
-//             and decayed into -A (off-diagonal blocks), the fp32 diagonal
-//             blocks of A, and M = D o (Q K^T) (s <= t);
-//   4. inv    (wave 0) inverses of the 16x16 unit-lower diagonal blocks of
-//             I + A by forward substitution in fp32 (one column per lane);
-//   5. state  every wave owns 16-column tiles of the slice and, entirely in
-//             registers: R = [Q; K] S0 (MFMA, S0 rounded to the operand
-//             type), X, block forward substitution for U using the inverted
-//             diagonal blocks and the off-diagonal -A blocks, Y = Gam R_Q +
-//             M U, the output store, and S <- Gam_{C-1} S + K^T (D(C-1,.) U).
-// The state's accumulator tiles are laid out so that they are directly the B
-// operand of the next product (see the fragment notes in gdn_device.hpp):
-// the state chain needs no LDS round trip and no barrier among waves.
+// Mapping onto gfx950.  One workgroup of 8 waves owns one (request, value
+// head, slice of DVS <= 64 value columns) and walks the request's chunks in
+// order.  The waves are specialised and software-pipelined:
+//  * state waves 0..3 each own one 16-column tile of the slice and keep their
+//    part of the state in MFMA accumulators for the whole request.  For chunk
+//    c they compute, entirely in registers,
+//      part 1: R = [Q; K] S0 (MFMA; S0 rounded to the operand type),
+//              X = beta (V - Gam R_K), Y = Gam R_Q,
+//      part 2: U by block forward substitution over 16-token blocks using the
+//              inverted diagonal blocks and the off-diagonal -A blocks,
+//              Y += M U, the output store, S <- Gam_{C-1} S + K^T (D(C-1,.) U);
+//  * prep waves 4..7 meanwhile
+//      part 1: store chunk c+1 (loaded into registers one iteration earlier)
+//              into the other LDS buffer -- Q, K and a transposed K -- and
+//              issue the global loads of chunk c+2;
+//      part 2: scan log2 gamma of chunk c+1, compute the lower-triangular
+//              16x16 tiles of K K^T and Q K^T (MFMA), mask and decay them into
+//              -A and M = D o (Q K^T), and invert the four unit-lower 16x16
+//              diagonal blocks of I + A (fp32 forward substitution).
+// Two workgroup barriers per chunk separate the parts.  Accumulator tiles
+// are laid out so that they are directly the B operand of the next product
+// (see the fragment notes in gdn_device.hpp), so the state chain needs no LDS
+// round trip.  The key index of the state tiles is permuted (dk_of) so that
+// the [Q; K] S0 product reads its A fragments as 16-byte LDS vectors.
 //
 // Operand precision: bf16 inputs use bf16 MFMA operands (the state, U, X, M
 // and the inverse blocks are rounded to bf16 as operands; every accumulation,
@@ -77,43 +80,94 @@ struct PrefillSmem {
   static constexpr int NT = C / 16;
   static constexpr int LDK = DK + PAD;        // Q, K rows
   static constexpr int LDC = C + PAD;         // K^T, -A, M rows
-  static constexpr int LDV = DVS + PAD;       // V rows
   static constexpr int LDT = 16 + PAD;        // inverse blocks
-  E q[C][LDK];
-  E k[C][LDK];
-  E kt[DK][LDC];
-  E v[C][LDV];
-  E negA[C][LDC];
-  E m[C][LDC];
-  E tinv[NT][16][LDT];
-  float adiag[NT][16][17];
-  float F[C];     // prefix sum of log2 gamma over non-zero gammas
-  int zr[C];      // last index <= t with gamma == 0, or -1
-  float gam[C];   // Gam_t
-  float bet[C];   // beta_t (0 on padded tokens)
-  float dc[C];    // D(C-1, t)
+  struct Raw {       // one chunk's inputs
+    E q[C][LDK];
+    E k[C][LDK];
+    E kt[DK][LDC];
+  };
+  struct Derived {   // one chunk's prep results
+    E negA[C][LDC];  // -A, off-diagonal 16x16 blocks only
+    E m[C][LDC];     // D o (Q K^T), lower-triangular blocks only
+    E tinv[NT][16][LDT];
+    float gam[C];    // Gam_t
+    float bet[C];    // beta_t (0 on padded tokens)
+    float dc[C];     // D(C-1, t)
+  };
+  Raw raw[2];
+  Derived der[2];
+  float adiag[4][16][16];  // per prep wave: fp32 diagonal block of A
 };
 
+// Row r (0..15) of state tile j holds key index dk_of(j, r).  With pairs of
+// tiles, lane group g of a 32-key block holds keys 8g .. 8g+7, contiguous.
+template <int NKT>
+__device__ __forceinline__ int dk_of(int j, int r) {
+  if constexpr (NKT % 2 == 0) return 32 * (j >> 1) + 8 * (r >> 2) + 4 * (j & 1) + (r & 3);
+  else return 16 * j + r;
+}
+
+// 8 consecutive operand elements from LDS as two K16 fragments.
+__device__ __forceinline__ void lds_frag8(const __bf16* p, bf4& a0, bf4& a1) {
+  const bf8 v = *reinterpret_cast<const bf8*>(p);
+  a0 = bf4{v[0], v[1], v[2], v[3]};
+  a1 = bf4{v[4], v[5], v[6], v[7]};
+}
+__device__ __forceinline__ void lds_frag8(const float* p, f4& a0, f4& a1) {
+  a0 = *reinterpret_cast<const f4*>(p);
+  a1 = *reinterpret_cast<const f4*>(p + 4);
+}
+
+// Element e of a 16-byte vector of E.
+template <typename E> __device__ __forceinline__ E elem16(const uint4& v, int e);
+template <> __device__ __forceinline__ __bf16 elem16<__bf16>(const uint4& v, int e) {
+  const uint32_t word = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+  return __builtin_bit_cast(__bf16, (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu)));
+}
+template <> __device__ __forceinline__ float elem16<float>(const uint4& v, int e) {
+  const uint32_t word = e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+  return __uint_as_float(word);
+}
+
+// 4 elements of E packed from 4 separate E values (transposed LDS stores).
+template <typename E> struct pack4;
+template <> struct pack4<__bf16> { typedef bf4 type; };
+template <> struct pack4<float> { typedef f4 type; };
+
 template <typename E, int DK, int DVS, int C>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 prefill_kernel(const PrefillParams p) {
   typedef typename frag_of<E>::type Fr;
-  constexpr int NT = C / 16;      // token tiles per chunk
-  constexpr int NKT = DK / 16;    // key tiles
-  constexpr int NVT = DVS / 16;   // value tiles per workgroup
-  constexpr int VTW = (NVT + 3) / 4;  // value tiles per wave
-  constexpr int VE = 16 / sizeof(E);  // elements per 16-byte vector
   typedef PrefillSmem<E, DK, DVS, C> Sm;
+  constexpr int NT = C / 16;            // token tiles per chunk
+  constexpr int NKT = DK / 16;          // key tiles
+  constexpr int NVT = DVS / 16;         // value tiles per workgroup (<= 4)
+  constexpr int VE = 16 / sizeof(E);    // elements per 16-byte vector
+  constexpr int NOCT = DK / VE;         // 16-byte vectors per token row
+  constexpr int NPAIR = (C / 4) * NOCT; // (4-token quad, vector) load units
+  constexpr int NPT = (NPAIR + 255) / 256;
+  constexpr int NOFF = NT * (NT - 1) / 2;
+  static_assert(NVT <= 4, "one value tile per state wave");
   __shared__ Sm sm;
+  // Transposed-K layout: token t of key row r lives at column t ^ kt_swz(r)
+  // (an XOR of 4-token groups), so that the prep waves' transposed stores --
+  // 16 lanes writing rows VE keys apart -- hit distinct banks.
+  auto kt_swz = [](int r) { return 4 * ((r / VE) % (C / 4)); };
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int x = lane & 15;   // row/column inside a 16x16 tile
-  const int g = lane >> 4;   // lane group: contraction indices 4g..4g+3
+  const int g = lane >> 4;   // lane group
+  const bool is_prep = wave >= 4;
+  const int pw = wave - 4;   // prep wave index
+  const int ptid = tid - 256;
 
-  // workgroup -> (request, value head, value slice)
-  const int blk = blockIdx.x;
+  // Workgroups sharing a query/key head are consecutive; keep them on one XCD
+  // (workgroups are dealt to the 8 XCDs round-robin).
+  int blk = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 31) == 0) blk = (blk & 7) * (nblk >> 3) + (blk >> 3);
   const int split = blk % p.nsplit;
   const int h = (blk / p.nsplit) % p.hv;
   const int r = blk / (p.nsplit * p.hv);
@@ -129,71 +183,265 @@ prefill_kernel(const PrefillParams p) {
     end = start + p.seq_len;
   }
   if (end < start) end = start;
+  const int nch = (int)((end - start + C - 1) / C);
 
   const E* __restrict__ gq = (const E*)p.q + (int64_t)qh * p.q_sh;
   const E* __restrict__ gk = (const E*)p.k + (int64_t)qh * p.k_sh;
   const E* __restrict__ gv = (const E*)p.v + (int64_t)h * p.v_sh + v0;
   E* __restrict__ gout = (E*)p.out + (int64_t)h * p.o_sh + v0;
-
-  // ---- state slice: accumulator tiles S[vv][kt], rows = key index, cols = value index
-  f4 S[VTW][NKT];
+  const float* __restrict__ gdec = p.decay + h;
+  const float* __restrict__ gbet = p.beta + h;
   const int64_t st_base = (((int64_t)r * p.hv + h) * p.dv + v0) * DK;
+
+  // ------------------------------------------------------------ state waves
+  // Every role runs its own loop with the same two barriers per chunk, so the
+  // registers one role carries across chunks are not live in the other's.
+  if (!is_prep) {
+    const bool active = wave < NVT;  // waves beyond the slice only keep the barriers
+    const int vc = 16 * wave + x;    // this lane's value column inside the slice
+    f4 S[NKT];
+    E vreg[NT][4];
 #pragma unroll
-  for (int vv = 0; vv < VTW; ++vv) {
-    const int vt = wave + 4 * vv;
+    for (int j = 0; j < NKT; ++j) S[j] = f4{0.f, 0.f, 0.f, 0.f};
+    auto load_v = [&](int c) {  // V(c) in accumulator layout: rows t = 16i+4g+e
+      const int64_t t0 = start + (int64_t)c * C;
+      const int rem = (int)min((int64_t)C, end - t0);
+      const E* vb = gv + t0 * p.v_st + vc;
+      const int vst = (int)p.v_st;
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-      S[vv][kt] = f4{0.f, 0.f, 0.f, 0.f};
-      if (p.init && vt < NVT)
-        S[vv][kt] = *reinterpret_cast<const f4*>(p.init + st_base + (int64_t)(16 * vt + x) * DK + 16 * kt + 4 * g);
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * i + 4 * g + e;
+          vreg[i][e] = t < rem ? vb[t * vst] : from_f32<E>(0.f);
+        }
+    };
+    if (active) {
+      if (p.init) {
+#pragma unroll
+        for (int j = 0; j < NKT; ++j)
+          S[j] = *reinterpret_cast<const f4*>(p.init + st_base + (int64_t)vc * DK + dk_of<NKT>(j, 4 * g));
+      }
+      if (nch > 0) load_v(0);
     }
+    f4 X[NT], Y[NT];  // carried from part 1 to part 2
+    for (int c = -1; c < nch; ++c) {
+      const int cur = c & 1;
+      const bool work = active && c >= 0;
+      // ============================================================== part 1
+      if (work) {
+        const typename Sm::Raw& R = sm.raw[cur];
+        const typename Sm::Derived& Dd = sm.der[cur];
+        Fr Sb[NKT];
+#pragma unroll
+        for (int j = 0; j < NKT; ++j) cvt_frag(S[j], Sb[j]);
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          f4 rq = {0.f, 0.f, 0.f, 0.f}, rk = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (NKT % 2 == 0) {
+#pragma unroll
+            for (int pp = 0; pp < NKT / 2; ++pp) {
+              Fr aq0, aq1, ak0, ak1;
+              lds_frag8(&R.q[16 * i + x][32 * pp + 8 * g], aq0, aq1);
+              lds_frag8(&R.k[16 * i + x][32 * pp + 8 * g], ak0, ak1);
+              rq = mma_k32(rq, aq0, aq1, Sb[2 * pp], Sb[2 * pp + 1]);
+              rk = mma_k32(rk, ak0, ak1, Sb[2 * pp], Sb[2 * pp + 1]);
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < NKT; ++j) {
+              Fr aq, ak;
+              lds_frag(&R.q[16 * i + x][16 * j + 4 * g], aq);
+              lds_frag(&R.k[16 * i + x][16 * j + 4 * g], ak);
+              rq = mma_k16(rq, aq, Sb[j]);
+              rk = mma_k16(rk, ak, Sb[j]);
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 16 * i + 4 * g + e;
+            const float gm = Dd.gam[t];
+            X[i][e] = Dd.bet[t] * (to_f32(vreg[i][e]) - gm * rk[e]);
+            Y[i][e] = gm * rq[e];
+          }
+        }
+        if (c + 1 < nch) load_v(c + 1);
+      }
+      __syncthreads();
+      // ============================================================== part 2
+      if (work) {
+        const typename Sm::Raw& R = sm.raw[cur];
+        const typename Sm::Derived& Dd = sm.der[cur];
+        // (I + A) U = X by 16-token blocks: U_i = Tinv_i (X_i - sum_{m<i} A_im U_m)
+        f4 U[NT];
+        Fr Ub[NT];
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          f4 P = X[i];
+#pragma unroll
+          for (int m = 0; m < i; ++m) {
+            Fr a;
+            lds_frag(&Dd.negA[16 * i + x][16 * m + 4 * g], a);
+            P = mma_k16(P, a, Ub[m]);
+          }
+          Fr Pb, ti;
+          cvt_frag(P, Pb);
+          lds_frag(&Dd.tinv[i][x][4 * g], ti);
+          U[i] = mma_k16(f4{0.f, 0.f, 0.f, 0.f}, ti, Pb);
+          cvt_frag(U[i], Ub[i]);
+        }
+        // Y += M U ; store
+        const int64_t tok0 = start + (int64_t)c * C;
+        const int nvalid = (int)min((int64_t)C, end - tok0);
+        E* ob = gout + tok0 * p.o_st + vc;
+        const int ost = (int)p.o_st;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+#pragma unroll
+          for (int m = 0; m <= i; ++m) {
+            Fr a;
+            lds_frag(&Dd.m[16 * i + x][16 * m + 4 * g], a);
+            Y[i] = mma_k16(Y[i], a, Ub[m]);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 16 * i + 4 * g + e;
+            if (t < nvalid) ob[t * ost] = from_f32<E>(p.scale * Y[i][e]);
+          }
+        }
+        // S <- Gam_{C-1} S + K^T (D(C-1, .) U)
+        Fr DU[NT];
+#pragma unroll
+        for (int m = 0; m < NT; ++m) {
+          f4 du;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) du[e] = Dd.dc[16 * m + 4 * g + e] * U[m][e];
+          cvt_frag(du, DU[m]);
+        }
+        const float gC = Dd.gam[C - 1];
+#pragma unroll
+        for (int j = 0; j < NKT; ++j) {
+          const int krow = dk_of<NKT>(j, x);
+          const int sw = kt_swz(krow);
+          f4 acc = gC * S[j];
+          if constexpr (NT % 2 == 0) {
+#pragma unroll
+            for (int m = 0; m < NT; m += 2) {
+              Fr a0, a1;
+              lds_frag(&R.kt[krow][(16 * m + 4 * g) ^ sw], a0);
+              lds_frag(&R.kt[krow][(16 * m + 16 + 4 * g) ^ sw], a1);
+              acc = mma_k32(acc, a0, a1, DU[m], DU[m + 1]);
+            }
+          } else {
+#pragma unroll
+            for (int m = 0; m < NT; ++m) {
+              Fr a;
+              lds_frag(&R.kt[krow][(16 * m + 4 * g) ^ sw], a);
+              acc = mma_k16(acc, a, DU[m]);
+            }
+          }
+          S[j] = acc;
+        }
+      }
+      __syncthreads();
+    }
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < NKT; ++j)
+        *reinterpret_cast<f4*>(p.fin + st_base + (int64_t)vc * DK + dk_of<NKT>(j, 4 * g)) = S[j];
+    }
+    return;
   }
 
-  for (int64_t tok0 = start; tok0 < end; tok0 += C) {
-    const int nvalid = (int)min((int64_t)C, end - tok0);
+  // ------------------------------------------------------------- prep waves
+  uint4 pq[NPT][4], pk[NPT][4];
+  float pg = 0.f, pb = 0.f;     // prefetched decay/beta of token `lane`
+  bool pvalid = false;
 
-    // ---------------------------------------------------------------- 1. load
-    for (int idx = tid; idx < C * (DK / VE); idx += 256) {
-      const int t = idx / (DK / VE);
-      const int cv = (idx % (DK / VE)) * VE;
-      uint4 vq = {0u, 0u, 0u, 0u}, vk = {0u, 0u, 0u, 0u};
-      if (t < nvalid) {
-        vq = *reinterpret_cast<const uint4*>(gq + (tok0 + t) * p.q_st + cv);
-        vk = *reinterpret_cast<const uint4*>(gk + (tok0 + t) * p.k_st + cv);
-      }
-      *reinterpret_cast<uint4*>(&sm.q[t][cv]) = vq;
-      *reinterpret_cast<uint4*>(&sm.k[t][cv]) = vk;
-      const E* ke = reinterpret_cast<const E*>(&vk);
+  auto prefetch = [&](int c) {
+    const int64_t t0 = start + (int64_t)c * C;
+    const int rem = (int)min((int64_t)C, end - t0);
+    const E* qb = gq + t0 * p.q_st;
+    const E* kb = gk + t0 * p.k_st;
+    const int qst = (int)p.q_st, kst = (int)p.k_st;
 #pragma unroll
-      for (int e = 0; e < VE; ++e) sm.kt[cv + e][t] = ke[e];
+    for (int u = 0; u < NPT; ++u) {
+      const int pr = ptid + 256 * u;
+      const int quad = pr / NOCT, oct = pr % NOCT;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int t = 4 * quad + w;
+        uint4 vq = {0u, 0u, 0u, 0u}, vk = {0u, 0u, 0u, 0u};
+        if (pr < NPAIR && t < rem) {
+          vq = *reinterpret_cast<const uint4*>(qb + t * qst + oct * VE);
+          vk = *reinterpret_cast<const uint4*>(kb + t * kst + oct * VE);
+        }
+        pq[u][w] = vq;
+        pk[u][w] = vk;
+      }
     }
-    for (int idx = tid; idx < C * (DVS / VE); idx += 256) {
-      const int t = idx / (DVS / VE);
-      const int cv = (idx % (DVS / VE)) * VE;
-      uint4 vv = {0u, 0u, 0u, 0u};
-      if (t < nvalid) vv = *reinterpret_cast<const uint4*>(gv + (tok0 + t) * p.v_st + cv);
-      *reinterpret_cast<uint4*>(&sm.v[t][cv]) = vv;
+    pvalid = lane < rem;
+    pg = pvalid ? gdec[(t0 + lane) * p.hv] : 0.f;
+    pb = pvalid ? gbet[(t0 + lane) * p.hv] : 0.f;
+  };
+
+  auto store_raw = [&](int buf) {
+    typename Sm::Raw& R = sm.raw[buf];
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+      const int pr = ptid + 256 * u;
+      if (pr < NPAIR) {
+        const int quad = pr / NOCT, oct = pr % NOCT;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          *reinterpret_cast<uint4*>(&R.q[4 * quad + w][oct * VE]) = pq[u][w];
+          *reinterpret_cast<uint4*>(&R.k[4 * quad + w][oct * VE]) = pk[u][w];
+        }
+        // transposed K: for each key of the vector, 4 consecutive tokens
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          const int krow = oct * VE + e;
+          typename pack4<E>::type col;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) col[w] = elem16<E>(pk[u][w], e);
+          *reinterpret_cast<typename pack4<E>::type*>(&R.kt[krow][(4 * quad) ^ kt_swz(krow)]) = col;
+        }
+      }
+    }
+  };
+
+  if (nch > 0) prefetch(0);
+  float cg = 0.f, cb = 0.f;     // decay/beta of the chunk being prepared
+  bool cvalid = false;
+  for (int c = -1; c < nch; ++c) {
+    const int nxt = (c + 1) & 1;
+    const bool work = c + 1 < nch;
+    // ================================================================ part 1
+    if (work) {
+      store_raw(nxt);
+      cg = pg; cb = pb; cvalid = pvalid;
+      if (c + 2 < nch) prefetch(c + 2);
     }
     __syncthreads();
-
-    // ---------------------------------------------------------------- 2. scan
-    if (wave == 0) {
-      const int t = lane;
-      float lg = 0.f, bt = 0.f;
+    // ================================================================ part 2
+    if (work) {
+      const typename Sm::Raw& R = sm.raw[nxt];
+      typename Sm::Derived& Dd = sm.der[nxt];
+      // scan: every prep wave keeps F_t (prefix sum of log2 gamma over non-zero
+      // gammas) and z_t (last zero index, -1 if none) of token t = lane
+      float lg = 0.f;
       bool reset = false;
-      if (t < nvalid) {
-        const float d = p.decay[(tok0 + t) * p.hv + h];
-        bt = p.beta[(tok0 + t) * p.hv + h];
+      if (cvalid) {
         if (p.decay_is_gamma) {
-          reset = !(d > 0.f);
-          lg = reset ? 0.f : __log2f(d);
+          reset = !(cg > 0.f);
+          lg = reset ? 0.f : __log2f(cg);
         } else {
-          reset = !(d > -INFINITY);
-          lg = reset ? 0.f : d * 1.4426950408889634f;
+          reset = !(cg > -INFINITY);
+          lg = reset ? 0.f : cg * 1.4426950408889634f;
         }
       }
       float F = lg;
-      int z = reset ? t : -1;
+      int z = reset ? lane : -1;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float Fo = __shfl_up(F, off);
@@ -203,224 +451,136 @@ prefill_kernel(const PrefillParams p) {
           z = max(z, zo);
         }
       }
+      const float bt = cvalid ? cb : 0.f;
       const float Flast = __shfl(F, C - 1);
       const int zlast = __shfl(z, C - 1);
-      if (t < C) {
-        sm.F[t] = F;
-        sm.zr[t] = z;
-        sm.gam[t] = z < 0 ? exp2f(F) : 0.f;
-        sm.bet[t] = bt;
-        sm.dc[t] = zlast <= t ? exp2f(Flast - F) : 0.f;
+      if (pw == 0 && lane < C) {
+        Dd.gam[lane] = z < 0 ? exp2f(F) : 0.f;
+        Dd.bet[lane] = bt;
+        Dd.dc[lane] = zlast <= lane ? exp2f(Flast - F) : 0.f;
       }
-    }
-    __syncthreads();
 
-    // ---------------------------------------------------------------- 3. gram
-    {
-      constexpr int NTILES = NT * (NT + 1) / 2;
-      for (int tile = wave; tile < NTILES; tile += 4) {
-        int i = 0, rem = tile;
-        while (rem > i) { rem -= i + 1; ++i; }
-        const int m = rem;  // m <= i
-        f4 kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
+      // tiles: prep wave pw owns diagonal tile (pw, pw) and every NOFF-list
+      // off-diagonal tile whose index is pw mod 4
+      auto gram_tile = [&](int i, int m, f4& kk, f4& qk) {
+        kk = f4{0.f, 0.f, 0.f, 0.f};
+        qk = f4{0.f, 0.f, 0.f, 0.f};
         if constexpr (NKT % 2 == 0) {
 #pragma unroll
-          for (int kb = 0; kb < NKT; kb += 2) {
+          for (int pp = 0; pp < NKT / 2; ++pp) {
             Fr ak0, ak1, aq0, aq1, b0, b1;
-            lds_frag(&sm.k[16 * i + x][16 * kb + 4 * g], ak0);
-            lds_frag(&sm.k[16 * i + x][16 * kb + 16 + 4 * g], ak1);
-            lds_frag(&sm.q[16 * i + x][16 * kb + 4 * g], aq0);
-            lds_frag(&sm.q[16 * i + x][16 * kb + 16 + 4 * g], aq1);
-            lds_frag(&sm.k[16 * m + x][16 * kb + 4 * g], b0);
-            lds_frag(&sm.k[16 * m + x][16 * kb + 16 + 4 * g], b1);
+            lds_frag8(&R.k[16 * i + x][32 * pp + 8 * g], ak0, ak1);
+            lds_frag8(&R.q[16 * i + x][32 * pp + 8 * g], aq0, aq1);
+            lds_frag8(&R.k[16 * m + x][32 * pp + 8 * g], b0, b1);
             kk = mma_k32(kk, ak0, ak1, b0, b1);
             qk = mma_k32(qk, aq0, aq1, b0, b1);
           }
         } else {
 #pragma unroll
-          for (int kb = 0; kb < NKT; ++kb) {
+          for (int j = 0; j < NKT; ++j) {
             Fr ak, aq, b;
-            lds_frag(&sm.k[16 * i + x][16 * kb + 4 * g], ak);
-            lds_frag(&sm.q[16 * i + x][16 * kb + 4 * g], aq);
-            lds_frag(&sm.k[16 * m + x][16 * kb + 4 * g], b);
+            lds_frag(&R.k[16 * i + x][16 * j + 4 * g], ak);
+            lds_frag(&R.q[16 * i + x][16 * j + 4 * g], aq);
+            lds_frag(&R.k[16 * m + x][16 * j + 4 * g], b);
             kk = mma_k16(kk, ak, b);
             qk = mma_k16(qk, aq, b);
           }
         }
+      };
+      // decay factor D(t, s) for this lane's 4 rows t of tile i and column s of tile m
+      auto decay4 = [&](int i, int m, float d[4], float bt4[4]) {
         const int s = 16 * m + x;
-        const float Fs = sm.F[s];
+        const float Fs = __shfl(F, s);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 16 * i + 4 * g + e;
-          const float d = (s <= t && sm.zr[t] <= s) ? exp2f(sm.F[t] - Fs) : 0.f;
-          sm.m[t][s] = from_f32<E>(d * qk[e]);
-          const float av = (s < t) ? sm.bet[t] * d * kk[e] : 0.f;
-          if (i == m) sm.adiag[i][4 * g + e][x] = av;
-          else sm.negA[t][s] = from_f32<E>(-av);
+          const float Ft = __shfl(F, t);
+          const int zt = __shfl(z, t);
+          bt4[e] = __shfl(bt, t);
+          d[e] = (s <= t && zt <= s) ? exp2f(Ft - Fs) : 0.f;
+        }
+      };
+
+      if (pw < NT) {
+        const int i = pw;
+        f4 kk, qk;
+        gram_tile(i, i, kk, qk);
+        float d[4], bt4[4];
+        decay4(i, i, d, bt4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * i + 4 * g + e;
+          const int s = 16 * i + x;
+          Dd.m[t][s] = from_f32<E>(d[e] * qk[e]);
+          sm.adiag[pw][4 * g + e][x] = (s < t) ? bt4[e] * d[e] * kk[e] : 0.f;
+        }
+        // column x of (I + A_ii)^-1 by forward substitution (lanes of group 0);
+        // the block was written by this wave only, so no barrier is needed
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (g == 0) {
+          float col[16];
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            float acc = (rr == x) ? 1.f : 0.f;
+#pragma unroll
+            for (int j4 = 0; j4 < rr; j4 += 4) {
+              const f4 arow = *reinterpret_cast<const f4*>(&sm.adiag[pw][rr][j4]);
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj)
+                if (j4 + jj < rr) acc -= arow[jj] * col[j4 + jj];
+            }
+            col[rr] = acc;
+          }
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) Dd.tinv[i][rr][x] = from_f32<E>(col[rr]);
+        }
+      }
+      for (int o = pw; o < NOFF; o += 4) {
+        int i = 1, rem = o;
+        while (rem >= i) { rem -= i; ++i; }
+        const int m = rem;  // m < i
+        f4 kk, qk;
+        gram_tile(i, m, kk, qk);
+        float d[4], bt4[4];
+        decay4(i, m, d, bt4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * i + 4 * g + e;
+          const int s = 16 * m + x;
+          Dd.m[t][s] = from_f32<E>(d[e] * qk[e]);
+          Dd.negA[t][s] = from_f32<E>(-bt4[e] * d[e] * kk[e]);
         }
       }
     }
     __syncthreads();
-
-    // ----------------------------------------------------------------- 4. inv
-    if (wave == 0 && g < NT) {
-      // column x of (I + A_gg)^-1 by forward substitution
-      float col[16];
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        float acc = (rr == x) ? 1.f : 0.f;
-#pragma unroll
-        for (int j = 0; j < rr; ++j) acc -= sm.adiag[g][rr][j] * col[j];
-        col[rr] = acc;
-      }
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) sm.tinv[g][rr][x] = from_f32<E>(col[rr]);
-    }
-    __syncthreads();
-
-    // --------------------------------------------------------------- 5. state
-#pragma unroll
-    for (int vv = 0; vv < VTW; ++vv) {
-      const int vt = wave + 4 * vv;
-      if (vt >= NVT) break;
-      const int vc = 16 * vt + x;  // this lane's value column inside the slice
-
-      Fr Sb[NKT];
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) cvt_frag(S[vv][kt], Sb[kt]);
-
-      // R = [Q; K] S0 ;  X = beta (V - Gam R_K) ;  Y = Gam R_Q
-      f4 X[NT], Y[NT];
-#pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        f4 rq = {0.f, 0.f, 0.f, 0.f}, rk = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (NKT % 2 == 0) {
-#pragma unroll
-          for (int kt = 0; kt < NKT; kt += 2) {
-            Fr aq0, aq1, ak0, ak1;
-            lds_frag(&sm.q[16 * i + x][16 * kt + 4 * g], aq0);
-            lds_frag(&sm.q[16 * i + x][16 * kt + 16 + 4 * g], aq1);
-            lds_frag(&sm.k[16 * i + x][16 * kt + 4 * g], ak0);
-            lds_frag(&sm.k[16 * i + x][16 * kt + 16 + 4 * g], ak1);
-            rq = mma_k32(rq, aq0, aq1, Sb[kt], Sb[kt + 1]);
-            rk = mma_k32(rk, ak0, ak1, Sb[kt], Sb[kt + 1]);
-          }
-        } else {
-#pragma unroll
-          for (int kt = 0; kt < NKT; ++kt) {
-            Fr aq, ak;
-            lds_frag(&sm.q[16 * i + x][16 * kt + 4 * g], aq);
-            lds_frag(&sm.k[16 * i + x][16 * kt + 4 * g], ak);
-            rq = mma_k16(rq, aq, Sb[kt]);
-            rk = mma_k16(rk, ak, Sb[kt]);
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * i + 4 * g + e;
-          const float gm = sm.gam[t];
-          X[i][e] = sm.bet[t] * (to_f32(sm.v[t][vc]) - gm * rk[e]);
-          Y[i][e] = gm * rq[e];
-        }
-      }
-
-      // (I + A) U = X by 16-row blocks: U_i = Tinv_i (X_i - sum_{m<i} A_im U_m)
-      f4 U[NT];
-      Fr Ub[NT];
-#pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        f4 P = X[i];
-#pragma unroll
-        for (int m = 0; m < i; ++m) {
-          Fr a;
-          lds_frag(&sm.negA[16 * i + x][16 * m + 4 * g], a);
-          P = mma_k16(P, a, Ub[m]);
-        }
-        Fr Pb, ti;
-        cvt_frag(P, Pb);
-        lds_frag(&sm.tinv[i][x][4 * g], ti);
-        U[i] = mma_k16(f4{0.f, 0.f, 0.f, 0.f}, ti, Pb);
-        cvt_frag(U[i], Ub[i]);
-      }
-
-      // Y += M U ; store
-#pragma unroll
-      for (int i = 0; i < NT; ++i) {
-#pragma unroll
-        for (int m = 0; m <= i; ++m) {
-          Fr a;
-          lds_frag(&sm.m[16 * i + x][16 * m + 4 * g], a);
-          Y[i] = mma_k16(Y[i], a, Ub[m]);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * i + 4 * g + e;
-          if (t < nvalid) gout[(tok0 + t) * p.o_st + vc] = from_f32<E>(p.scale * Y[i][e]);
-        }
-      }
-
-      // S <- Gam_{C-1} S + K^T (D(C-1, .) U)
-      Fr DU[NT];
-#pragma unroll
-      for (int m = 0; m < NT; ++m) {
-        f4 du;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) du[e] = sm.dc[16 * m + 4 * g + e] * U[m][e];
-        cvt_frag(du, DU[m]);
-      }
-      const float gC = sm.gam[C - 1];
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
-        f4 acc = gC * S[vv][kt];
-        if constexpr (NT % 2 == 0) {
-#pragma unroll
-          for (int m = 0; m < NT; m += 2) {
-            Fr a0, a1;
-            lds_frag(&sm.kt[16 * kt + x][16 * m + 4 * g], a0);
-            lds_frag(&sm.kt[16 * kt + x][16 * m + 16 + 4 * g], a1);
-            acc = mma_k32(acc, a0, a1, DU[m], DU[m + 1]);
-          }
-        } else {
-#pragma unroll
-          for (int m = 0; m < NT; ++m) {
-            Fr a;
-            lds_frag(&sm.kt[16 * kt + x][16 * m + 4 * g], a);
-            acc = mma_k16(acc, a, DU[m]);
-          }
-        }
-        S[vv][kt] = acc;
-      }
-    }
-    __syncthreads();
-  }
-
-  // ------------------------------------------------------------ final state
-#pragma unroll
-  for (int vv = 0; vv < VTW; ++vv) {
-    const int vt = wave + 4 * vv;
-    if (vt < NVT) {
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-        *reinterpret_cast<f4*>(p.fin + st_base + (int64_t)(16 * vt + x) * DK + 16 * kt + 4 * g) = S[vv][kt];
-    }
   }
 }
 
-// Value columns per workgroup for an operand type and chunk (LDS budget).
-template <typename E, int DV, int C>
+// Value columns per workgroup: one 16-column tile per state wave.
+template <int DV>
 constexpr int prefill_dvs() {
-  if constexpr (sizeof(E) == 2) return DV < 64 ? DV : 64;
-  else return (C == 64) ? (DV < 32 ? DV : 32) : (DV < 64 ? DV : 64);
+  return DV < 64 ? DV : 64;
+}
+
+// Whether the chunk fits the 160 KiB of LDS a workgroup may use on gfx950.
+template <typename E, int DK, int DV, int C>
+constexpr bool prefill_fits() {
+  return sizeof(PrefillSmem<E, DK, prefill_dvs<DV>(), C>) <= 160 * 1024;
 }
 
 template <typename E, int DK, int DV, int C>
 hipError_t launch_prefill_t(PrefillParams p, hipStream_t stream) {
-  constexpr int DVS = prefill_dvs<E, DV, C>();
-  static_assert(sizeof(PrefillSmem<E, DK, DVS, C>) <= 160 * 1024, "LDS budget");
-  p.nsplit = DV / DVS;
-  const int64_t nblk = (int64_t)p.n_seqs * p.hv * p.nsplit;
-  hipLaunchKernelGGL((prefill_kernel<E, DK, DVS, C>), dim3((unsigned)nblk), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  if constexpr (!prefill_fits<E, DK, DV, C>()) {
+    return hipErrorInvalidValue;  // the host never selects such a chunk
+  } else {
+    constexpr int DVS = prefill_dvs<DV>();
+    p.nsplit = DV / DVS;
+    const int64_t nblk = (int64_t)p.n_seqs * p.hv * p.nsplit;
+    hipLaunchKernelGGL((prefill_kernel<E, DK, DVS, C>), dim3((unsigned)nblk), dim3(512), 0, stream, p);
+    return hipGetLastError();
+  }
 }
 
 template <typename E, int C>
@@ -441,6 +601,25 @@ hipError_t dispatch_prefill_dk_dv(PrefillParams p, int dk, int dv, hipStream_t s
   }
 #undef GDN_DV_CASES
   return hipErrorInvalidValue;
+}
+
+// Largest chunk <= hint (16, 32 or 64) whose working set fits LDS.
+template <typename E>
+int prefill_chunk_for(int dk, int dv, int hint) {
+  auto fits = [&](int c) -> bool {
+#define GDN_FIT(DK, DV)                                                              \
+  if (dk == DK && dv == DV)                                                          \
+    return c == 64 ? prefill_fits<E, DK, DV, 64>()                                   \
+                   : (c == 32 ? prefill_fits<E, DK, DV, 32>() : prefill_fits<E, DK, DV, 16>());
+#define GDN_FIT_DK(DK) GDN_FIT(DK, 16) GDN_FIT(DK, 32) GDN_FIT(DK, 64) GDN_FIT(DK, 128)
+    GDN_FIT_DK(16) GDN_FIT_DK(32) GDN_FIT_DK(64) GDN_FIT_DK(128)
+#undef GDN_FIT_DK
+#undef GDN_FIT
+    return false;
+  };
+  for (int c = hint; c >= 16; c >>= 1)
+    if (fits(c)) return c;
+  return 16;
 }
 
 // One instantiation unit per (operand type, chunk): gdn_prefill_<t>_c<C>.hip

@@ -118,7 +118,7 @@ gdn_status gdn_gate(const float* A_log, const float* dt_bias,
  *                state slice is read completely before it is written) but
  *                must not partially overlap it.
  * Requirements: pointers 16-byte aligned; head and token strides multiples of
- * 8 elements; io_dtype in {GDN_F32, GDN_BF16}.  total_tokens == 0 still
+ * 8 elements and below 2^25; io_dtype in {GDN_F32, GDN_BF16}.  total_tokens == 0 still
  * writes final_state (copies / zeros).  n_seqs == 0 is a no-op.
  * ------------------------------------------------------------------------- */
 typedef struct {

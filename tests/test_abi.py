@@ -92,6 +92,7 @@ PREFILL_ERRORS = [
     (dict(q=FAKE + 8), 4),                # misaligned pointer
     (dict(v_stride_head=68), 4),          # stride not a multiple of 8
     (dict(q_stride_token=64), 4),         # token stride smaller than heads * dk
+    (dict(v_stride_token=1 << 25), 4),    # stride too large for 32-bit in-chunk offsets
     (dict(initial_state=FAKE * 7 + 1024), 4),  # partial overlap with final_state
     (dict(n_seqs=-1), 2),
 ]
