@@ -80,6 +80,19 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// ------------------------------------------------------------- barriers --
+// Workgroup barrier for LDS hand-offs only: waits for this wave's own LDS
+// operations (lgkmcnt 0) but not for its outstanding global loads, so loads
+// issued before the barrier keep flying across it (the compiler still waits
+// for them before their first use).  The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------ MFMA tiles --
 // All products are built from 16x16 output tiles.  A "K16 fragment" of an
 // operand is what one lane holds for 16 contraction indices: lane l

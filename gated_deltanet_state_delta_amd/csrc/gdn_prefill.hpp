@@ -90,13 +90,15 @@ struct PrefillSmem {
     E negA[C][LDC];  // -A, off-diagonal 16x16 blocks only
     E m[C][LDC];     // D o (Q K^T), lower-triangular blocks only
     E tinv[NT][16][LDT];
-    float gam[C];    // Gam_t
-    float bet[C];    // beta_t (0 on padded tokens)
-    float dc[C];     // D(C-1, t)
+    alignas(16) float F[C];    // prefix sum of log2 gamma over non-zero gammas
+    alignas(16) int z[C];      // last index <= t whose gamma is 0, or -1
+    alignas(16) float gam[C];  // Gam_t
+    alignas(16) float bet[C];  // beta_t (0 on padded tokens)
+    alignas(16) float dc[C];   // D(C-1, t)
   };
   Raw raw[2];
   Derived der[2];
-  float adiag[4][16][16];  // per prep wave: fp32 diagonal block of A
+  alignas(16) float adiagT[4][16][16];  // per prep wave: transposed fp32 diagonal block of A
 };
 
 // Row r (0..15) of state tile j holds key index dk_of(j, r).  With pairs of
@@ -267,7 +269,7 @@ prefill_kernel(const PrefillParams p) {
         }
         if (c + 1 < nch) load_v(c + 1);
       }
-      __syncthreads();
+      lds_barrier();
       // ============================================================== part 2
       if (work) {
         const typename Sm::Raw& R = sm.raw[cur];
@@ -343,7 +345,7 @@ prefill_kernel(const PrefillParams p) {
           S[j] = acc;
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
     if (active) {
 #pragma unroll
@@ -410,58 +412,58 @@ prefill_kernel(const PrefillParams p) {
     }
   };
 
+  // scan of the prefetched chunk (prep wave 0): F, z and the per-token factors
+  auto scan = [&](typename Sm::Derived& Dd) {
+    float lg = 0.f;
+    bool reset = false;
+    if (pvalid) {
+      if (p.decay_is_gamma) {
+        reset = !(pg > 0.f);
+        lg = reset ? 0.f : __log2f(pg);
+      } else {
+        reset = !(pg > -INFINITY);
+        lg = reset ? 0.f : pg * 1.4426950408889634f;
+      }
+    }
+    float F = lg;
+    int z = reset ? lane : -1;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float Fo = __shfl_up(F, off);
+      const int zo = __shfl_up(z, off);
+      if (lane >= off) {
+        F += Fo;
+        z = max(z, zo);
+      }
+    }
+    const float Flast = __shfl(F, C - 1);
+    const int zlast = __shfl(z, C - 1);
+    if (lane < C) {
+      Dd.F[lane] = F;
+      Dd.z[lane] = z;
+      Dd.gam[lane] = z < 0 ? exp2f(F) : 0.f;
+      Dd.bet[lane] = pvalid ? pb : 0.f;
+      Dd.dc[lane] = zlast <= lane ? exp2f(Flast - F) : 0.f;
+    }
+  };
+
   if (nch > 0) prefetch(0);
-  float cg = 0.f, cb = 0.f;     // decay/beta of the chunk being prepared
-  bool cvalid = false;
   for (int c = -1; c < nch; ++c) {
     const int nxt = (c + 1) & 1;
     const bool work = c + 1 < nch;
     // ================================================================ part 1
     if (work) {
       store_raw(nxt);
-      cg = pg; cb = pb; cvalid = pvalid;
+      if (pw == 0) scan(sm.der[nxt]);
       if (c + 2 < nch) prefetch(c + 2);
     }
-    __syncthreads();
+    lds_barrier();
     // ================================================================ part 2
     if (work) {
       const typename Sm::Raw& R = sm.raw[nxt];
       typename Sm::Derived& Dd = sm.der[nxt];
-      // scan: every prep wave keeps F_t (prefix sum of log2 gamma over non-zero
-      // gammas) and z_t (last zero index, -1 if none) of token t = lane
-      float lg = 0.f;
-      bool reset = false;
-      if (cvalid) {
-        if (p.decay_is_gamma) {
-          reset = !(cg > 0.f);
-          lg = reset ? 0.f : __log2f(cg);
-        } else {
-          reset = !(cg > -INFINITY);
-          lg = reset ? 0.f : cg * 1.4426950408889634f;
-        }
-      }
-      float F = lg;
-      int z = reset ? lane : -1;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float Fo = __shfl_up(F, off);
-        const int zo = __shfl_up(z, off);
-        if (lane >= off) {
-          F += Fo;
-          z = max(z, zo);
-        }
-      }
-      const float bt = cvalid ? cb : 0.f;
-      const float Flast = __shfl(F, C - 1);
-      const int zlast = __shfl(z, C - 1);
-      if (pw == 0 && lane < C) {
-        Dd.gam[lane] = z < 0 ? exp2f(F) : 0.f;
-        Dd.bet[lane] = bt;
-        Dd.dc[lane] = zlast <= lane ? exp2f(Flast - F) : 0.f;
-      }
-
-      // tiles: prep wave pw owns diagonal tile (pw, pw) and every NOFF-list
-      // off-diagonal tile whose index is pw mod 4
+      // tiles: prep wave pw owns diagonal tile (pw, pw) and every off-diagonal
+      // tile whose list index is pw mod 4
       auto gram_tile = [&](int i, int m, f4& kk, f4& qk) {
         kk = f4{0.f, 0.f, 0.f, 0.f};
         qk = f4{0.f, 0.f, 0.f, 0.f};
@@ -487,17 +489,19 @@ prefill_kernel(const PrefillParams p) {
           }
         }
       };
-      // decay factor D(t, s) for this lane's 4 rows t of tile i and column s of tile m
-      auto decay4 = [&](int i, int m, float d[4], float bt4[4]) {
+      // decay factor D(t, s) for this lane's rows t = 16i+4g+e and column
+      // s = 16m+x, and beta_t
+      auto decay4 = [&](int i, int m, float d[4], f4& bt4) {
         const int s = 16 * m + x;
-        const float Fs = __shfl(F, s);
+        const float Fs = Dd.F[s];
+        const f4 Ft = *reinterpret_cast<const f4*>(&Dd.F[16 * i + 4 * g]);
+        const int4 zt = *reinterpret_cast<const int4*>(&Dd.z[16 * i + 4 * g]);
+        bt4 = *reinterpret_cast<const f4*>(&Dd.bet[16 * i + 4 * g]);
+        const int zz[4] = {zt.x, zt.y, zt.z, zt.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 16 * i + 4 * g + e;
-          const float Ft = __shfl(F, t);
-          const int zt = __shfl(z, t);
-          bt4[e] = __shfl(bt, t);
-          d[e] = (s <= t && zt <= s) ? exp2f(Ft - Fs) : 0.f;
+          d[e] = (s <= t && zz[e] <= s) ? exp2f(Ft[e] - Fs) : 0.f;
         }
       };
 
@@ -505,37 +509,38 @@ prefill_kernel(const PrefillParams p) {
         const int i = pw;
         f4 kk, qk;
         gram_tile(i, i, kk, qk);
-        float d[4], bt4[4];
+        float d[4];
+        f4 bt4;
         decay4(i, i, d, bt4);
+        f4 acol;  // A[4g+e][x] of the diagonal block = row x of its transpose
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 16 * i + 4 * g + e;
           const int s = 16 * i + x;
           Dd.m[t][s] = from_f32<E>(d[e] * qk[e]);
-          sm.adiag[pw][4 * g + e][x] = (s < t) ? bt4[e] * d[e] * kk[e] : 0.f;
+          acol[e] = (s < t) ? bt4[e] * d[e] * kk[e] : 0.f;
         }
-        // column x of (I + A_ii)^-1 by forward substitution (lanes of group 0);
-        // the block was written by this wave only, so no barrier is needed
+        *reinterpret_cast<f4*>(&sm.adiagT[pw][x][4 * g]) = acol;
+        // column x of (I + A_ii)^-1, column sweep: once entry j is final,
+        // subtract its multiple from every later entry (a 16-step chain).
+        // The block was written by this wave only, so no barrier is needed.
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (g == 0) {
-          float col[16];
+        float col[16];
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            float acc = (rr == x) ? 1.f : 0.f;
+        for (int rr = 0; rr < 16; ++rr) col[rr] = (rr == x) ? 1.f : 0.f;
 #pragma unroll
-            for (int j4 = 0; j4 < rr; j4 += 4) {
-              const f4 arow = *reinterpret_cast<const f4*>(&sm.adiag[pw][rr][j4]);
+        for (int j = 0; j < 15; ++j) {
+          f4 aT[4];  // A[r][j] for r = 0..15
 #pragma unroll
-              for (int jj = 0; jj < 4; ++jj)
-                if (j4 + jj < rr) acc -= arow[jj] * col[j4 + jj];
-            }
-            col[rr] = acc;
-          }
+          for (int q4 = 0; q4 < 4; ++q4) aT[q4] = *reinterpret_cast<const f4*>(&sm.adiagT[pw][j][4 * q4]);
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) Dd.tinv[i][rr][x] = from_f32<E>(col[rr]);
+          for (int rr = j + 1; rr < 16; ++rr) col[rr] -= aT[rr >> 2][rr & 3] * col[j];
         }
+        // lane group g stores rows 4g .. 4g+3 of the column
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Dd.tinv[i][4 * g + e][x] = from_f32<E>(col[4 * g + e]);
       }
       for (int o = pw; o < NOFF; o += 4) {
         int i = 1, rem = o;
@@ -543,7 +548,8 @@ prefill_kernel(const PrefillParams p) {
         const int m = rem;  // m < i
         f4 kk, qk;
         gram_tile(i, m, kk, qk);
-        float d[4], bt4[4];
+        float d[4];
+        f4 bt4;
         decay4(i, m, d, bt4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -554,7 +560,7 @@ prefill_kernel(const PrefillParams p) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
