@@ -46,6 +46,11 @@
 // round trip.  The key index of the state tiles is permuted (dk_of) so that
 // the [Q; K] S0 product reads its A fragments as 16-byte LDS vectors.
 //
+// MFMA shapes: an accumulator chain never mixes 16x16x32 and 16x16x16 bf16
+// MFMAs.  With this compiler a 16x16x16 MFMA issued right after a 16x16x32
+// MFMA into the same accumulator was given no wait states and read a
+// partially written accumulator; keeping one shape per chain avoids that.
+//
 // Operand precision: bf16 inputs use bf16 MFMA operands (the state, U, X, M
 // and the inverse blocks are rounded to bf16 as operands; every accumulation,
 // the state itself and all decay/gate arithmetic are fp32).  fp32 inputs use
@@ -84,21 +89,27 @@ struct PrefillSmem {
   struct Raw {       // one chunk's inputs
     E q[C][LDK];
     E k[C][LDK];
-    E kt[DK][LDC];
+    E kt[DK][LDC];   // transposed K, 4-token groups XOR-swizzled per row
   };
   struct Derived {   // one chunk's prep results
     E negA[C][LDC];  // -A, off-diagonal 16x16 blocks only
-    E m[C][LDC];     // D o (Q K^T), lower-triangular blocks only
+    E m[C][LDC];     // scale * D o (Q K^T), lower-triangular blocks only
     E tinv[NT][16][LDT];
     alignas(16) float F[C];    // prefix sum of log2 gamma over non-zero gammas
     alignas(16) int z[C];      // last index <= t whose gamma is 0, or -1
-    alignas(16) float gam[C];  // Gam_t
     alignas(16) float bet[C];  // beta_t (0 on padded tokens)
+    alignas(16) float gb[C];   // beta_t Gam_t
+    alignas(16) float gs[C];   // scale Gam_t
     alignas(16) float dc[C];   // D(C-1, t)
+    float gC;                  // Gam_{C-1}
+    int any_zero;              // some gamma of the chunk is exactly 0
   };
   Raw raw[2];
   Derived der[2];
-  alignas(16) float adiagT[4][16][16];  // per prep wave: transposed fp32 diagonal block of A
+  // transposed fp32 diagonal blocks of A of the chunk being prepared:
+  // adiagT[i][s][t] = A[16i+t][16i+s]; rows padded so the 4 blocks' rows sit
+  // in different banks
+  alignas(16) float adiagT[4][16][20];
 };
 
 // Row r (0..15) of state tile j holds key index dk_of(j, r).  With pairs of
@@ -121,20 +132,26 @@ __device__ __forceinline__ void lds_frag8(const float* p, f4& a0, f4& a1) {
 }
 
 // Element e of a 16-byte vector of E.
-template <typename E> __device__ __forceinline__ E elem16(const uint4& v, int e);
-template <> __device__ __forceinline__ __bf16 elem16<__bf16>(const uint4& v, int e) {
-  const uint32_t word = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+template <typename E> __device__ __forceinline__ E elem16(const u32x4& v, int e);
+template <> __device__ __forceinline__ __bf16 elem16<__bf16>(const u32x4& v, int e) {
+  const uint32_t word = v[e >> 1];
   return __builtin_bit_cast(__bf16, (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu)));
 }
-template <> __device__ __forceinline__ float elem16<float>(const uint4& v, int e) {
-  const uint32_t word = e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
-  return __uint_as_float(word);
+template <> __device__ __forceinline__ float elem16<float>(const u32x4& v, int e) {
+  return __uint_as_float(v[e]);
 }
 
-// 4 elements of E packed from 4 separate E values (transposed LDS stores).
+// 4 elements of E packed for one LDS store.
 template <typename E> struct pack4;
 template <> struct pack4<__bf16> { typedef bf4 type; };
 template <> struct pack4<float> { typedef f4 type; };
+template <typename E>
+__device__ __forceinline__ typename pack4<E>::type to_pack4(f4 v) {
+  typename pack4<E>::type o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = from_f32<E>(v[e]);
+  return o;
+}
 
 template <typename E, int DK, int DVS, int C>
 __global__ void __launch_bounds__(512)
@@ -195,28 +212,48 @@ prefill_kernel(const PrefillParams p) {
   const float* __restrict__ gbet = p.beta + h;
   const int64_t st_base = (((int64_t)r * p.hv + h) * p.dv + v0) * DK;
 
+  // M is only written on and below the diagonal; the readout reads the 16x16
+  // blocks just above the diagonal as zeros, so clear M once.
+  for (int idx = tid; idx < 2 * C * Sm::LDC; idx += 512)
+    (&sm.der[idx / (C * Sm::LDC)].m[0][0])[idx % (C * Sm::LDC)] = from_f32<E>(0.f);
+
   // ------------------------------------------------------------ state waves
   // Every role runs its own loop with the same two barriers per chunk, so the
   // registers one role carries across chunks are not live in the other's.
   if (!is_prep) {
     const bool active = wave < NVT;  // waves beyond the slice only keep the barriers
     const int vc = 16 * wave + x;    // this lane's value column inside the slice
+    const int vst = (int)p.v_st, ost = (int)p.o_st;
+    const int v_lane = 4 * g * vst + x;  // lane part of the V / output offsets
+    const int o_lane = 4 * g * ost + x;
     f4 S[NKT];
     E vreg[NT][4];
 #pragma unroll
     for (int j = 0; j < NKT; ++j) S[j] = f4{0.f, 0.f, 0.f, 0.f};
-    auto load_v = [&](int c) {  // V(c) in accumulator layout: rows t = 16i+4g+e
+    // V(c) in accumulator layout (rows t = 16i+4g+e, column vc): buffer loads
+    // with the lane's offset fixed and the row in soffset; predicates only on
+    // the last (partial) chunk of a request
+    auto load_v = [&](int c) {
       const int64_t t0 = start + (int64_t)c * C;
-      const int rem = (int)min((int64_t)C, end - t0);
-      const E* vb = gv + t0 * p.v_st + vc;
-      const int vst = (int)p.v_st;
+      const int rem = (int)min((int64_t)C, end - t0);  // >= 1
+      const E* vb = gv + t0 * p.v_st + 16 * wave;
+      if (rem == C) {
+        const __amdgpu_buffer_rsrc_t rs = buf_rsrc(vb);
 #pragma unroll
-      for (int i = 0; i < NT; ++i)
+        for (int i = 0; i < NT; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * i + 4 * g + e;
-          vreg[i][e] = t < rem ? vb[t * vst] : from_f32<E>(0.f);
-        }
+          for (int e = 0; e < 4; ++e)
+            vreg[i][e] = buf_load<E>(rs, v_lane * (uint32_t)sizeof(E), (16 * i + e) * vst * (uint32_t)sizeof(E));
+      } else {
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 16 * i + 4 * g + e;
+            const E v = vb[min(t, rem - 1) * vst + x];  // clamped: inside the request
+            vreg[i][e] = t < rem ? v : from_f32<E>(0.f);
+          }
+      }
     };
     if (active) {
       if (p.init) {
@@ -231,118 +268,159 @@ prefill_kernel(const PrefillParams p) {
       const int cur = c & 1;
       const bool work = active && c >= 0;
       // ============================================================== part 1
+      // R = [Q; K] S0 with the key blocks outermost: 2*NT independent
+      // accumulator chains per block keep the MFMA pipe and LDS busy.
       if (work) {
         const typename Sm::Raw& R = sm.raw[cur];
         const typename Sm::Derived& Dd = sm.der[cur];
         Fr Sb[NKT];
 #pragma unroll
         for (int j = 0; j < NKT; ++j) cvt_frag(S[j], Sb[j]);
+        f4 rq[NT], rk[NT];
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
-          f4 rq = {0.f, 0.f, 0.f, 0.f}, rk = {0.f, 0.f, 0.f, 0.f};
-          if constexpr (NKT % 2 == 0) {
+        for (int i = 0; i < NT; ++i) rq[i] = rk[i] = f4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (NKT % 2 == 0) {
 #pragma unroll
-            for (int pp = 0; pp < NKT / 2; ++pp) {
-              Fr aq0, aq1, ak0, ak1;
-              lds_frag8(&R.q[16 * i + x][32 * pp + 8 * g], aq0, aq1);
-              lds_frag8(&R.k[16 * i + x][32 * pp + 8 * g], ak0, ak1);
-              rq = mma_k32(rq, aq0, aq1, Sb[2 * pp], Sb[2 * pp + 1]);
-              rk = mma_k32(rk, ak0, ak1, Sb[2 * pp], Sb[2 * pp + 1]);
+          for (int pp = 0; pp < NKT / 2; ++pp) {
+            Fr aq0[NT], aq1[NT], ak0[NT], ak1[NT];
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+              lds_frag8(&R.q[16 * i + x][32 * pp + 8 * g], aq0[i], aq1[i]);
+              lds_frag8(&R.k[16 * i + x][32 * pp + 8 * g], ak0[i], ak1[i]);
             }
-          } else {
 #pragma unroll
-            for (int j = 0; j < NKT; ++j) {
+            for (int i = 0; i < NT; ++i) {
+              rq[i] = mma_k32(rq[i], aq0[i], aq1[i], Sb[2 * pp], Sb[2 * pp + 1]);
+              rk[i] = mma_k32(rk[i], ak0[i], ak1[i], Sb[2 * pp], Sb[2 * pp + 1]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NKT; ++j) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
               Fr aq, ak;
               lds_frag(&R.q[16 * i + x][16 * j + 4 * g], aq);
               lds_frag(&R.k[16 * i + x][16 * j + 4 * g], ak);
-              rq = mma_k16(rq, aq, Sb[j]);
-              rk = mma_k16(rk, ak, Sb[j]);
+              rq[i] = mma_k16(rq[i], aq, Sb[j]);
+              rk[i] = mma_k16(rk[i], ak, Sb[j]);
             }
           }
+        }
+        // X = beta V - beta Gam R_K ; Y = scale Gam R_Q
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          const f4 bt = *reinterpret_cast<const f4*>(&Dd.bet[16 * i + 4 * g]);
+          const f4 gb = *reinterpret_cast<const f4*>(&Dd.gb[16 * i + 4 * g]);
+          const f4 gs = *reinterpret_cast<const f4*>(&Dd.gs[16 * i + 4 * g]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int t = 16 * i + 4 * g + e;
-            const float gm = Dd.gam[t];
-            X[i][e] = Dd.bet[t] * (to_f32(vreg[i][e]) - gm * rk[e]);
-            Y[i][e] = gm * rq[e];
+            X[i][e] = bt[e] * to_f32(vreg[i][e]) - gb[e] * rk[i][e];
+            Y[i][e] = gs[e] * rq[i][e];
           }
         }
         if (c + 1 < nch) load_v(c + 1);
       }
       lds_barrier();
       // ============================================================== part 2
+      // (I + A) U = X, right-looking over 16-token blocks: once U_m is known
+      // the products that consume it are issued (-A_im U_m for later blocks,
+      // M_im U_m for the readout, K^T D U for the state), paired over two
+      // token blocks where possible, so that only U_m -> P_{m+1} -> U_{m+1}
+      // is a dependent chain.
       if (work) {
         const typename Sm::Raw& R = sm.raw[cur];
         const typename Sm::Derived& Dd = sm.der[cur];
-        // (I + A) U = X by 16-token blocks: U_i = Tinv_i (X_i - sum_{m<i} A_im U_m)
-        f4 U[NT];
-        Fr Ub[NT];
+        const float gC = Dd.gC;
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
-          f4 P = X[i];
-#pragma unroll
-          for (int m = 0; m < i; ++m) {
-            Fr a;
-            lds_frag(&Dd.negA[16 * i + x][16 * m + 4 * g], a);
-            P = mma_k16(P, a, Ub[m]);
-          }
-          Fr Pb, ti;
-          cvt_frag(P, Pb);
-          lds_frag(&Dd.tinv[i][x][4 * g], ti);
-          U[i] = mma_k16(f4{0.f, 0.f, 0.f, 0.f}, ti, Pb);
-          cvt_frag(U[i], Ub[i]);
-        }
-        // Y += M U ; store
-        const int64_t tok0 = start + (int64_t)c * C;
-        const int nvalid = (int)min((int64_t)C, end - tok0);
-        E* ob = gout + tok0 * p.o_st + vc;
-        const int ost = (int)p.o_st;
-#pragma unroll
-        for (int i = 0; i < NT; ++i) {
-#pragma unroll
-          for (int m = 0; m <= i; ++m) {
-            Fr a;
-            lds_frag(&Dd.m[16 * i + x][16 * m + 4 * g], a);
-            Y[i] = mma_k16(Y[i], a, Ub[m]);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int t = 16 * i + 4 * g + e;
-            if (t < nvalid) ob[t * ost] = from_f32<E>(p.scale * Y[i][e]);
-          }
-        }
-        // S <- Gam_{C-1} S + K^T (D(C-1, .) U)
-        Fr DU[NT];
+        for (int j = 0; j < NKT; ++j) S[j] = gC * S[j];
+        Fr Ub[NT], DU[NT];
 #pragma unroll
         for (int m = 0; m < NT; ++m) {
-          f4 du;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) du[e] = Dd.dc[16 * m + 4 * g + e] * U[m][e];
-          cvt_frag(du, DU[m]);
-        }
-        const float gC = Dd.gam[C - 1];
-#pragma unroll
-        for (int j = 0; j < NKT; ++j) {
-          const int krow = dk_of<NKT>(j, x);
-          const int sw = kt_swz(krow);
-          f4 acc = gC * S[j];
+          Fr Pb, ti;
+          cvt_frag(X[m], Pb);
+          lds_frag(&Dd.tinv[m][x][4 * g], ti);
+          const f4 U = mma_k16(f4{0.f, 0.f, 0.f, 0.f}, ti, Pb);
+          cvt_frag(U, Ub[m]);
+          const f4 dc = *reinterpret_cast<const f4*>(&Dd.dc[16 * m + 4 * g]);
+          cvt_frag(dc * U, DU[m]);
           if constexpr (NT % 2 == 0) {
+            if ((m & 1) == 0) {
+              // the next block needs U_m now; the rest waits for the pair
+              Fr a;
+              lds_frag(&Dd.negA[16 * (m + 1) + x][16 * m + 4 * g], a);
+              X[m + 1] = mma_k16(X[m + 1], a, Ub[m]);
+            } else {
+              const int m0 = m - 1;
 #pragma unroll
-            for (int m = 0; m < NT; m += 2) {
-              Fr a0, a1;
-              lds_frag(&R.kt[krow][(16 * m + 4 * g) ^ sw], a0);
-              lds_frag(&R.kt[krow][(16 * m + 16 + 4 * g) ^ sw], a1);
-              acc = mma_k32(acc, a0, a1, DU[m], DU[m + 1]);
+              for (int i = m + 1; i < NT; ++i) {
+                Fr a0, a1;
+                lds_frag(&Dd.negA[16 * i + x][16 * m0 + 4 * g], a0);
+                lds_frag(&Dd.negA[16 * i + x][16 * m + 4 * g], a1);
+                X[i] = mma_k32(X[i], a0, a1, Ub[m0], Ub[m]);
+              }
+              // every readout update is a 32-deep product (the block above
+              // the diagonal, M[m0][m], is zero): one accumulator never mixes
+              // MFMA shapes (see the note at the top of this file)
+#pragma unroll
+              for (int i = m0; i < NT; ++i) {
+                Fr a0, a1;
+                lds_frag(&Dd.m[16 * i + x][16 * m0 + 4 * g], a0);
+                lds_frag(&Dd.m[16 * i + x][16 * m + 4 * g], a1);
+                Y[i] = mma_k32(Y[i], a0, a1, Ub[m0], Ub[m]);
+              }
+#pragma unroll
+              for (int j = 0; j < NKT; ++j) {
+                const int krow = dk_of<NKT>(j, x);
+                const int sw = kt_swz(krow);
+                Fr a0, a1;
+                lds_frag(&R.kt[krow][(16 * m0 + 4 * g) ^ sw], a0);
+                lds_frag(&R.kt[krow][(16 * m + 4 * g) ^ sw], a1);
+                S[j] = mma_k32(S[j], a0, a1, DU[m0], DU[m]);
+              }
             }
           } else {
 #pragma unroll
-            for (int m = 0; m < NT; ++m) {
+            for (int i = m + 1; i < NT; ++i) {
               Fr a;
-              lds_frag(&R.kt[krow][(16 * m + 4 * g) ^ sw], a);
-              acc = mma_k16(acc, a, DU[m]);
+              lds_frag(&Dd.negA[16 * i + x][16 * m + 4 * g], a);
+              X[i] = mma_k16(X[i], a, Ub[m]);
+            }
+#pragma unroll
+            for (int i = m; i < NT; ++i) {
+              Fr a;
+              lds_frag(&Dd.m[16 * i + x][16 * m + 4 * g], a);
+              Y[i] = mma_k16(Y[i], a, Ub[m]);
+            }
+#pragma unroll
+            for (int j = 0; j < NKT; ++j) {
+              const int krow = dk_of<NKT>(j, x);
+              Fr a;
+              lds_frag(&R.kt[krow][(16 * m + 4 * g) ^ kt_swz(krow)], a);
+              S[j] = mma_k16(S[j], a, DU[m]);
             }
           }
-          S[j] = acc;
+        }
+        // output rows (scale already folded into Gam and M)
+        const int64_t tok0 = start + (int64_t)c * C;
+        const int nvalid = (int)min((int64_t)C, end - tok0);
+        E* ob = gout + tok0 * p.o_st + 16 * wave;
+        if (nvalid == C) {
+          const __amdgpu_buffer_rsrc_t rs = buf_rsrc(ob);
+#pragma unroll
+          for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              buf_store(rs, o_lane * (uint32_t)sizeof(E), (16 * i + e) * ost * (uint32_t)sizeof(E),
+                        from_f32<E>(Y[i][e]));
+        } else {
+#pragma unroll
+          for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int t = 16 * i + 4 * g + e;
+              if (t < nvalid) ob[t * ost + x] = from_f32<E>(Y[i][e]);
+            }
         }
       }
       lds_barrier();
@@ -356,13 +434,13 @@ prefill_kernel(const PrefillParams p) {
   }
 
   // ------------------------------------------------------------- prep waves
-  uint4 pq[NPT][4], pk[NPT][4];
+  u32x4 pq[NPT][4], pk[NPT][4];
   float pg = 0.f, pb = 0.f;     // prefetched decay/beta of token `lane`
   bool pvalid = false;
 
   auto prefetch = [&](int c) {
     const int64_t t0 = start + (int64_t)c * C;
-    const int rem = (int)min((int64_t)C, end - t0);
+    const int rem = (int)min((int64_t)C, end - t0);  // >= 1
     const E* qb = gq + t0 * p.q_st;
     const E* kb = gk + t0 * p.k_st;
     const int qst = (int)p.q_st, kst = (int)p.k_st;
@@ -370,21 +448,31 @@ prefill_kernel(const PrefillParams p) {
     for (int u = 0; u < NPT; ++u) {
       const int pr = ptid + 256 * u;
       const int quad = pr / NOCT, oct = pr % NOCT;
+      if (pr < NPAIR) {
+        const __amdgpu_buffer_rsrc_t rq = buf_rsrc(qb), rk = buf_rsrc(kb);
+        const uint32_t lq = (uint32_t)((4 * quad * qst + oct * VE) * sizeof(E));
+        const uint32_t lk = (uint32_t)((4 * quad * kst + oct * VE) * sizeof(E));
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int t = 4 * quad + w;
-        uint4 vq = {0u, 0u, 0u, 0u}, vk = {0u, 0u, 0u, 0u};
-        if (pr < NPAIR && t < rem) {
-          vq = *reinterpret_cast<const uint4*>(qb + t * qst + oct * VE);
-          vk = *reinterpret_cast<const uint4*>(kb + t * kst + oct * VE);
+        for (int w = 0; w < 4; ++w) {
+          const int t = 4 * quad + w;
+          if (rem == C) {
+            pq[u][w] = buf_load16(rq, lq, w * qst * (uint32_t)sizeof(E));
+            pk[u][w] = buf_load16(rk, lk, w * kst * (uint32_t)sizeof(E));
+          } else {
+            const int tc = min(t, rem - 1);  // clamped: always inside the request
+            const u32x4 vq = *reinterpret_cast<const u32x4*>(qb + tc * qst + oct * VE);
+            const u32x4 vk = *reinterpret_cast<const u32x4*>(kb + tc * kst + oct * VE);
+            const uint32_t keep = t < rem ? 0xffffffffu : 0u;
+            pq[u][w] = vq & keep;
+            pk[u][w] = vk & keep;
+          }
         }
-        pq[u][w] = vq;
-        pk[u][w] = vk;
       }
     }
     pvalid = lane < rem;
-    pg = pvalid ? gdec[(t0 + lane) * p.hv] : 0.f;
-    pb = pvalid ? gbet[(t0 + lane) * p.hv] : 0.f;
+    const int tl = min(lane, rem - 1);
+    pg = gdec[(t0 + tl) * p.hv];
+    pb = gbet[(t0 + tl) * p.hv];
   };
 
   auto store_raw = [&](int buf) {
@@ -396,8 +484,8 @@ prefill_kernel(const PrefillParams p) {
         const int quad = pr / NOCT, oct = pr % NOCT;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          *reinterpret_cast<uint4*>(&R.q[4 * quad + w][oct * VE]) = pq[u][w];
-          *reinterpret_cast<uint4*>(&R.k[4 * quad + w][oct * VE]) = pk[u][w];
+          *reinterpret_cast<u32x4*>(&R.q[4 * quad + w][oct * VE]) = pq[u][w];
+          *reinterpret_cast<u32x4*>(&R.k[4 * quad + w][oct * VE]) = pk[u][w];
         }
         // transposed K: for each key of the vector, 4 consecutive tokens
 #pragma unroll
@@ -439,125 +527,168 @@ prefill_kernel(const PrefillParams p) {
     const float Flast = __shfl(F, C - 1);
     const int zlast = __shfl(z, C - 1);
     if (lane < C) {
+      const float gam = z < 0 ? exp2f(F) : 0.f;
+      const float bt = pvalid ? pb : 0.f;
       Dd.F[lane] = F;
       Dd.z[lane] = z;
-      Dd.gam[lane] = z < 0 ? exp2f(F) : 0.f;
-      Dd.bet[lane] = pvalid ? pb : 0.f;
+      Dd.bet[lane] = bt;
+      Dd.gb[lane] = bt * gam;
+      Dd.gs[lane] = p.scale * gam;
       Dd.dc[lane] = zlast <= lane ? exp2f(Flast - F) : 0.f;
+      if (lane == C - 1) {
+        Dd.gC = gam;
+        Dd.any_zero = zlast >= 0;
+      }
     }
+  };
+
+  // Inverses of the four unit-lower diagonal blocks (I + A_ii) of chunk c, one
+  // block per lane group: lane (x, i) computes row x of T_i = (I + A_ii)^-1 by
+  // back substitution on the transposed block, T_i[x][j] = [j == x] -
+  // sum_{k > j} A_i[k][j] T_i[x][k] for j = 15 .. 0, and stores it as one row.
+  auto invert_diag = [&](typename Sm::Derived& Dd) {
+    const int i = g;
+    if (i >= NT) return;
+    float row[16];
+    f4 cur[4], nx[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) cur[q4] = *reinterpret_cast<const f4*>(&sm.adiagT[i][15][4 * q4]);
+#pragma unroll
+    for (int j = 15; j >= 0; --j) {
+      if (j > 0) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) nx[q4] = *reinterpret_cast<const f4*>(&sm.adiagT[i][j - 1][4 * q4]);
+      }
+      // cur[k/4][k%4] = A_i[k][j]
+      float a0 = (j == x) ? 1.f : 0.f, a1 = 0.f;
+#pragma unroll
+      for (int k = 15; k > j + 1; --k) {
+        if (k & 1) a1 -= cur[k >> 2][k & 3] * row[k];
+        else a0 -= cur[k >> 2][k & 3] * row[k];
+      }
+      row[j] = j < 15 ? (a0 + a1) - cur[(j + 1) >> 2][(j + 1) & 3] * row[j + 1] : a0;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nx[q4];
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      *reinterpret_cast<typename pack4<E>::type*>(&Dd.tinv[i][x][4 * q4]) =
+          to_pack4<E>(f4{row[4 * q4], row[4 * q4 + 1], row[4 * q4 + 2], row[4 * q4 + 3]});
   };
 
   if (nch > 0) prefetch(0);
   for (int c = -1; c < nch; ++c) {
-    const int nxt = (c + 1) & 1;
+    const int cur = c & 1, nxt = (c + 1) & 1;
     const bool work = c + 1 < nch;
     // ================================================================ part 1
     if (work) {
       store_raw(nxt);
       if (pw == 0) scan(sm.der[nxt]);
-      if (c + 2 < nch) prefetch(c + 2);
     }
+    // the diagonal blocks of chunk c (staged in the previous part 2)
+    if (pw == 1 && c >= 0) invert_diag(sm.der[cur]);
+    if (work && c + 2 < nch) prefetch(c + 2);
     lds_barrier();
     // ================================================================ part 2
     if (work) {
       const typename Sm::Raw& R = sm.raw[nxt];
       typename Sm::Derived& Dd = sm.der[nxt];
-      // tiles: prep wave pw owns diagonal tile (pw, pw) and every off-diagonal
-      // tile whose list index is pw mod 4
-      auto gram_tile = [&](int i, int m, f4& kk, f4& qk) {
-        kk = f4{0.f, 0.f, 0.f, 0.f};
-        qk = f4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (NKT % 2 == 0) {
+      // Tiles of K K^T and K Q^T computed transposed -- rows s (key token),
+      // columns t (query token) -- so that each lane (t = 16i + x) ends with
+      // 4 consecutive s of row t and stores -A and M rows as vectors.  Prep
+      // wave pw owns diagonal tile (pw, pw) (slot 0) and the off-diagonal
+      // tiles whose list index is pw mod 4 (slots 1..); all of a wave's tiles
+      // share one pass over the key blocks.
+      constexpr int MT = 1 + (NOFF + 3) / 4;
+      int ti[MT], tm[MT];
+      bool tv[MT];
+      ti[0] = tm[0] = pw;
+      tv[0] = pw < NT;
 #pragma unroll
-          for (int pp = 0; pp < NKT / 2; ++pp) {
-            Fr ak0, ak1, aq0, aq1, b0, b1;
-            lds_frag8(&R.k[16 * i + x][32 * pp + 8 * g], ak0, ak1);
-            lds_frag8(&R.q[16 * i + x][32 * pp + 8 * g], aq0, aq1);
-            lds_frag8(&R.k[16 * m + x][32 * pp + 8 * g], b0, b1);
-            kk = mma_k32(kk, ak0, ak1, b0, b1);
-            qk = mma_k32(qk, aq0, aq1, b0, b1);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < NKT; ++j) {
-            Fr ak, aq, b;
-            lds_frag(&R.k[16 * i + x][16 * j + 4 * g], ak);
-            lds_frag(&R.q[16 * i + x][16 * j + 4 * g], aq);
-            lds_frag(&R.k[16 * m + x][16 * j + 4 * g], b);
-            kk = mma_k16(kk, ak, b);
-            qk = mma_k16(qk, aq, b);
-          }
-        }
-      };
-      // decay factor D(t, s) for this lane's rows t = 16i+4g+e and column
-      // s = 16m+x, and beta_t
-      auto decay4 = [&](int i, int m, float d[4], f4& bt4) {
-        const int s = 16 * m + x;
-        const float Fs = Dd.F[s];
-        const f4 Ft = *reinterpret_cast<const f4*>(&Dd.F[16 * i + 4 * g]);
-        const int4 zt = *reinterpret_cast<const int4*>(&Dd.z[16 * i + 4 * g]);
-        bt4 = *reinterpret_cast<const f4*>(&Dd.bet[16 * i + 4 * g]);
-        const int zz[4] = {zt.x, zt.y, zt.z, zt.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * i + 4 * g + e;
-          d[e] = (s <= t && zz[e] <= s) ? exp2f(Ft[e] - Fs) : 0.f;
-        }
-      };
-
-      if (pw < NT) {
-        const int i = pw;
-        f4 kk, qk;
-        gram_tile(i, i, kk, qk);
-        float d[4];
-        f4 bt4;
-        decay4(i, i, d, bt4);
-        f4 acol;  // A[4g+e][x] of the diagonal block = row x of its transpose
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * i + 4 * g + e;
-          const int s = 16 * i + x;
-          Dd.m[t][s] = from_f32<E>(d[e] * qk[e]);
-          acol[e] = (s < t) ? bt4[e] * d[e] * kk[e] : 0.f;
-        }
-        *reinterpret_cast<f4*>(&sm.adiagT[pw][x][4 * g]) = acol;
-        // column x of (I + A_ii)^-1, column sweep: once entry j is final,
-        // subtract its multiple from every later entry (a 16-step chain).
-        // The block was written by this wave only, so no barrier is needed.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        float col[16];
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) col[rr] = (rr == x) ? 1.f : 0.f;
-#pragma unroll
-        for (int j = 0; j < 15; ++j) {
-          f4 aT[4];  // A[r][j] for r = 0..15
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) aT[q4] = *reinterpret_cast<const f4*>(&sm.adiagT[pw][j][4 * q4]);
-#pragma unroll
-          for (int rr = j + 1; rr < 16; ++rr) col[rr] -= aT[rr >> 2][rr & 3] * col[j];
-        }
-        // lane group g stores rows 4g .. 4g+3 of the column
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Dd.tinv[i][4 * g + e][x] = from_f32<E>(col[4 * g + e]);
-      }
-      for (int o = pw; o < NOFF; o += 4) {
+      for (int k = 1; k < MT; ++k) {
+        const int o = pw + 4 * (k - 1);
         int i = 1, rem = o;
         while (rem >= i) { rem -= i; ++i; }
-        const int m = rem;  // m < i
-        f4 kk, qk;
-        gram_tile(i, m, kk, qk);
-        float d[4];
-        f4 bt4;
-        decay4(i, m, d, bt4);
+        ti[k] = i;
+        tm[k] = rem;
+        tv[k] = o < NOFF;
+      }
+      f4 kk[MT], qk[MT];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * i + 4 * g + e;
-          const int s = 16 * m + x;
-          Dd.m[t][s] = from_f32<E>(d[e] * qk[e]);
-          Dd.negA[t][s] = from_f32<E>(-bt4[e] * d[e] * kk[e]);
+      for (int k = 0; k < MT; ++k) kk[k] = qk[k] = f4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (NKT % 2 == 0) {
+#pragma unroll
+        for (int pp = 0; pp < NKT / 2; ++pp) {
+#pragma unroll
+          for (int k = 0; k < MT; ++k) {
+            if (!tv[k]) continue;
+            Fr as0, as1, bk0, bk1, bq0, bq1;
+            lds_frag8(&R.k[16 * tm[k] + x][32 * pp + 8 * g], as0, as1);
+            lds_frag8(&R.k[16 * ti[k] + x][32 * pp + 8 * g], bk0, bk1);
+            lds_frag8(&R.q[16 * ti[k] + x][32 * pp + 8 * g], bq0, bq1);
+            kk[k] = mma_k32(kk[k], as0, as1, bk0, bk1);
+            qk[k] = mma_k32(qk[k], as0, as1, bq0, bq1);
+          }
         }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NKT; ++j) {
+#pragma unroll
+          for (int k = 0; k < MT; ++k) {
+            if (!tv[k]) continue;
+            Fr as, bk, bq;
+            lds_frag(&R.k[16 * tm[k] + x][16 * j + 4 * g], as);
+            lds_frag(&R.k[16 * ti[k] + x][16 * j + 4 * g], bk);
+            lds_frag(&R.q[16 * ti[k] + x][16 * j + 4 * g], bq);
+            kk[k] = mma_k16(kk[k], as, bk);
+            qk[k] = mma_k16(qk[k], as, bq);
+          }
+        }
+      }
+      const bool any_zero = Dd.any_zero;
+      // D(t, s) for this lane's row t = 16i+x and columns s = 16m+4g+e
+      auto decay4 = [&](int i, int m, bool diag) -> f4 {
+        const int t = 16 * i + x;
+        const float Ft = Dd.F[t];
+        const f4 Fs = *reinterpret_cast<const f4*>(&Dd.F[16 * m + 4 * g]);
+        f4 d;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = exp2f(Ft - Fs[e]);
+        if (diag) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) d[e] = (16 * m + 4 * g + e <= t) ? d[e] : 0.f;
+        }
+        if (any_zero) {  // a gamma of 0 between s and t cuts the product
+          const int zt = Dd.z[t];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) d[e] = (zt <= 16 * m + 4 * g + e) ? d[e] : 0.f;
+        }
+        return d;
+      };
+      // off-diagonal tiles: M and -A
+#pragma unroll
+      for (int k = 1; k < MT; ++k) {
+        if (!tv[k]) continue;
+        const int t = 16 * ti[k] + x;
+        const f4 d = decay4(ti[k], tm[k], false);
+        const float bt = Dd.bet[t];
+        *reinterpret_cast<typename pack4<E>::type*>(&Dd.m[t][16 * tm[k] + 4 * g]) =
+            to_pack4<E>(p.scale * d * qk[k]);
+        *reinterpret_cast<typename pack4<E>::type*>(&Dd.negA[t][16 * tm[k] + 4 * g]) =
+            to_pack4<E>(-bt * d * kk[k]);
+      }
+      // diagonal tile: M, and A_ii (fp32, transposed) for the inverse that the
+      // next staging part computes
+      if (tv[0]) {
+        const int i = pw;
+        const int t = 16 * i + x;
+        const f4 d = decay4(i, i, true);
+        const float bt = Dd.bet[t];
+        *reinterpret_cast<typename pack4<E>::type*>(&Dd.m[t][16 * i + 4 * g]) =
+            to_pack4<E>(p.scale * d * qk[0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sm.adiagT[i][4 * g + e][x] = (4 * g + e < x) ? bt * d[e] * kk[0][e] : 0.f;
       }
     }
     lds_barrier();
