@@ -12,12 +12,24 @@ from HIP events recorded on the launch stream; `value` is prefill tokens/s
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--only prefill|decode] [--copy-calib]
+    python bench.py --summarize-traffic FETCH.csv WRITE.csv   (no GPU)
 
 Prints one JSON line.
+
+HBM traffic.  `roofline.traffic` and `decode.traffic` come from two
+rocprofv3 counter runs of this script with --copy-calib (one collecting
+FETCH_SIZE, one WRITE_SIZE); each counter is scaled by what it reads for a
+plain 1 GiB streaming pass (torch.neg: 1 GiB read, 1 GiB written).  --summarize-traffic
+turns the two counter CSVs into profiles/hbm_traffic_prefill_b4s4096_decode_b256.json, stamped with a hash
+of the kernel sources; a later run reports the traffic only while that hash
+still matches, and null otherwise.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -33,6 +45,71 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 
 METRIC = "GDN prefill tokens/s (B4×S4096,Hv32,d128) + decode state HBM GB/s % of peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_b4s4096_decode_b256.json")
+CALIB_BYTES = 2 * (1 << 30)   # the calibration copy reads 1 GiB and writes 1 GiB
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP/C++ sources of libgdn (any change invalidates traffic)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_deltanet_state_delta_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _counter_means(path, counter):
+    """Mean counter value (KiB for FETCH_SIZE/WRITE_SIZE) per kernel family."""
+    vals = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        name = r["Kernel_Name"]
+        if "prefill_kernel" in name:
+            key = "prefill"
+        elif "decode_kernel" in name:
+            key = "decode"
+        elif "gate_kernel" in name:
+            key = "gate"
+        elif "neg_kernel" in name:
+            key = "copy"
+        else:
+            continue
+        vals.setdefault(key, []).append(float(r["Counter_Value"]))
+    out = {k: statistics.mean(v) for k, v in vals.items() if k != "copy"}
+    if "copy" in vals:
+        out["copy"] = max(vals["copy"])
+    return out
+
+
+def summarize_traffic(fetch_csv, write_csv):
+    f = _counter_means(fetch_csv, "FETCH_SIZE")
+    w = _counter_means(write_csv, "WRITE_SIZE")
+    # the copy reads and writes 1 GiB each: scale each counter separately
+    f_scale = (CALIB_BYTES / 2) / (f["copy"] * 1024.0)
+    w_scale = (CALIB_BYTES / 2) / (w["copy"] * 1024.0)
+    res = {"source_hash": kernel_source_hash(), "calibration_copy_bytes": CALIB_BYTES,
+           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    for k in ("prefill", "decode", "gate"):
+        if k in f and k in w:
+            rb = f[k] * 1024.0 * f_scale
+            wb = w[k] * 1024.0 * w_scale
+            res["kernels"][k] = {"fetch_kib_raw": f[k], "write_kib_raw": w[k],
+                                 "read_bytes": rb, "write_bytes": wb, "bytes": rb + wb}
+    return res
+
+
+def load_traffic(kernel):
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k["bytes"]
 
 
 def prefill_algorithmic(T, hq, hv, dk, dv, n_seqs, chunk, io_bytes=2):
@@ -95,7 +172,11 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+    if args.summarize_traffic:
+        print(json.dumps(summarize_traffic(*args.summarize_traffic), indent=1))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -175,11 +256,12 @@ def main():
     wall = time.perf_counter() - t0
 
     if args.copy_calib:
+        # a plain streaming pass over known bytes: reads 1 GiB, writes 1 GiB
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
 
     timed = ev[args.warmup:]
@@ -204,7 +286,7 @@ def main():
         tfl = pf / (pm * 1e-3) / 1e12
         res["roofline"] = {"kernel": "prefill_kernel<bf16,128,64,64>", "bound": "hbm",
                            "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                           "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic("prefill"),
                            "algorithmic_bytes": pb, "algorithmic_flops": pf,
                            "mfma_tflops": tfl, "mfma_peak_tflops": BF16_PEAK_TFLOPS,
                            "mfma_frac": tfl / BF16_PEAK_TFLOPS, "avg_ms": pm}
@@ -217,12 +299,13 @@ def main():
         gbs = db_ / (dm * 1e-3) / 1e9
         res["decode"] = {"kernel": "decode_kernel<bf16,128,128,32>", "bound": "hbm",
                          "ms": dm, "ms_min": min(dec_ms), "algorithmic_bytes": db_,
+                         "traffic": load_traffic("decode"),
                          "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS}
         if not do_prefill:
             res["value"] = gbs
             res["unit"] = "GB/s"
-            res["roofline"] = dict(res["decode"], traffic=None)
+            res["roofline"] = dict(res["decode"])
 
     if not args.no_cpu_baseline and do_prefill:
         res["cpu_baseline"] = cpu_baseline_prefill(px)
