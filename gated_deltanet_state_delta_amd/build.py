@@ -23,6 +23,13 @@ LIB = os.path.join(PKG, "libgdn.so")
 ARCH = "gfx950"
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-file device flags.  The pair-role prefill runs one wave per SIMD, so its
+# speed depends on latency hiding inside each wave: its MFMA accumulators stay
+# in VGPRs (its state is scaled and converted by VALU code every chunk, and
+# accumulators in AGPRs would cost a copy each way), and the ILP-oriented
+# scheduler is used (about 18% faster than the default on B4 x S4096).
+FILE_FLAGS = {"gdn_prefill_pair.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form",
+                                     "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Wno-unused-function", "-Wno-unused-variable", "-I", os.path.join(ROOT, "include")]
 
@@ -40,7 +47,8 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + COMMON + DEVICE_FLAGS + ["-c", src, "-o", obj]
+    extra = FILE_FLAGS.get(os.path.basename(src), [])
+    cmd = [hipcc()] + COMMON + DEVICE_FLAGS + extra + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [hipcc()] + COMMON + ["-x", "hip"] + DEVICE_FLAGS + ["-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)

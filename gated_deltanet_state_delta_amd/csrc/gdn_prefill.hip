@@ -1,10 +1,14 @@
-// gdn_prefill.hip -- host dispatch of the chunked prefill kernel.
+// gdn_prefill.hip -- host dispatch of the chunked prefill.
 //
-// Picks the chunk -- the ONNX card's chunk_size is a scheduling hint that
-// never changes the result: 0 means 64, and a hint is lowered to the largest
-// chunk whose double-buffered working set fits one workgroup's LDS (for fp32
-// operands with dk = 128 that is 32) -- and the (dk, dv) instantiation.
+// bf16 problems with dk, dv in {64, 128} and the default chunk go to the
+// pair-role kernel (gdn_prefill_pair.hpp).  Everything else goes to
+// prefill_kernel (gdn_prefill.hpp), which picks the chunk -- the ONNX card's
+// chunk_size is a scheduling hint that never changes the result: 0 means 64,
+// and a hint is lowered to the largest chunk whose double-buffered working
+// set fits one workgroup's LDS (for fp32 operands with dk = 128 that is 32)
+// -- and the (dk, dv) instantiation.
 #include "gdn_prefill.hpp"
+#include "gdn_prefill_pair.hpp"
 
 namespace gdn {
 
@@ -22,6 +26,7 @@ hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream) {
   p.decay_is_gamma = a.decay_kind == GDN_DECAY_GAMMA;
   p.scale = a.scale;
   const bool bf = a.io_dtype == GDN_BF16;
+  if (bf && prefill_pair_supported(a.dk, a.dv, a.chunk_size)) return prefill_pair_bf16(p, a.dk, stream);
   const int hint = a.chunk_size != 0 ? a.chunk_size : 64;
   const int c = bf ? prefill_chunk_for<__bf16>(a.dk, a.dv, hint)
                    : prefill_chunk_for<float>(a.dk, a.dv, hint);

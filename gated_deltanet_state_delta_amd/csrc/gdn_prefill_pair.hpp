@@ -1,0 +1,641 @@
+// gdn_prefill_pair.hpp -- chunked prefill for bf16 inputs with dk, dv in
+// {64, 128} and 64-token chunks (gfx950).
+//
+// Same chunked form of the "Gated DeltaNet State Update" recurrence as
+// prefill_kernel (gdn_prefill.hpp has the derivation): inside a chunk,
+// (I + A) U = X with A_ts = beta_t D(t,s) k_t.k_s and X = beta (V - Gam K S0),
+// Y = scale (Gam Q S0 + (D o Q K^T) U), S_C = Gam_{C-1} S0 + K^T (D(C-1,.) U).
+// Only the schedule differs; it is built for this case:
+//
+//  * one workgroup of 4 waves -- one per SIMD, so each may hold up to 512
+//    registers -- per (request, value head, 64-column slice of the state);
+//  * state waves 0 and 1 each own 32 value columns (two 16-column MFMA
+//    tiles), so every Q, K and K^T fragment read from LDS feeds two MFMAs;
+//    they run [Q; K] S0, the block forward substitution, Y += M U and the
+//    state update for chunk c, and write the outputs through LDS as 16-byte
+//    rows;
+//  * prep waves 2 and 3 prepare chunk c+1 meanwhile.  Each loads half of the
+//    chunk's Q, K and V rows (two chunks ahead: token-strided loads have a
+//    long latency) and stages them in LDS; after an LDS counter shows both
+//    halves written, wave 2 computes the four diagonal 16x16 Gram tiles, the
+//    M blocks on the diagonal and the inverses of the unit-lower blocks
+//    I + A_ii (right-looking, so each step is a set of independent FMAs) and
+//    the per-token factors, while wave 3 computes the six off-diagonal tiles
+//    and their -A and M blocks, with the decay D(t,s) factored into three
+//    per-tile factors <= 1 unless the chunk holds a gamma of exactly 0;
+//  * one workgroup barrier per chunk: the state waves read buffer c & 1 while
+//    the prep waves fill buffer (c+1) & 1.
+// K^T fragments for the state update, V in accumulator layout and the output
+// rows come from LDS through the gfx950 transposing LDS read
+// (ds_read_b64_tr_b16): lane 4a+b of a 16-lane group receives element b of
+// the 8-byte block addressed by lane a+4e as its element e.
+//
+// LDS rows of Q and K hold 16-byte slots permuted by an XOR of the row
+// (slot ^ f(row)), so fragment reads of 8 consecutive rows hit 8 distinct
+// bank groups.  All accumulator chains use one MFMA shape (see the note in
+// gdn_prefill.hpp).
+#pragma once
+
+#include "gdn_prefill.hpp"
+
+namespace gdn {
+
+template <int DK>
+struct PairSmem {
+  static constexpr int C = 64, NT = 4, DVS = 64;
+  static constexpr int LDV = DVS + 16;  // 160-byte V rows
+  static constexpr int LDC = C + 4;     // 136-byte -A / M rows
+  static constexpr int LDT = 20;        // 40-byte inverse rows
+  struct Buf {
+    __bf16 q[C][DK];      // slot-swizzled rows
+    __bf16 k[C][DK];
+    __bf16 v[C][LDV];
+    __bf16 negA[C][LDC];  // -A, off-diagonal 16x16 blocks
+    __bf16 m[C][LDC];     // scale D o Q K^T, blocks on and below the diagonal
+    __bf16 tinv[NT][16][LDT];
+    alignas(16) float bet[C];  // beta_t (0 on padded tokens)
+    alignas(16) float gb[C];   // beta_t Gam_t
+    alignas(16) float gs[C];   // scale Gam_t
+    alignas(16) float dc[C];   // D(C-1, t)
+    float gC;                  // Gam_{C-1}
+  };
+  struct Scan {                // decay scan of the chunk being prepared (per prep wave)
+    alignas(16) float F[C];    // prefix sum of log2 gamma over non-zero gammas
+    alignas(16) int z[C];      // last index <= t whose gamma is 0, or -1
+    alignas(16) float bt[C];   // beta_t (0 on padded tokens)
+    alignas(16) float E[C];    // 2^(F_t - F at the start of t's 16-token tile)
+    alignas(16) float Fx[C];   // 2^(F at the end of t's 16-token tile - F_t)
+  };
+  alignas(16) Buf buf[2];
+  Scan scan[2];  // one per prep wave
+  // rows of the fp32 diagonal blocks of A (wave 2 only): block i, row r at
+  // 20 r (padded rows and blocks keep the row reads of the four blocks on
+  // distinct banks)
+  alignas(16) float adiag[4][16 * 20 + 4];
+  // outputs of state wave w, transposed: column c (of its 32), token t at
+  // yt[w][64 c + 4 ((t / 4) ^ f(c)) + t % 4]
+  alignas(16) __bf16 yt[2][32 * 64];
+  int prep_cnt;  // staging halves written by the prep waves so far
+};
+
+// 16-byte slot permutation of a Q/K row.
+__device__ __forceinline__ int pair_swz(int row, int slot) {
+  return slot ^ (((row & 1) << 2) | ((row >> 1) & 3));
+}
+// 8-byte block permutation of an output column (4 tokens per block).
+__device__ __forceinline__ int yt_swz(int col) { return ((col & 3) << 2) | ((col >> 2) & 3); }
+
+typedef __attribute__((address_space(3))) s4 lds_s4;
+
+// Transposing LDS read (see the header comment).
+__device__ __forceinline__ bf4 lds_tr(const __bf16* p) {
+  return __builtin_bit_cast(bf4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p)));
+}
+__device__ __forceinline__ bf4 lds_b64(const __bf16* p) { return *reinterpret_cast<const bf4*>(p); }
+__device__ __forceinline__ bf8 lds_b128(const __bf16* p) { return *reinterpret_cast<const bf8*>(p); }
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, bf2));
+}
+__device__ __forceinline__ bf4 to_bf4(f4 v) {
+  return __builtin_bit_cast(bf4, (u32x2){pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3])});
+}
+__device__ __forceinline__ f4 bf4_to_f4(bf4 v) {
+  return f4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f4 mfma32(f4 acc, bf8 a, bf8 b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ bf8 cat8(bf4 lo, bf4 hi) {
+  return bf8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// DPP moves: lanes whose row is not in ROWMASK (or whose source lane lies
+// outside the row for the shifts) receive `fill`.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_f(float fill, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(v), CTRL, ROWMASK, 0xF, false));
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int dpp_i(int fill, int v) {
+  return __builtin_amdgcn_update_dpp(fill, v, CTRL, ROWMASK, 0xF, false);
+}
+// Inclusive wave-wide scans (sum, max) in lane order: shifts within 16-lane
+// rows (row_shr 1, 2, 4, 8), then the row totals carried across rows
+// (row_bcast 15 into rows 1 and 3, row_bcast 31 into rows 2 and 3).
+__device__ __forceinline__ float wave_scan_add(float v) {
+  v += dpp_f<0x111, 0xF>(0.f, v);
+  v += dpp_f<0x112, 0xF>(0.f, v);
+  v += dpp_f<0x114, 0xF>(0.f, v);
+  v += dpp_f<0x118, 0xF>(0.f, v);
+  v += dpp_f<0x142, 0xA>(0.f, v);
+  v += dpp_f<0x143, 0xC>(0.f, v);
+  return v;
+}
+__device__ __forceinline__ int wave_scan_max(int v) {
+  v = max(v, dpp_i<0x111, 0xF>(-1, v));
+  v = max(v, dpp_i<0x112, 0xF>(-1, v));
+  v = max(v, dpp_i<0x114, 0xF>(-1, v));
+  v = max(v, dpp_i<0x118, 0xF>(-1, v));
+  v = max(v, dpp_i<0x142, 0xA>(-1, v));
+  v = max(v, dpp_i<0x143, 0xC>(-1, v));
+  return v;
+}
+
+// One prep wave's half of a chunk, as loaded from global memory: Q and K
+// tiles 2pw and 2pw+1 (16-byte fragment rows: row 16i + x, keys 32pp + 8g
+// .. +7), V rows 32pw .. 32pw+31 (row 32pw + 8u + lane/8, columns 8 (lane % 8)
+// .. +7), and the gate of token `lane`.  (Loads of 16 rows x 64 bytes measured
+// faster here than loads of 4 rows x 256 bytes.)
+template <int DK>
+struct PairPrepSet {
+  static constexpr int NPP = DK / 32;
+  u32x4 q[2][NPP];
+  u32x4 k[2][NPP];
+  u32x4 v[4];
+  float gd, bt;
+};
+
+// Prep wave PW of the pair kernel (see the header comment).
+template <int DK, int PW>
+__device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& sm, int64_t start,
+                                          int64_t end, int nch, const __bf16* gq, const __bf16* gk,
+                                          const __bf16* gv, const float* gdec, const float* gbet) {
+  typedef PairSmem<DK> Sm;
+  constexpr int C = 64, NPP = DK / 32;
+  const int lane = threadIdx.x & 63, x = lane & 15, g = lane >> 4;
+
+  auto prefetch = [&](int c, PairPrepSet<DK>& s) {
+    const int64_t t0 = start + (int64_t)c * C;
+    const int rem = (int)min((int64_t)C, end - t0);  // >= 1
+    {
+      const int tl = min(lane, rem - 1);
+      const float gd = gdec[(t0 + tl) * p.hv], bt = gbet[(t0 + tl) * p.hv];
+      // padded tokens: no decay (log-decay 0 / gamma 1) and beta 0
+      s.gd = lane < rem ? gd : (p.decay_is_gamma ? 1.f : 0.f);
+      s.bt = lane < rem ? bt : 0.f;
+    }
+    const __bf16* qb = gq + t0 * p.q_st;
+    const __bf16* kb = gk + t0 * p.k_st;
+    const __bf16* vb = gv + t0 * p.v_st;
+    const int qst = (int)p.q_st, kst = (int)p.k_st, vst = (int)p.v_st;
+    if (rem == C) {
+      const __amdgpu_buffer_rsrc_t rq = buf_rsrc(qb), rk = buf_rsrc(kb), rv = buf_rsrc(vb);
+      const uint32_t lq = (uint32_t)((x * qst + 8 * g) * 2), lk = (uint32_t)((x * kst + 8 * g) * 2);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int pp = 0; pp < NPP; ++pp) {
+          s.q[i][pp] = buf_load16(rq, lq, (uint32_t)((16 * (2 * PW + i) * qst + 32 * pp) * 2));
+          s.k[i][pp] = buf_load16(rk, lk, (uint32_t)((16 * (2 * PW + i) * kst + 32 * pp) * 2));
+        }
+      const uint32_t lv = (uint32_t)(((lane >> 3) * vst + 8 * (lane & 7)) * 2);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s.v[u] = buf_load16(rv, lv, (uint32_t)((32 * PW + 8 * u) * vst * 2));
+    } else {
+      auto ld = [&](const __bf16* base, int st, int row, int col) -> u32x4 {
+        const u32x4 val = *reinterpret_cast<const u32x4*>(base + (int64_t)min(row, rem - 1) * st + col);
+        return val & (row < rem ? 0xffffffffu : 0u);
+      };
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int pp = 0; pp < NPP; ++pp) {
+          s.q[i][pp] = ld(qb, qst, 16 * (2 * PW + i) + x, 32 * pp + 8 * g);
+          s.k[i][pp] = ld(kb, kst, 16 * (2 * PW + i) + x, 32 * pp + 8 * g);
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s.v[u] = ld(vb, vst, 32 * PW + 8 * u + (lane >> 3), 8 * (lane & 7));
+    }
+  };
+
+  auto frag_col = [&](int row, int pp) -> int { return 8 * pair_swz(row, 4 * pp + g); };
+
+  int staged = 0;  // chunks staged by this wave so far
+  // One iteration: prepare chunk c+1 from `s`, then refill `s` with chunk c+3.
+  auto iter = [&](int c, PairPrepSet<DK>& s) {
+    if (c + 1 < nch) {
+      typename Sm::Buf& B = sm.buf[(c + 1) & 1];
+      // ---- stage this wave's half
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int pp = 0; pp < NPP; ++pp) {
+          const int r = 16 * (2 * PW + i) + x;
+          *reinterpret_cast<u32x4*>(&B.q[r][frag_col(r, pp)]) = s.q[i][pp];
+          *reinterpret_cast<u32x4*>(&B.k[r][frag_col(r, pp)]) = s.k[i][pp];
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        *reinterpret_cast<u32x4*>(&B.v[32 * PW + 8 * u + (lane >> 3)][8 * (lane & 7)]) = s.v[u];
+      const float gd = s.gd, btl = s.bt;
+      // ---- signal this half written and refill the registers; the wait for
+      // the other prep wave's half comes after the scan.  Both prep waves
+      // stage every chunk, so that wait ends; its bound only guards against a
+      // wave that never arrives.
+      ++staged;
+      if (lane == 0) __hip_atomic_fetch_add(&sm.prep_cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (c + 3 < nch) prefetch(c + 3, s);
+      // ---- decay scan (lane = token)
+      typename Sm::Scan& sc = sm.scan[PW];
+      bool reset;
+      float lg;
+      if (p.decay_is_gamma) {
+        reset = !(gd > 0.f);
+        lg = reset ? 0.f : __log2f(gd);
+      } else {
+        reset = !(gd > -INFINITY);
+        lg = reset ? 0.f : gd * 1.4426950408889634f;
+      }
+      const float F = wave_scan_add(lg);
+      const int z = wave_scan_max(reset ? lane : -1);
+      const float Flast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(F), C - 1));
+      const int zlast = __builtin_amdgcn_readlane(z, C - 1);
+      sc.F[lane] = F;
+      sc.z[lane] = z;
+      sc.bt[lane] = btl;
+      if constexpr (PW == 1) {
+        // F at the first and last lane of this lane's 16-lane row (row_newbcast)
+        const float Fb0 = dpp_f<0x150, 0xF>(0.f, F), Fb1 = dpp_f<0x15F, 0xF>(0.f, F);
+        sc.E[lane] = __builtin_amdgcn_exp2f(F - Fb0);
+        sc.Fx[lane] = __builtin_amdgcn_exp2f(Fb1 - F);
+      }
+      for (int spin = 0; spin < (1 << 22); ++spin) {
+        if (__hip_atomic_load(&sm.prep_cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= 2 * staged) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      const bool any_zero = zlast >= 0;  // wave-uniform
+
+      if constexpr (PW == 0) {
+        // ---- per-token factors of the state waves
+        const float gam = z < 0 ? __builtin_amdgcn_exp2f(F) : 0.f;
+        B.bet[lane] = btl;
+        B.gb[lane] = btl * gam;
+        B.gs[lane] = p.scale * gam;
+        B.dc[lane] = zlast <= lane ? __builtin_amdgcn_exp2f(Flast - F) : 0.f;
+        if (lane == C - 1) B.gC = gam;
+        // ---- diagonal Gram tiles (i, i), computed transposed: rows s, columns t
+        f4 kk[4], qk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kk[i] = qk[i] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int pp = 0; pp < NPP; ++pp) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * i + x;
+            const bf8 kf = lds_b128(&B.k[r][frag_col(r, pp)]);
+            const bf8 qf = lds_b128(&B.q[r][frag_col(r, pp)]);
+            kk[i] = mfma32(kk[i], kf, kf);
+            qk[i] = mfma32(qk[i], kf, qf);
+          }
+        }
+        // ---- M blocks and the rows of A_ii (fp32) for the inverses
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * i + x;
+          const float Ft = sc.F[t];
+          const f4 Fs = *reinterpret_cast<const f4*>(&sc.F[16 * i + 4 * g]);
+          const float bt = sc.bt[t];
+          const int zt = sc.z[t];
+          f4 d, arow;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int sidx = 16 * i + 4 * g + e;
+            const bool live = sidx <= t && (!any_zero || zt <= sidx);
+            d[e] = live ? __builtin_amdgcn_exp2f(Ft - Fs[e]) : 0.f;
+            arow[e] = sidx < t ? bt * d[e] * kk[i][e] : 0.f;
+          }
+          *reinterpret_cast<bf4*>(&B.m[t][16 * i + 4 * g]) = to_bf4(p.scale * d * qk[i]);
+          *reinterpret_cast<f4*>(&sm.adiag[i][20 * x + 4 * g]) = arow;
+        }
+        // ---- inverses, right-looking: lane group g owns block g, lane x its
+        // row x.  T[x][j] = [j == x] - sum_{k > j} T[x][k] A[k][j]; once
+        // T[x][k] is final its contribution goes to every j < k.
+        {
+          float acc[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) acc[j] = j == x ? 1.f : 0.f;
+#pragma unroll
+          for (int kr = 15; kr >= 1; --kr) {
+            f4 ar[4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+              if (4 * q4 < kr) ar[q4] = *reinterpret_cast<const f4*>(&sm.adiag[g][20 * kr + 4 * q4]);
+            const float tk = acc[kr];
+#pragma unroll
+            for (int j = 0; j < kr; ++j) acc[j] -= tk * ar[j >> 2][j & 3];
+          }
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<bf4*>(&B.tinv[g][x][4 * q4]) =
+                to_bf4(f4{acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]});
+        }
+      } else {
+        // ---- off-diagonal Gram tiles n: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+        constexpr int TI[6] = {1, 2, 2, 3, 3, 3}, TM[6] = {0, 0, 1, 0, 1, 2};
+        f4 kk[6], qk[6];
+#pragma unroll
+        for (int n = 0; n < 6; ++n) kk[n] = qk[n] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int pp = 0; pp < NPP; ++pp) {
+          bf8 kf[4], qf[3];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * i + x;
+            kf[i] = lds_b128(&B.k[r][frag_col(r, pp)]);
+          }
+#pragma unroll
+          for (int i = 1; i < 4; ++i) {
+            const int r = 16 * i + x;
+            qf[i - 1] = lds_b128(&B.q[r][frag_col(r, pp)]);
+          }
+#pragma unroll
+          for (int n = 0; n < 6; ++n) {
+            kk[n] = mfma32(kk[n], kf[TM[n]], kf[TI[n]]);
+            qk[n] = mfma32(qk[n], kf[TM[n]], qf[TI[n] - 1]);
+          }
+        }
+        // ---- -A and M blocks: D(t, s) = e_t c_im f_s for s in tile m < i,
+        // t in tile i, with e_t = 2^(F_t - F_16i), f_s = 2^(F_16m+15 - F_s),
+        // c_im = 2^(F_16i - F_16m+15), each <= 1; exact form when a gamma is 0
+#pragma unroll
+        for (int n = 0; n < 6; ++n) {
+          const int i = TI[n], m = TM[n];
+          const int t = 16 * i + x;
+          const float bt = sc.bt[t];
+          f4 dm, da;  // decay times scale, decay times -beta_t
+          if (!any_zero) {
+            const float cim = __builtin_amdgcn_exp2f(sc.F[16 * i] - sc.F[16 * m + 15]);
+            const float et = sc.E[t] * cim;
+            const f4 fs = *reinterpret_cast<const f4*>(&sc.Fx[16 * m + 4 * g]);
+            dm = (p.scale * et) * fs;
+            da = (-bt * et) * fs;
+          } else {
+            const float Ft = sc.F[t];
+            const int zt = sc.z[t];
+            const f4 Fs = *reinterpret_cast<const f4*>(&sc.F[16 * m + 4 * g]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float d = zt <= 16 * m + 4 * g + e ? __builtin_amdgcn_exp2f(Ft - Fs[e]) : 0.f;
+              dm[e] = p.scale * d;
+              da[e] = -bt * d;
+            }
+          }
+          *reinterpret_cast<bf4*>(&B.m[t][16 * m + 4 * g]) = to_bf4(dm * qk[n]);
+          *reinterpret_cast<bf4*>(&B.negA[t][16 * m + 4 * g]) = to_bf4(da * kk[n]);
+        }
+      }
+    }
+    lds_barrier();
+  };
+
+  PairPrepSet<DK> sa, sb;
+  if (nch > 0) prefetch(0, sa);
+  if (nch > 1) prefetch(1, sb);
+  for (int c = -1; c < nch; c += 2) {
+    iter(c, sa);
+    if (c + 1 < nch) iter(c + 1, sb);
+  }
+}
+
+template <int DK>
+__global__ void __launch_bounds__(256, 1)
+prefill_pair_kernel(const PrefillParams p) {
+  typedef PairSmem<DK> Sm;
+  constexpr int C = 64, NKT = DK / 16, NPP = DK / 32;
+  __shared__ Sm sm;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int x = lane & 15;
+  const int g = lane >> 4;
+
+  int blk = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 31) == 0) blk = (blk & 7) * (nblk >> 3) + (blk >> 3);
+  const int split = blk % p.nsplit;
+  const int h = (blk / p.nsplit) % p.hv;
+  const int r = blk / (p.nsplit * p.hv);
+  const int qh = (int)(((int64_t)h * p.hq) / p.hv);
+  const int v0 = split * 64;
+
+  int64_t start, end;
+  if (p.cu) {
+    start = min(max((int64_t)p.cu[r], (int64_t)0), p.T);
+    end = min(max((int64_t)p.cu[r + 1], (int64_t)0), p.T);
+  } else {
+    start = (int64_t)r * p.seq_len;
+    end = start + p.seq_len;
+  }
+  if (end < start) end = start;
+  const int nch = (int)((end - start + C - 1) / C);
+
+  const __bf16* __restrict__ gq = (const __bf16*)p.q + (int64_t)qh * p.q_sh;
+  const __bf16* __restrict__ gk = (const __bf16*)p.k + (int64_t)qh * p.k_sh;
+  const __bf16* __restrict__ gv = (const __bf16*)p.v + (int64_t)h * p.v_sh + v0;
+  __bf16* __restrict__ gout = (__bf16*)p.out + (int64_t)h * p.o_sh + v0;
+  const int64_t st_base = (((int64_t)r * p.hv + h) * p.dv + v0) * DK;
+
+  // The readout pairs each diagonal block of M with the block to its right,
+  // which the prep waves never write: clear those two blocks once.
+  for (int idx = tid; idx < 2 * 2 * 256; idx += 256) {
+    const int b = idx >> 9, blk2 = (idx >> 8) & 1, e = idx & 255;
+    sm.buf[b].m[32 * blk2 + (e >> 4)][32 * blk2 + 16 + (e & 15)] = (__bf16)0.f;
+  }
+  if (tid == 0) sm.prep_cnt = 0;
+  lds_barrier();
+
+  if (wave >= 2) {
+    const float* gdec = p.decay + h;
+    const float* gbet = p.beta + h;
+    if (wave == 2) pair_prep<DK, 0>(p, sm, start, end, nch, gq, gk, gv, gdec, gbet);
+    else pair_prep<DK, 1>(p, sm, start, end, nch, gq, gk, gv, gdec, gbet);
+    return;
+  }
+
+  // ------------------------------------------------------------ state waves
+  const int w = wave;  // value columns 32w .. 32w + 31 of the slice
+  const int ta = x & 3, te = x >> 2;  // transposing-read block of this lane
+  f4 S[NKT][2];
+#pragma unroll
+  for (int j = 0; j < NKT; ++j) S[j][0] = S[j][1] = f4{0.f, 0.f, 0.f, 0.f};
+  if (p.init) {
+#pragma unroll
+    for (int j = 0; j < NKT; ++j)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        S[j][ct] = *reinterpret_cast<const f4*>(p.init + st_base + (int64_t)(32 * w + 16 * ct + x) * DK +
+                                                dk_of<NKT>(j, 4 * g));
+  }
+  const int ost = (int)p.o_st;
+  __bf16* yt = sm.yt[w];
+
+  for (int c = -1; c < nch; ++c) {
+    if (c >= 0) {
+      const typename Sm::Buf& B = sm.buf[c & 1];
+      // ---- R = [Q; K] S0 (state rounded to bf16 as the B operand)
+      bf8 Sb[NPP][2];
+#pragma unroll
+      for (int pp = 0; pp < NPP; ++pp)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) Sb[pp][ct] = cat8(to_bf4(S[2 * pp][ct]), to_bf4(S[2 * pp + 1][ct]));
+      f4 rq[4][2], rk[4][2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rq[i][0] = rq[i][1] = rk[i][0] = rk[i][1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int pp = 0; pp < NPP; ++pp) {
+        bf8 aq[4], ak[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * i + x;
+          aq[i] = lds_b128(&B.q[row][8 * pair_swz(row, 4 * pp + g)]);
+          ak[i] = lds_b128(&B.k[row][8 * pair_swz(row, 4 * pp + g)]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            rq[i][ct] = mfma32(rq[i][ct], aq[i], Sb[pp][ct]);
+            rk[i][ct] = mfma32(rk[i][ct], ak[i], Sb[pp][ct]);
+          }
+      }
+      // ---- X = beta V - beta Gam R_K ; Y = scale Gam R_Q
+      f4 X[4][2], Y[4][2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f4 bt = *reinterpret_cast<const f4*>(&B.bet[16 * i + 4 * g]);
+        const f4 gb = *reinterpret_cast<const f4*>(&B.gb[16 * i + 4 * g]);
+        const f4 gs = *reinterpret_cast<const f4*>(&B.gs[16 * i + 4 * g]);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const f4 vv = bf4_to_f4(lds_tr(&B.v[16 * i + 4 * g + te][32 * w + 16 * ct + 4 * ta]));
+          X[i][ct] = bt * vv - gb * rk[i][ct];
+          Y[i][ct] = gs * rq[i][ct];
+        }
+      }
+      // ---- (I + A) U = X by block forward substitution; Y += M U; state update
+      const float gC = B.gC;
+#pragma unroll
+      for (int j = 0; j < NKT; ++j) {
+        S[j][0] = gC * S[j][0];
+        S[j][1] = gC * S[j][1];
+      }
+      const bf4 zero4 = bf4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+      // operands of the substitution chain, read before it starts
+      bf4 tiv[4], na[4][4];
+      f4 dcs[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        tiv[m] = lds_b64(&B.tinv[m][x][4 * g]);
+        dcs[m] = *reinterpret_cast<const f4*>(&B.dc[16 * m + 4 * g]);
+#pragma unroll
+        for (int i = m + 1; i < 4; ++i) na[i][m] = lds_b64(&B.negA[16 * i + x][16 * m + 4 * g]);
+      }
+      bf4 Ub[4][2], DU[4][2];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const bf4 ti = tiv[m];
+        const f4 dcv = dcs[m];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const f4 U = mma_k16(f4{0.f, 0.f, 0.f, 0.f}, ti, to_bf4(X[m][ct]));
+          Ub[m][ct] = to_bf4(U);
+          DU[m][ct] = to_bf4(dcv * U);
+        }
+        if ((m & 1) == 0) {
+          const bf4 a = na[m + 1][m];
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+            X[m + 1][ct] = mfma32(X[m + 1][ct], cat8(a, zero4), cat8(Ub[m][ct], zero4));
+        } else {
+          const int m0 = m - 1;
+#pragma unroll
+          for (int i = m + 1; i < 4; ++i) {
+            const bf8 a = cat8(na[i][m0], na[i][m]);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) X[i][ct] = mfma32(X[i][ct], a, cat8(Ub[m0][ct], Ub[m][ct]));
+          }
+#pragma unroll
+          for (int i = m0; i < 4; ++i) {
+            const bf8 a = cat8(lds_b64(&B.m[16 * i + x][16 * m0 + 4 * g]),
+                               lds_b64(&B.m[16 * i + x][16 * m + 4 * g]));
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) Y[i][ct] = mfma32(Y[i][ct], a, cat8(Ub[m0][ct], Ub[m][ct]));
+          }
+#pragma unroll
+          for (int j = 0; j < NKT; ++j) {
+            const int key = 32 * (j >> 1) + 8 * ta + 4 * (j & 1);
+            const int r0 = 16 * m0 + 4 * g + te, r1 = 16 * m + 4 * g + te;
+            const bf8 a = cat8(lds_tr(&B.k[r0][8 * pair_swz(r0, key >> 3) + 4 * (j & 1)]),
+                               lds_tr(&B.k[r1][8 * pair_swz(r1, key >> 3) + 4 * (j & 1)]));
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) S[j][ct] = mfma32(S[j][ct], a, cat8(DU[m0][ct], DU[m][ct]));
+          }
+        }
+      }
+      // ---- outputs (scale is folded into Gam and M)
+      const int64_t tok0 = start + (int64_t)c * C;
+      const int nvalid = (int)min((int64_t)C, end - tok0);
+      __bf16* ob = gout + tok0 * p.o_st + 32 * w;
+      if (nvalid == C) {
+        // transpose through LDS: each lane writes 4 tokens of one column,
+        // then reads 16-byte rows (token 16i + x, columns 8g .. 8g+7)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            const int col = 16 * ct + x;
+            *reinterpret_cast<bf4*>(&yt[64 * col + 4 * ((4 * i + g) ^ yt_swz(col))]) = to_bf4(Y[i][ct]);
+          }
+        const __amdgpu_buffer_rsrc_t rs = buf_rsrc(ob);
+        const uint32_t o_lane = (uint32_t)((x * ost + 8 * g) * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c0 = 8 * g + te, c1 = 8 * g + 4 + te;
+          const bf4 lo = lds_tr(&yt[64 * c0 + 4 * ((4 * i + ta) ^ yt_swz(c0))]);
+          const bf4 hi = lds_tr(&yt[64 * c1 + 4 * ((4 * i + ta) ^ yt_swz(c1))]);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, cat8(lo, hi)), rs, o_lane,
+                                                 (uint32_t)(16 * i * ost * 2), 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int t = 16 * i + 4 * g + e;
+              if (t < nvalid) ob[(int64_t)t * ost + 16 * ct + x] = (__bf16)Y[i][ct][e];
+            }
+      }
+    }
+    lds_barrier();
+  }
+#pragma unroll
+  for (int j = 0; j < NKT; ++j)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+      *reinterpret_cast<f4*>(p.fin + st_base + (int64_t)(32 * w + 16 * ct + x) * DK + dk_of<NKT>(j, 4 * g)) =
+          S[j][ct];
+}
+
+// Whether the pair kernel covers a bf16 problem of this shape and chunk hint.
+inline bool prefill_pair_supported(int dk, int dv, int chunk_hint) {
+  return (dk == 64 || dk == 128) && (dv == 64 || dv == 128) && (chunk_hint == 0 || chunk_hint == 64);
+}
+
+template <int DK>
+hipError_t launch_prefill_pair_t(PrefillParams p, hipStream_t stream) {
+  p.nsplit = p.dv / 64;
+  const int64_t nblk = (int64_t)p.n_seqs * p.hv * p.nsplit;
+  hipLaunchKernelGGL((prefill_pair_kernel<DK>), dim3((unsigned)nblk), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t prefill_pair_bf16(PrefillParams p, int dk, hipStream_t s);
+
+}  // namespace gdn
