@@ -17,12 +17,12 @@
 //  * prep waves 2 and 3 prepare chunk c+1 meanwhile.  Each loads half of the
 //    chunk's Q, K and V rows (two chunks ahead: token-strided loads have a
 //    long latency) and stages them in LDS; after an LDS counter shows both
-//    halves written, wave 2 computes the four diagonal 16x16 Gram tiles, the
-//    M blocks on the diagonal and the inverses of the unit-lower blocks
-//    I + A_ii (right-looking, so each step is a set of independent FMAs) and
-//    the per-token factors, while wave 3 computes the six off-diagonal tiles
-//    and their -A and M blocks, with the decay D(t,s) factored into three
-//    per-tile factors <= 1 unless the chunk holds a gamma of exactly 0;
+//    halves written, each computes two diagonal and three off-diagonal
+//    16x16 Gram tiles, their M and -A blocks (the decay D(t,s) of an
+//    off-diagonal tile factored into three per-tile factors <= 1 unless the
+//    chunk holds a gamma of exactly 0), and the inverses of its two
+//    unit-lower blocks I + A_ii (right-looking, one lane pair per row);
+//    wave 2 also writes the per-token factors;
 //  * one workgroup barrier per chunk: the state waves read buffer c & 1 while
 //    the prep waves fill buffer (c+1) & 1.
 // K^T fragments for the state update, V in accumulator layout and the output
@@ -257,7 +257,7 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
       sc.F[lane] = F;
       sc.z[lane] = z;
       sc.bt[lane] = btl;
-      if constexpr (PW == 1) {
+      {
         // F at the first and last lane of this lane's 16-lane row (row_newbcast)
         const float Fb0 = dpp_f<0x150, 0xF>(0.f, F), Fb1 = dpp_f<0x15F, 0xF>(0.f, F);
         sc.E[lane] = __builtin_amdgcn_exp2f(F - Fb0);
@@ -277,116 +277,141 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
         B.gs[lane] = p.scale * gam;
         B.dc[lane] = zlast <= lane ? __builtin_amdgcn_exp2f(Flast - F) : 0.f;
         if (lane == C - 1) B.gC = gam;
-        // ---- diagonal Gram tiles (i, i), computed transposed: rows s, columns t
-        f4 kk[4], qk[4];
+      }
+      // ---- Gram tiles, computed transposed (rows s, columns t): this wave's
+      // diagonal tiles (D0, D0), (D0+1, D0+1) and three off-diagonal tiles
+      // (TI[n], TM[n]): wave 2 (1,0) (2,0) (3,0), wave 3 (2,1) (3,1) (3,2)
+      constexpr int D0 = 2 * PW;
+      constexpr int TI[3] = {PW == 0 ? 1 : 2, PW == 0 ? 2 : 3, 3};
+      constexpr int TM[3] = {PW == 0 ? 0 : 1, PW == 0 ? 0 : 1, PW == 0 ? 0 : 2};
+      constexpr int KLO = PW == 0 ? 0 : 1, QLO = PW == 0 ? 0 : 2;  // tiles read
+      f4 kkd[2], qkd[2], kko[3], qko[3];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kk[i] = qk[i] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < 2; ++n) kkd[n] = qkd[n] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int pp = 0; pp < NPP; ++pp) {
+      for (int n = 0; n < 3; ++n) kko[n] = qko[n] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * i + x;
-            const bf8 kf = lds_b128(&B.k[r][frag_col(r, pp)]);
-            const bf8 qf = lds_b128(&B.q[r][frag_col(r, pp)]);
-            kk[i] = mfma32(kk[i], kf, kf);
-            qk[i] = mfma32(qk[i], kf, qf);
-          }
+      for (int pp = 0; pp < NPP; ++pp) {
+        bf8 kf[4], qf[4];
+#pragma unroll
+        for (int i = KLO; i < 4; ++i) {
+          const int r = 16 * i + x;
+          kf[i] = lds_b128(&B.k[r][frag_col(r, pp)]);
         }
-        // ---- M blocks and the rows of A_ii (fp32) for the inverses
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * i + x;
+        for (int i = QLO; i < 4; ++i) {
+          const int r = 16 * i + x;
+          qf[i] = lds_b128(&B.q[r][frag_col(r, pp)]);
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          kkd[n] = mfma32(kkd[n], kf[D0 + n], kf[D0 + n]);
+          qkd[n] = mfma32(qkd[n], kf[D0 + n], qf[D0 + n]);
+        }
+#pragma unroll
+        for (int n = 0; n < 3; ++n) {
+          kko[n] = mfma32(kko[n], kf[TM[n]], kf[TI[n]]);
+          qko[n] = mfma32(qko[n], kf[TM[n]], qf[TI[n]]);
+        }
+      }
+      // ---- diagonal tiles: M blocks, and the rows of A_ii (fp32) split by
+      // column parity for the inverses: adiag[i][20 r + 8 h + jj] = A_ii[r][2 jj + h]
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int i = D0 + n;
+        const int t = 16 * i + x;
+        const float Ft = sc.F[t];
+        const f4 Fs = *reinterpret_cast<const f4*>(&sc.F[16 * i + 4 * g]);
+        const float bt = sc.bt[t];
+        const int zt = sc.z[t];
+        f4 d, arow;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int sidx = 16 * i + 4 * g + e;
+          const bool live = sidx <= t && (!any_zero || zt <= sidx);
+          d[e] = live ? __builtin_amdgcn_exp2f(Ft - Fs[e]) : 0.f;
+          arow[e] = sidx < t ? bt * d[e] * kkd[n][e] : 0.f;
+        }
+        *reinterpret_cast<bf4*>(&B.m[t][16 * i + 4 * g]) = to_bf4(p.scale * d * qkd[n]);
+        *reinterpret_cast<f2*>(&sm.adiag[i][20 * x + 2 * g]) = f2{arow[0], arow[2]};
+        *reinterpret_cast<f2*>(&sm.adiag[i][20 * x + 8 + 2 * g]) = f2{arow[1], arow[3]};
+      }
+      // ---- off-diagonal tiles: -A and M blocks.  D(t, s) = e_t c_im f_s for
+      // s in tile m < i, t in tile i, with e_t = 2^(F_t - F_16i),
+      // f_s = 2^(F_16m+15 - F_s), c_im = 2^(F_16i - F_16m+15), each <= 1;
+      // the exact form when the chunk holds a gamma of 0
+#pragma unroll
+      for (int n = 0; n < 3; ++n) {
+        const int i = TI[n], m = TM[n];
+        const int t = 16 * i + x;
+        const float bt = sc.bt[t];
+        f4 dm, da;  // decay times scale, decay times -beta_t
+        if (!any_zero) {
+          const float cim = __builtin_amdgcn_exp2f(sc.F[16 * i] - sc.F[16 * m + 15]);
+          const float et = sc.E[t] * cim;
+          const f4 fs = *reinterpret_cast<const f4*>(&sc.Fx[16 * m + 4 * g]);
+          dm = (p.scale * et) * fs;
+          da = (-bt * et) * fs;
+        } else {
           const float Ft = sc.F[t];
-          const f4 Fs = *reinterpret_cast<const f4*>(&sc.F[16 * i + 4 * g]);
-          const float bt = sc.bt[t];
           const int zt = sc.z[t];
-          f4 d, arow;
+          const f4 Fs = *reinterpret_cast<const f4*>(&sc.F[16 * m + 4 * g]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int sidx = 16 * i + 4 * g + e;
-            const bool live = sidx <= t && (!any_zero || zt <= sidx);
-            d[e] = live ? __builtin_amdgcn_exp2f(Ft - Fs[e]) : 0.f;
-            arow[e] = sidx < t ? bt * d[e] * kk[i][e] : 0.f;
-          }
-          *reinterpret_cast<bf4*>(&B.m[t][16 * i + 4 * g]) = to_bf4(p.scale * d * qk[i]);
-          *reinterpret_cast<f4*>(&sm.adiag[i][20 * x + 4 * g]) = arow;
-        }
-        // ---- inverses, right-looking: lane group g owns block g, lane x its
-        // row x.  T[x][j] = [j == x] - sum_{k > j} T[x][k] A[k][j]; once
-        // T[x][k] is final its contribution goes to every j < k.
-        {
-          float acc[16];
-#pragma unroll
-          for (int j = 0; j < 16; ++j) acc[j] = j == x ? 1.f : 0.f;
-#pragma unroll
-          for (int kr = 15; kr >= 1; --kr) {
-            f4 ar[4];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-              if (4 * q4 < kr) ar[q4] = *reinterpret_cast<const f4*>(&sm.adiag[g][20 * kr + 4 * q4]);
-            const float tk = acc[kr];
-#pragma unroll
-            for (int j = 0; j < kr; ++j) acc[j] -= tk * ar[j >> 2][j & 3];
-          }
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            *reinterpret_cast<bf4*>(&B.tinv[g][x][4 * q4]) =
-                to_bf4(f4{acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]});
-        }
-      } else {
-        // ---- off-diagonal Gram tiles n: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
-        constexpr int TI[6] = {1, 2, 2, 3, 3, 3}, TM[6] = {0, 0, 1, 0, 1, 2};
-        f4 kk[6], qk[6];
-#pragma unroll
-        for (int n = 0; n < 6; ++n) kk[n] = qk[n] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int pp = 0; pp < NPP; ++pp) {
-          bf8 kf[4], qf[3];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * i + x;
-            kf[i] = lds_b128(&B.k[r][frag_col(r, pp)]);
-          }
-#pragma unroll
-          for (int i = 1; i < 4; ++i) {
-            const int r = 16 * i + x;
-            qf[i - 1] = lds_b128(&B.q[r][frag_col(r, pp)]);
-          }
-#pragma unroll
-          for (int n = 0; n < 6; ++n) {
-            kk[n] = mfma32(kk[n], kf[TM[n]], kf[TI[n]]);
-            qk[n] = mfma32(qk[n], kf[TM[n]], qf[TI[n] - 1]);
+            const float d = zt <= 16 * m + 4 * g + e ? __builtin_amdgcn_exp2f(Ft - Fs[e]) : 0.f;
+            dm[e] = p.scale * d;
+            da[e] = -bt * d;
           }
         }
-        // ---- -A and M blocks: D(t, s) = e_t c_im f_s for s in tile m < i,
-        // t in tile i, with e_t = 2^(F_t - F_16i), f_s = 2^(F_16m+15 - F_s),
-        // c_im = 2^(F_16i - F_16m+15), each <= 1; exact form when a gamma is 0
+        *reinterpret_cast<bf4*>(&B.m[t][16 * m + 4 * g]) = to_bf4(dm * qko[n]);
+        *reinterpret_cast<bf4*>(&B.negA[t][16 * m + 4 * g]) = to_bf4(da * kko[n]);
+      }
+      // ---- inverses of the two diagonal blocks, right-looking: a lane pair
+      // owns row r of block i; lane parity h keeps T[r][j] for j = h mod 2.
+      // T[r][j] = [j == r] - sum_{k > j} T[r][k] A[k][j]; once T[r][k] is final
+      // (its owner lane passes it to the partner) it updates every j < k.
+      // A is strictly lower, so updates of entries j >= k add zero.
+      {
+        const int i = D0 + (lane >> 5), r = (lane >> 1) & 15, h = lane & 1;
+        const float* arow = &sm.adiag[i][8 * h];
+        float acc[8];
 #pragma unroll
-        for (int n = 0; n < 6; ++n) {
-          const int i = TI[n], m = TM[n];
-          const int t = 16 * i + x;
-          const float bt = sc.bt[t];
-          f4 dm, da;  // decay times scale, decay times -beta_t
-          if (!any_zero) {
-            const float cim = __builtin_amdgcn_exp2f(sc.F[16 * i] - sc.F[16 * m + 15]);
-            const float et = sc.E[t] * cim;
-            const f4 fs = *reinterpret_cast<const f4*>(&sc.Fx[16 * m + 4 * g]);
-            dm = (p.scale * et) * fs;
-            da = (-bt * et) * fs;
-          } else {
-            const float Ft = sc.F[t];
-            const int zt = sc.z[t];
-            const f4 Fs = *reinterpret_cast<const f4*>(&sc.F[16 * m + 4 * g]);
+        for (int jj = 0; jj < 8; ++jj) acc[jj] = 2 * jj + h == r ? 1.f : 0.f;
+        f4 a0 = *reinterpret_cast<const f4*>(arow + 20 * 15);
+        f4 a1 = *reinterpret_cast<const f4*>(arow + 20 * 15 + 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float d = zt <= 16 * m + 4 * g + e ? __builtin_amdgcn_exp2f(Ft - Fs[e]) : 0.f;
-              dm[e] = p.scale * d;
-              da[e] = -bt * d;
-            }
+        for (int k = 15; k >= 1; --k) {
+          f4 n0 = a0, n1 = a1;
+          if (k > 1) {
+            n0 = *reinterpret_cast<const f4*>(arow + 20 * (k - 1));
+            n1 = *reinterpret_cast<const f4*>(arow + 20 * (k - 1) + 4);
           }
-          *reinterpret_cast<bf4*>(&B.m[t][16 * m + 4 * g]) = to_bf4(dm * qk[n]);
-          *reinterpret_cast<bf4*>(&B.negA[t][16 * m + 4 * g]) = to_bf4(da * kk[n]);
+          const float mine = acc[k >> 1];
+          const float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mine), 0xB1, 0xF, 0xF, false));
+          const float tk = (k & 1) == h ? mine : other;
+          const float ak[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          // the entry the next step reads first, then the rest
+          acc[(k - 1) >> 1] -= tk * ak[(k - 1) >> 1];
+#pragma unroll
+          for (int jj = 0; jj < ((k - 1) >> 1); ++jj) acc[jj] -= tk * ak[jj];
+          a0 = n0;
+          a1 = n1;
         }
+        // row r, columns 8 hh .. 8 hh + 7 with hh = h: even entries from lane
+        // parity 0, odd ones from parity 1
+        float o[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float even_lo = acc[q], even_hi = acc[4 + q];  // my parity's values
+          const float sw_lo = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(even_lo), 0xB1, 0xF, 0xF, false));
+          const float sw_hi = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(even_hi), 0xB1, 0xF, 0xF, false));
+          // h == 0 assembles columns 0..7: T[r][2q] (mine, jj = q), T[r][2q+1] (partner's jj = q)
+          // h == 1 assembles columns 8..15: T[r][8+2q] (partner's jj = 4+q), T[r][9+2q] (mine, jj = 4+q)
+          o[2 * q] = h == 0 ? even_lo : sw_hi;
+          o[2 * q + 1] = h == 0 ? sw_lo : even_hi;
+        }
+        *reinterpret_cast<bf4*>(&B.tinv[i][r][8 * h]) = to_bf4(f4{o[0], o[1], o[2], o[3]});
+        *reinterpret_cast<bf4*>(&B.tinv[i][r][8 * h + 4]) = to_bf4(f4{o[4], o[5], o[6], o[7]});
       }
     }
     lds_barrier();
@@ -535,9 +560,23 @@ prefill_pair_kernel(const PrefillParams p) {
 #pragma unroll
         for (int i = m + 1; i < 4; ++i) na[i][m] = lds_b64(&B.negA[16 * i + x][16 * m + 4 * g]);
       }
+      // K^T fragments for the state update of token blocks (m0, m0+1): read
+      // one pair ahead of its use
+      auto load_kt = [&](int m0, bf8* kt) {
+#pragma unroll
+        for (int j = 0; j < NKT; ++j) {
+          const int key = 32 * (j >> 1) + 8 * ta + 4 * (j & 1);
+          const int r0 = 16 * m0 + 4 * g + te, r1 = r0 + 16;
+          kt[j] = cat8(lds_tr(&B.k[r0][8 * pair_swz(r0, key >> 3) + 4 * (j & 1)]),
+                       lds_tr(&B.k[r1][8 * pair_swz(r1, key >> 3) + 4 * (j & 1)]));
+        }
+      };
+      bf8 kt01[NKT], kt23[NKT];
+      load_kt(0, kt01);
       bf4 Ub[4][2], DU[4][2];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
+        if (m == 1) load_kt(2, kt23);
         const bf4 ti = tiv[m];
         const f4 dcv = dcs[m];
 #pragma unroll
@@ -568,10 +607,7 @@ prefill_pair_kernel(const PrefillParams p) {
           }
 #pragma unroll
           for (int j = 0; j < NKT; ++j) {
-            const int key = 32 * (j >> 1) + 8 * ta + 4 * (j & 1);
-            const int r0 = 16 * m0 + 4 * g + te, r1 = 16 * m + 4 * g + te;
-            const bf8 a = cat8(lds_tr(&B.k[r0][8 * pair_swz(r0, key >> 3) + 4 * (j & 1)]),
-                               lds_tr(&B.k[r1][8 * pair_swz(r1, key >> 3) + 4 * (j & 1)]));
+            const bf8 a = m0 == 0 ? kt01[j] : kt23[j];
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) S[j][ct] = mfma32(S[j][ct], a, cat8(DU[m0][ct], DU[m][ct]));
           }
