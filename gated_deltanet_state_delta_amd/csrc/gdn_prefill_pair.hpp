@@ -11,18 +11,19 @@
 //    registers -- per (request, value head, 64-column slice of the state);
 //  * state waves 0 and 1 each own 32 value columns (two 16-column MFMA
 //    tiles), so every Q, K and K^T fragment read from LDS feeds two MFMAs;
-//    they run [Q; K] S0, the block forward substitution, Y += M U and the
-//    state update for chunk c, and write the outputs through LDS as 16-byte
-//    rows;
+//    state wave w inverts the unit-lower diagonal blocks I + A_ii,
+//    i = 2w, 2w+1, of chunk c (right-looking, one lane pair per row) and
+//    shares them through LDS (a counter tells when both halves are there);
+//    both then run [Q; K] S0, the block forward substitution, Y += M U and
+//    the state update, and write the outputs through LDS as 16-byte rows;
 //  * prep waves 2 and 3 prepare chunk c+1 meanwhile.  Each loads half of the
 //    chunk's Q, K and V rows (two chunks ahead: token-strided loads have a
 //    long latency) and stages them in LDS; after an LDS counter shows both
 //    halves written, each computes two diagonal and three off-diagonal
 //    16x16 Gram tiles, their M and -A blocks (the decay D(t,s) of an
 //    off-diagonal tile factored into three per-tile factors <= 1 unless the
-//    chunk holds a gamma of exactly 0), and the inverses of its two
-//    unit-lower blocks I + A_ii (right-looking, one lane pair per row);
-//    wave 2 also writes the per-token factors;
+//    chunk holds a gamma of exactly 0), and the fp32 rows of its two
+//    diagonal blocks A_ii; wave 2 also writes the per-token factors;
 //  * one workgroup barrier per chunk: the state waves read buffer c & 1 while
 //    the prep waves fill buffer (c+1) & 1.
 // K^T fragments for the state update, V in accumulator layout and the output
@@ -52,7 +53,6 @@ struct PairSmem {
     __bf16 v[C][LDV];
     __bf16 negA[C][LDC];  // -A, off-diagonal 16x16 blocks
     __bf16 m[C][LDC];     // scale D o Q K^T, blocks on and below the diagonal
-    __bf16 tinv[NT][16][LDT];
     alignas(16) float bet[C];  // beta_t (0 on padded tokens)
     alignas(16) float gb[C];   // beta_t Gam_t
     alignas(16) float gs[C];   // scale Gam_t
@@ -68,14 +68,19 @@ struct PairSmem {
   };
   alignas(16) Buf buf[2];
   Scan scan[2];  // one per prep wave
-  // rows of the fp32 diagonal blocks of A (wave 2 only): block i, row r at
-  // 20 r (padded rows and blocks keep the row reads of the four blocks on
-  // distinct banks)
-  alignas(16) float adiag[4][16 * 20 + 4];
+  // rows of the fp32 diagonal blocks of A, one set per chunk parity: block
+  // i, row r at 20 r, split by column parity (adiag[b][i][20 r + 8 h + jj] =
+  // A_ii[r][2 jj + h]; padded rows and blocks keep the row reads of the four
+  // blocks on distinct banks)
+  alignas(16) float adiag[2][NT][16 * 20 + 4];
+  // (I + A_ii)^-1 of the current chunk, bf16 (blocks 2w, 2w+1 written by
+  // state wave w)
+  alignas(16) __bf16 tinv[NT][16][LDT];
   // outputs of state wave w, transposed: column c (of its 32), token t at
   // yt[w][64 c + 4 ((t / 4) ^ f(c)) + t % 4]
   alignas(16) __bf16 yt[2][32 * 64];
   int prep_cnt;  // staging halves written by the prep waves so far
+  int inv_cnt;   // inverse halves written by the state waves so far
 };
 
 // 16-byte slot permutation of a Q/K row.
@@ -158,6 +163,56 @@ struct PairPrepSet {
   u32x4 v[4];
   float gd, bt;
 };
+
+// Inverse of the unit-lower block I + A_i (A_i strictly lower, fp32 rows in
+// `ad` as laid out by the prep waves), right-looking: a lane pair owns row
+// r = (lane / 2) % 16 of block i = i0 + lane / 32; lane parity h keeps
+// T[r][j] for j = h mod 2.  T[r][j] = [j == r] - sum_{k > j} T[r][k] A[k][j];
+// once T[r][k] is final (its owner lane passes it to the partner) it updates
+// every j < k.  A is strictly lower, so updates of entries j >= k add zero.
+// Writes row r of T_i in bf16 to tout[i][r][0..15].
+template <int LDT>
+__device__ __forceinline__ void pair_tri_inverse(const float (*ad)[16 * 20 + 4], __bf16 (*tout)[16][LDT], int i0,
+                                                 int lane) {
+  const int i = i0 + (lane >> 5), r = (lane >> 1) & 15, h = lane & 1;
+  const float* arow = &ad[i][8 * h];
+  float acc[8];
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) acc[jj] = 2 * jj + h == r ? 1.f : 0.f;
+  // row k of A: entries 2 jj + h for jj < (k + 1) / 2 can be nonzero
+  f4 a[16][2];
+#pragma unroll
+  for (int k = 1; k < 16; ++k) {
+    a[k][0] = *reinterpret_cast<const f4*>(arow + 20 * k);
+    if (k > 8) a[k][1] = *reinterpret_cast<const f4*>(arow + 20 * k + 4);
+  }
+#pragma unroll
+  for (int k = 15; k >= 1; --k) {
+    const float mine = acc[k >> 1];
+    const float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mine), 0xB1, 0xF, 0xF, false));
+    const float tk = (k & 1) == h ? mine : other;
+    auto ak = [&](int jj) -> float { return jj < 4 ? a[k][0][jj] : a[k][1][jj - 4]; };
+    // the entry the next step reads first, then the rest
+    acc[(k - 1) >> 1] -= tk * ak((k - 1) >> 1);
+#pragma unroll
+    for (int jj = 0; jj < ((k - 1) >> 1); ++jj) acc[jj] -= tk * ak(jj);
+  }
+  // row r, columns 8 h .. 8 h + 7: even entries from lane parity 0, odd ones
+  // from parity 1
+  float o[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float even_lo = acc[q], even_hi = acc[4 + q];  // my parity's values
+    const float sw_lo = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(even_lo), 0xB1, 0xF, 0xF, false));
+    const float sw_hi = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(even_hi), 0xB1, 0xF, 0xF, false));
+    // h == 0 assembles columns 0..7: T[r][2q] (mine, jj = q), T[r][2q+1] (partner's jj = q)
+    // h == 1 assembles columns 8..15: T[r][8+2q] (partner's jj = 4+q), T[r][9+2q] (mine, jj = 4+q)
+    o[2 * q] = h == 0 ? even_lo : sw_hi;
+    o[2 * q + 1] = h == 0 ? sw_lo : even_hi;
+  }
+  *reinterpret_cast<bf4*>(&tout[i][r][8 * h]) = to_bf4(f4{o[0], o[1], o[2], o[3]});
+  *reinterpret_cast<bf4*>(&tout[i][r][8 * h + 4]) = to_bf4(f4{o[4], o[5], o[6], o[7]});
+}
 
 // Prep wave PW of the pair kernel (see the header comment).
 template <int DK, int PW>
@@ -315,7 +370,7 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
         }
       }
       // ---- diagonal tiles: M blocks, and the rows of A_ii (fp32) split by
-      // column parity for the inverses: adiag[i][20 r + 8 h + jj] = A_ii[r][2 jj + h]
+      // column parity for the inverses
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         const int i = D0 + n;
@@ -333,8 +388,9 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
           arow[e] = sidx < t ? bt * d[e] * kkd[n][e] : 0.f;
         }
         *reinterpret_cast<bf4*>(&B.m[t][16 * i + 4 * g]) = to_bf4(p.scale * d * qkd[n]);
-        *reinterpret_cast<f2*>(&sm.adiag[i][20 * x + 2 * g]) = f2{arow[0], arow[2]};
-        *reinterpret_cast<f2*>(&sm.adiag[i][20 * x + 8 + 2 * g]) = f2{arow[1], arow[3]};
+        float* ad = sm.adiag[(c + 1) & 1][i];
+        *reinterpret_cast<f2*>(&ad[20 * x + 2 * g]) = f2{arow[0], arow[2]};
+        *reinterpret_cast<f2*>(&ad[20 * x + 8 + 2 * g]) = f2{arow[1], arow[3]};
       }
       // ---- off-diagonal tiles: -A and M blocks.  D(t, s) = e_t c_im f_s for
       // s in tile m < i, t in tile i, with e_t = 2^(F_t - F_16i),
@@ -365,53 +421,6 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
         }
         *reinterpret_cast<bf4*>(&B.m[t][16 * m + 4 * g]) = to_bf4(dm * qko[n]);
         *reinterpret_cast<bf4*>(&B.negA[t][16 * m + 4 * g]) = to_bf4(da * kko[n]);
-      }
-      // ---- inverses of the two diagonal blocks, right-looking: a lane pair
-      // owns row r of block i; lane parity h keeps T[r][j] for j = h mod 2.
-      // T[r][j] = [j == r] - sum_{k > j} T[r][k] A[k][j]; once T[r][k] is final
-      // (its owner lane passes it to the partner) it updates every j < k.
-      // A is strictly lower, so updates of entries j >= k add zero.
-      {
-        const int i = D0 + (lane >> 5), r = (lane >> 1) & 15, h = lane & 1;
-        const float* arow = &sm.adiag[i][8 * h];
-        float acc[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) acc[jj] = 2 * jj + h == r ? 1.f : 0.f;
-        f4 a0 = *reinterpret_cast<const f4*>(arow + 20 * 15);
-        f4 a1 = *reinterpret_cast<const f4*>(arow + 20 * 15 + 4);
-#pragma unroll
-        for (int k = 15; k >= 1; --k) {
-          f4 n0 = a0, n1 = a1;
-          if (k > 1) {
-            n0 = *reinterpret_cast<const f4*>(arow + 20 * (k - 1));
-            n1 = *reinterpret_cast<const f4*>(arow + 20 * (k - 1) + 4);
-          }
-          const float mine = acc[k >> 1];
-          const float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mine), 0xB1, 0xF, 0xF, false));
-          const float tk = (k & 1) == h ? mine : other;
-          const float ak[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-          // the entry the next step reads first, then the rest
-          acc[(k - 1) >> 1] -= tk * ak[(k - 1) >> 1];
-#pragma unroll
-          for (int jj = 0; jj < ((k - 1) >> 1); ++jj) acc[jj] -= tk * ak[jj];
-          a0 = n0;
-          a1 = n1;
-        }
-        // row r, columns 8 hh .. 8 hh + 7 with hh = h: even entries from lane
-        // parity 0, odd ones from parity 1
-        float o[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float even_lo = acc[q], even_hi = acc[4 + q];  // my parity's values
-          const float sw_lo = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(even_lo), 0xB1, 0xF, 0xF, false));
-          const float sw_hi = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(even_hi), 0xB1, 0xF, 0xF, false));
-          // h == 0 assembles columns 0..7: T[r][2q] (mine, jj = q), T[r][2q+1] (partner's jj = q)
-          // h == 1 assembles columns 8..15: T[r][8+2q] (partner's jj = 4+q), T[r][9+2q] (mine, jj = 4+q)
-          o[2 * q] = h == 0 ? even_lo : sw_hi;
-          o[2 * q + 1] = h == 0 ? sw_lo : even_hi;
-        }
-        *reinterpret_cast<bf4*>(&B.tinv[i][r][8 * h]) = to_bf4(f4{o[0], o[1], o[2], o[3]});
-        *reinterpret_cast<bf4*>(&B.tinv[i][r][8 * h + 4]) = to_bf4(f4{o[4], o[5], o[6], o[7]});
       }
     }
     lds_barrier();
@@ -471,7 +480,10 @@ prefill_pair_kernel(const PrefillParams p) {
     const int b = idx >> 9, blk2 = (idx >> 8) & 1, e = idx & 255;
     sm.buf[b].m[32 * blk2 + (e >> 4)][32 * blk2 + 16 + (e & 15)] = (__bf16)0.f;
   }
-  if (tid == 0) sm.prep_cnt = 0;
+  if (tid == 0) {
+    sm.prep_cnt = 0;
+    sm.inv_cnt = 0;
+  }
   lds_barrier();
 
   if (wave >= 2) {
@@ -502,6 +514,9 @@ prefill_pair_kernel(const PrefillParams p) {
   for (int c = -1; c < nch; ++c) {
     if (c >= 0) {
       const typename Sm::Buf& B = sm.buf[c & 1];
+      // ---- (I + A_ii)^-1 for blocks 2w, 2w+1; the other wave does the rest
+      pair_tri_inverse<Sm::LDT>(sm.adiag[c & 1], sm.tinv, 2 * w, lane);
+      if (lane == 0) __hip_atomic_fetch_add(&sm.inv_cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       // ---- R = [Q; K] S0 (state rounded to bf16 as the B operand)
       bf8 Sb[NPP][2];
 #pragma unroll
@@ -550,12 +565,18 @@ prefill_pair_kernel(const PrefillParams p) {
         S[j][1] = gC * S[j][1];
       }
       const bf4 zero4 = bf4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
-      // operands of the substitution chain, read before it starts
+      // operands of the substitution chain, read before it starts (the
+      // other state wave inverts every chunk too, so the wait for its
+      // blocks ends; its bound only guards against a wave that never arrives)
+      for (int spin = 0; spin < (1 << 22); ++spin) {
+        if (__hip_atomic_load(&sm.inv_cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= 2 * (c + 1)) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
       bf4 tiv[4], na[4][4];
       f4 dcs[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        tiv[m] = lds_b64(&B.tinv[m][x][4 * g]);
+        tiv[m] = lds_b64(&sm.tinv[m][x][4 * g]);
         dcs[m] = *reinterpret_cast<const f4*>(&B.dc[16 * m + 4 * g]);
 #pragma unroll
         for (int i = m + 1; i < 4; ++i) na[i][m] = lds_b64(&B.negA[16 * i + x][16 * m + 4 * g]);
