@@ -67,7 +67,7 @@ def _counter_means(path, counter):
         if r["Counter_Name"] != counter:
             continue
         name = r["Kernel_Name"]
-        if "prefill_kernel" in name:
+        if "prefill_kernel" in name or "prefill_pair_kernel" in name:
             key = "prefill"
         elif "decode_kernel" in name:
             key = "decode"
@@ -284,7 +284,7 @@ def main():
         res["unit"] = "tokens/s"
         gbs = pb / (pm * 1e-3) / 1e9
         tfl = pf / (pm * 1e-3) / 1e12
-        res["roofline"] = {"kernel": "prefill_kernel<bf16,128,64,64>", "bound": "hbm",
+        res["roofline"] = {"kernel": "prefill_pair_kernel<128>", "bound": "hbm",
                            "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic("prefill"),
                            "algorithmic_bytes": pb, "algorithmic_flops": pf,
