@@ -10,6 +10,13 @@ neither reads its inputs out of the 256 MB last-level cache.  Kernel times come
 from HIP events recorded on the launch stream; `value` is prefill tokens/s
 (16384 tokens over the gate + prefill time).
 
+Beside the step, the other workloads are timed the same way (flush, then the
+launch; median of the timed runs): the single-head scan (B2 x S64, d16, fp32:
+launch latency), the ragged fp32 prefill (8 requests, Hv32, d128, initial
+state; bound by the fp32 matrix rate) and the multi-token decode (pool
+[512, 16, 64, 128], B64, T4, n2, per-token scatter), plus a plain 1 GiB
+device copy as the achievable-bandwidth reference.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--only prefill|decode] [--copy-calib]
     python bench.py --summarize-traffic FETCH.csv WRITE.csv   (no GPU)
@@ -43,6 +50,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+FP32_MATRIX_PEAK_TFLOPS = 157.3  # MI355X fp32 matrix, TFLOP/s
 
 METRIC = "GDN prefill tokens/s (B4×S4096,Hv32,d128) + decode state HBM GB/s % of peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_b4s4096_decode_b256.json")
@@ -163,6 +171,85 @@ def cpu_baseline_prefill(x, budget_units=None):
             "sample": sample, "seconds": dt}
 
 
+def _time_launches(torch, fn, warmup=3, runs=20, flush=None):
+    """Median milliseconds of `fn` over `runs` launches, each after a cache flush."""
+    stream = torch.cuda.current_stream()
+    ts = []
+    for i in range(warmup + runs):
+        if flush is not None:
+            flush.zero_()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        if i >= warmup:
+            ts.append((a, b))
+    torch.cuda.synchronize()
+    return statistics.median(x.elapsed_time(y) for x, y in ts)
+
+
+def extra_workloads(torch, gdn, synth, dev):
+    """The other workloads of the scope table, each timed on its own."""
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    out = {}
+
+    # plain device copy: the achievable streaming bandwidth on this box
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    cm = _time_launches(torch, lambda: dst.copy_(src), flush=flush)
+    out["copy_1gib"] = {"ms": cm, "gbs": 2 * (1 << 30) / (cm * 1e-3) / 1e9}
+    del src, dst
+
+    # single-head scan: B2 x S64, d16, fp32 (launch latency)
+    x = synth.single_head_scan()
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    gam, bet = x["gamma"].to(dev), x["beta"].to(dev)
+    o1 = torch.empty_like(v)
+    f1 = torch.empty(x["n_seqs"], 1, x["dv"], x["dk"], device=dev)
+    B1, S1 = x["n_seqs"], x["seq_len"]
+    fn = lambda: gdn.prefill(q.view(B1, S1, 1, -1), k.view(B1, S1, 1, -1), v.view(B1, S1, 1, -1),
+                             gam.view(B1, S1, 1), bet.view(B1, S1, 1), decay_kind="gamma",
+                             scale=x["scale"], out=o1.view(B1, S1, 1, -1), final_state=f1)
+    out["single_head_scan_b2_s64_d16_f32"] = {"ms": _time_launches(torch, fn, runs=50)}
+
+    # ragged fp32 prefill: 8 requests, initial state, gamma gates
+    x = synth.ragged_prefill_8req()
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    gam, bet, cu = x["gamma"].to(dev), x["beta"].to(dev), x["cu_seqlens"].to(dev)
+    init = x["initial_state"].to(dev)
+    o3 = torch.empty_like(v)
+    f3 = torch.empty_like(init)
+    fn = lambda: gdn.prefill(q, k, v, gam, bet, decay_kind="gamma", cu_seqlens=cu,
+                             initial_state=init, scale=x["scale"], out=o3, final_state=f3)
+    ms = _time_launches(torch, fn, flush=flush)
+    T = x["T"]
+    nb, nf = prefill_algorithmic(T, x["hq"], x["hv"], x["dk"], x["dv"], x["n_seqs"], 64, io_bytes=4)
+    nb += x["n_seqs"] * x["hv"] * x["dv"] * x["dk"] * 4  # the initial state is read too
+    out["ragged_prefill_8req_hv32_d128_f32"] = {
+        "ms": ms, "tokens": T, "tokens_per_s": T / (ms * 1e-3),
+        "algorithmic_bytes": nb, "algorithmic_flops": nf,
+        "gbs": nb / (ms * 1e-3) / 1e9, "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "fp32_matrix_tflops": nf / (ms * 1e-3) / 1e12,
+        "fp32_matrix_frac": nf / (ms * 1e-3) / 1e12 / FP32_MATRIX_PEAK_TFLOPS}
+    del q, k, v, o3, f3, init
+
+    # multi-token decode: pool [512, 16, 64, 128], B64, T4, n2, scatter
+    x = synth.mtp_decode_b64_t4()
+    t = {n: x[n].to(dev) for n in ("q", "k", "v", "A_log", "dt_bias", "a", "b", "pool",
+                                   "read_idx", "scatter_idx")}
+    o5 = torch.zeros(x["batch"], x["T"], x["hv"], x["dv"], dtype=torch.bfloat16, device=dev)
+    fn = lambda: gdn.decode(t["q"], t["k"], t["v"], t["A_log"], t["dt_bias"], t["a"], t["b"],
+                            t["pool"], t["read_idx"], scatter_idx=t["scatter_idx"],
+                            scale=x["scale"], out=o5)
+    ms = _time_launches(torch, fn, flush=flush)
+    by = decode_algorithmic(x)
+    out["mtp_decode_b64_t4_n2_h16_dv64_bf16"] = {
+        "ms": ms, "algorithmic_bytes": by, "gbs": by / (ms * 1e-3) / 1e9,
+        "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +260,8 @@ def main():
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the single-head, ragged-fp32 and multi-token-decode timings")
     args = ap.parse_args()
     if args.summarize_traffic:
         print(json.dumps(summarize_traffic(*args.summarize_traffic), indent=1))
@@ -277,9 +366,9 @@ def main():
     if do_prefill:
         gate_ms = [e[0].elapsed_time(e[1]) for e in timed]
         pre_ms = [e[1].elapsed_time(e[2]) for e in timed]
-        tot = statistics.mean(g_ + p_ for g_, p_ in zip(gate_ms, pre_ms))
+        tot = statistics.median(g_ + p_ for g_, p_ in zip(gate_ms, pre_ms))
         pb, pf = prefill_algorithmic(px["T"], px["hq"], px["hv"], px["dk"], px["dv"], B, 64)
-        pm = statistics.mean(pre_ms)
+        pm = statistics.median(pre_ms)
         res["value"] = px["T"] / (tot * 1e-3)
         res["unit"] = "tokens/s"
         gbs = pb / (pm * 1e-3) / 1e9
@@ -290,11 +379,11 @@ def main():
                            "algorithmic_bytes": pb, "algorithmic_flops": pf,
                            "mfma_tflops": tfl, "mfma_peak_tflops": BF16_PEAK_TFLOPS,
                            "mfma_frac": tfl / BF16_PEAK_TFLOPS, "avg_ms": pm}
-        res["prefill"] = {"gate_ms": statistics.mean(gate_ms), "prefill_ms": pm,
+        res["prefill"] = {"gate_ms": statistics.median(gate_ms), "prefill_ms": pm,
                           "prefill_ms_min": min(pre_ms), "tokens_per_s": res["value"]}
     if do_decode:
         dec_ms = [e[3].elapsed_time(e[4]) for e in timed]
-        dm = statistics.mean(dec_ms)
+        dm = statistics.median(dec_ms)
         db_ = decode_algorithmic(dx)
         gbs = db_ / (dm * 1e-3) / 1e9
         res["decode"] = {"kernel": "decode_kernel<bf16,128,128,32>", "bound": "hbm",
@@ -306,6 +395,11 @@ def main():
             res["value"] = gbs
             res["unit"] = "GB/s"
             res["roofline"] = dict(res["decode"])
+
+    if not args.no_extra and args.only is None:
+        del pool, flush
+        torch.cuda.empty_cache()
+        res["extra"] = extra_workloads(torch, gdn, synth, dev)
 
     if not args.no_cpu_baseline and do_prefill:
         res["cpu_baseline"] = cpu_baseline_prefill(px)
