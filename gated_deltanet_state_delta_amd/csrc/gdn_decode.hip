@@ -14,7 +14,10 @@
 // updated in registers for every token and sub-step (dot products reduced
 // across the L lanes with DPP), and written once per required slot with
 // non-temporal 16-byte stores.  One workgroup covers ROWS rows of one
-// (batch row, head); skipped rows exit before touching memory.
+// (batch row, head); skipped rows exit before touching memory.  The per-token
+// inputs of the workgroup (k and q rows, its slice of v, and the gates, which
+// one thread per token computes) are staged in LDS up to TT tokens at a time,
+// so the per-token chain reads LDS instead of waiting on global loads.
 #include "gdn_device.hpp"
 #include "gdn_kernels.hpp"
 
@@ -38,11 +41,23 @@ struct DecodeParams {
   float scale;
 };
 
+// Four io elements moved as one word group (8 bytes for bf16, 16 for fp32).
+template <typename IO> struct Quad4 { typedef u32x4 type; };
+template <> struct Quad4<__bf16> { typedef uint32_t type __attribute__((ext_vector_type(2))); };
+
 template <typename IO, int DK, int DV, int ROWS>
 __global__ void __launch_bounds__(ROWS * (DK / 16))
 decode_kernel(const DecodeParams p) {
   constexpr int L = DK / 16;          // lanes per V-row
   constexpr int NRB = DV / ROWS;      // row blocks per head
+  constexpr int NT = ROWS * L;        // threads
+  constexpr int TT = 8;               // tokens staged per pass
+  constexpr int NJ = 4;               // most sub-steps per token
+  typedef typename Quad4<IO>::type Q4;
+  __shared__ __attribute__((aligned(16))) IO sk[TT * NJ * DK];    // [t][j][DK]
+  __shared__ __attribute__((aligned(16))) IO sq[TT * DK];         // [t][DK]
+  __shared__ __attribute__((aligned(16))) IO sv[TT * NJ * ROWS];  // [t][j][rows of this block]
+  __shared__ float sgam[TT], sbet[TT * NJ];
   const int blk = blockIdx.x;
   const int rb = blk % NRB;
   const int h = (blk / NRB) % p.hv;
@@ -74,29 +89,27 @@ decode_kernel(const DecodeParams p) {
   const float A_log = p.A_log[h];
   const float dt_bias = p.dt_bias[h];
 
-  for (int t = 0; t < p.T; ++t) {
+  // One token: decay, the sub-steps, the readout and the optional scatter.
+  // kp(j): this lane's k of sub-step j; vj(j), beta(j): the row's v and beta;
+  // qp: this lane's q.
+  auto token = [&](int t, float gamma, auto kp, auto vj, auto beta, const IO* qp) {
     const int64_t bt = (int64_t)b * p.T + t;
-    const float gamma = expf(gate_log_decay(A_log, dt_bias, to_f32(ga[bt * p.hv + h])));
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] *= gamma;
     for (int j = 0; j < p.nhh; ++j) {
-      const int64_t btj = bt * p.nhh + j;
-      const IO* kp = k + (btj * p.hq + qh) * DK + 4 * o;
+      const IO* kj = kp(j);
       f4 kf[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kf[i] = load4(kp + i * 4 * L);
-      const float vj = to_f32(v[(btj * p.hv + h) * DV + row]);
-      const float beta = sigmoidf(to_f32(gb[btj * p.hv + h]));
+      for (int i = 0; i < 4; ++i) kf[i] = load4(kj + i * 4 * L);
       float r = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         r += x[i][0] * kf[i][0] + x[i][1] * kf[i][1] + x[i][2] * kf[i][2] + x[i][3] * kf[i][3];
       r = group_sum<L>(r);
-      const float u = beta * (vj - r);
+      const float u = beta(j) * (vj(j) - r);
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] += u * kf[i];
     }
-    const IO* qp = q + (bt * p.hq + qh) * DK + 4 * o;
     float y = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -112,6 +125,53 @@ decode_kernel(const DecodeParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) st_nt(dst + i * 4 * L, x[i]);
       }
+    }
+  };
+
+  if (p.T == 1 && p.nhh == 1) {
+    // a single step: its inputs straight from global memory, issued beside
+    // the state loads (staging would only add a round trip)
+    const int64_t bt = (int64_t)b;
+    const float gamma = expf(gate_log_decay(A_log, dt_bias, to_f32(ga[bt * p.hv + h])));
+    token(0, gamma, [&](int) { return k + (bt * p.hq + qh) * DK + 4 * o; },
+          [&](int) { return to_f32(v[(bt * p.hv + h) * DV + row]); },
+          [&](int) { return sigmoidf(to_f32(gb[bt * p.hv + h])); }, q + (bt * p.hq + qh) * DK + 4 * o);
+  } else {
+    for (int t0 = 0; t0 < p.T; t0 += TT) {
+      const int nt = min(TT, p.T - t0);
+      const int ntj = nt * p.nhh;
+      if (t0 > 0) __syncthreads();  // the previous pass has read the staging area
+      // stage k rows [t][j], q rows [t], v slices [t][j] (4-element groups)
+      // and the gates of this pass
+      const int64_t bt0 = (int64_t)b * p.T + t0;
+      for (int idx = tid; idx < ntj * (DK / 4); idx += NT) {
+        const int tj = idx / (DK / 4), c = idx % (DK / 4);
+        const int t = tj / p.nhh, j = tj % p.nhh;
+        reinterpret_cast<Q4*>(sk)[(t * NJ + j) * (DK / 4) + c] =
+            reinterpret_cast<const Q4*>(k + ((bt0 * p.nhh + tj) * p.hq + qh) * DK)[c];
+      }
+      for (int idx = tid; idx < nt * (DK / 4); idx += NT) {
+        const int t = idx / (DK / 4), c = idx % (DK / 4);
+        reinterpret_cast<Q4*>(sq)[t * (DK / 4) + c] =
+            reinterpret_cast<const Q4*>(q + ((bt0 + t) * p.hq + qh) * DK)[c];
+      }
+      for (int idx = tid; idx < ntj * (ROWS / 4); idx += NT) {
+        const int tj = idx / (ROWS / 4), c = idx % (ROWS / 4);
+        const int t = tj / p.nhh, j = tj % p.nhh;
+        reinterpret_cast<Q4*>(sv)[(t * NJ + j) * (ROWS / 4) + c] =
+            reinterpret_cast<const Q4*>(v + ((bt0 * p.nhh + tj) * p.hv + h) * DV + rb * ROWS)[c];
+      }
+      for (int idx = tid; idx < nt; idx += NT)
+        sgam[idx] = expf(gate_log_decay(A_log, dt_bias, to_f32(ga[(bt0 + idx) * p.hv + h])));
+      for (int idx = tid; idx < ntj; idx += NT) {
+        const int t = idx / p.nhh, j = idx % p.nhh;
+        sbet[t * NJ + j] = sigmoidf(to_f32(gb[(bt0 * p.nhh + idx) * p.hv + h]));
+      }
+      __syncthreads();
+      for (int tl = 0; tl < nt; ++tl)
+        token(t0 + tl, sgam[tl], [&](int j) -> const IO* { return sk + (tl * NJ + j) * DK + 4 * o; },
+              [&](int j) { return to_f32(sv[(tl * NJ + j) * ROWS + (row - rb * ROWS)]); },
+              [&](int j) { return sbet[tl * NJ + j]; }, sq + tl * DK + 4 * o);
     }
   }
   if (!p.scatter_idx && !p.disable && wr >= 0 && wr < p.pool_size) {
