@@ -63,14 +63,14 @@ def _load():
                 ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                 _dp, _dp, _dp, _dp, ctypes.c_int32, _dp, _ip, _dp, ctypes.c_double,
-                _dp, _dp, ctypes.c_int32]
+                _dp, _dp, ctypes.c_int32, ctypes.c_double, _dp, _dp, _dp, _dp]
             lib.gdno_decode.restype = ctypes.c_int
             lib.gdno_decode.argtypes = [
                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                 ctypes.c_int32, ctypes.c_int32,
                 _dp, _dp, _dp, _dp, _dp, _dp, _dp,
                 _dp, ctypes.c_int32, _ip, _ip, _ip, ctypes.c_int32, ctypes.c_double,
-                _dp, ctypes.c_int32]
+                _dp, ctypes.c_int32, ctypes.c_double]
             _lib = lib
     return _lib
 
@@ -136,12 +136,16 @@ def gate(A_log, dt_bias, a=None, b=None):
 
 def prefill(q, k, v, decay, beta, *, decay_is_gamma=False, cu_seqlens=None,
             n_seqs=None, seq_len=None, initial_state=None, scale=1.0,
-            out_init=None, nthreads=None):
+            out_init=None, nthreads=None, qk_l2norm_eps=None, A_log=None, dt_bias=None,
+            a=None, b=None):
     """Sequential fp64 prefill.
 
     q, k: [T, hq, dk]; v: [T, hv, dv]; decay, beta: [T, hv];
     cu_seqlens: [N+1] or None (then n_seqs * seq_len == T);
     initial_state: [N, hv, dv, dk] V-major or None.
+    qk_l2norm_eps: None (q, k used as given) or the epsilon of the in-kernel
+    L2 norm x / sqrt(sum x^2 + eps).  a, b [T, hv] with A_log, dt_bias [hv]:
+    the fused gate (decay and beta are then ignored and may be None).
     Returns (out [T, hv, dv], final_state [N, hv, dv, dk]) as float64 arrays.
     out rows no request covers hold out_init (default NaN).
     """
@@ -165,10 +169,13 @@ def prefill(q, k, v, decay, beta, *, decay_is_gamma=False, cu_seqlens=None,
     else:
         out = _f64(out_init).copy()
     fin = np.zeros((n_seqs, hv, dv, dk))
+    fused = [_f64(x) for x in (A_log, dt_bias, a, b)]
     rc = lib.gdno_prefill(n_seqs, T, seq_len, hq, hv, dk, dv, _p(q64), _p(k64), _p(v64),
                           _p(d64), 1 if decay_is_gamma else 0, _p(b64), _p(cu, _ip),
                           _p(init), float(scale), _p(out), _p(fin),
-                          nthreads or default_threads())
+                          nthreads or default_threads(),
+                          -1.0 if qk_l2norm_eps is None else float(qk_l2norm_eps),
+                          *[_p(x) for x in fused])
     if rc != 0:
         raise ValueError("gdno_prefill rejected its arguments")
     return out, fin
@@ -176,13 +183,14 @@ def prefill(q, k, v, decay, beta, *, decay_is_gamma=False, cu_seqlens=None,
 
 def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None,
            scatter_idx=None, disable_state_update=False, scale=1.0, out_init=None,
-           nthreads=None):
+           nthreads=None, qk_l2norm_eps=None):
     """fp64 slot-pool decode.
 
     q [B,T,hq,dk]; k [B,T,n,hq,dk]; v [B,T,n,hv,dv]; A_log, dt_bias [hv];
     a [B,T,hv]; b [B,T,n,hv]; pool [P,hv,dv,dk] (not modified: a float64 copy is
     updated and returned); read_idx [B]; write_idx [B] or None;
-    scatter_idx [B,T] or None.
+    scatter_idx [B,T] or None; qk_l2norm_eps: None or the epsilon of the
+    in-kernel L2 norm of q and k (use_qk_l2norm).
     Returns (out [B,T,hv,dv], pool_after [P,hv,dv,dk]) as float64 arrays;
     out rows of skipped batch rows hold out_init (default zeros).
     """
@@ -198,7 +206,8 @@ def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None,
                          _p(_f64(A_log)), _p(_f64(dt_bias)), _p(_f64(a)), _p(_f64(b)),
                          _p(pool64), P, _p(_i64(read_idx), _ip), _p(_i64(write_idx), _ip),
                          _p(_i64(scatter_idx), _ip), 1 if disable_state_update else 0,
-                         float(scale), _p(out), nthreads or default_threads())
+                         float(scale), _p(out), nthreads or default_threads(),
+                         -1.0 if qk_l2norm_eps is None else float(qk_l2norm_eps))
     if rc != 0:
         raise ValueError("gdno_decode rejected its arguments")
     return out, pool64

@@ -84,6 +84,17 @@ static void readout(int dk, int dv, const double* S, const double* q, double sca
   }
 }
 
+/* In-kernel L2 normalisation of a query or key head vector, as the FlashInfer
+ * decode page states it for use_qk_l2norm: x * rsqrt(sum(x^2) + eps).  The
+ * ONNX card's qk_l2_norm names only the epsilon (1e-12); the same form is
+ * read there. */
+static void l2_normalize(int n, const double* x, double eps, double* out) {
+  double ss = 0.0;
+  for (int i = 0; i < n; ++i) ss += x[i] * x[i];
+  const double r = 1.0 / sqrt(ss + eps);
+  for (int i = 0; i < n; ++i) out[i] = x[i] * r;
+}
+
 /* V-major [dv][dk] <-> K-major [dk][dv]. */
 static void vmajor_to_kmajor(int dk, int dv, const double* vm, double* km) {
   for (int j = 0; j < dv; ++j)
@@ -142,6 +153,8 @@ typedef struct {
   const int64_t* cu;
   double scale;
   double *out, *final_state;
+  double qk_eps;                      /* < 0: no in-kernel L2 norm */
+  const double *A_log, *dt_bias, *a, *b;  /* fused gate when a != NULL */
 } prefill_ctx;
 
 static int64_t clamp64(int64_t x, int64_t lo, int64_t hi) {
@@ -170,6 +183,8 @@ static void prefill_unit(void* vctx, int64_t unit) {
 
   double* S = (double*)calloc((size_t)dk * dv, sizeof(double));
   double* tmp = (double*)malloc(sizeof(double) * (size_t)dv);
+  double* qn = (double*)malloc(sizeof(double) * (size_t)dk);
+  double* kn = (double*)malloc(sizeof(double) * (size_t)dk);
   const size_t st_off = ((size_t)r * c->hv + h) * (size_t)dv * dk;
   if (c->init) vmajor_to_kmajor(dk, dv, c->init + st_off, S);
 
@@ -177,12 +192,26 @@ static void prefill_unit(void* vctx, int64_t unit) {
     const double* q = c->q + ((size_t)t * c->hq + qh) * dk;
     const double* k = c->k + ((size_t)t * c->hq + qh) * dk;
     const double* v = c->v + ((size_t)t * c->hv + h) * dv;
-    const double d = c->decay[(size_t)t * c->hv + h];
-    const double gamma = c->decay_is_gamma ? d : exp(d);
-    const double beta = c->beta[(size_t)t * c->hv + h];
+    if (c->qk_eps >= 0.0) {
+      l2_normalize(dk, q, c->qk_eps, qn);
+      l2_normalize(dk, k, c->qk_eps, kn);
+      q = qn;
+      k = kn;
+    }
+    const size_t e = (size_t)t * c->hv + h;
+    double gamma, beta;
+    if (c->a) {  /* fused gate: the qwen gate and a sigmoid beta */
+      gamma = exp(gate_log_decay(c->A_log[h], c->dt_bias[h], c->a[e]));
+      beta = sigmoid(c->b[e]);
+    } else {
+      gamma = c->decay_is_gamma ? c->decay[e] : exp(c->decay[e]);
+      beta = c->beta[e];
+    }
     gd_step(dk, dv, S, k, v, gamma, beta, tmp);
     readout(dk, dv, S, q, c->scale, c->out + ((size_t)t * c->hv + h) * dv);
   }
+  free(kn);
+  free(qn);
   /* final state after the request's last token; an empty request copies its
    * incoming state (zeros when there is none) */
   kmajor_to_vmajor(dk, dv, S, c->final_state + st_off);
@@ -195,13 +224,18 @@ int gdno_prefill(int32_t n_seqs, int64_t total_tokens, int32_t seq_len,
                  const double* q, const double* k, const double* v,
                  const double* decay, int32_t decay_is_gamma, const double* beta,
                  const int64_t* cu, const double* init, double scale,
-                 double* out, double* final_state, int32_t nthreads) {
+                 double* out, double* final_state, int32_t nthreads,
+                 double qk_l2norm_eps, const double* A_log, const double* dt_bias,
+                 const double* a, const double* b) {
   if (n_seqs < 0 || total_tokens < 0 || hq <= 0 || hv <= 0 || dk <= 0 || dv <= 0)
     return -1;
   if (hv % hq != 0) return -1;
   if (!cu && (int64_t)n_seqs * seq_len != total_tokens) return -1;
+  if (a && (!b || !A_log || !dt_bias)) return -1;
+  if (!a && (!decay || !beta) && total_tokens > 0) return -1;
   prefill_ctx c = {n_seqs, seq_len, hq, hv, dk, dv, decay_is_gamma, total_tokens,
-                   q, k, v, decay, beta, init, cu, scale, out, final_state};
+                   q, k, v, decay, beta, init, cu, scale, out, final_state,
+                   qk_l2norm_eps, A_log, dt_bias, a, b};
   run_units(prefill_unit, &c, (int64_t)n_seqs * hv, nthreads);
   return 0;
 }
@@ -216,6 +250,7 @@ typedef struct {
   const int64_t *read, *write, *scatter;
   double scale;
   double* out;
+  double qk_eps; /* < 0: no in-kernel L2 norm */
 } decode_ctx;
 
 static int slot_ok(int64_t s, int32_t P) { return s >= 0 && s < P; }
@@ -239,6 +274,8 @@ static void decode_unit(void* vctx, int64_t unit) {
 
   double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
   double* tmp = (double*)malloc(sizeof(double) * (size_t)dv);
+  double* qn = (double*)malloc(sizeof(double) * (size_t)dk);
+  double* kn = (double*)malloc(sizeof(double) * (size_t)dk);
   vmajor_to_kmajor(dk, dv, c->pool0 + (size_t)rd * slot_elems + head_off, S);
 
   for (int32_t t = 0; t < c->T; ++t) {
@@ -250,11 +287,19 @@ static void decode_unit(void* vctx, int64_t unit) {
     for (int32_t j = 0; j < c->n_hh; ++j) {
       const size_t btj = bt * c->n_hh + j;
       const double* k = c->k + (btj * c->hq + qh) * dk;
+      if (c->qk_eps >= 0.0) {
+        l2_normalize(dk, k, c->qk_eps, kn);
+        k = kn;
+      }
       const double* v = c->v + (btj * c->hv + h) * dv;
       const double beta = sigmoid(c->b[btj * c->hv + h]);
       gd_step(dk, dv, S, k, v, 1.0, beta, tmp); /* delta sub-step, no decay */
     }
     const double* q = c->q + (bt * c->hq + qh) * dk;
+    if (c->qk_eps >= 0.0) {
+      l2_normalize(dk, q, c->qk_eps, qn);
+      q = qn;
+    }
     readout(dk, dv, S, q, c->scale, c->out + (bt * c->hv + h) * dv);
     if (c->scatter) {
       const int64_t s = c->scatter[bt];
@@ -263,6 +308,8 @@ static void decode_unit(void* vctx, int64_t unit) {
   }
   if (!c->scatter && !c->disable && slot_ok(wr, c->P))
     kmajor_to_vmajor(dk, dv, S, c->pool + (size_t)wr * slot_elems + head_off);
+  free(kn);
+  free(qn);
   free(tmp);
   free(S);
 }
@@ -275,7 +322,7 @@ int gdno_decode(int32_t B, int32_t T, int32_t n_hh, int32_t hq, int32_t hv,
                 double* pool, int32_t P,
                 const int64_t* read, const int64_t* write, const int64_t* scatter,
                 int32_t disable_state_update, double scale,
-                double* out, int32_t nthreads) {
+                double* out, int32_t nthreads, double qk_l2norm_eps) {
   if (B < 0 || T <= 0 || n_hh <= 0 || hq <= 0 || hv <= 0 || dk <= 0 || dv <= 0 || P < 0)
     return -1;
   if (hv % hq != 0) return -1;
@@ -286,7 +333,7 @@ int gdno_decode(int32_t B, int32_t T, int32_t n_hh, int32_t hq, int32_t hv,
   memcpy(pool0, pool, sizeof(double) * pool_elems);
   decode_ctx c = {B, T, n_hh, hq, hv, dk, dv, P, disable_state_update,
                   q, k, v, A_log, dt_bias, a, b, pool0, pool,
-                  read, write, scatter, scale, out};
+                  read, write, scatter, scale, out, qk_l2norm_eps};
   run_units(decode_unit, &c, (int64_t)B * hv, nthreads);
   free(pool0);
   return 0;

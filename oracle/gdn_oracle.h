@@ -51,6 +51,11 @@ void gdno_gate(int64_t n, int32_t hv, const double* A_log, const double* dt_bias
  *   decay    [T, hv]          log-space decay when decay_is_gamma == 0,
  *                             gamma itself when decay_is_gamma != 0
  *   beta     [T, hv]          effective update rate
+ *   A_log, dt_bias [hv], a, b [T, hv]: when a != NULL the gates come from
+ *                             them (fused gate, as gdno_gate) and decay / beta
+ *                             are not read
+ *   qk_l2norm_eps             >= 0: every q and k head vector is replaced by
+ *                             x / sqrt(sum(x^2) + qk_l2norm_eps) first; < 0: none
  *   cu       [n_seqs + 1]     or NULL: request r covers [r*seq_len, (r+1)*seq_len)
  *   init     [n_seqs, hv, dv, dk] V-major, or NULL (zeros)
  *   out      [T, hv, dv]      rows of tokens that no request covers are left as given
@@ -61,9 +66,13 @@ int gdno_prefill(int32_t n_seqs, int64_t total_tokens, int32_t seq_len,
                  const double* q, const double* k, const double* v,
                  const double* decay, int32_t decay_is_gamma, const double* beta,
                  const int64_t* cu, const double* init, double scale,
-                 double* out, double* final_state, int32_t nthreads);
+                 double* out, double* final_state, int32_t nthreads,
+                 double qk_l2norm_eps, const double* A_log, const double* dt_bias,
+                 const double* a, const double* b);
 
-/* Slot-pool decode with n_hh Householder sub-steps per token.
+/* Slot-pool decode with n_hh Householder sub-steps per token.  With
+ * qk_l2norm_eps >= 0 every q and k head vector is first replaced by
+ * x / sqrt(sum(x^2) + qk_l2norm_eps) (use_qk_l2norm); < 0: none.
  *   q [B, T, hq, dk]   k [B, T, n_hh, hq, dk]   v [B, T, n_hh, hv, dv]
  *   A_log, dt_bias [hv]   a [B, T, hv]   b [B, T, n_hh, hv]
  *   pool [P, hv, dv, dk]  V-major, updated in place (snapshot semantics: every
@@ -79,7 +88,7 @@ int gdno_decode(int32_t B, int32_t T, int32_t n_hh, int32_t hq, int32_t hv,
                 double* pool, int32_t P,
                 const int64_t* read, const int64_t* write, const int64_t* scatter,
                 int32_t disable_state_update, double scale,
-                double* out, int32_t nthreads);
+                double* out, int32_t nthreads, double qk_l2norm_eps);
 
 #ifdef __cplusplus
 }

@@ -452,3 +452,113 @@ def test_decode_scatter_first_token_equals_one_token_call():
     for b in range(2):
         s = int(sc1[b, 0])
         np.testing.assert_array_equal(pool[s], pool1[s])
+
+
+# ----------------------------------------------------------------------------
+# in-kernel q/k L2 norm and the fused gate inside prefill (the ONNX card's
+# qk_l2_norm attribute; the FlashInfer page's use_qk_l2norm and fused gate)
+# ----------------------------------------------------------------------------
+
+def _raw_qk(seed, T=40, hq=2, dk=8):
+    """q and k that are far from unit length (norms spread over 0.2 .. 5)."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(T, hq, dk, generator=g, dtype=torch.float64)
+    k = torch.randn(T, hq, dk, generator=g, dtype=torch.float64)
+    s = torch.rand(T, hq, 1, generator=g, dtype=torch.float64) * 4.8 + 0.2
+    return (q * s).numpy(), (k / s).numpy()
+
+
+def test_qk_l2norm_invariant_to_rescaling_q_and_k():
+    """With the norm on (eps = 0), scaling any q or k head vector by a positive
+    factor changes nothing; with it off the outputs change."""
+    x = synth.prefill_inputs(60, lengths=[40], hq=2, hv=4, dk=8, dv=6, gate="gamma",
+                             gamma_range=(0.6, 1.0), init_std=0.3)
+    q, k = _raw_qk(61)
+    g = torch.Generator().manual_seed(62)
+    cq = (torch.rand(40, 2, 1, generator=g, dtype=torch.float64) * 3 + 0.1).numpy()
+    ck = (torch.rand(40, 2, 1, generator=g, dtype=torch.float64) * 3 + 0.1).numpy()
+    kw = dict(decay_is_gamma=True, cu_seqlens=x["cu_seqlens"], initial_state=x["initial_state"],
+              scale=0.7)
+    o1, f1 = oracle.prefill(q, k, x["v"], x["gamma"], x["beta"], qk_l2norm_eps=0.0, **kw)
+    o2, f2 = oracle.prefill(q * cq, k * ck, x["v"], x["gamma"], x["beta"], qk_l2norm_eps=0.0, **kw)
+    np.testing.assert_allclose(o2, o1, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(f2, f1, rtol=1e-11, atol=1e-12)
+    o3, _ = oracle.prefill(q * cq, k * ck, x["v"], x["gamma"], x["beta"], **kw)
+    assert np.abs(o3 - o1).max() > 1e-3
+
+
+def test_qk_l2norm_equals_prenormalised_inputs():
+    """The norm is x / sqrt(sum x^2 + eps): the same as normalising the inputs
+    with numpy (eps folded into the norm) and running without it."""
+    x = synth.prefill_inputs(63, lengths=[17, 0, 23], hq=1, hv=2, dk=16, dv=8, gate="log",
+                             gamma_range=(0.5, 1.0))
+    q, k = _raw_qk(64, T=40, hq=1, dk=16)
+    eps = 0.25  # large enough to matter
+    qn = q / np.sqrt((q * q).sum(-1, keepdims=True) + eps)
+    kn = k / np.sqrt(np.einsum("thd,thd->th", k, k)[..., None] + eps)
+    kw = dict(cu_seqlens=x["cu_seqlens"], scale=0.5)
+    o1, f1 = oracle.prefill(q, k, x["v"], x["log_decay"], x["beta"], qk_l2norm_eps=eps, **kw)
+    o2, f2 = oracle.prefill(qn, kn, x["v"], x["log_decay"], x["beta"], **kw)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(f1, f2, rtol=1e-12, atol=1e-13)
+
+
+def test_qk_l2norm_of_a_zero_vector_is_zero():
+    """eps > 0 keeps an all-zero key finite: it normalises to zero, so the
+    token writes nothing and only decays the state."""
+    x = synth.prefill_inputs(65, n_seqs=1, seq_len=6, hq=1, hv=1, dk=4, dv=3, gate="gamma",
+                             gamma_range=(0.5, 0.9), init_std=1.0)
+    k = x["k"].clone().double()
+    k[2] = 0.0
+    q = x["q"].clone().double()
+    q[2] = 0.0
+    out, fin = oracle.prefill(q, k, x["v"], x["gamma"], x["beta"], decay_is_gamma=True,
+                              n_seqs=1, seq_len=6, initial_state=x["initial_state"],
+                              qk_l2norm_eps=1e-12)
+    assert np.isfinite(out).all() and np.isfinite(fin).all()
+    assert np.abs(out[2]).max() == 0.0
+    # the state after token 2 is the state after token 1 times gamma_2
+    _, f1 = oracle.prefill(q[:2], k[:2], x["v"][:2], x["gamma"][:2], x["beta"][:2],
+                           decay_is_gamma=True, n_seqs=1, seq_len=2,
+                           initial_state=x["initial_state"], qk_l2norm_eps=1e-12)
+    _, f2 = oracle.prefill(q[:3], k[:3], x["v"][:3], x["gamma"][:3], x["beta"][:3],
+                           decay_is_gamma=True, n_seqs=1, seq_len=3,
+                           initial_state=x["initial_state"], qk_l2norm_eps=1e-12)
+    np.testing.assert_allclose(f2, f1 * float(x["gamma"][2, 0]), rtol=1e-13, atol=1e-15)
+
+
+def test_fused_gate_prefill_equals_gate_then_prefill():
+    """Gates computed inside the prefill (qwen gate, sigmoid beta) equal the
+    separate gate call (itself pinned to torch's routines above)."""
+    x = synth.prefill_inputs(66, lengths=[30, 11], hq=2, hv=4, dk=8, dv=8, gate="qwen",
+                             init_std=0.2)
+    g, _, beta = oracle.gate(x["A_log"], x["dt_bias"], x["a"], x["b"])
+    kw = dict(cu_seqlens=x["cu_seqlens"], initial_state=x["initial_state"], scale=0.3)
+    o1, f1 = oracle.prefill(x["q"], x["k"], x["v"], g, beta, **kw)
+    o2, f2 = oracle.prefill(x["q"], x["k"], x["v"], None, None, A_log=x["A_log"],
+                            dt_bias=x["dt_bias"], a=x["a"], b=x["b"], **kw)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(f1, f2)
+
+
+def test_decode_qk_l2norm_invariance_and_prenormalised_inputs():
+    x = _dec(67, T=3, n_hh=2, dk=8)
+    g = torch.Generator().manual_seed(68)
+    cq = (torch.rand(*x["q"].shape[:3], 1, generator=g, dtype=torch.float64) * 3 + 0.1)
+    ck = (torch.rand(*x["k"].shape[:4], 1, generator=g, dtype=torch.float64) * 3 + 0.1)
+    o1, p1 = _run_dec(x, qk_l2norm_eps=0.0)
+    y = dict(x)
+    y["q"] = x["q"].double() * cq
+    y["k"] = x["k"].double() * ck
+    o2, p2 = _run_dec(y, qk_l2norm_eps=0.0)
+    np.testing.assert_allclose(o2, o1, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(p2, p1, rtol=1e-11, atol=1e-12)
+    eps = 0.5
+    z = dict(y)
+    qd, kd = y["q"].numpy(), y["k"].numpy()
+    z["q"] = qd / np.sqrt((qd * qd).sum(-1, keepdims=True) + eps)
+    z["k"] = kd / np.sqrt((kd * kd).sum(-1, keepdims=True) + eps)
+    o3, p3 = _run_dec(y, qk_l2norm_eps=eps)
+    o4, p4 = _run_dec(z)
+    np.testing.assert_allclose(o3, o4, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(p3, p4, rtol=1e-12, atol=1e-13)
