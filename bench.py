@@ -201,6 +201,24 @@ def extra_workloads(torch, gdn, synth, dev):
     out["copy_1gib"] = {"ms": cm, "gbs": 2 * (1 << 30) / (cm * 1e-3) / 1e9}
     del src, dst
 
+    # the chunked-prefill workload with the gate fused into the prefill and the
+    # in-kernel q/k L2 norm (one launch instead of gate + prefill)
+    px = synth.chunked_prefill_b4_s4096()
+    B, S = px["n_seqs"], px["seq_len"]
+    q = px["q"].to(dev).view(B, S, px["hq"], px["dk"])
+    k = px["k"].to(dev).view(B, S, px["hq"], px["dk"])
+    v = px["v"].to(dev).view(B, S, px["hv"], px["dv"])
+    A_log, dt_bias = px["A_log"].to(dev), px["dt_bias"].to(dev)
+    a = px["a"].to(dev).view(B, S, -1)
+    b = px["b"].to(dev).view(B, S, -1)
+    o2 = torch.empty_like(v)
+    f2 = torch.empty(B, px["hv"], px["dv"], px["dk"], dtype=torch.float32, device=dev)
+    fn = lambda: gdn.prefill(q, k, v, None, None, scale=px["scale"], out=o2, final_state=f2,
+                             A_log=A_log, dt_bias=dt_bias, a=a, b=b, qk_l2norm=True)
+    ms = _time_launches(torch, fn, flush=flush)
+    out["chunked_prefill_fused_gate_qk_l2norm"] = {"ms": ms, "tokens_per_s": px["T"] / (ms * 1e-3)}
+    del q, k, v, o2, f2
+
     # single-head scan: B2 x S64, d16, fp32 (launch latency)
     x = synth.single_head_scan()
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))

@@ -125,7 +125,9 @@ def gate(A_log, dt_bias, a=None, b=None, *, want_gamma=False, log_decay_out=None
 
 
 def prefill_args(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None,
-                 initial_state=None, scale=None, chunk_size=0, out=None, final_state=None):
+                 initial_state=None, scale=None, chunk_size=0, out=None, final_state=None,
+                 qk_l2norm=False, qk_l2norm_eps=1e-12, A_log=None, dt_bias=None, a=None,
+                 b=None):
     """Validate shapes and build the gdn_prefill_args struct (device-agnostic).
 
     Returns (args, keep, out, final_state): `keep` holds every tensor whose
@@ -154,8 +156,26 @@ def prefill_args(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None,
         raise ValueError("q, k and v must share a dtype")
     dt = _io_dtype(q3)
     q3, k3, v3 = _strided3(q3), _strided3(k3), _strided3(v3)
-    decay = _f32c(decay.reshape(-1, hv) if decay.dim() == 3 else decay, "decay", (T, hv))
-    beta = _f32c(beta.reshape(-1, hv) if beta.dim() == 3 else beta, "beta", (T, hv))
+    fused = a is not None
+    if fused:
+        if b is None or A_log is None or dt_bias is None:
+            raise ValueError("the fused gate needs A_log, dt_bias, a and b")
+        ga = a.reshape(-1, hv) if a.dim() == 3 else a
+        gb = b.reshape(-1, hv) if b.dim() == 3 else b
+        _shape(ga, "a", (T, hv))
+        _shape(gb, "b", (T, hv))
+        if ga.dtype != q3.dtype or gb.dtype != q3.dtype:
+            raise ValueError("a and b must have q's dtype")
+        ga, gb = ga.contiguous(), gb.contiguous()
+        A_log = _f32c(A_log, "A_log", (hv,))
+        dt_bias = _f32c(dt_bias, "dt_bias", (hv,))
+        decay = beta = None
+    else:
+        if decay is None or beta is None:
+            raise ValueError("decay and beta are required without the fused gate")
+        decay = _f32c(decay.reshape(-1, hv) if decay.dim() == 3 else decay, "decay", (T, hv))
+        beta = _f32c(beta.reshape(-1, hv) if beta.dim() == 3 else beta, "beta", (T, hv))
+        ga = gb = None
     if cu_seqlens is not None:
         if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
             raise ValueError("cu_seqlens must be [N + 1]")
@@ -182,52 +202,67 @@ def prefill_args(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None,
     _shape(final_state, "final_state", (n_seqs, hv, dv, dk))
     if final_state.dtype != torch.float32 or not final_state.is_contiguous():
         raise ValueError("final_state must be contiguous float32")
-    a = _lib.PrefillArgs()
-    a.n_seqs, a.seq_len, a.total_tokens = n_seqs, seq_len, T
-    a.hq, a.hv, a.dk, a.dv = hq, hv, dk, dv
-    a.io_dtype = dt
-    a.decay_kind = _lib.GDN_DECAY_GAMMA if decay_kind == "gamma" else _lib.GDN_DECAY_LOG
-    a.chunk_size = int(chunk_size)
-    a.scale = (1.0 / math.sqrt(dk)) if scale is None else float(scale)
-    a.q, a.q_stride_token, a.q_stride_head = q3.data_ptr(), q3.stride(0), q3.stride(1)
-    a.k, a.k_stride_token, a.k_stride_head = k3.data_ptr(), k3.stride(0), k3.stride(1)
-    a.v, a.v_stride_token, a.v_stride_head = v3.data_ptr(), v3.stride(0), v3.stride(1)
-    a.out, a.out_stride_token, a.out_stride_head = out3.data_ptr(), out3.stride(0), out3.stride(1)
-    a.decay, a.beta = decay.data_ptr(), beta.data_ptr()
-    a.cu_seqlens = None if cu is None else cu.data_ptr()
-    a.initial_state = None if initial_state is None else initial_state.data_ptr()
-    a.final_state = final_state.data_ptr()
-    keep = (q3, k3, v3, decay, beta, cu, initial_state, out3, final_state)
-    return a, keep, out, final_state
+    args = _lib.PrefillArgs()
+    args.n_seqs, args.seq_len, args.total_tokens = n_seqs, seq_len, T
+    args.hq, args.hv, args.dk, args.dv = hq, hv, dk, dv
+    args.io_dtype = dt
+    args.decay_kind = _lib.GDN_DECAY_GAMMA if decay_kind == "gamma" else _lib.GDN_DECAY_LOG
+    args.chunk_size = int(chunk_size)
+    args.scale = (1.0 / math.sqrt(dk)) if scale is None else float(scale)
+    args.q, args.q_stride_token, args.q_stride_head = q3.data_ptr(), q3.stride(0), q3.stride(1)
+    args.k, args.k_stride_token, args.k_stride_head = k3.data_ptr(), k3.stride(0), k3.stride(1)
+    args.v, args.v_stride_token, args.v_stride_head = v3.data_ptr(), v3.stride(0), v3.stride(1)
+    args.out, args.out_stride_token, args.out_stride_head = \
+        out3.data_ptr(), out3.stride(0), out3.stride(1)
+    args.decay = None if decay is None else decay.data_ptr()
+    args.beta = None if beta is None else beta.data_ptr()
+    args.cu_seqlens = None if cu is None else cu.data_ptr()
+    args.initial_state = None if initial_state is None else initial_state.data_ptr()
+    args.final_state = final_state.data_ptr()
+    args.qk_l2norm = 1 if qk_l2norm else 0
+    args.qk_l2norm_eps = float(qk_l2norm_eps)
+    if fused:
+        args.A_log, args.dt_bias = A_log.data_ptr(), dt_bias.data_ptr()
+        args.gate_a, args.gate_b = ga.data_ptr(), gb.data_ptr()
+    keep = (q3, k3, v3, decay, beta, cu, initial_state, out3, final_state, A_log, dt_bias, ga, gb)
+    return args, keep, out, final_state
 
 
 def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_state=None,
-            scale=None, chunk_size=0, out=None, final_state=None, stream=None):
+            scale=None, chunk_size=0, out=None, final_state=None, stream=None,
+            qk_l2norm=False, qk_l2norm_eps=1e-12, A_log=None, dt_bias=None, a=None, b=None):
     """Chunked prefill.
 
     q, k: [T, hq, dk] (or [B, S, hq, dk], then uniform packing with seq_len S);
     v: [T, hv, dv] (or [B, S, hv, dv]); decay, beta: [T, hv] float32 (decay is
     log-space for decay_kind="log", gamma for "gamma"); cu_seqlens: [N+1]
     int32/int64 or None; initial_state: [N, hv, dv, dk] float32 or None.
-    scale None means 1/sqrt(dk).  Returns (out, final_state [N, hv, dv, dk]
-    float32); out is [T, hv, dv] (or [B, S, hv, dv]) in q's dtype.
+    scale None means 1/sqrt(dk).  qk_l2norm: use every q and k head vector as
+    x / sqrt(sum x^2 + qk_l2norm_eps) (the ONNX card's qk_l2_norm).  a, b
+    ([T, hv] or [B, S, hv] in q's dtype) with A_log, dt_bias [hv]: the fused
+    gate, computed in the kernel (decay and beta are then ignored; pass None).
+    Returns (out, final_state [N, hv, dv, dk] float32); out is [T, hv, dv] (or
+    [B, S, hv, dv]) in q's dtype.
     """
     lib = _lib.load()
     for name, t in (("q", q), ("k", k), ("v", v), ("decay", decay), ("beta", beta),
                     ("cu_seqlens", cu_seqlens), ("initial_state", initial_state),
-                    ("out", out), ("final_state", final_state)):
+                    ("out", out), ("final_state", final_state), ("A_log", A_log),
+                    ("dt_bias", dt_bias), ("a", a), ("b", b)):
         _dev(t, name)
-    a, keep, out, final_state = prefill_args(
+    args, keep, out, final_state = prefill_args(
         q, k, v, decay, beta, decay_kind=decay_kind, cu_seqlens=cu_seqlens,
         initial_state=initial_state, scale=scale, chunk_size=chunk_size, out=out,
-        final_state=final_state)
-    _lib.check(lib.gdn_prefill(ctypes.byref(a), _stream(stream)))
+        final_state=final_state, qk_l2norm=qk_l2norm, qk_l2norm_eps=qk_l2norm_eps,
+        A_log=A_log, dt_bias=dt_bias, a=a, b=b)
+    _lib.check(lib.gdn_prefill(ctypes.byref(args), _stream(stream)))
     del keep
     return out, final_state
 
 
 def decode_args(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None,
-                scatter_idx=None, disable_state_update=False, scale=None, out=None):
+                scatter_idx=None, disable_state_update=False, scale=None, out=None,
+                use_qk_l2norm=False, qk_l2norm_eps=1e-6):
     """Validate shapes and build the gdn_decode_args struct (device-agnostic).
 
     Returns (args, keep, out)."""
@@ -273,18 +308,23 @@ def decode_args(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None
     d.write_idx = None if write_idx is None else write_idx.data_ptr()
     d.scatter_idx = None if scatter_idx is None else scatter_idx.data_ptr()
     d.out = out.data_ptr()
+    d.qk_l2norm = 1 if use_qk_l2norm else 0
+    d.qk_l2norm_eps = float(qk_l2norm_eps)
     keep = (q, k, v, a, b, A_log, dt_bias, read_idx, write_idx, scatter_idx)
     return d, keep, out
 
 
 def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None, scatter_idx=None,
-           disable_state_update=False, scale=None, out=None, stream=None):
+           disable_state_update=False, scale=None, out=None, stream=None, use_qk_l2norm=False,
+           qk_l2norm_eps=1e-6):
     """Slot-pool decode with Householder sub-steps (one fused launch).
 
     q [B, T, hq, dk]; k [B, T, n, hq, dk]; v [B, T, n, hv, dv]; A_log, dt_bias
     [hv] float32; a [B, T, hv]; b [B, T, n, hv]; pool [P, hv, dv, dk] float32
     (updated in place); read_idx [B]; write_idx [B] or None; scatter_idx [B, T]
-    or None.  scale None means 1/sqrt(dk).  Returns (out [B, T, hv, dv], pool);
+    or None.  scale None means 1/sqrt(dk).  use_qk_l2norm: use every q and k
+    head vector as x / sqrt(sum x^2 + qk_l2norm_eps) (the FlashInfer page's
+    use_qk_l2norm; off by default here).  Returns (out [B, T, hv, dv], pool);
     rows of skipped batch rows keep out's previous contents (zeros when out is
     None).
     """
@@ -295,7 +335,8 @@ def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None, sca
         _dev(t, name)
     d, keep, out = decode_args(q, k, v, A_log, dt_bias, a, b, pool, read_idx,
                                write_idx=write_idx, scatter_idx=scatter_idx,
-                               disable_state_update=disable_state_update, scale=scale, out=out)
+                               disable_state_update=disable_state_update, scale=scale, out=out,
+                               use_qk_l2norm=use_qk_l2norm, qk_l2norm_eps=qk_l2norm_eps)
     _lib.check(lib.gdn_decode(ctypes.byref(d), _stream(stream)))
     del keep
     return out, pool

@@ -36,6 +36,8 @@ class PrefillArgs(ctypes.Structure):
         ("out", _vp), ("out_stride_token", _i64), ("out_stride_head", _i64),
         ("decay", _vp), ("beta", _vp), ("cu_seqlens", _vp),
         ("initial_state", _vp), ("final_state", _vp),
+        ("qk_l2norm", _i32), ("qk_l2norm_eps", _f32),
+        ("A_log", _vp), ("dt_bias", _vp), ("gate_a", _vp), ("gate_b", _vp),
     ]
 
 
@@ -50,6 +52,7 @@ class DecodeArgs(ctypes.Structure):
         ("pool_slot_stride", _i64), ("pool_head_stride", _i64),
         ("read_idx", _vp), ("write_idx", _vp), ("scatter_idx", _vp),
         ("out", _vp),
+        ("qk_l2norm", _i32), ("qk_l2norm_eps", _f32),
     ]
 
 

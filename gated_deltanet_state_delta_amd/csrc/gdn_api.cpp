@@ -80,10 +80,17 @@ gdn_status gdn_prefill(const gdn_prefill_args* p, void* stream) {
   if (!a.cu_seqlens && (a.seq_len < 0 || (int64_t)a.n_seqs * a.seq_len != a.total_tokens))
     return fail(GDN_ERR_SHAPE, "gdn_prefill: without cu_seqlens n_seqs*seq_len (%d*%d) must equal total_tokens %lld",
                 a.n_seqs, a.seq_len, (long long)a.total_tokens);
+  if (a.qk_l2norm && !(a.qk_l2norm_eps >= 0.f && a.qk_l2norm_eps <= 3.0e38f))
+    return fail(GDN_ERR_SHAPE, "gdn_prefill: qk_l2norm_eps must be finite and >= 0");
   if (a.n_seqs == 0) return GDN_OK;
   if (!a.final_state) return fail(GDN_ERR_NULL, "gdn_prefill: final_state is NULL");
-  if (a.total_tokens > 0 && (!a.q || !a.k || !a.v || !a.out || !a.decay || !a.beta))
-    return fail(GDN_ERR_NULL, "gdn_prefill: q, k, v, out, decay and beta are required");
+  const bool fused = a.gate_a != nullptr;
+  if (a.total_tokens > 0 && (!a.q || !a.k || !a.v || !a.out))
+    return fail(GDN_ERR_NULL, "gdn_prefill: q, k, v and out are required");
+  if (a.total_tokens > 0 && fused && (!a.gate_b || !a.A_log || !a.dt_bias))
+    return fail(GDN_ERR_NULL, "gdn_prefill: the fused gate needs A_log, dt_bias, gate_a and gate_b");
+  if (a.total_tokens > 0 && !fused && (!a.decay || !a.beta))
+    return fail(GDN_ERR_NULL, "gdn_prefill: decay and beta are required (or the fused gate inputs)");
   const void* ptrs[] = {a.q, a.k, a.v, a.out, a.decay, a.beta, a.initial_state, a.final_state, a.cu_seqlens};
   for (const void* q : ptrs)
     if (q && !aligned(q, 16)) return fail(GDN_ERR_LAYOUT, "gdn_prefill: pointers must be 16-byte aligned");
@@ -120,6 +127,8 @@ gdn_status gdn_decode(const gdn_decode_args* p, void* stream) {
   if (a.n_householder < 1 || a.n_householder > 4)
     return fail(GDN_ERR_UNSUPPORTED, "gdn_decode: n_householder=%d (supported 1..4)", a.n_householder);
   if (a.hv % a.hq != 0) return fail(GDN_ERR_SHAPE, "gdn_decode: hv=%d is not a multiple of hq=%d", a.hv, a.hq);
+  if (a.qk_l2norm && !(a.qk_l2norm_eps >= 0.f && a.qk_l2norm_eps <= 3.0e38f))
+    return fail(GDN_ERR_SHAPE, "gdn_decode: qk_l2norm_eps must be finite and >= 0");
   if (!head_size_ok(a.dk) || !head_size_ok(a.dv))
     return fail(GDN_ERR_UNSUPPORTED, "gdn_decode: dk=%d dv=%d (supported: 16, 32, 64, 128)", a.dk, a.dv);
   if (a.scatter_idx && a.disable_state_update)

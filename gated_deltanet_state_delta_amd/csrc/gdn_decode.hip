@@ -39,6 +39,8 @@ struct DecodeParams {
   void* out;
   int batch, T, nhh, hq, hv, pool_size, disable;
   float scale;
+  int qk_norm;    // q, k used as x * rsqrt(sum x^2 + qk_eps) (use_qk_l2norm)
+  float qk_eps;
 };
 
 // Four io elements moved as one word group (8 bytes for bf16, 16 for fp32).
@@ -92,6 +94,18 @@ decode_kernel(const DecodeParams p) {
   // One token: decay, the sub-steps, the readout and the optional scatter.
   // kp(j): this lane's k of sub-step j; vj(j), beta(j): the row's v and beta;
   // qp: this lane's q.
+  // in-kernel L2 norm of a vector spread over the row's L lanes (16 elements
+  // each); an all-zero vector stays zero
+  auto l2n = [&](f4* v4) {
+    if (!p.qk_norm) return;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ss += v4[i][0] * v4[i][0] + v4[i][1] * v4[i][1] + v4[i][2] * v4[i][2] + v4[i][3] * v4[i][3];
+    ss = group_sum<L>(ss) + p.qk_eps;
+    const float r = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v4[i] *= r;
+  };
   auto token = [&](int t, float gamma, auto kp, auto vj, auto beta, const IO* qp) {
     const int64_t bt = (int64_t)b * p.T + t;
 #pragma unroll
@@ -101,6 +115,7 @@ decode_kernel(const DecodeParams p) {
       f4 kf[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) kf[i] = load4(kj + i * 4 * L);
+      l2n(kf);
       float r = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -110,12 +125,13 @@ decode_kernel(const DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] += u * kf[i];
     }
+    f4 qf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qf[i] = load4(qp + i * 4 * L);
+    l2n(qf);
     float y = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f4 qf = load4(qp + i * 4 * L);
-      y += x[i][0] * qf[0] + x[i][1] * qf[1] + x[i][2] * qf[2] + x[i][3] * qf[3];
-    }
+    for (int i = 0; i < 4; ++i) y += x[i][0] * qf[i][0] + x[i][1] * qf[i][1] + x[i][2] * qf[i][2] + x[i][3] * qf[i][3];
     y = group_sum<L>(y);
     if (o == 0) out[(bt * p.hv + h) * DV + row] = from_f32<IO>(p.scale * y);
     if (p.scatter_idx) {
@@ -226,6 +242,7 @@ hipError_t launch_decode(const gdn_decode_args& a, hipStream_t stream) {
   p.out = a.out;
   p.batch = a.batch; p.T = a.T; p.nhh = a.n_householder; p.hq = a.hq; p.hv = a.hv;
   p.pool_size = a.pool_size; p.disable = a.disable_state_update; p.scale = a.scale;
+  p.qk_norm = a.qk_l2norm != 0; p.qk_eps = a.qk_l2norm_eps;
   if (a.io_dtype == GDN_BF16) return dispatch_dk<__bf16>(p, a.dk, a.dv, stream);
   return dispatch_dk<float>(p, a.dk, a.dv, stream);
 }

@@ -25,6 +25,10 @@ hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream) {
   p.hq = a.hq; p.hv = a.hv; p.dv = a.dv; p.nsplit = 1;
   p.decay_is_gamma = a.decay_kind == GDN_DECAY_GAMMA;
   p.scale = a.scale;
+  p.qk_norm = a.qk_l2norm != 0;
+  p.qk_eps = a.qk_l2norm_eps;
+  p.A_log = a.A_log; p.dt_bias = a.dt_bias; p.ga = a.gate_a; p.gb = a.gate_b;
+  if (p.ga) p.decay_is_gamma = 0;  // the fused gate yields log-space decay
   const bool bf = a.io_dtype == GDN_BF16;
   if (bf && prefill_pair_supported(a.dk, a.dv, a.chunk_size)) return prefill_pair_bf16(p, a.dk, stream);
   const int hint = a.chunk_size != 0 ? a.chunk_size : 64;

@@ -76,6 +76,12 @@ struct PrefillParams {
   int64_t T;
   int n_seqs, seq_len, hq, hv, dv, nsplit, decay_is_gamma;
   float scale;
+  int qk_norm;      // q, k used as x * rsqrt(sum x^2 + qk_eps)
+  float qk_eps;
+  const float* A_log;    // fused gate when ga != nullptr (decay is then log-space)
+  const float* dt_bias;
+  const void* ga;        // [T, hv] io dtype
+  const void* gb;        // [T, hv] io dtype
 };
 
 // LDS layout of one workgroup.
@@ -101,6 +107,8 @@ struct PrefillSmem {
     alignas(16) float gb[C];   // beta_t Gam_t
     alignas(16) float gs[C];   // scale Gam_t
     alignas(16) float dc[C];   // D(C-1, t)
+    alignas(16) float rqn[C];  // 1 / |q_t| and 1 / |k_t| (in-kernel L2 norm only)
+    alignas(16) float rkn[C];
     float gC;                  // Gam_{C-1}
     int any_zero;              // some gamma of the chunk is exactly 0
   };
@@ -153,7 +161,9 @@ __device__ __forceinline__ typename pack4<E>::type to_pack4(f4 v) {
   return o;
 }
 
-template <typename E, int DK, int DVS, int C>
+// EXT compiles the optional fused gate and in-kernel q/k L2 norm in (each
+// still switched by its argument); without it the code has neither.
+template <typename E, int DK, int DVS, int C, bool EXT>
 __global__ void __launch_bounds__(512)
 prefill_kernel(const PrefillParams p) {
   typedef typename frag_of<E>::type Fr;
@@ -436,7 +446,15 @@ prefill_kernel(const PrefillParams p) {
   // ------------------------------------------------------------- prep waves
   u32x4 pq[NPT][4], pk[NPT][4];
   float pg = 0.f, pb = 0.f;     // prefetched decay/beta of token `lane`
+  E pga = from_f32<E>(0.f), pgb = from_f32<E>(0.f);  // or the fused gate's raw a, b
   bool pvalid = false;
+  // gates: given (decay, beta) or fused (the qwen gate and a sigmoid beta
+  // from A_log, dt_bias, a, b, computed here per token)
+  const bool fused = EXT && p.ga != nullptr;
+  const E* gga = (const E*)p.ga + h;
+  const E* ggb = (const E*)p.gb + h;
+  const float ealog = fused ? expf(p.A_log[h]) : 0.f, dtb = fused ? p.dt_bias[h] : 0.f;
+  const bool nrm = EXT && p.qk_norm != 0;
 
   auto prefetch = [&](int c) {
     const int64_t t0 = start + (int64_t)c * C;
@@ -471,8 +489,49 @@ prefill_kernel(const PrefillParams p) {
     }
     pvalid = lane < rem;
     const int tl = min(lane, rem - 1);
-    pg = gdec[(t0 + tl) * p.hv];
-    pb = gbet[(t0 + tl) * p.hv];
+    if (fused) {
+      // raw a and b as loaded (the gates are computed in the scan, so that
+      // nothing waits on these loads here)
+      pga = gga[(t0 + tl) * p.hv];
+      pgb = ggb[(t0 + tl) * p.hv];
+    } else {
+      pg = gdec[(t0 + tl) * p.hv];
+      pb = gbet[(t0 + tl) * p.hv];
+    }
+  };
+
+  // 1/|q_t| and 1/|k_t| of the prefetched rows (in-kernel L2 norm): each
+  // row's vectors sit on NOCT consecutive lanes; an all-zero row (a padded
+  // token, or eps == 0) keeps the factor 0
+  auto row_norms = [&](typename Sm::Derived& Dd) {
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+      const int pr = ptid + 256 * u;
+      const int quad = pr / NOCT, oct = pr % NOCT;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float sq = 0.f, sk = 0.f;
+        if (pr < NPAIR) {
+#pragma unroll
+          for (int e = 0; e < VE; ++e) {
+            const float a = to_f32(elem16<E>(pq[u][w], e)), b = to_f32(elem16<E>(pk[u][w], e));
+            sq += a * a;
+            sk += b * b;
+          }
+        }
+#pragma unroll
+        for (int off = NOCT / 2; off >= 1; off >>= 1) {
+          sq += __shfl_xor(sq, off);
+          sk += __shfl_xor(sk, off);
+        }
+        sq += p.qk_eps;
+        sk += p.qk_eps;
+        if (pr < NPAIR && oct == 0) {
+          Dd.rqn[4 * quad + w] = sq > 0.f ? 1.f / sqrtf(sq) : 0.f;
+          Dd.rkn[4 * quad + w] = sk > 0.f ? 1.f / sqrtf(sk) : 0.f;
+        }
+      }
+    }
   };
 
   auto store_raw = [&](int buf) {
@@ -504,6 +563,10 @@ prefill_kernel(const PrefillParams p) {
   auto scan = [&](typename Sm::Derived& Dd) {
     float lg = 0.f;
     bool reset = false;
+    if (fused) {
+      pg = gate_log_decay_fast(ealog, dtb, to_f32(pga));
+      pb = sigmoid_fast(to_f32(pgb));
+    }
     if (pvalid) {
       if (p.decay_is_gamma) {
         reset = !(pg > 0.f);
@@ -583,6 +646,7 @@ prefill_kernel(const PrefillParams p) {
     // ================================================================ part 1
     if (work) {
       store_raw(nxt);
+      if (nrm) row_norms(sm.der[nxt]);
       if (pw == 0) scan(sm.der[nxt]);
     }
     // the diagonal blocks of chunk c (staged in the previous part 2)
@@ -593,6 +657,12 @@ prefill_kernel(const PrefillParams p) {
     if (work) {
       const typename Sm::Raw& R = sm.raw[nxt];
       typename Sm::Derived& Dd = sm.der[nxt];
+      if (nrm && pw == 0 && lane < C) {
+        // fold the norms (written in part 1) into the per-token factors
+        Dd.gb[lane] *= Dd.rkn[lane];
+        Dd.gs[lane] *= Dd.rqn[lane];
+        Dd.dc[lane] *= Dd.rkn[lane];
+      }
       // Tiles of K K^T and K Q^T computed transposed -- rows s (key token),
       // columns t (query token) -- so that each lane (t = 16i + x) ends with
       // 4 consecutive s of row t and stores -A and M rows as vectors.  Prep
@@ -670,12 +740,18 @@ prefill_kernel(const PrefillParams p) {
       for (int k = 1; k < MT; ++k) {
         if (!tv[k]) continue;
         const int t = 16 * ti[k] + x;
-        const f4 d = decay4(ti[k], tm[k], false);
+        f4 d = decay4(ti[k], tm[k], false);
         const float bt = Dd.bet[t];
+        f4 dq = d, dk = d;
+        if (nrm) {
+          const f4 rks = *reinterpret_cast<const f4*>(&Dd.rkn[16 * tm[k] + 4 * g]);
+          dq = d * (rks * Dd.rqn[t]);
+          dk = d * (rks * Dd.rkn[t]);
+        }
         *reinterpret_cast<typename pack4<E>::type*>(&Dd.m[t][16 * tm[k] + 4 * g]) =
-            to_pack4<E>(p.scale * d * qk[k]);
+            to_pack4<E>(p.scale * dq * qk[k]);
         *reinterpret_cast<typename pack4<E>::type*>(&Dd.negA[t][16 * tm[k] + 4 * g]) =
-            to_pack4<E>(-bt * d * kk[k]);
+            to_pack4<E>(-bt * dk * kk[k]);
       }
       // diagonal tile: M, and A_ii (fp32, transposed) for the inverse that the
       // next staging part computes
@@ -684,11 +760,17 @@ prefill_kernel(const PrefillParams p) {
         const int t = 16 * i + x;
         const f4 d = decay4(i, i, true);
         const float bt = Dd.bet[t];
+        f4 dq = d, dk = d;
+        if (nrm) {
+          const f4 rks = *reinterpret_cast<const f4*>(&Dd.rkn[16 * i + 4 * g]);
+          dq = d * (rks * Dd.rqn[t]);
+          dk = d * (rks * Dd.rkn[t]);
+        }
         *reinterpret_cast<typename pack4<E>::type*>(&Dd.m[t][16 * i + 4 * g]) =
-            to_pack4<E>(p.scale * d * qk[0]);
+            to_pack4<E>(p.scale * dq * qk[0]);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          sm.adiagT[i][4 * g + e][x] = (4 * g + e < x) ? bt * d[e] * kk[0][e] : 0.f;
+          sm.adiagT[i][4 * g + e][x] = (4 * g + e < x) ? bt * dk[e] * kk[0][e] : 0.f;
       }
     }
     lds_barrier();
@@ -715,7 +797,10 @@ hipError_t launch_prefill_t(PrefillParams p, hipStream_t stream) {
     constexpr int DVS = prefill_dvs<DV>();
     p.nsplit = DV / DVS;
     const int64_t nblk = (int64_t)p.n_seqs * p.hv * p.nsplit;
-    hipLaunchKernelGGL((prefill_kernel<E, DK, DVS, C>), dim3((unsigned)nblk), dim3(512), 0, stream, p);
+    if (p.ga || p.qk_norm)
+      hipLaunchKernelGGL((prefill_kernel<E, DK, DVS, C, true>), dim3((unsigned)nblk), dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL((prefill_kernel<E, DK, DVS, C, false>), dim3((unsigned)nblk), dim3(512), 0, stream, p);
     return hipGetLastError();
   }
 }

@@ -25,7 +25,11 @@
 //    chunk holds a gamma of exactly 0), and the fp32 rows of its two
 //    diagonal blocks A_ii; wave 2 also writes the per-token factors;
 //  * one workgroup barrier per chunk: the state waves read buffer c & 1 while
-//    the prep waves fill buffer (c+1) & 1.
+//    the prep waves fill buffer (c+1) & 1;
+//  * options, each its own instantiation: the fused gate (the prep waves gate
+//    a and b when they stage a chunk) and the in-kernel q/k L2 norm (1/|q_t|
+//    and 1/|k_t| from the diagonals of the diagonal Gram tiles, folded into
+//    the per-token factors and the -A and M blocks; q and k stay as given).
 // K^T fragments for the state update, V in accumulator layout and the output
 // rows come from LDS through the gfx950 transposing LDS read
 // (ds_read_b64_tr_b16): lane 4a+b of a 16-lane group receives element b of
@@ -57,6 +61,8 @@ struct PairSmem {
     alignas(16) float gb[C];   // beta_t Gam_t
     alignas(16) float gs[C];   // scale Gam_t
     alignas(16) float dc[C];   // D(C-1, t)
+    alignas(16) float rqn[C];  // 1 / |q_t| and 1 / |k_t| (in-kernel L2 norm only)
+    alignas(16) float rkn[C];
     float gC;                  // Gam_{C-1}
   };
   struct Scan {                // decay scan of the chunk being prepared (per prep wave)
@@ -80,6 +86,7 @@ struct PairSmem {
   // yt[w][64 c + 4 ((t / 4) ^ f(c)) + t % 4]
   alignas(16) __bf16 yt[2][32 * 64];
   int prep_cnt;  // staging halves written by the prep waves so far
+  int nrm_cnt;   // norm halves written by the prep waves so far (L2 norm only)
   int inv_cnt;   // inverse halves written by the state waves so far
 };
 
@@ -161,7 +168,8 @@ struct PairPrepSet {
   u32x4 q[2][NPP];
   u32x4 k[2][NPP];
   u32x4 v[4];
-  float gd, bt;
+  float gd, bt;      // decay and beta of token `lane` as loaded (clamped to the chunk)
+  __bf16 ga, gbr;    // or the fused gate's raw a and b
 };
 
 // Inverse of the unit-lower block I + A_i (A_i strictly lower, fp32 rows in
@@ -214,24 +222,41 @@ __device__ __forceinline__ void pair_tri_inverse(const float (*ad)[16 * 20 + 4],
   *reinterpret_cast<bf4*>(&tout[i][r][8 * h + 4]) = to_bf4(f4{o[4], o[5], o[6], o[7]});
 }
 
-// Prep wave PW of the pair kernel (see the header comment).
-template <int DK, int PW>
+// Prep wave PW of the pair kernel (see the header comment).  FUSED: the gates
+// come from A_log, dt_bias, a, b (computed here); NORM: the in-kernel q/k L2
+// norm.  Each combination is its own instantiation, so none carries branches
+// for the options it does not use.
+template <int DK, int PW, bool FUSED, bool NORM>
 __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& sm, int64_t start,
                                           int64_t end, int nch, const __bf16* gq, const __bf16* gk,
-                                          const __bf16* gv, const float* gdec, const float* gbet) {
+                                          const __bf16* gv, int h) {
   typedef PairSmem<DK> Sm;
   constexpr int C = 64, NPP = DK / 32;
   const int lane = threadIdx.x & 63, x = lane & 15, g = lane >> 4;
+  // gates: given (decay, beta) or fused (A_log, dt_bias, a, b: the qwen gate
+  // and a sigmoid beta, computed here per token)
+  constexpr bool fused = FUSED;
+  const float* gdec = p.decay + h;
+  const float* gbet = p.beta + h;
+  const __bf16* gga = (const __bf16*)p.ga + h;
+  const __bf16* ggb = (const __bf16*)p.gb + h;
+  const float ealog = fused ? expf(p.A_log[h]) : 0.f, dtb = fused ? p.dt_bias[h] : 0.f;
+  constexpr bool nrm = NORM;
 
   auto prefetch = [&](int c, PairPrepSet<DK>& s) {
     const int64_t t0 = start + (int64_t)c * C;
     const int rem = (int)min((int64_t)C, end - t0);  // >= 1
     {
+      // the values exactly as loaded: nothing here may wait on these loads
+      // (padding and the fused gate are applied when the set is staged)
       const int tl = min(lane, rem - 1);
-      const float gd = gdec[(t0 + tl) * p.hv], bt = gbet[(t0 + tl) * p.hv];
-      // padded tokens: no decay (log-decay 0 / gamma 1) and beta 0
-      s.gd = lane < rem ? gd : (p.decay_is_gamma ? 1.f : 0.f);
-      s.bt = lane < rem ? bt : 0.f;
+      if constexpr (FUSED) {
+        s.ga = gga[(t0 + tl) * p.hv];
+        s.gbr = ggb[(t0 + tl) * p.hv];
+      } else {
+        s.gd = gdec[(t0 + tl) * p.hv];
+        s.bt = gbet[(t0 + tl) * p.hv];
+      }
     }
     const __bf16* qb = gq + t0 * p.q_st;
     const __bf16* kb = gk + t0 * p.k_st;
@@ -286,7 +311,17 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         *reinterpret_cast<u32x4*>(&B.v[32 * PW + 8 * u + (lane >> 3)][8 * (lane & 7)]) = s.v[u];
-      const float gd = s.gd, btl = s.bt;
+      // gates of token `lane`; padded tokens: no decay (log-decay 0 / gamma
+      // 1) and beta 0
+      const bool live = lane < (int)min((int64_t)C, end - (start + (int64_t)(c + 1) * C));
+      float gd, btl;
+      if constexpr (FUSED) {
+        gd = live ? gate_log_decay_fast(ealog, dtb, (float)s.ga) : 0.f;
+        btl = live ? sigmoid_fast((float)s.gbr) : 0.f;
+      } else {
+        gd = live ? s.gd : (p.decay_is_gamma ? 1.f : 0.f);
+        btl = live ? s.bt : 0.f;
+      }
       // ---- signal this half written and refill the registers; the wait for
       // the other prep wave's half comes after the scan.  Both prep waves
       // stage every chunk, so that wait ends; its bound only guards against a
@@ -324,15 +359,20 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
       }
       const bool any_zero = zlast >= 0;  // wave-uniform
 
-      if constexpr (PW == 0) {
-        // ---- per-token factors of the state waves
-        const float gam = z < 0 ? __builtin_amdgcn_exp2f(F) : 0.f;
-        B.bet[lane] = btl;
-        B.gb[lane] = btl * gam;
-        B.gs[lane] = p.scale * gam;
-        B.dc[lane] = zlast <= lane ? __builtin_amdgcn_exp2f(Flast - F) : 0.f;
-        if (lane == C - 1) B.gC = gam;
-      }
+      // ---- per-token factors of the state waves (wave 2), after the norms
+      // of all tokens are known when the in-kernel L2 norm is on
+      auto factors = [&]() {
+        if constexpr (PW == 0) {
+          const float gam = z < 0 ? __builtin_amdgcn_exp2f(F) : 0.f;
+          const float rq = nrm ? B.rqn[lane] : 1.f, rk = nrm ? B.rkn[lane] : 1.f;
+          B.bet[lane] = btl;
+          B.gb[lane] = btl * gam * rk;
+          B.gs[lane] = p.scale * gam * rq;
+          B.dc[lane] = zlast <= lane ? __builtin_amdgcn_exp2f(Flast - F) * rk : 0.f;
+          if (lane == C - 1) B.gC = gam;
+        }
+      };
+      if constexpr (!NORM) factors();
       // ---- Gram tiles, computed transposed (rows s, columns t): this wave's
       // diagonal tiles (D0, D0), (D0+1, D0+1) and three off-diagonal tiles
       // (TI[n], TM[n]): wave 2 (1,0) (2,0) (3,0), wave 3 (2,1) (3,1) (3,2)
@@ -340,9 +380,9 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
       constexpr int TI[3] = {PW == 0 ? 1 : 2, PW == 0 ? 2 : 3, 3};
       constexpr int TM[3] = {PW == 0 ? 0 : 1, PW == 0 ? 0 : 1, PW == 0 ? 0 : 2};
       constexpr int KLO = PW == 0 ? 0 : 1, QLO = PW == 0 ? 0 : 2;  // tiles read
-      f4 kkd[2], qkd[2], kko[3], qko[3];
+      f4 kkd[2], qkd[2], qqd[2], kko[3], qko[3];
 #pragma unroll
-      for (int n = 0; n < 2; ++n) kkd[n] = qkd[n] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < 2; ++n) kkd[n] = qkd[n] = qqd[n] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int n = 0; n < 3; ++n) kko[n] = qko[n] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -362,12 +402,33 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
         for (int n = 0; n < 2; ++n) {
           kkd[n] = mfma32(kkd[n], kf[D0 + n], kf[D0 + n]);
           qkd[n] = mfma32(qkd[n], kf[D0 + n], qf[D0 + n]);
+          if constexpr (NORM) qqd[n] = mfma32(qqd[n], qf[D0 + n], qf[D0 + n]);
         }
 #pragma unroll
         for (int n = 0; n < 3; ++n) {
           kko[n] = mfma32(kko[n], kf[TM[n]], kf[TI[n]]);
           qko[n] = mfma32(qko[n], kf[TM[n]], qf[TI[n]]);
         }
+      }
+      if constexpr (NORM) {
+        // ---- in-kernel L2 norm: |k_t|^2 and |q_t|^2 are the diagonals of this
+        // wave's diagonal tiles K K^T and Q Q^T (token t = 16i + x sits on lane
+        // (x, x/4), element x % 4).  The factors 1/|.| go to LDS; the other
+        // wave's are waited for (a counter) after the diagonal epilogue, which
+        // needs only this wave's.  Both waves write every chunk, so the wait
+        // ends.  An all-zero vector (a padded token, or eps == 0) keeps the
+        // factor 0.
+        if (g == (x >> 2)) {
+#pragma unroll
+          for (int n = 0; n < 2; ++n) {
+            const int e = x & 3;
+            const float k2 = (e == 0 ? kkd[n][0] : e == 1 ? kkd[n][1] : e == 2 ? kkd[n][2] : kkd[n][3]) + p.qk_eps;
+            const float q2 = (e == 0 ? qqd[n][0] : e == 1 ? qqd[n][1] : e == 2 ? qqd[n][2] : qqd[n][3]) + p.qk_eps;
+            B.rkn[16 * (D0 + n) + x] = k2 > 0.f ? __builtin_amdgcn_rsqf(k2) : 0.f;
+            B.rqn[16 * (D0 + n) + x] = q2 > 0.f ? __builtin_amdgcn_rsqf(q2) : 0.f;
+          }
+        }
+        if (lane == 0) __hip_atomic_fetch_add(&sm.nrm_cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
       // ---- diagonal tiles: M blocks, and the rows of A_ii (fp32) split by
       // column parity for the inverses
@@ -379,18 +440,29 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
         const f4 Fs = *reinterpret_cast<const f4*>(&sc.F[16 * i + 4 * g]);
         const float bt = sc.bt[t];
         const int zt = sc.z[t];
+        // in-kernel L2 norm: row factor 1/|q_t| or 1/|k_t|, column 1/|k_s|
+        const f4 one4 = f4{1.f, 1.f, 1.f, 1.f};
+        const f4 rks = nrm ? *reinterpret_cast<const f4*>(&B.rkn[16 * i + 4 * g]) : one4;
+        const f4 fq = rks * (nrm ? B.rqn[t] : 1.f), fk = rks * (nrm ? B.rkn[t] : 1.f);
         f4 d, arow;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int sidx = 16 * i + 4 * g + e;
           const bool live = sidx <= t && (!any_zero || zt <= sidx);
           d[e] = live ? __builtin_amdgcn_exp2f(Ft - Fs[e]) : 0.f;
-          arow[e] = sidx < t ? bt * d[e] * kkd[n][e] : 0.f;
+          arow[e] = sidx < t ? bt * d[e] * kkd[n][e] * fk[e] : 0.f;
         }
-        *reinterpret_cast<bf4*>(&B.m[t][16 * i + 4 * g]) = to_bf4(p.scale * d * qkd[n]);
+        *reinterpret_cast<bf4*>(&B.m[t][16 * i + 4 * g]) = to_bf4(p.scale * d * qkd[n] * fq);
         float* ad = sm.adiag[(c + 1) & 1][i];
         *reinterpret_cast<f2*>(&ad[20 * x + 2 * g]) = f2{arow[0], arow[2]};
         *reinterpret_cast<f2*>(&ad[20 * x + 8 + 2 * g]) = f2{arow[1], arow[3]};
+      }
+      if constexpr (NORM) {
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+          if (__hip_atomic_load(&sm.nrm_cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= 2 * staged) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        factors();
       }
       // ---- off-diagonal tiles: -A and M blocks.  D(t, s) = e_t c_im f_s for
       // s in tile m < i, t in tile i, with e_t = 2^(F_t - F_16i),
@@ -419,6 +491,11 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
             da[e] = -bt * d;
           }
         }
+        if constexpr (NORM) {
+          const f4 rks = *reinterpret_cast<const f4*>(&B.rkn[16 * m + 4 * g]);
+          dm = dm * (rks * B.rqn[t]);
+          da = da * (rks * B.rkn[t]);
+        }
         *reinterpret_cast<bf4*>(&B.m[t][16 * m + 4 * g]) = to_bf4(dm * qko[n]);
         *reinterpret_cast<bf4*>(&B.negA[t][16 * m + 4 * g]) = to_bf4(da * kko[n]);
       }
@@ -435,7 +512,7 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
   }
 }
 
-template <int DK>
+template <int DK, bool FUSED, bool NORM>
 __global__ void __launch_bounds__(256, 1)
 prefill_pair_kernel(const PrefillParams p) {
   typedef PairSmem<DK> Sm;
@@ -483,14 +560,13 @@ prefill_pair_kernel(const PrefillParams p) {
   if (tid == 0) {
     sm.prep_cnt = 0;
     sm.inv_cnt = 0;
+    sm.nrm_cnt = 0;
   }
   lds_barrier();
 
   if (wave >= 2) {
-    const float* gdec = p.decay + h;
-    const float* gbet = p.beta + h;
-    if (wave == 2) pair_prep<DK, 0>(p, sm, start, end, nch, gq, gk, gv, gdec, gbet);
-    else pair_prep<DK, 1>(p, sm, start, end, nch, gq, gk, gv, gdec, gbet);
+    if (wave == 2) pair_prep<DK, 0, FUSED, NORM>(p, sm, start, end, nch, gq, gk, gv, h);
+    else pair_prep<DK, 1, FUSED, NORM>(p, sm, start, end, nch, gq, gk, gv, h);
     return;
   }
 
@@ -689,7 +765,11 @@ template <int DK>
 hipError_t launch_prefill_pair_t(PrefillParams p, hipStream_t stream) {
   p.nsplit = p.dv / 64;
   const int64_t nblk = (int64_t)p.n_seqs * p.hv * p.nsplit;
-  hipLaunchKernelGGL((prefill_pair_kernel<DK>), dim3((unsigned)nblk), dim3(256), 0, stream, p);
+  const dim3 grid((unsigned)nblk), block(256);
+  if (p.ga && p.qk_norm) hipLaunchKernelGGL((prefill_pair_kernel<DK, true, true>), grid, block, 0, stream, p);
+  else if (p.ga) hipLaunchKernelGGL((prefill_pair_kernel<DK, true, false>), grid, block, 0, stream, p);
+  else if (p.qk_norm) hipLaunchKernelGGL((prefill_pair_kernel<DK, false, true>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((prefill_pair_kernel<DK, false, false>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

@@ -92,8 +92,9 @@ gdn_status gdn_gate(const float* A_log, const float* dt_bias,
  *
  * Contract of "com.microsoft.GatedDeltaNet" (Inputs, Outputs, Attributes) with
  * update_rule gated_delta, gate_activation none and beta_activation none
- * (gates come from gdn_gate or the caller), qk_l2_norm 0 (keys arrive
- * normalised, as "Gated DeltaNet State Update" Constraints require):
+ * (gates come from gdn_gate or the caller, or from the fused gate fields),
+ * qk_l2_norm as the qk_l2norm field says (off: keys arrive normalised, as
+ * "Gated DeltaNet State Update" Constraints require):
  *  - request r covers tokens [cu_seqlens[r], cu_seqlens[r+1]), both offsets
  *    clamped to [0, total_tokens]; a decreasing pair is an empty request.
  *    cu_seqlens == NULL means uniform packing, request r = [r*seq_len,
@@ -139,6 +140,21 @@ typedef struct {
   const int32_t* cu_seqlens;
   const float* initial_state;
   float* final_state;
+  /* Optional, zero = off (appended; a zero-filled struct keeps the behaviour
+   * above).  qk_l2_norm of the ONNX card: with qk_l2norm != 0 every q and k
+   * head vector x is used as x / sqrt(sum(x^2) + qk_l2norm_eps) (the card's
+   * epsilon is 1e-12); the inputs are not modified. */
+  int32_t qk_l2norm;
+  float qk_l2norm_eps;     /* >= 0 and finite                                  */
+  /* Fused gate: when gate_a != NULL the gates are computed in the kernel as
+   * gdn_gate computes them -- log-decay -exp(A_log[h]) softplus(a + dt_bias[h])
+   * (threshold 20) and beta = sigmoid(b) -- and decay, beta, decay_kind are
+   * ignored (decay and beta may be NULL).  A_log, dt_bias [hv] fp32;
+   * gate_a, gate_b [total_tokens, hv] io_dtype, dense. */
+  const float* A_log;
+  const float* dt_bias;
+  const void* gate_a;
+  const void* gate_b;
 } gdn_prefill_args;
 
 gdn_status gdn_prefill(const gdn_prefill_args* args, void* stream);
@@ -148,7 +164,8 @@ gdn_status gdn_prefill(const gdn_prefill_args* args, void* stream);
  *
  * Contract of "flashinfer.cake_gdp.cake_gated_delta_product_mtp" (parameters
  * and notes), generalised to grouped value heads (hv a multiple of hq) and to
- * dk, dv in {16, 32, 64, 128}; q/k arrive normalised (no in-kernel L2 norm).
+ * dk, dv in {16, 32, 64, 128}; q/k arrive normalised unless qk_l2norm asks
+ * for the in-kernel L2 norm (use_qk_l2norm).
  * For every batch row b and value head h:
  *  - rd = read_idx[b]; rd < 0 or rd >= pool_size skips the row entirely: no
  *    pool read, no output store, no write-back, no scatter.
@@ -200,6 +217,11 @@ typedef struct {
   const int32_t* write_idx;
   const int32_t* scatter_idx;
   void* out;
+  /* Optional, zero = off (appended).  use_qk_l2norm of the FlashInfer page:
+   * with qk_l2norm != 0 every q and k head vector x is used as
+   * x / sqrt(sum(x^2) + qk_l2norm_eps) (the page's epsilon is 1e-6). */
+  int32_t qk_l2norm;
+  float qk_l2norm_eps;     /* >= 0 and finite                                  */
 } gdn_decode_args;
 
 gdn_status gdn_decode(const gdn_decode_args* args, void* stream);

@@ -150,3 +150,25 @@ def test_gate_rejects(lib):
     assert lib.gdn_gate(None, None, FAKE, None, 1, 4, 4, None, None, FAKE, None) == 1  # beta w/o b
     assert lib.gdn_gate(None, None, FAKE, None, 1, 4, 4, FAKE, None, None, None) == 1  # a w/o A_log
     assert lib.gdn_gate(None, None, None, None, 1, 0, 4, None, None, None, None) == 0  # n == 0
+
+
+@pytest.mark.parametrize("cname,pycls", [("gdn_prefill_args", "PrefillArgs"), ("gdn_decode_args", "DecodeArgs")])
+def test_struct_layout_matches_the_binding(cname, pycls, tmp_path):
+    """Every field of the argument structs sits at the same offset in C (gcc
+    on the header) and in the Python binding's ctypes mirror."""
+    import subprocess
+    cls = getattr(L, pycls)
+    fields = [f[0] for f in cls._fields_]
+    src = tmp_path / "layout.c"
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "libgdn.h"', "int main(void) {",
+             '  printf("%%zu\\n", sizeof(%s));' % cname]
+    lines += ['  printf("%%zu\\n", offsetof(%s, %s));' % (cname, f) for f in fields]
+    lines += ["  return 0;", "}"]
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    want = [ctypes.sizeof(cls)] + [getattr(cls, f).offset for f in fields]
+    assert got == want

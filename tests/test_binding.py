@@ -23,7 +23,7 @@ def _span_ok(ptr, max_elem, t):
 
 
 def _check_prefill(a, keep, T):
-    q3, k3, v3, decay, beta, cu, init, out3, fin = keep
+    q3, k3, v3, decay, beta, cu, init, out3, fin, A_log, dt_bias, ga, gb = keep
     last_q = (T - 1) * a.q_stride_token + (a.hq - 1) * a.q_stride_head + a.dk - 1
     last_k = (T - 1) * a.k_stride_token + (a.hq - 1) * a.k_stride_head + a.dk - 1
     last_v = (T - 1) * a.v_stride_token + (a.hv - 1) * a.v_stride_head + a.dv - 1
@@ -32,8 +32,13 @@ def _check_prefill(a, keep, T):
     assert _span_ok(a.k, last_k, k3)
     assert _span_ok(a.v, last_v, v3)
     assert _span_ok(a.out, last_o, out3)
-    assert _span_ok(a.decay, T * a.hv - 1, decay)
-    assert _span_ok(a.beta, T * a.hv - 1, beta)
+    if a.gate_a:
+        assert not a.decay and not a.beta
+        assert _span_ok(a.gate_a, T * a.hv - 1, ga) and _span_ok(a.gate_b, T * a.hv - 1, gb)
+        assert _span_ok(a.A_log, a.hv - 1, A_log) and _span_ok(a.dt_bias, a.hv - 1, dt_bias)
+    else:
+        assert _span_ok(a.decay, T * a.hv - 1, decay)
+        assert _span_ok(a.beta, T * a.hv - 1, beta)
     assert _span_ok(a.final_state, a.n_seqs * a.hv * a.dv * a.dk - 1, fin)
     if a.initial_state:
         assert _span_ok(a.initial_state, a.n_seqs * a.hv * a.dv * a.dk - 1, init)
@@ -151,3 +156,21 @@ def test_decode_rejects_bad_shapes(key, val):
     with pytest.raises(ValueError):
         gdn.decode_args(x["q"], x["k"], x["v"], x["A_log"], x["dt_bias"], x["a"], x["b"],
                         x["pool"], x["read_idx"], **kw)
+
+
+def test_fused_gate_and_norm_arguments():
+    """The fused-gate form: [B, S, hv] a/b in q's dtype, decay and beta None;
+    the norm flag and epsilon reach the struct."""
+    B, S, hq, hv, d = 2, 48, 2, 4, 64
+    q = torch.zeros(B, S, hq, d, dtype=torch.bfloat16)
+    v = torch.zeros(B, S, hv, d, dtype=torch.bfloat16)
+    ab = torch.zeros(B, S, hv, dtype=torch.bfloat16)
+    A = torch.zeros(hv)
+    a, keep, o, f = gdn.prefill_args(q, q, v, None, None, A_log=A, dt_bias=A, a=ab, b=ab.clone(),
+                                     qk_l2norm=True, qk_l2norm_eps=1e-12)
+    assert a.qk_l2norm == 1 and abs(a.qk_l2norm_eps - 1e-12) < 1e-18
+    _check_prefill(a, keep, B * S)
+    with pytest.raises(ValueError):
+        gdn.prefill_args(q, q, v, None, None)                        # no gates at all
+    with pytest.raises(ValueError):
+        gdn.prefill_args(q, q, v, None, None, A_log=A, dt_bias=A, a=ab.float(), b=ab.float())
