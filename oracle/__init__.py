@@ -71,6 +71,10 @@ def _load():
                 _dp, _dp, _dp, _dp, _dp, _dp, _dp,
                 _dp, ctypes.c_int32, _ip, _ip, _ip, ctypes.c_int32, ctypes.c_double,
                 _dp, ctypes.c_int32, ctypes.c_double]
+            lib.gdno_conv1d.restype = ctypes.c_int
+            lib.gdno_conv1d.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, _dp, _dp, _dp, ctypes.c_int64, _ip,
+                                        _ip, ctypes.c_int32, _dp]
             _lib = lib
     return _lib
 
@@ -211,3 +215,25 @@ def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None,
     if rc != 0:
         raise ValueError("gdno_decode rejected its arguments")
     return out, pool64
+
+
+def conv1d(x, weight, conv_state, slot_idx, row_offsets, *, write_state=True, out_init=None):
+    """fp64 causal depthwise conv1d with a slot-indexed conv-state pool.
+
+    x [T, conv_dim]; weight [conv_dim, K]; conv_state [max_slots, conv_dim, K-1]
+    (not modified: a float64 copy is updated and returned); slot_idx [B];
+    row_offsets [B+1].  Returns (out [T, conv_dim], state_after) as float64
+    arrays; out rows no sequence covers hold out_init (default NaN).
+    """
+    lib = _load()
+    x64, w64 = _f64(x), _f64(weight)
+    T, conv_dim = x64.shape
+    K = w64.shape[1]
+    st = _f64(conv_state).copy()
+    slots, offs = _i64(slot_idx), _i64(row_offsets)
+    out = np.full((T, conv_dim), np.nan) if out_init is None else _f64(out_init).copy()
+    rc = lib.gdno_conv1d(T, conv_dim, K, slots.shape[0], _p(x64), _p(w64), _p(st), st.shape[0],
+                         _p(slots, _ip), _p(offs, _ip), 1 if write_state else 0, _p(out))
+    if rc != 0:
+        raise ValueError("gdno_conv1d rejected its arguments")
+    return out, st

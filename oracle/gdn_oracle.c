@@ -338,3 +338,44 @@ int gdno_decode(int32_t B, int32_t T, int32_t n_hh, int32_t hq, int32_t hv,
   free(pool0);
   return 0;
 }
+
+/* ---------------------------------------------------------------- conv1d -- */
+
+/* Causal depthwise conv1d over a ragged batch with a slot-indexed conv-state
+ * pool ("gated_delta_conv1d_fwd", parameters and example).  For sequence b
+ * (rows [off[b], off[b+1]) of x) and channel c, the window is the slot's
+ * K-1 saved inputs (oldest first) followed by the sequence's inputs:
+ *   win = state[slot_b, c, 0 .. K-2] ++ x[off[b] .., c]
+ *   out[off[b] + t, c] = sum_{j < K} w[c, j] * win[t + j]
+ * so w[c, K-1] multiplies the current input.  With write_state the slot then
+ * holds the last K-1 entries of win.  A slot outside [0, max_slots) reads
+ * zeros and is not written (the page leaves it undefined).  Offsets are
+ * clamped to [0, T]; a decreasing pair is an empty sequence. */
+int gdno_conv1d(int64_t T, int32_t conv_dim, int32_t K, int32_t n_seqs,
+                const double* x, const double* w, double* state, int64_t max_slots,
+                const int64_t* slot, const int64_t* off, int32_t write_state, double* out) {
+  if (T < 0 || conv_dim <= 0 || K < 1 || n_seqs < 0 || max_slots < 0) return -1;
+  const int H = K - 1;
+  double* win = (double*)malloc(sizeof(double) * (size_t)(H + (T > 0 ? T : 1)));
+  if (!win) return -1;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    int64_t s0 = clamp64(off[b], 0, T), s1 = clamp64(off[b + 1], 0, T);
+    if (s1 < s0) s1 = s0;
+    const int64_t len = s1 - s0;
+    const int ok = slot[b] >= 0 && slot[b] < max_slots;
+    for (int32_t c = 0; c < conv_dim; ++c) {
+      double* st = ok ? state + ((size_t)slot[b] * conv_dim + c) * (size_t)H : NULL;
+      for (int i = 0; i < H; ++i) win[i] = st ? st[i] : 0.0;
+      for (int64_t t = 0; t < len; ++t) win[H + t] = x[(size_t)(s0 + t) * conv_dim + c];
+      for (int64_t t = 0; t < len; ++t) {
+        double acc = 0.0;
+        for (int j = 0; j < K; ++j) acc += w[(size_t)c * K + j] * win[t + j];
+        out[(size_t)(s0 + t) * conv_dim + c] = acc;
+      }
+      if (write_state && st)
+        for (int i = 0; i < H; ++i) st[i] = win[len + i];
+    }
+  }
+  free(win);
+  return 0;
+}

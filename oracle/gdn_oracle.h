@@ -1,5 +1,6 @@
 /*
- * gdn_oracle.h -- plain fp64 CPU oracle for the gated delta rule.
+ * gdn_oracle.h -- plain fp64 CPU oracle for the gated delta rule (and the
+ * causal conv1d that runs before it in a layer).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link or
  * call this library; only the tests, the smoke check and the benchmark's CPU
@@ -23,6 +24,8 @@
  *    pool, decay once per token then num_householder delta sub-steps, fused
  *    gate with softplus threshold 20 and sigmoid beta, skip / write-slot /
  *    scatter / disable_state_update rules.
+ *  - "gated_delta_conv1d_fwd": causal depthwise conv1d with a slot-indexed
+ *    conv-state pool, ragged offsets, write_state.
  *  - "Circuit.LLM.Mixer" (Haskell source): gatedDeltaStep -- scale the state
  *    by alpha first, then the delta write.
  */
@@ -89,6 +92,19 @@ int gdno_decode(int32_t B, int32_t T, int32_t n_hh, int32_t hq, int32_t hv,
                 const int64_t* read, const int64_t* write, const int64_t* scatter,
                 int32_t disable_state_update, double scale,
                 double* out, int32_t nthreads, double qk_l2norm_eps);
+
+/* Causal depthwise conv1d over a ragged batch with a slot-indexed conv-state
+ * pool ("gated_delta_conv1d_fwd").
+ *   x [T, conv_dim]   w [conv_dim, K]   state [max_slots, conv_dim, K-1]
+ *   (updated in place when write_state != 0)   slot [n_seqs]
+ *   off [n_seqs + 1]   out [T, conv_dim] (rows no sequence covers are left)
+ * Sequence b's window is state[slot[b], c, :] (oldest first) followed by its
+ * inputs; out = sum_j w[c, j] * window[t + j]; the slot then holds the last
+ * K-1 window entries.  A slot outside [0, max_slots) reads zeros and is not
+ * written.  Returns 0, or -1 on an argument error. */
+int gdno_conv1d(int64_t T, int32_t conv_dim, int32_t K, int32_t n_seqs,
+                const double* x, const double* w, double* state, int64_t max_slots,
+                const int64_t* slot, const int64_t* off, int32_t write_state, double* out);
 
 #ifdef __cplusplus
 }

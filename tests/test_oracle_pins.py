@@ -562,3 +562,85 @@ def test_decode_qk_l2norm_invariance_and_prenormalised_inputs():
     o4, p4 = _run_dec(z)
     np.testing.assert_allclose(o3, o4, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(p3, p4, rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# causal conv1d with a slot-indexed conv-state pool ("gated_delta_conv1d_fwd")
+# ----------------------------------------------------------------------------
+
+def test_conv1d_page_example_invariants():
+    """The page's example: two sequences (lengths 3 and 2) on slots 2 and 0
+    of a 3-slot pool, K = 4: afterwards slot 2 holds the first sequence's
+    three inputs, slot 0 holds the last three entries of its window, slot 1
+    is unchanged.  Inputs drawn as the example draws them."""
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((5, 8), dtype=np.float32)
+    w = rng.standard_normal((8, 4), dtype=np.float32)
+    st = rng.standard_normal((3, 8, 3), dtype=np.float32)
+    out, st2 = oracle.conv1d(x, w, st, np.array([2, 0]), np.array([0, 3, 5]))
+    np.testing.assert_array_equal(st2[2], x[0:3].T)
+    np.testing.assert_array_equal(st2[0][:, 1:], x[3:5].T)
+    np.testing.assert_array_equal(st2[0][:, 0], st[0][:, 2])
+    np.testing.assert_array_equal(st2[1], st[1])
+    assert out.shape == (5, 8) and np.isfinite(out).all()
+
+
+def test_conv1d_against_torch_grouped_conv():
+    """Each sequence equals torch's depthwise conv1d (groups = channels) over
+    its slot's saved inputs followed by its own."""
+    g = torch.Generator().manual_seed(90)
+    T, C, K = 37, 12, 4
+    x = torch.randn(T, C, generator=g, dtype=torch.float64)
+    w = torch.randn(C, K, generator=g, dtype=torch.float64)
+    st = torch.randn(5, C, K - 1, generator=g, dtype=torch.float64)
+    offs = np.array([0, 10, 10, 29, 37])
+    slots = np.array([3, 1, 4, 0])
+    out, _ = oracle.conv1d(x, w, st, slots, offs)
+    for b in range(4):
+        s0, s1 = offs[b], offs[b + 1]
+        if s1 == s0:
+            continue
+        inp = torch.cat([st[slots[b]], x[s0:s1].T], dim=1)[None]  # [1, C, K-1+len]
+        ref = torch.nn.functional.conv1d(inp, w[:, None, :], groups=C)[0].T
+        np.testing.assert_allclose(out[s0:s1], ref.numpy(), rtol=1e-13, atol=1e-13)
+
+
+def test_conv1d_split_calls_equal_one_call():
+    g = torch.Generator().manual_seed(91)
+    T, C, K = 50, 6, 4
+    x = torch.randn(T, C, generator=g, dtype=torch.float64).numpy()
+    w = torch.randn(C, K, generator=g, dtype=torch.float64).numpy()
+    st = torch.randn(2, C, K - 1, generator=g, dtype=torch.float64).numpy()
+    out, st_end = oracle.conv1d(x, w, st, np.array([1]), np.array([0, T]))
+    for cut in (1, 2, 3, 17):
+        o1, s1 = oracle.conv1d(x[:cut], w, st, np.array([1]), np.array([0, cut]))
+        o2, s2 = oracle.conv1d(x[cut:], w, s1, np.array([1]), np.array([0, T - cut]))
+        np.testing.assert_array_equal(np.concatenate([o1, o2]), out)
+        np.testing.assert_array_equal(s2, st_end)
+
+
+def test_conv1d_delay_weights_closed_form_and_write_state_flag():
+    """A one-hot weight at tap K-1-d delays the input by d (the saved inputs
+    supply the first d outputs); write_state=False leaves the pool alone."""
+    g = torch.Generator().manual_seed(92)
+    T, C, K = 9, 5, 4
+    x = torch.randn(T, C, generator=g, dtype=torch.float64).numpy()
+    st = torch.randn(1, C, K - 1, generator=g, dtype=torch.float64).numpy()
+    for d in range(K):
+        w = np.zeros((C, K))
+        w[:, K - 1 - d] = 1.0
+        out, st2 = oracle.conv1d(x, w, st, np.array([0]), np.array([0, T]), write_state=False)
+        hist = np.concatenate([st[0].T, x])  # [K-1+T, C]
+        np.testing.assert_array_equal(out, hist[K - 1 - d:K - 1 - d + T])
+        np.testing.assert_array_equal(st2, st)
+
+
+def test_conv1d_out_of_range_slot_reads_zeros_and_writes_nothing():
+    g = torch.Generator().manual_seed(93)
+    x = torch.randn(6, 3, generator=g, dtype=torch.float64).numpy()
+    w = torch.randn(3, 3, generator=g, dtype=torch.float64).numpy()
+    st = torch.randn(2, 3, 2, generator=g, dtype=torch.float64).numpy()
+    out, st2 = oracle.conv1d(x, w, st, np.array([7]), np.array([0, 6]))
+    out0, _ = oracle.conv1d(x, w, np.zeros_like(st), np.array([0]), np.array([0, 6]))
+    np.testing.assert_array_equal(out, out0)
+    np.testing.assert_array_equal(st2, st)
