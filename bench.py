@@ -151,6 +151,16 @@ def decode_algorithmic(x):
     return reads + writes + act
 
 
+def conv1d_algorithmic(x):
+    """HBM bytes a conv1d call must move: x read and out written once, the
+    weights read once, and each sequence's K-1 saved inputs per channel read
+    and written back."""
+    es = 2 if x["dtype"] == "bf16" else 4
+    T, C, K = x["T"], x["conv_dim"], x["K"]
+    n = len(x["lengths"])
+    return es * (2 * T * C + C * K + 2 * n * C * (K - 1)) + 4 * (2 * n + 1)
+
+
 def cpu_baseline_prefill(x, budget_units=None):
     """The fp64 oracle on the prefill workload (all of it unless budget_units)."""
     import oracle
@@ -265,6 +275,23 @@ def extra_workloads(torch, gdn, synth, dev):
     out["mtp_decode_b64_t4_n2_h16_dv64_bf16"] = {
         "ms": ms, "algorithmic_bytes": by, "gbs": by / (ms * 1e-3) / 1e9,
         "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del t, o5
+
+    # causal conv1d over the QKV rows with the conv-state pool: the prefill
+    # batch (B4 x S4096, 8192 channels) and one decode step (256 x 1 row)
+    for name, make in (("conv1d_prefill_b4_s4096_c8192_k4_bf16", synth.conv1d_prefill_b4_s4096),
+                       ("conv1d_decode_b256_c8192_k4_bf16", synth.conv1d_decode_b256)):
+        x = make()
+        xd, wd, pool = x["x"].to(dev), x["weight"].to(dev), x["conv_state"].to(dev)
+        sl = x["slot_idx"].to(torch.int32).to(dev)
+        off = x["row_offsets"].to(torch.int32).to(dev)
+        oc = torch.empty_like(xd)
+        fn = lambda: gdn.conv1d(xd, wd, pool, sl, off, out=oc)
+        ms = _time_launches(torch, fn, flush=flush)
+        by = conv1d_algorithmic(x)
+        out[name] = {"ms": ms, "tokens": x["T"], "algorithmic_bytes": by,
+                     "gbs": by / (ms * 1e-3) / 1e9, "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del xd, wd, pool, oc
     return out
 
 

@@ -10,6 +10,7 @@ because the kernels trust the sizes and strides they are given.
   gate(A_log, dt_bias, a, b)            -> (log_decay, gamma | None, beta)
   prefill(q, k, v, decay, beta, ...)    -> (out, final_state)
   decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, ...) -> (out, pool)
+  conv1d(x, weight, conv_state, slot_idx, row_offsets, ...) -> out
 """
 from __future__ import annotations
 
@@ -21,8 +22,8 @@ import torch
 from . import _lib
 from ._lib import GdnError
 
-__all__ = ["gate", "prefill", "decode", "version", "GdnError",
-           "prefill_args", "decode_args"]
+__all__ = ["gate", "prefill", "decode", "conv1d", "version", "GdnError",
+           "prefill_args", "decode_args", "conv1d_args"]
 
 _DT = {torch.float32: _lib.GDN_F32, torch.bfloat16: _lib.GDN_BF16}
 
@@ -340,3 +341,94 @@ def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None, sca
     _lib.check(lib.gdn_decode(ctypes.byref(d), _stream(stream)))
     del keep
     return out, pool
+
+
+_U32_MAX = 0xFFFFFFFF
+
+
+def _u32(t, name, shape, negative):
+    """An index tensor as the uint32 bit pattern the C ABI reads (held in an
+    int32 tensor).  int32 tensors pass through as their bit pattern (no extra
+    launch); in int64 / uint32 tensors negative entries become `negative` and
+    entries above 2^32-1 are clamped to it."""
+    if t.dtype not in (torch.int32, torch.int64, torch.uint32):
+        raise ValueError("%s must be int32, int64 or uint32" % name)
+    _shape(t, name, shape)
+    if t.dtype == torch.int32:
+        return t.contiguous()
+    t64 = t.to(torch.int64)
+    t64 = torch.where(t64 < 0, torch.full_like(t64, negative), t64.clamp(max=_U32_MAX))
+    return torch.where(t64 > 0x7FFFFFFF, t64 - (1 << 32), t64).to(torch.int32).contiguous()
+
+
+def conv1d_args(x, weight, conv_state, slot_idx, row_offsets, *, write_state=True, out=None):
+    """Marshal a gdn_conv1d call: returns (args struct, tensors to keep alive, out)."""
+    if x.dim() != 2:
+        raise ValueError("x must be [total_tokens, conv_dim]")
+    T, C = x.shape
+    dt = _io_dtype(x)
+    if weight.dim() != 2 or weight.shape[0] != C:
+        raise ValueError("weight must be [conv_dim, kernel_size]")
+    K = weight.shape[1]
+    if weight.dtype != x.dtype:
+        raise ValueError("weight must have x's dtype")
+    weight = weight.contiguous()
+    n = slot_idx.shape[0] if slot_idx.dim() == 1 else -1
+    if n < 0:
+        raise ValueError("slot_idx must be [n_seqs]")
+    if conv_state is not None:
+        if conv_state.dim() != 3 or conv_state.shape[1:] != (C, K - 1):
+            raise ValueError("conv_state must be [max_slots, conv_dim, kernel_size - 1]")
+        if conv_state.dtype != x.dtype or not conv_state.is_contiguous() or conv_state.data_ptr() % 16:
+            raise ValueError("conv_state must be dense, 16-byte aligned, with x's dtype "
+                             "(it is updated in place)")
+    elif K > 1:
+        raise ValueError("conv_state is required when kernel_size > 1")
+    slots = _u32(slot_idx, "slot_idx", (n,), _U32_MAX)
+    offs = _u32(row_offsets, "row_offsets", (n + 1,), 0)
+    ve = 8 if dt == _lib.GDN_BF16 else 4
+    if x.stride(1) != 1 or x.stride(0) % ve or x.stride(0) < C or x.data_ptr() % 16:
+        x = x.contiguous()
+    if out is None:
+        out = torch.zeros((T, C), dtype=x.dtype, device=x.device)
+    else:
+        _shape(out, "out", (T, C))
+        if out.dtype != x.dtype or out.stride(1) != 1 or out.stride(0) % ve or out.data_ptr() % 16:
+            raise ValueError("out must have x's dtype, a dense last dim, 16-byte rows")
+    d = _lib.Conv1dArgs()
+    d.total_tokens, d.conv_dim, d.kernel_size, d.n_seqs = T, C, K, n
+    d.io_dtype, d.write_state = dt, 1 if write_state else 0
+    d.max_slots = 0 if conv_state is None else conv_state.shape[0]
+    d.x, d.x_stride_token = x.data_ptr(), x.stride(0)
+    d.weight = weight.data_ptr()
+    d.conv_state = None if conv_state is None else conv_state.data_ptr()
+    d.slot_idx, d.row_offsets = slots.data_ptr(), offs.data_ptr()
+    d.out, d.out_stride_token = out.data_ptr(), out.stride(0)
+    keep = (x, weight, slots, offs)
+    return d, keep, out
+
+
+def conv1d(x, weight, conv_state, slot_idx, row_offsets, *, write_state=True, out=None,
+           stream=None):
+    """Causal depthwise conv1d over a ragged batch with a slot-indexed conv-state
+    pool ("gated_delta_conv1d_fwd").
+
+    x [T, conv_dim]; weight [conv_dim, K] (x's dtype); conv_state
+    [max_slots, conv_dim, K-1] (x's dtype, dense, updated in place when
+    write_state); slot_idx [n_seqs]; row_offsets [n_seqs + 1], uint32-valued
+    as on the page (int32 tensors are read as their uint32 bit pattern, so a
+    negative int32 slot is out of range and a negative int32 offset is past
+    the end; int64 offsets below 0 count as 0).  Slots outside the pool read
+    zeros and are not written.  Returns out
+    [T, conv_dim]; rows no sequence covers keep out's previous contents (zeros
+    when out is None).
+    """
+    lib = _lib.load()
+    for name, t in (("x", x), ("weight", weight), ("conv_state", conv_state),
+                    ("slot_idx", slot_idx), ("row_offsets", row_offsets), ("out", out)):
+        _dev(t, name)
+    d, keep, out = conv1d_args(x, weight, conv_state, slot_idx, row_offsets,
+                               write_state=write_state, out=out)
+    _lib.check(lib.gdn_conv1d(ctypes.byref(d), _stream(stream)))
+    del keep
+    return out

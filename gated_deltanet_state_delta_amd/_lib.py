@@ -20,7 +20,7 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_
                 4: "GDN_ERR_LAYOUT", 5: "GDN_ERR_UNSUPPORTED", 6: "GDN_ERR_HIP"}
 
 # every extern "C" symbol include/libgdn.h declares
-EXPORTED = ("gdn_last_error", "gdn_version", "gdn_gate", "gdn_prefill", "gdn_decode")
+EXPORTED = ("gdn_last_error", "gdn_version", "gdn_gate", "gdn_prefill", "gdn_decode", "gdn_conv1d")
 
 _i32, _i64, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 
@@ -56,6 +56,17 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class Conv1dArgs(ctypes.Structure):
+    _fields_ = [
+        ("total_tokens", _i64), ("conv_dim", _i32), ("kernel_size", _i32),
+        ("n_seqs", _i32), ("io_dtype", _i32), ("write_state", _i32), ("max_slots", _i32),
+        ("x", _vp), ("x_stride_token", _i64),
+        ("weight", _vp), ("conv_state", _vp),
+        ("slot_idx", _vp), ("row_offsets", _vp),
+        ("out", _vp), ("out_stride_token", _i64),
+    ]
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -81,6 +92,8 @@ def load(path: str | None = None):
         lib.gdn_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
         lib.gdn_decode.restype = ctypes.c_int
         lib.gdn_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
+        lib.gdn_conv1d.restype = ctypes.c_int
+        lib.gdn_conv1d.argtypes = [ctypes.POINTER(Conv1dArgs), _vp]
         if path is None:
             _lib = lib
         return lib

@@ -148,4 +148,35 @@ gdn_status gdn_decode(const gdn_decode_args* p, void* stream) {
   return from_hip(gdn::launch_decode(a, (hipStream_t)stream), "gdn_decode launch");
 }
 
+gdn_status gdn_conv1d(const gdn_conv1d_args* p, void* stream) {
+  g_err[0] = 0;
+  if (!p) return fail(GDN_ERR_NULL, "gdn_conv1d: args is NULL");
+  const gdn_conv1d_args& a = *p;
+  if (a.io_dtype != GDN_F32 && a.io_dtype != GDN_BF16) return fail(GDN_ERR_DTYPE, "gdn_conv1d: io_dtype %d", a.io_dtype);
+  if (a.total_tokens < 0 || a.conv_dim <= 0 || a.n_seqs < 0 || a.max_slots < 0)
+    return fail(GDN_ERR_SHAPE, "gdn_conv1d: bad sizes T=%lld conv_dim=%d n_seqs=%d max_slots=%d",
+                (long long)a.total_tokens, a.conv_dim, a.n_seqs, a.max_slots);
+  if (a.kernel_size < 1 || a.kernel_size > 8)
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_conv1d: kernel_size=%d (supported 1..8)", a.kernel_size);
+  const int64_t ve = a.io_dtype == GDN_BF16 ? 8 : 4;
+  if (a.conv_dim % ve != 0)
+    return fail(GDN_ERR_LAYOUT, "gdn_conv1d: conv_dim=%d is not a multiple of %lld elements", a.conv_dim, (long long)ve);
+  if (a.n_seqs == 0 || a.total_tokens == 0) return GDN_OK;
+  if (!a.x || !a.weight || !a.slot_idx || !a.row_offsets || !a.out || (a.kernel_size > 1 && !a.conv_state))
+    return fail(GDN_ERR_NULL, "gdn_conv1d: x, weight, slot_idx, row_offsets, out (and conv_state for kernel_size > 1) are required");
+  if (a.x_stride_token < a.conv_dim || a.out_stride_token < a.conv_dim || a.x_stride_token % ve != 0 ||
+      a.out_stride_token % ve != 0)
+    return fail(GDN_ERR_LAYOUT, "gdn_conv1d: row strides must be >= conv_dim and multiples of %lld elements", (long long)ve);
+  if (!aligned(a.x, 16) || !aligned(a.out, 16) || !aligned(a.conv_state, 16))
+    return fail(GDN_ERR_LAYOUT, "gdn_conv1d: x, out and conv_state must be 16-byte aligned");
+  {
+    const size_t es = elem_size(a.io_dtype);
+    const uintptr_t x0 = (uintptr_t)a.x, o0 = (uintptr_t)a.out;
+    const uintptr_t x1 = x0 + ((size_t)(a.total_tokens - 1) * a.x_stride_token + a.conv_dim) * es;
+    const uintptr_t o1 = o0 + ((size_t)(a.total_tokens - 1) * a.out_stride_token + a.conv_dim) * es;
+    if (x0 < o1 && o0 < x1) return fail(GDN_ERR_LAYOUT, "gdn_conv1d: out overlaps x");
+  }
+  return from_hip(gdn::launch_conv1d(a, (hipStream_t)stream), "gdn_conv1d launch");
+}
+
 }  // extern "C"

@@ -18,4 +18,6 @@ hipError_t launch_decode(const gdn_decode_args& args, hipStream_t stream);
 
 hipError_t launch_prefill(const gdn_prefill_args& args, hipStream_t stream);
 
+hipError_t launch_conv1d(const gdn_conv1d_args& args, hipStream_t stream);
+
 }  // namespace gdn

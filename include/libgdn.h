@@ -226,6 +226,59 @@ typedef struct {
 
 gdn_status gdn_decode(const gdn_decode_args* args, void* stream);
 
+/* ----------------------------------------------------------------------------
+ * gdn_conv1d -- causal depthwise conv1d over a ragged batch, reading and
+ * updating a slot-indexed conv-state pool in place.
+ *
+ * Contract of "gated_delta_conv1d_fwd" (parameters and example).  Sequence b
+ * covers rows [row_offsets[b], row_offsets[b+1]) of x (offsets clamped to
+ * total_tokens; a decreasing pair is an empty sequence).  For every channel c
+ * the window is the slot's kernel_size-1 saved inputs, oldest first, followed
+ * by the sequence's inputs:
+ *     win = conv_state[slot_idx[b], c, :] ++ x[row_offsets[b] .., c]
+ *     out[row_offsets[b] + t, c] = sum_{j < K} weight[c, j] * win[t + j]
+ * so weight[c, K-1] multiplies the current input; products are summed in
+ * fp32 and rounded once to io_dtype.  With write_state != 0 the slot then
+ * holds the last K-1 entries of win (an empty sequence leaves it unchanged);
+ * with write_state == 0 the pool is only read.  A slot_idx entry >= max_slots
+ * reads zeros as its saved inputs and is never written.  Rows of x that no
+ * sequence covers leave their out rows untouched.
+ *
+ * Layouts (row-major):
+ *   x    [total_tokens, conv_dim] io_dtype, row stride x_stride_token
+ *   out  [total_tokens, conv_dim] io_dtype, row stride out_stride_token
+ *   weight     [conv_dim, kernel_size] io_dtype, dense
+ *   conv_state [max_slots, conv_dim, kernel_size - 1] io_dtype, dense
+ *   slot_idx [n_seqs] uint32; row_offsets [n_seqs + 1] uint32, non-decreasing
+ *       (rows that several sequences cover get an unspecified one's output)
+ * Requirements: 1 <= kernel_size <= 8; conv_dim a multiple of 16 bytes of
+ * io_dtype (8 bf16 / 4 fp32 elements); x, out and conv_state 16-byte aligned;
+ * row strides of x and out at least conv_dim and multiples of that same
+ * count; out must not overlap x.  conv_state may be NULL only when
+ * kernel_size == 1.
+ * n_seqs == 0 or total_tokens == 0 is a no-op (every sequence is empty).  Two
+ * sequences of one call that name the same valid slot are undefined
+ * behaviour.  Two launches: the outputs, then the state write-back, in stream
+ * order.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int64_t total_tokens;
+  int32_t conv_dim;
+  int32_t kernel_size;
+  int32_t n_seqs;
+  int32_t io_dtype;
+  int32_t write_state;
+  int32_t max_slots;
+  const void* x;        int64_t x_stride_token;
+  const void* weight;
+  void* conv_state;
+  const uint32_t* slot_idx;
+  const uint32_t* row_offsets;
+  void* out;            int64_t out_stride_token;
+} gdn_conv1d_args;
+
+gdn_status gdn_conv1d(const gdn_conv1d_args* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -183,6 +183,51 @@ def mtp_decode_b64_t4():
                          dv=64, dtype="bf16", scatter=True)
 
 
+def conv1d_inputs(seed: int, *, lengths, conv_dim, kernel_size=4, max_slots=8, dtype="bf16",
+                  slots=None, state_std=1.0, x_std=1.0):
+    """Inputs for one conv1d call (all CPU tensors), after the page example of
+    "gated_delta_conv1d_fwd": x [T, conv_dim], weight [conv_dim, K] and the
+    pool [max_slots, conv_dim, K-1] all standard normal (scaled by x_std /
+    state_std), in the io dtype.  ``lengths`` lists the per-sequence row
+    counts, packed back to back (row_offsets uint32-valued, held as int64).
+    ``slots`` None draws distinct slots (a random choice without replacement
+    from the pool); otherwise the given list is used as is."""
+    g = _gen(seed)
+    lengths = [int(x) for x in lengths]
+    n = len(lengths)
+    T = sum(lengths)
+    off = torch.zeros(n + 1, dtype=torch.int64)
+    off[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0)
+    dt = DTYPES[dtype]
+    K = int(kernel_size)
+    x = _randn(g, (T, conv_dim), x_std).to(dt)
+    w = _randn(g, (conv_dim, K)).to(dt)
+    st = _randn(g, (max_slots, conv_dim, K - 1), state_std).to(dt)
+    if slots is None:
+        if n > max_slots:
+            raise ValueError("distinct slots need n_seqs <= max_slots")
+        slot = torch.randperm(max_slots, generator=g)[:n].to(torch.int64)
+    else:
+        slot = torch.tensor([int(v) for v in slots], dtype=torch.int64)
+    return dict(x=x, weight=w, conv_state=st, slot_idx=slot, row_offsets=off, T=T,
+                conv_dim=conv_dim, K=K, dtype=dtype, lengths=lengths)
+
+
+def conv1d_prefill_b4_s4096():
+    """The prefill batch's QKV projection ahead of the delta rule: B=4 x S=4096
+    packed, conv_dim = 2*16*128 + 32*128 = 8192 (q, k of Hq=16 and v of Hv=32
+    heads of size 128), K=4, bf16; pool of 64 slots, 4 distinct slots."""
+    return conv1d_inputs(6, lengths=[4096] * 4, conv_dim=8192, kernel_size=4, max_slots=64,
+                         dtype="bf16")
+
+
+def conv1d_decode_b256():
+    """One decode step's QKV rows: 256 sequences of length 1, conv_dim 8192,
+    K=4, bf16; pool of 1024 slots, 256 distinct slots."""
+    return conv1d_inputs(7, lengths=[1] * 256, conv_dim=8192, kernel_size=4, max_slots=1024,
+                         dtype="bf16")
+
+
 WORKLOADS = {
     "single_head_scan_b2_s64_d16_f32": single_head_scan,
     "chunked_prefill_b4_s4096_hv32_d128_bf16": chunked_prefill_b4_s4096,

@@ -27,7 +27,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_exported_set(lib):
@@ -152,7 +152,58 @@ def test_gate_rejects(lib):
     assert lib.gdn_gate(None, None, None, None, 1, 0, 4, None, None, None, None) == 0  # n == 0
 
 
-@pytest.mark.parametrize("cname,pycls", [("gdn_prefill_args", "PrefillArgs"), ("gdn_decode_args", "DecodeArgs")])
+def _conv1d(**over):
+    c = L.Conv1dArgs()
+    c.total_tokens, c.conv_dim, c.kernel_size, c.n_seqs = 64, 256, 4, 3
+    c.io_dtype, c.write_state, c.max_slots = L.GDN_BF16, 1, 8
+    c.x, c.x_stride_token = FAKE, 256
+    c.weight, c.conv_state, c.slot_idx, c.row_offsets = FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5
+    c.out, c.out_stride_token = FAKE * 6, 256
+    for k, v in over.items():
+        setattr(c, k, v)
+    return c
+
+
+CONV1D_ERRORS = [
+    (dict(io_dtype=3), 3),
+    (dict(total_tokens=-1), 2),
+    (dict(conv_dim=0), 2),
+    (dict(n_seqs=-2), 2),
+    (dict(max_slots=-1), 2),
+    (dict(kernel_size=0), 5),
+    (dict(kernel_size=9), 5),
+    (dict(conv_dim=252, x_stride_token=252, out_stride_token=252), 4),  # not a multiple of 8 bf16
+    (dict(x=None), 1),
+    (dict(weight=None), 1),
+    (dict(conv_state=None), 1),           # required for kernel_size > 1
+    (dict(slot_idx=None), 1),
+    (dict(row_offsets=None), 1),
+    (dict(out=None), 1),
+    (dict(x=FAKE + 8), 4),                # not 16-byte aligned
+    (dict(conv_state=FAKE * 3 + 4), 4),
+    (dict(out_stride_token=200), 4),      # smaller than conv_dim
+    (dict(x_stride_token=260), 4),        # not a multiple of 8 elements
+    (dict(out=FAKE + 256 * 2 * 10), 4),   # out overlaps x
+]
+
+
+@pytest.mark.parametrize("over,status", CONV1D_ERRORS)
+def test_conv1d_rejects(lib, over, status):
+    c = _conv1d(**over)
+    assert lib.gdn_conv1d(ctypes.byref(c), None) == status
+    assert lib.gdn_last_error()
+
+
+def test_conv1d_null_args_and_noop(lib):
+    assert lib.gdn_conv1d(None, None) == 1
+    assert lib.gdn_conv1d(ctypes.byref(_conv1d(n_seqs=0)), None) == 0
+    assert lib.gdn_conv1d(ctypes.byref(_conv1d(total_tokens=0)), None) == 0
+    # kernel_size 1 needs no conv state; nothing to do without sequences
+    assert lib.gdn_conv1d(ctypes.byref(_conv1d(kernel_size=1, conv_state=None, n_seqs=0)), None) == 0
+
+
+@pytest.mark.parametrize("cname,pycls", [("gdn_prefill_args", "PrefillArgs"), ("gdn_decode_args", "DecodeArgs"),
+                                         ("gdn_conv1d_args", "Conv1dArgs")])
 def test_struct_layout_matches_the_binding(cname, pycls, tmp_path):
     """Every field of the argument structs sits at the same offset in C (gcc
     on the header) and in the Python binding's ctypes mirror."""
