@@ -174,3 +174,77 @@ def test_fused_gate_and_norm_arguments():
         gdn.prefill_args(q, q, v, None, None)                        # no gates at all
     with pytest.raises(ValueError):
         gdn.prefill_args(q, q, v, None, None, A_log=A, dt_bias=A, a=ab.float(), b=ab.float())
+
+
+def _conv(T=40, C=64, K=4, n=3, P=5, dtype=torch.bfloat16):
+    x = torch.randn(T, C).to(dtype)
+    w = torch.randn(C, K).to(dtype)
+    st = torch.randn(P, C, K - 1).to(dtype) if K > 1 else None
+    sl = torch.tensor(list(range(n)), dtype=torch.int64)
+    off = torch.tensor([0] + [T * (i + 1) // n for i in range(n)], dtype=torch.int64)
+    return x, w, st, sl, off
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("K", [1, 4, 8])
+def test_conv1d_struct_in_bounds(dtype, K):
+    x, w, st, sl, off = _conv(K=K, dtype=dtype)
+    # x as a column slice of a wider buffer: passed in place with its row stride
+    wide = torch.zeros(x.shape[0], x.shape[1] + 16, dtype=dtype)
+    wide[:, 8:8 + x.shape[1]] = x
+    xv = wide[:, 8:8 + x.shape[1]]
+    a, keep, out = gdn.conv1d_args(xv, w, st, sl, off)
+    x2, w2, slots, offs = keep
+    T, C = a.total_tokens, a.conv_dim
+    assert (T, C, a.kernel_size, a.n_seqs) == (40, 64, K, 3)
+    assert a.x_stride_token == x2.stride(0) and a.out_stride_token == out.stride(0)
+    assert _span_ok(a.x, (T - 1) * a.x_stride_token + C - 1, x2)
+    assert _span_ok(a.out, (T - 1) * a.out_stride_token + C - 1, out)
+    assert _span_ok(a.weight, C * K - 1, w2)
+    if K > 1:
+        assert a.max_slots == st.shape[0]
+        assert _span_ok(a.conv_state, a.max_slots * C * (K - 1) - 1, st)
+    else:
+        assert not a.conv_state
+    assert _span_ok(a.slot_idx, a.n_seqs - 1, slots) and _span_ok(a.row_offsets, a.n_seqs, offs)
+
+
+def test_conv1d_index_marshalling():
+    """Indices reach the C ABI as the uint32 values the page's dtype holds:
+    int64 negatives become 0xFFFFFFFF (slots: outside every pool) or 0
+    (offsets), values past 2^32 - 1 are clamped, int32 passes bit for bit."""
+    x, w, st, _, _ = _conv()
+    sl = torch.tensor([-1, 2, 2**33], dtype=torch.int64)
+    off = torch.tensor([-5, 10, 2**32 + 7, 40], dtype=torch.int64)
+    a, (x2, w2, slots, offs), out = gdn.conv1d_args(x, w, st, sl, off)
+    assert slots.dtype == torch.int32 and offs.dtype == torch.int32
+    assert [v & 0xFFFFFFFF for v in slots.tolist()] == [0xFFFFFFFF, 2, 0xFFFFFFFF]
+    assert [v & 0xFFFFFFFF for v in offs.tolist()] == [0, 10, 0xFFFFFFFF, 40]
+    s32 = torch.tensor([-1, 0, 7], dtype=torch.int32)
+    _, (_, _, slots32, _), _ = gdn.conv1d_args(x, w, st, s32, off)
+    assert slots32.tolist() == [-1, 0, 7]
+
+
+@pytest.mark.parametrize("bad", ["weight_shape", "weight_dtype", "state_shape", "state_dtype",
+                                 "state_missing", "offsets_len", "x_3d", "out_shape"])
+def test_conv1d_rejects_bad_shapes(bad):
+    x, w, st, sl, off = _conv()
+    kw = {}
+    if bad == "weight_shape":
+        w = torch.randn(63, 4).to(x.dtype)
+    elif bad == "weight_dtype":
+        w = w.float()
+    elif bad == "state_shape":
+        st = torch.randn(5, 64, 4).to(x.dtype)
+    elif bad == "state_dtype":
+        st = st.float()
+    elif bad == "state_missing":
+        st = None
+    elif bad == "offsets_len":
+        off = off[:-1]
+    elif bad == "x_3d":
+        x = x.view(40, 8, 8)
+    elif bad == "out_shape":
+        kw["out"] = torch.empty(40, 32, dtype=x.dtype)
+    with pytest.raises(ValueError):
+        gdn.conv1d_args(x, w, st, sl, off, **kw)
