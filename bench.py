@@ -27,7 +27,7 @@ HBM traffic.  `roofline.traffic` and `decode.traffic` come from two
 rocprofv3 counter runs of this script with --copy-calib (one collecting
 FETCH_SIZE, one WRITE_SIZE); each counter is scaled by what it reads for a
 plain 1 GiB streaming pass (torch.neg: 1 GiB read, 1 GiB written).  --summarize-traffic
-turns the two counter CSVs into profiles/hbm_traffic_prefill_b4s4096_decode_b256.json, stamped with a hash
+turns the two counter CSVs into profiles/hbm_traffic_prefill_b4s4096_decode_b256_conv1d_b4s4096.json, stamped with a hash
 of the kernel sources; a later run reports the traffic only while that hash
 still matches, and null otherwise.
 """
@@ -53,7 +53,7 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 FP32_MATRIX_PEAK_TFLOPS = 157.3  # MI355X fp32 matrix, TFLOP/s
 
 METRIC = "GDN prefill tokens/s (B4×S4096,Hv32,d128) + decode state HBM GB/s % of peak"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_b4s4096_decode_b256.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_b4s4096_decode_b256_conv1d_b4s4096.json")
 CALIB_BYTES = 2 * (1 << 30)   # the calibration copy reads 1 GiB and writes 1 GiB
 
 
@@ -68,22 +68,33 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+# The kernels each traffic figure belongs to, by the instantiation the timed
+# workloads launch (demangled or mangled, as the profiler prints them).
+KERNEL_KEYS = (
+    ("prefill", ("prefill_pair_kernel<128, false, false>", "prefill_pair_kernelILi128ELb0ELb0E")),
+    ("decode", ("decode_kernel<__bf16, 128, 128, 32>", "decode_kernelIDF16bLi128ELi128ELi32E")),
+    ("gate", ("gate_kernel",)),
+    ("conv1d_out", ("conv1d_out_kernel<__bf16, 4, 16>", "conv1d_out_kernelIDF16bLi4ELi16E")),
+    ("conv1d_state", ("conv1d_state_kernel<__bf16, 4>", "conv1d_state_kernelIDF16bLi4E")),
+    ("copy", ("neg_kernel",)),
+)
+
+
+def _kernel_key(name):
+    for key, pats in KERNEL_KEYS:
+        if any(p in name for p in pats):
+            return key
+    return None
+
+
 def _counter_means(path, counter):
     """Mean counter value (KiB for FETCH_SIZE/WRITE_SIZE) per kernel family."""
     vals = {}
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != counter:
             continue
-        name = r["Kernel_Name"]
-        if "prefill_kernel" in name or "prefill_pair_kernel" in name:
-            key = "prefill"
-        elif "decode_kernel" in name:
-            key = "decode"
-        elif "gate_kernel" in name:
-            key = "gate"
-        elif "neg_kernel" in name:
-            key = "copy"
-        else:
+        key = _kernel_key(r["Kernel_Name"])
+        if key is None:
             continue
         vals.setdefault(key, []).append(float(r["Counter_Value"]))
     out = {k: statistics.mean(v) for k, v in vals.items() if k != "copy"}
@@ -100,12 +111,17 @@ def summarize_traffic(fetch_csv, write_csv):
     w_scale = (CALIB_BYTES / 2) / (w["copy"] * 1024.0)
     res = {"source_hash": kernel_source_hash(), "calibration_copy_bytes": CALIB_BYTES,
            "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
-    for k in ("prefill", "decode", "gate"):
+    for k in ("prefill", "decode", "gate", "conv1d_out", "conv1d_state"):
         if k in f and k in w:
             rb = f[k] * 1024.0 * f_scale
             wb = w[k] * 1024.0 * w_scale
             res["kernels"][k] = {"fetch_kib_raw": f[k], "write_kib_raw": w[k],
                                  "read_bytes": rb, "write_bytes": wb, "bytes": rb + wb}
+    if "conv1d_out" in res["kernels"]:
+        # one conv1d call = the output launch + the write-back launch
+        parts = [res["kernels"][k] for k in ("conv1d_out", "conv1d_state") if k in res["kernels"]]
+        res["kernels"]["conv1d"] = {n: sum(p[n] for p in parts)
+                                    for n in ("read_bytes", "write_bytes", "bytes")}
     return res
 
 
@@ -301,7 +317,9 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "conv1d"], nargs="+", default=None,
+                    help="parts of the step to run (default: prefill and decode); conv1d adds "
+                         "the causal conv1d over the prefill batch's QKV rows")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -324,8 +342,8 @@ def main():
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
 
-    do_prefill = args.only in (None, "prefill")
-    do_decode = args.only in (None, "decode")
+    parts = set(args.only or ("prefill", "decode"))
+    do_prefill, do_decode, do_conv = ("prefill" in parts), ("decode" in parts), ("conv1d" in parts)
 
     # ---------------------------------------------------------------- inputs
     px = synth.chunked_prefill_b4_s4096()
@@ -347,6 +365,13 @@ def main():
     rd, wr = dx["read_idx"].to(dev), dx["write_idx"].to(dev)
     dout = torch.zeros(dx["batch"], 1, dx["hv"], dx["dv"], dtype=torch.bfloat16, device=dev)
 
+    if do_conv:
+        cx = synth.conv1d_prefill_b4_s4096()
+        c_x, c_w, c_pool = cx["x"].to(dev), cx["weight"].to(dev), cx["conv_state"].to(dev)
+        c_sl = cx["slot_idx"].to(torch.int32).to(dev)
+        c_off = cx["row_offsets"].to(torch.int32).to(dev)
+        c_out = torch.empty_like(c_x)
+
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
     stream = torch.cuda.current_stream()
 
@@ -361,9 +386,12 @@ def main():
         gdn.decode(dq, dk_, dv_, dA, ddt, da, db, pool, rd, write_idx=wr, scale=dx["scale"],
                    out=dout)
 
+    def run_conv():
+        gdn.conv1d(c_x, c_w, c_pool, c_sl, c_off, out=c_out)
+
     E = lambda: torch.cuda.Event(enable_timing=True)
     n_ev = args.warmup + args.steps
-    ev = [[E() for _ in range(5)] for _ in range(n_ev)]
+    ev = [[E() for _ in range(7)] for _ in range(n_ev)]
 
     def step(i):
         e = ev[i]
@@ -379,6 +407,11 @@ def main():
             e[3].record(stream)
             run_decode()
             e[4].record(stream)
+        if do_conv:
+            flush.zero_()
+            e[5].record(stream)
+            run_conv()
+            e[6].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -418,7 +451,7 @@ def main():
         res["unit"] = "tokens/s"
         gbs = pb / (pm * 1e-3) / 1e9
         tfl = pf / (pm * 1e-3) / 1e12
-        res["roofline"] = {"kernel": "prefill_pair_kernel<128>", "bound": "hbm",
+        res["roofline"] = {"kernel": "prefill_pair_kernel<128,false,false>", "bound": "hbm",
                            "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic("prefill"),
                            "algorithmic_bytes": pb, "algorithmic_flops": pf,
@@ -440,6 +473,20 @@ def main():
             res["value"] = gbs
             res["unit"] = "GB/s"
             res["roofline"] = dict(res["decode"])
+    if do_conv:
+        c_ms = [e[5].elapsed_time(e[6]) for e in timed]
+        cm = statistics.median(c_ms)
+        cb = conv1d_algorithmic(cx)
+        gbs = cb / (cm * 1e-3) / 1e9
+        res["conv1d"] = {"kernel": "conv1d_out_kernel<bf16,4,16> + conv1d_state_kernel<bf16,4>",
+                         "workload": "conv1d_prefill_b4_s4096_c8192_k4_bf16", "bound": "hbm",
+                         "ms": cm, "ms_min": min(c_ms), "algorithmic_bytes": cb,
+                         "traffic": load_traffic("conv1d"), "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
+        if not (do_prefill or do_decode):
+            res["value"] = gbs
+            res["unit"] = "GB/s"
+            res["roofline"] = dict(res["conv1d"])
 
     if not args.no_extra and args.only is None:
         del pool, flush
