@@ -13,7 +13,8 @@ Page citations (by title and section):
   * "Gated DeltaNet State Update": recurrence, readout after the update,
     zero initial state, per-batch independence, constraints.
   * "com.microsoft.GatedDeltaNet": GVA head map h*Hq/Hv, cu_seqlens clamping,
-    V-major fp32 states, empty-request copy-through, qwen gate, scale.
+    V-major fp32 states, empty-request copy-through, qwen gate, scale,
+    update_rule (linear / gated / delta / gated_delta).
   * "flashinfer.cake_gdp.cake_gated_delta_product_mtp": slot-pool decode,
     Householder sub-steps, skip / write-slot / scatter / disable rules.
 """
@@ -63,7 +64,7 @@ def _load():
                 ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                 _dp, _dp, _dp, _dp, ctypes.c_int32, _dp, _ip, _dp, ctypes.c_double,
-                _dp, _dp, ctypes.c_int32, ctypes.c_double, _dp, _dp, _dp, _dp]
+                _dp, _dp, ctypes.c_int32, ctypes.c_double, _dp, _dp, _dp, _dp, ctypes.c_int32]
             lib.gdno_decode.restype = ctypes.c_int
             lib.gdno_decode.argtypes = [
                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -138,18 +139,24 @@ def gate(A_log, dt_bias, a=None, b=None):
     return g, gam, bet
 
 
+RULES = {"gated_delta": 0, "gated": 1, "delta": 2, "linear": 3}
+
+
 def prefill(q, k, v, decay, beta, *, decay_is_gamma=False, cu_seqlens=None,
             n_seqs=None, seq_len=None, initial_state=None, scale=1.0,
             out_init=None, nthreads=None, qk_l2norm_eps=None, A_log=None, dt_bias=None,
-            a=None, b=None):
+            a=None, b=None, update_rule="gated_delta"):
     """Sequential fp64 prefill.
 
     q, k: [T, hq, dk]; v: [T, hv, dv]; decay, beta: [T, hv];
     cu_seqlens: [N+1] or None (then n_seqs * seq_len == T);
     initial_state: [N, hv, dv, dk] V-major or None.
     qk_l2norm_eps: None (q, k used as given) or the epsilon of the in-kernel
-    L2 norm x / sqrt(sum x^2 + eps).  a, b [T, hv] with A_log, dt_bias [hv]:
-    the fused gate (decay and beta are then ignored and may be None).
+    L2 norm x / sqrt(sum x^2 + eps).  a [T, hv] with A_log, dt_bias [hv]: the
+    fused qwen decay (decay is then ignored); b [T, hv]: beta = sigmoid(b)
+    (beta is then ignored).  update_rule: "gated_delta", "gated", "delta" or
+    "linear" (the ONNX card's update_rule); rules without the decay ignore
+    decay / a, rules without beta ignore beta / b.
     Returns (out [T, hv, dv], final_state [N, hv, dv, dk]) as float64 arrays.
     out rows no request covers hold out_init (default NaN).
     """
@@ -179,7 +186,7 @@ def prefill(q, k, v, decay, beta, *, decay_is_gamma=False, cu_seqlens=None,
                           _p(init), float(scale), _p(out), _p(fin),
                           nthreads or default_threads(),
                           -1.0 if qk_l2norm_eps is None else float(qk_l2norm_eps),
-                          *[_p(x) for x in fused])
+                          *[_p(x) for x in fused], RULES[update_rule])
     if rc != 0:
         raise ValueError("gdno_prefill rejected its arguments")
     return out, fin

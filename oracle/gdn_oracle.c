@@ -74,6 +74,25 @@ static void gd_step(int dk, int dv, double* S, const double* k, const double* v,
   }
 }
 
+/* One step of the ONNX card's recurrence with its update_rule ("Description"
+ * and the update_rule attribute):
+ *   S_t = exp(g_t) S_{t-1} + k_t (beta_t (v_t - exp(g_t) S_{t-1}^T k_t))^T
+ * taken literally: decay the state, retrieve from the decayed state when the
+ * rule keeps the delta retrieval (retrieve != 0), then add k u^T.  Rules
+ * without the decay pass gamma = 1, rules without beta pass beta = 1. */
+static void rule_step(int dk, int dv, double* S, const double* k, const double* v,
+                      double gamma, double beta, int retrieve, double* tmp) {
+  for (size_t e = 0; e < (size_t)dk * dv; ++e) S[e] *= gamma;
+  for (int j = 0; j < dv; ++j) {
+    double r = 0.0;
+    if (retrieve)
+      for (int i = 0; i < dk; ++i) r += S[(size_t)i * dv + j] * k[i];
+    tmp[j] = beta * (v[j] - r); /* u_j */
+  }
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += k[i] * tmp[j];
+}
+
 /* Readout y = scale * q^T S (a dv-vector), taken after the update. */
 static void readout(int dk, int dv, const double* S, const double* q, double scale,
                     double* y) {
@@ -154,7 +173,8 @@ typedef struct {
   double scale;
   double *out, *final_state;
   double qk_eps;                      /* < 0: no in-kernel L2 norm */
-  const double *A_log, *dt_bias, *a, *b;  /* fused gate when a != NULL */
+  const double *A_log, *dt_bias, *a, *b;  /* fused decay when a != NULL, fused beta when b != NULL */
+  int32_t rule;                       /* GDNO_RULE_* */
 } prefill_ctx;
 
 static int64_t clamp64(int64_t x, int64_t lo, int64_t hi) {
@@ -199,15 +219,18 @@ static void prefill_unit(void* vctx, int64_t unit) {
       k = kn;
     }
     const size_t e = (size_t)t * c->hv + h;
-    double gamma, beta;
-    if (c->a) {  /* fused gate: the qwen gate and a sigmoid beta */
-      gamma = exp(gate_log_decay(c->A_log[h], c->dt_bias[h], c->a[e]));
-      beta = sigmoid(c->b[e]);
-    } else {
-      gamma = c->decay_is_gamma ? c->decay[e] : exp(c->decay[e]);
-      beta = c->beta[e];
-    }
-    gd_step(dk, dv, S, k, v, gamma, beta, tmp);
+    const int has_decay = c->rule == GDNO_RULE_GATED_DELTA || c->rule == GDNO_RULE_GATED;
+    const int has_beta = c->rule == GDNO_RULE_GATED_DELTA || c->rule == GDNO_RULE_DELTA;
+    double gamma = 1.0, beta = 1.0;
+    if (has_decay) /* fused: the qwen gate on a */
+      gamma = c->a ? exp(gate_log_decay(c->A_log[h], c->dt_bias[h], c->a[e]))
+                   : (c->decay_is_gamma ? c->decay[e] : exp(c->decay[e]));
+    if (has_beta) /* fused: a sigmoid of b */
+      beta = c->b ? sigmoid(c->b[e]) : c->beta[e];
+    if (c->rule == GDNO_RULE_GATED_DELTA)
+      gd_step(dk, dv, S, k, v, gamma, beta, tmp);
+    else
+      rule_step(dk, dv, S, k, v, gamma, beta, c->rule == GDNO_RULE_DELTA, tmp);
     readout(dk, dv, S, q, c->scale, c->out + ((size_t)t * c->hv + h) * dv);
   }
   free(kn);
@@ -226,16 +249,20 @@ int gdno_prefill(int32_t n_seqs, int64_t total_tokens, int32_t seq_len,
                  const int64_t* cu, const double* init, double scale,
                  double* out, double* final_state, int32_t nthreads,
                  double qk_l2norm_eps, const double* A_log, const double* dt_bias,
-                 const double* a, const double* b) {
+                 const double* a, const double* b, int32_t update_rule) {
   if (n_seqs < 0 || total_tokens < 0 || hq <= 0 || hv <= 0 || dk <= 0 || dv <= 0)
     return -1;
   if (hv % hq != 0) return -1;
   if (!cu && (int64_t)n_seqs * seq_len != total_tokens) return -1;
-  if (a && (!b || !A_log || !dt_bias)) return -1;
-  if (!a && (!decay || !beta) && total_tokens > 0) return -1;
+  if (update_rule < GDNO_RULE_GATED_DELTA || update_rule > GDNO_RULE_LINEAR) return -1;
+  const int has_decay = update_rule == GDNO_RULE_GATED_DELTA || update_rule == GDNO_RULE_GATED;
+  const int has_beta = update_rule == GDNO_RULE_GATED_DELTA || update_rule == GDNO_RULE_DELTA;
+  if (a && (!A_log || !dt_bias)) return -1;
+  if (total_tokens > 0 && has_decay && !a && !decay) return -1;
+  if (total_tokens > 0 && has_beta && !b && !beta) return -1;
   prefill_ctx c = {n_seqs, seq_len, hq, hv, dk, dv, decay_is_gamma, total_tokens,
                    q, k, v, decay, beta, init, cu, scale, out, final_state,
-                   qk_l2norm_eps, A_log, dt_bias, a, b};
+                   qk_l2norm_eps, A_log, dt_bias, a, b, update_rule};
   run_units(prefill_unit, &c, (int64_t)n_seqs * hv, nthreads);
   return 0;
 }

@@ -34,6 +34,14 @@
 
 #include <stdint.h>
 
+/* update_rule of the ONNX card (Attributes): which terms survive. */
+enum {
+  GDNO_RULE_GATED_DELTA = 0, /* decay and delta retrieval */
+  GDNO_RULE_GATED = 1,       /* decay only: S = gamma S + k v^T */
+  GDNO_RULE_DELTA = 2,       /* retrieval only: S = S + k (beta (v - S^T k))^T */
+  GDNO_RULE_LINEAR = 3       /* neither: S = S + k v^T */
+};
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -54,9 +62,16 @@ void gdno_gate(int64_t n, int32_t hv, const double* A_log, const double* dt_bias
  *   decay    [T, hv]          log-space decay when decay_is_gamma == 0,
  *                             gamma itself when decay_is_gamma != 0
  *   beta     [T, hv]          effective update rate
- *   A_log, dt_bias [hv], a, b [T, hv]: when a != NULL the gates come from
- *                             them (fused gate, as gdno_gate) and decay / beta
- *                             are not read
+ *   A_log, dt_bias [hv], a, b [T, hv]: the fused gate (as gdno_gate): a
+ *                             != NULL gives the decay (the qwen gate, needs
+ *                             A_log and dt_bias; decay is then not read), b
+ *                             != NULL gives beta = sigmoid(b) (beta is then
+ *                             not read)
+ *   update_rule               GDNO_RULE_*: which terms of the recurrence
+ *                             survive (the ONNX card's update_rule).  Rules
+ *                             without the decay read no decay (gamma = 1),
+ *                             rules without beta read no beta (beta = 1);
+ *                             linear and gated drop the delta retrieval
  *   qk_l2norm_eps             >= 0: every q and k head vector is replaced by
  *                             x / sqrt(sum(x^2) + qk_l2norm_eps) first; < 0: none
  *   cu       [n_seqs + 1]     or NULL: request r covers [r*seq_len, (r+1)*seq_len)
@@ -71,7 +86,7 @@ int gdno_prefill(int32_t n_seqs, int64_t total_tokens, int32_t seq_len,
                  const int64_t* cu, const double* init, double scale,
                  double* out, double* final_state, int32_t nthreads,
                  double qk_l2norm_eps, const double* A_log, const double* dt_bias,
-                 const double* a, const double* b);
+                 const double* a, const double* b, int32_t update_rule);
 
 /* Slot-pool decode with n_hh Householder sub-steps per token.  With
  * qk_l2norm_eps >= 0 every q and k head vector is first replaced by

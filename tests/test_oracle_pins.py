@@ -644,3 +644,127 @@ def test_conv1d_out_of_range_slot_reads_zeros_and_writes_nothing():
     out0, _ = oracle.conv1d(x, w, np.zeros_like(st), np.array([0]), np.array([0, 6]))
     np.testing.assert_array_equal(out, out0)
     np.testing.assert_array_equal(st2, st)
+
+
+# ---------------------------------------------------------------------------
+# update_rule variants ("com.microsoft.GatedDeltaNet", update_rule attribute)
+
+
+def _rule_inputs(seed, lengths=(5, 0, 12), hq=2, hv=4, dk=6, dv=5):
+    g = torch.Generator().manual_seed(seed)
+    T = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    q = torch.randn(T, hq, dk, generator=g, dtype=torch.float64).numpy()
+    k = torch.randn(T, hq, dk, generator=g, dtype=torch.float64).numpy() * 0.4
+    v = torch.randn(T, hv, dv, generator=g, dtype=torch.float64).numpy()
+    logd = -torch.rand(T, hv, generator=g, dtype=torch.float64).numpy() * 0.5
+    beta = torch.rand(T, hv, generator=g, dtype=torch.float64).numpy()
+    init = torch.randn(len(lengths), hv, dv, dk, generator=g, dtype=torch.float64).numpy()
+    return dict(q=q, k=k, v=v, logd=logd, beta=beta, init=init, cu=cu, hq=hq, hv=hv)
+
+
+def _masked_form(x, decayed, scale):
+    """Y = scale (D o (Q K^T)) V + scale diag(e^G) Q S0 and S = e^{G_T} S0 +
+    K^T diag(e^{G_T - G}) V per (request, head): the matrix form of linear
+    attention (D = causal ones) and of its decayed variant (D_ts = e^{G_t -
+    G_s}, s <= t), with no retrieval term."""
+    q, k, v, cu, hq, hv = x["q"], x["k"], x["v"], x["cu"], x["hq"], x["hv"]
+    T = q.shape[0]
+    out = np.full((T, hv, v.shape[2]), np.nan)
+    fin = np.zeros_like(x["init"])
+    for r in range(len(cu) - 1):
+        a, b = cu[r], cu[r + 1]
+        for h in range(hv):
+            qh = h * hq // hv
+            Q, K, V = q[a:b, qh], k[a:b, qh], v[a:b, h]
+            S0 = x["init"][r, h].T  # K-major [dk, dv]
+            G = np.cumsum(x["logd"][a:b, h]) if decayed else np.zeros(b - a)
+            D = np.tril(np.exp(G[:, None] - G[None, :]))
+            out[a:b, h] = scale * ((D * (Q @ K.T)) @ V + np.exp(G)[:, None] * (Q @ S0))
+            GT = G[-1] if b > a else 0.0
+            S = np.exp(GT) * S0 + K.T @ (np.exp(GT - G)[:, None] * V)
+            fin[r, h] = S.T
+    return out, fin
+
+
+@pytest.mark.parametrize("rule", ["linear", "gated"])
+def test_rules_without_retrieval_match_the_masked_matrix_form(rule):
+    x = _rule_inputs(101)
+    dec = x["logd"] if rule == "gated" else None
+    out, fin = oracle.prefill(x["q"], x["k"], x["v"], dec, None, cu_seqlens=x["cu"],
+                              initial_state=x["init"], scale=0.7, update_rule=rule)
+    ref_o, ref_f = _masked_form(x, rule == "gated", 0.7)
+    np.testing.assert_allclose(out, ref_o, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(fin, ref_f, rtol=1e-12, atol=1e-12)
+
+
+def test_delta_rule_with_one_hot_keys_is_a_per_row_ema():
+    """delta: S <- S + k (beta (v - S^T k))^T.  With one-hot keys e_i the
+    update touches row i only: row_i <- (1 - beta) row_i + beta v."""
+    g = torch.Generator().manual_seed(102)
+    T, dk, dv = 40, 5, 3
+    idx = torch.randint(0, dk, (T,), generator=g).numpy()
+    k = np.zeros((T, 1, dk))
+    k[np.arange(T), 0, idx] = 1.0
+    q = torch.randn(T, 1, dk, generator=g, dtype=torch.float64).numpy()
+    v = torch.randn(T, 1, dv, generator=g, dtype=torch.float64).numpy()
+    beta = torch.rand(T, 1, generator=g, dtype=torch.float64).numpy()
+    init = torch.randn(1, 1, dv, dk, generator=g, dtype=torch.float64).numpy()
+    out, fin = oracle.prefill(q, k, v, None, beta, n_seqs=1, seq_len=T, initial_state=init,
+                              scale=1.0, update_rule="delta")
+    S = init[0, 0].T.copy()  # rows = keys
+    for t in range(T):
+        i = idx[t]
+        S[i] = (1.0 - beta[t, 0]) * S[i] + beta[t, 0] * v[t, 0]
+        np.testing.assert_allclose(out[t, 0], q[t, 0] @ S, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(fin[0, 0], S.T, rtol=1e-13, atol=1e-13)
+
+
+def test_delta_equals_gated_delta_without_decay():
+    """The ONNX card's step form (delta) and the problem statement's
+    Householder form (gated_delta at gamma = 1) agree."""
+    x = _rule_inputs(103)
+    o1, f1 = oracle.prefill(x["q"], x["k"], x["v"], None, x["beta"], cu_seqlens=x["cu"],
+                            initial_state=x["init"], scale=0.5, update_rule="delta")
+    o2, f2 = oracle.prefill(x["q"], x["k"], x["v"], np.zeros_like(x["beta"]), x["beta"],
+                            cu_seqlens=x["cu"], initial_state=x["init"], scale=0.5)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(f1, f2, rtol=1e-12, atol=1e-12)
+
+
+def test_rules_ignore_the_inputs_they_drop_and_fuse_per_input():
+    """Rules read only their own inputs; the fused decay (a) and the fused
+    beta (b) each equal the separate gate's output."""
+    x = _rule_inputs(104)
+    g = torch.Generator().manual_seed(105)
+    T, hv = x["v"].shape[0], x["hv"]
+    A_log = torch.rand(hv, generator=g, dtype=torch.float64).numpy()
+    dt_bias = torch.randn(hv, generator=g, dtype=torch.float64).numpy() * 0.5
+    a = torch.randn(T, hv, generator=g, dtype=torch.float64).numpy()
+    b = torch.randn(T, hv, generator=g, dtype=torch.float64).numpy()
+    gd, _, gb = oracle.gate(A_log, dt_bias, a, b)
+    kw = dict(cu_seqlens=x["cu"], initial_state=x["init"], scale=0.9)
+    args = (x["q"], x["k"], x["v"])
+    # gated: beta is never read; fused a == separate gate
+    o1, f1 = oracle.prefill(*args, gd, None, update_rule="gated", **kw)
+    o2, f2 = oracle.prefill(*args, gd, np.full_like(gd, 7.0), update_rule="gated", **kw)
+    o3, f3 = oracle.prefill(*args, None, None, A_log=A_log, dt_bias=dt_bias, a=a,
+                            update_rule="gated", **kw)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_allclose(o1, o3, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(f1, f3, rtol=1e-12, atol=1e-12)
+    # delta: decay is never read; fused b == separate sigmoid
+    o1, _ = oracle.prefill(*args, None, gb, update_rule="delta", **kw)
+    o2, _ = oracle.prefill(*args, np.full_like(gb, -3.0), gb, update_rule="delta", **kw)
+    o3, _ = oracle.prefill(*args, None, None, b=b, update_rule="delta", **kw)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_allclose(o1, o3, rtol=1e-12, atol=1e-12)
+    # gated_delta with the decay fused and beta given == both given
+    o1, _ = oracle.prefill(*args, gd, gb, **kw)
+    o2, _ = oracle.prefill(*args, None, gb, A_log=A_log, dt_bias=dt_bias, a=a, **kw)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
+    # a rule missing an input it needs is an argument error
+    with pytest.raises(ValueError):
+        oracle.prefill(*args, None, gb, **kw)
+    with pytest.raises(ValueError):
+        oracle.prefill(*args, gd, None, update_rule="delta", **kw)
