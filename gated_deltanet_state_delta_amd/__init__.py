@@ -26,6 +26,8 @@ __all__ = ["gate", "prefill", "decode", "conv1d", "version", "GdnError",
            "prefill_args", "decode_args", "conv1d_args"]
 
 _DT = {torch.float32: _lib.GDN_F32, torch.bfloat16: _lib.GDN_BF16}
+# update_rule of the ONNX card -> gdn_update_rule
+RULES = {"gated_delta": 0, "gated": 1, "delta": 2, "linear": 3}
 
 
 def version() -> str:
@@ -128,7 +130,7 @@ def gate(A_log, dt_bias, a=None, b=None, *, want_gamma=False, log_decay_out=None
 def prefill_args(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None,
                  initial_state=None, scale=None, chunk_size=0, out=None, final_state=None,
                  qk_l2norm=False, qk_l2norm_eps=1e-12, A_log=None, dt_bias=None, a=None,
-                 b=None):
+                 b=None, update_rule="gated_delta"):
     """Validate shapes and build the gdn_prefill_args struct (device-agnostic).
 
     Returns (args, keep, out, final_state): `keep` holds every tensor whose
@@ -157,26 +159,43 @@ def prefill_args(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None,
         raise ValueError("q, k and v must share a dtype")
     dt = _io_dtype(q3)
     q3, k3, v3 = _strided3(q3), _strided3(k3), _strided3(v3)
-    fused = a is not None
-    if fused:
-        if b is None or A_log is None or dt_bias is None:
-            raise ValueError("the fused gate needs A_log, dt_bias, a and b")
+    if update_rule not in RULES:
+        raise ValueError("update_rule must be one of %s" % sorted(RULES))
+    uses_decay = update_rule in ("gated_delta", "gated")
+    uses_beta = update_rule in ("gated_delta", "delta")
+    fused = a is not None or b is not None
+    if fused and (decay is not None or beta is not None):
+        raise ValueError("give the gates either fused (a, b) or as decay / beta, not both "
+                         "(gdn.gate computes either one)")
+    if (a is not None or (decay is not None)) != uses_decay:
+        raise ValueError("update_rule %s %s a decay input (decay or a)"
+                         % (update_rule, "needs" if uses_decay else "takes no"))
+    if (b is not None or (beta is not None)) != uses_beta:
+        raise ValueError("update_rule %s %s a beta input (beta or b)"
+                         % (update_rule, "needs" if uses_beta else "takes no"))
+    ga = gb = None
+    if a is not None:
+        if A_log is None or dt_bias is None:
+            raise ValueError("the fused decay needs A_log and dt_bias")
         ga = a.reshape(-1, hv) if a.dim() == 3 else a
-        gb = b.reshape(-1, hv) if b.dim() == 3 else b
         _shape(ga, "a", (T, hv))
-        _shape(gb, "b", (T, hv))
-        if ga.dtype != q3.dtype or gb.dtype != q3.dtype:
-            raise ValueError("a and b must have q's dtype")
-        ga, gb = ga.contiguous(), gb.contiguous()
+        if ga.dtype != q3.dtype:
+            raise ValueError("a must have q's dtype")
+        ga = ga.contiguous()
         A_log = _f32c(A_log, "A_log", (hv,))
         dt_bias = _f32c(dt_bias, "dt_bias", (hv,))
-        decay = beta = None
     else:
-        if decay is None or beta is None:
-            raise ValueError("decay and beta are required without the fused gate")
+        A_log = dt_bias = None
+    if b is not None:
+        gb = b.reshape(-1, hv) if b.dim() == 3 else b
+        _shape(gb, "b", (T, hv))
+        if gb.dtype != q3.dtype:
+            raise ValueError("b must have q's dtype")
+        gb = gb.contiguous()
+    if decay is not None:
         decay = _f32c(decay.reshape(-1, hv) if decay.dim() == 3 else decay, "decay", (T, hv))
+    if beta is not None:
         beta = _f32c(beta.reshape(-1, hv) if beta.dim() == 3 else beta, "beta", (T, hv))
-        ga = gb = None
     if cu_seqlens is not None:
         if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
             raise ValueError("cu_seqlens must be [N + 1]")
@@ -222,16 +241,20 @@ def prefill_args(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None,
     args.final_state = final_state.data_ptr()
     args.qk_l2norm = 1 if qk_l2norm else 0
     args.qk_l2norm_eps = float(qk_l2norm_eps)
-    if fused:
+    if ga is not None:
         args.A_log, args.dt_bias = A_log.data_ptr(), dt_bias.data_ptr()
-        args.gate_a, args.gate_b = ga.data_ptr(), gb.data_ptr()
+        args.gate_a = ga.data_ptr()
+    if gb is not None:
+        args.gate_b = gb.data_ptr()
+    args.update_rule = RULES[update_rule]
     keep = (q3, k3, v3, decay, beta, cu, initial_state, out3, final_state, A_log, dt_bias, ga, gb)
     return args, keep, out, final_state
 
 
 def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_state=None,
             scale=None, chunk_size=0, out=None, final_state=None, stream=None,
-            qk_l2norm=False, qk_l2norm_eps=1e-12, A_log=None, dt_bias=None, a=None, b=None):
+            qk_l2norm=False, qk_l2norm_eps=1e-12, A_log=None, dt_bias=None, a=None, b=None,
+            update_rule="gated_delta"):
     """Chunked prefill.
 
     q, k: [T, hq, dk] (or [B, S, hq, dk], then uniform packing with seq_len S);
@@ -240,8 +263,12 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
     int32/int64 or None; initial_state: [N, hv, dv, dk] float32 or None.
     scale None means 1/sqrt(dk).  qk_l2norm: use every q and k head vector as
     x / sqrt(sum x^2 + qk_l2norm_eps) (the ONNX card's qk_l2_norm).  a, b
-    ([T, hv] or [B, S, hv] in q's dtype) with A_log, dt_bias [hv]: the fused
-    gate, computed in the kernel (decay and beta are then ignored; pass None).
+    ([T, hv] or [B, S, hv] in q's dtype): the fused gate, computed in the
+    kernel -- the qwen decay from a with A_log, dt_bias [hv], beta = sigmoid(b)
+    (pass decay and beta as None then).  update_rule ("gated_delta", "gated",
+    "delta", "linear"; the ONNX card's attribute) selects which terms of the
+    recurrence survive; a rule takes exactly the gate inputs it uses (gated:
+    decay or a only; delta: beta or b only; linear: neither).
     Returns (out, final_state [N, hv, dv, dk] float32); out is [T, hv, dv] (or
     [B, S, hv, dv]) in q's dtype.
     """
@@ -255,7 +282,7 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
         q, k, v, decay, beta, decay_kind=decay_kind, cu_seqlens=cu_seqlens,
         initial_state=initial_state, scale=scale, chunk_size=chunk_size, out=out,
         final_state=final_state, qk_l2norm=qk_l2norm, qk_l2norm_eps=qk_l2norm_eps,
-        A_log=A_log, dt_bias=dt_bias, a=a, b=b)
+        A_log=A_log, dt_bias=dt_bias, a=a, b=b, update_rule=update_rule)
     _lib.check(lib.gdn_prefill(ctypes.byref(args), _stream(stream)))
     del keep
     return out, final_state

@@ -38,6 +38,7 @@ class PrefillArgs(ctypes.Structure):
         ("initial_state", _vp), ("final_state", _vp),
         ("qk_l2norm", _i32), ("qk_l2norm_eps", _f32),
         ("A_log", _vp), ("dt_bias", _vp), ("gate_a", _vp), ("gate_b", _vp),
+        ("update_rule", _i32),
     ]
 
 

@@ -82,15 +82,33 @@ gdn_status gdn_prefill(const gdn_prefill_args* p, void* stream) {
                 a.n_seqs, a.seq_len, (long long)a.total_tokens);
   if (a.qk_l2norm && !(a.qk_l2norm_eps >= 0.f && a.qk_l2norm_eps <= 3.0e38f))
     return fail(GDN_ERR_SHAPE, "gdn_prefill: qk_l2norm_eps must be finite and >= 0");
+  if (a.update_rule < GDN_RULE_GATED_DELTA || a.update_rule > GDN_RULE_LINEAR)
+    return fail(GDN_ERR_DTYPE, "gdn_prefill: update_rule %d", a.update_rule);
+  if ((int64_t)a.total_tokens * a.hv >= (int64_t(1) << 31))
+    return fail(GDN_ERR_SHAPE, "gdn_prefill: total_tokens * hv must be below 2^31");
+  if (a.total_tokens > 0) {
+    // gate sources: present exactly for the rules that use them (not read
+    // at all when there are no tokens)
+    const bool uses_decay = a.update_rule == GDN_RULE_GATED_DELTA || a.update_rule == GDN_RULE_GATED;
+    const bool uses_beta = a.update_rule == GDN_RULE_GATED_DELTA || a.update_rule == GDN_RULE_DELTA;
+    const bool has_decay = a.decay || a.gate_a, has_beta = a.beta || a.gate_b;
+    const bool fused = a.gate_a || a.gate_b, given = a.decay || a.beta;
+    if (a.decay && a.gate_a) return fail(GDN_ERR_SHAPE, "gdn_prefill: decay and gate_a are both given");
+    if (a.beta && a.gate_b) return fail(GDN_ERR_SHAPE, "gdn_prefill: beta and gate_b are both given");
+    if (has_decay != uses_decay)
+      return fail(uses_decay ? GDN_ERR_NULL : GDN_ERR_SHAPE, "gdn_prefill: update_rule %d %s a decay input",
+                  a.update_rule, uses_decay ? "needs" : "takes no");
+    if (has_beta != uses_beta)
+      return fail(uses_beta ? GDN_ERR_NULL : GDN_ERR_SHAPE, "gdn_prefill: update_rule %d %s a beta input",
+                  a.update_rule, uses_beta ? "needs" : "takes no");
+    if (fused && given)
+      return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill: fused and given gate inputs mixed (use gdn_gate for both)");
+  }
+  if (a.gate_a && (!a.A_log || !a.dt_bias)) return fail(GDN_ERR_NULL, "gdn_prefill: gate_a needs A_log and dt_bias");
   if (a.n_seqs == 0) return GDN_OK;
   if (!a.final_state) return fail(GDN_ERR_NULL, "gdn_prefill: final_state is NULL");
-  const bool fused = a.gate_a != nullptr;
   if (a.total_tokens > 0 && (!a.q || !a.k || !a.v || !a.out))
     return fail(GDN_ERR_NULL, "gdn_prefill: q, k, v and out are required");
-  if (a.total_tokens > 0 && fused && (!a.gate_b || !a.A_log || !a.dt_bias))
-    return fail(GDN_ERR_NULL, "gdn_prefill: the fused gate needs A_log, dt_bias, gate_a and gate_b");
-  if (a.total_tokens > 0 && !fused && (!a.decay || !a.beta))
-    return fail(GDN_ERR_NULL, "gdn_prefill: decay and beta are required (or the fused gate inputs)");
   const void* ptrs[] = {a.q, a.k, a.v, a.out, a.decay, a.beta, a.initial_state, a.final_state, a.cu_seqlens};
   for (const void* q : ptrs)
     if (q && !aligned(q, 16)) return fail(GDN_ERR_LAYOUT, "gdn_prefill: pointers must be 16-byte aligned");

@@ -7,10 +7,36 @@
 // and a hint is lowered to the largest chunk whose double-buffered working
 // set fits one workgroup's LDS (for fp32 operands with dk = 128 that is 32)
 // -- and the (dk, dv) instantiation.
+#include <atomic>
+
 #include "gdn_prefill.hpp"
 #include "gdn_prefill_pair.hpp"
 
 namespace gdn {
+
+// What an absent gate input reads: log-decay 0 (or a raw gate input 0) at
+// [0], beta 1 at [1].  Each device holds its own copy; its address comes
+// from hipGetSymbolAddress on that device.
+__device__ float kGateConst[2] = {0.f, 1.f};
+
+static hipError_t gate_consts(float** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<float*> cache[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float* c = cache[dev].load(std::memory_order_acquire);
+  if (!c) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(kGateConst));
+    if (e != hipSuccess) return e;
+    c = static_cast<float*>(addr);
+    cache[dev].store(c, std::memory_order_release);
+  }
+  *out = c;
+  return hipSuccess;
+}
 
 hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream) {
   PrefillParams p;
@@ -28,7 +54,25 @@ hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream) {
   p.qk_norm = a.qk_l2norm != 0;
   p.qk_eps = a.qk_l2norm_eps;
   p.A_log = a.A_log; p.dt_bias = a.dt_bias; p.ga = a.gate_a; p.gb = a.gate_b;
-  if (p.ga) p.decay_is_gamma = 0;  // the fused gate yields log-space decay
+  // update_rule: the delta retrieval is kept by gated_delta and delta
+  p.rho = (a.update_rule == GDN_RULE_GATED_DELTA || a.update_rule == GDN_RULE_DELTA) ? 1.f : 0.f;
+  p.dmask = p.bmask = ~int64_t(0);
+  const bool fused = a.gate_a || a.gate_b;
+  if (fused) p.decay_is_gamma = 0;  // the fused gate yields log-space decay
+  const bool absent = fused ? (!a.gate_a || !a.gate_b) : (!a.decay || !a.beta);
+  if (absent) {
+    // a rule without decay or beta: the missing source reads the constants
+    float* c = nullptr;
+    const hipError_t e = gate_consts(&c);
+    if (e != hipSuccess) return e;
+    if (fused) {
+      if (!a.gate_a) { p.ga = c; p.A_log = c; p.dt_bias = c; p.dmask = 0; }
+      if (!a.gate_b) { p.gb = c; p.bmask = 0; }
+    } else {
+      if (!a.decay) { p.decay = c; p.dmask = 0; p.decay_is_gamma = 0; }
+      if (!a.beta) { p.beta = c + 1; p.bmask = 0; }
+    }
+  }
   const bool bf = a.io_dtype == GDN_BF16;
   if (bf && prefill_pair_supported(a.dk, a.dv, a.chunk_size)) return prefill_pair_bf16(p, a.dk, stream);
   const int hint = a.chunk_size != 0 ? a.chunk_size : 64;

@@ -78,10 +78,17 @@ struct PrefillParams {
   float scale;
   int qk_norm;      // q, k used as x * rsqrt(sum x^2 + qk_eps)
   float qk_eps;
-  const float* A_log;    // fused gate when ga != nullptr (decay is then log-space)
+  const float* A_log;    // fused gate when ga or gb != nullptr (decay is then log-space)
   const float* dt_bias;
   const void* ga;        // [T, hv] io dtype
   const void* gb;        // [T, hv] io dtype
+  // Gate inputs a rule does not take: the decay source (decay or ga, with
+  // A_log and dt_bias) and the beta source (beta or gb) are indexed through
+  // these masks, all ones for a present input and 0 for an absent one, whose
+  // pointer then holds a device constant: log-decay 0 (or a = 0, replaced by
+  // 0 at staging), beta 1 (or b = 0, replaced by 1).
+  int64_t dmask, bmask;
+  float rho;             // 1: delta retrieval kept; 0: linear / gated rules
 };
 
 // LDS layout of one workgroup.
@@ -218,8 +225,8 @@ prefill_kernel(const PrefillParams p) {
   const E* __restrict__ gk = (const E*)p.k + (int64_t)qh * p.k_sh;
   const E* __restrict__ gv = (const E*)p.v + (int64_t)h * p.v_sh + v0;
   E* __restrict__ gout = (E*)p.out + (int64_t)h * p.o_sh + v0;
-  const float* __restrict__ gdec = p.decay + h;
-  const float* __restrict__ gbet = p.beta + h;
+  const float* __restrict__ gdec = p.decay + (h & p.dmask);
+  const float* __restrict__ gbet = p.beta + (h & p.bmask);
   const int64_t st_base = (((int64_t)r * p.hv + h) * p.dv + v0) * DK;
 
   // M is only written on and below the diagonal; the readout reads the 16x16
@@ -450,10 +457,10 @@ prefill_kernel(const PrefillParams p) {
   bool pvalid = false;
   // gates: given (decay, beta) or fused (the qwen gate and a sigmoid beta
   // from A_log, dt_bias, a, b, computed here per token)
-  const bool fused = EXT && p.ga != nullptr;
-  const E* gga = (const E*)p.ga + h;
-  const E* ggb = (const E*)p.gb + h;
-  const float ealog = fused ? expf(p.A_log[h]) : 0.f, dtb = fused ? p.dt_bias[h] : 0.f;
+  const bool fused = EXT && (p.ga != nullptr || p.gb != nullptr);
+  const E* gga = (const E*)p.ga + (h & p.dmask);
+  const E* ggb = (const E*)p.gb + (h & p.bmask);
+  const float ealog = fused ? expf(p.A_log[h & p.dmask]) : 0.f, dtb = fused ? p.dt_bias[h & p.dmask] : 0.f;
   const bool nrm = EXT && p.qk_norm != 0;
 
   auto prefetch = [&](int c) {
@@ -489,14 +496,15 @@ prefill_kernel(const PrefillParams p) {
     }
     pvalid = lane < rem;
     const int tl = min(lane, rem - 1);
+    const int64_t tok = (t0 + tl) * p.hv;
     if (fused) {
       // raw a and b as loaded (the gates are computed in the scan, so that
       // nothing waits on these loads here)
-      pga = gga[(t0 + tl) * p.hv];
-      pgb = ggb[(t0 + tl) * p.hv];
+      pga = gga[tok & p.dmask];
+      pgb = ggb[tok & p.bmask];
     } else {
-      pg = gdec[(t0 + tl) * p.hv];
-      pb = gbet[(t0 + tl) * p.hv];
+      pg = gdec[tok & p.dmask];
+      pb = gbet[tok & p.bmask];
     }
   };
 
@@ -563,9 +571,9 @@ prefill_kernel(const PrefillParams p) {
   auto scan = [&](typename Sm::Derived& Dd) {
     float lg = 0.f;
     bool reset = false;
-    if (fused) {
-      pg = gate_log_decay_fast(ealog, dtb, to_f32(pga));
-      pb = sigmoid_fast(to_f32(pgb));
+    if (fused) {  // an absent input: no decay, beta 1
+      pg = p.dmask ? gate_log_decay_fast(ealog, dtb, to_f32(pga)) : 0.f;
+      pb = p.bmask ? sigmoid_fast(to_f32(pgb)) : 1.f;
     }
     if (pvalid) {
       if (p.decay_is_gamma) {
@@ -595,7 +603,7 @@ prefill_kernel(const PrefillParams p) {
       Dd.F[lane] = F;
       Dd.z[lane] = z;
       Dd.bet[lane] = bt;
-      Dd.gb[lane] = bt * gam;
+      Dd.gb[lane] = p.rho * bt * gam;  // the retrieval term of X
       Dd.gs[lane] = p.scale * gam;
       Dd.dc[lane] = zlast <= lane ? exp2f(Flast - F) : 0.f;
       if (lane == C - 1) {
@@ -741,7 +749,7 @@ prefill_kernel(const PrefillParams p) {
         if (!tv[k]) continue;
         const int t = 16 * ti[k] + x;
         f4 d = decay4(ti[k], tm[k], false);
-        const float bt = Dd.bet[t];
+        const float bt = p.rho * Dd.bet[t];  // A carries the retrieval term
         f4 dq = d, dk = d;
         if (nrm) {
           const f4 rks = *reinterpret_cast<const f4*>(&Dd.rkn[16 * tm[k] + 4 * g]);
@@ -759,7 +767,7 @@ prefill_kernel(const PrefillParams p) {
         const int i = pw;
         const int t = 16 * i + x;
         const f4 d = decay4(i, i, true);
-        const float bt = Dd.bet[t];
+        const float bt = p.rho * Dd.bet[t];  // A carries the retrieval term
         f4 dq = d, dk = d;
         if (nrm) {
           const f4 rks = *reinterpret_cast<const f4*>(&Dd.rkn[16 * i + 4 * g]);
@@ -797,7 +805,7 @@ hipError_t launch_prefill_t(PrefillParams p, hipStream_t stream) {
     constexpr int DVS = prefill_dvs<DV>();
     p.nsplit = DV / DVS;
     const int64_t nblk = (int64_t)p.n_seqs * p.hv * p.nsplit;
-    if (p.ga || p.qk_norm)
+    if (p.ga || p.gb || p.qk_norm)
       hipLaunchKernelGGL((prefill_kernel<E, DK, DVS, C, true>), dim3((unsigned)nblk), dim3(512), 0, stream, p);
     else
       hipLaunchKernelGGL((prefill_kernel<E, DK, DVS, C, false>), dim3((unsigned)nblk), dim3(512), 0, stream, p);

@@ -236,11 +236,11 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
   // gates: given (decay, beta) or fused (A_log, dt_bias, a, b: the qwen gate
   // and a sigmoid beta, computed here per token)
   constexpr bool fused = FUSED;
-  const float* gdec = p.decay + h;
-  const float* gbet = p.beta + h;
-  const __bf16* gga = (const __bf16*)p.ga + h;
-  const __bf16* ggb = (const __bf16*)p.gb + h;
-  const float ealog = fused ? expf(p.A_log[h]) : 0.f, dtb = fused ? p.dt_bias[h] : 0.f;
+  const float* gdec = p.decay + (h & p.dmask);
+  const float* gbet = p.beta + (h & p.bmask);
+  const __bf16* gga = (const __bf16*)p.ga + (h & p.dmask);
+  const __bf16* ggb = (const __bf16*)p.gb + (h & p.bmask);
+  const float ealog = fused ? expf(p.A_log[h & p.dmask]) : 0.f, dtb = fused ? p.dt_bias[h & p.dmask] : 0.f;
   constexpr bool nrm = NORM;
 
   auto prefetch = [&](int c, PairPrepSet<DK>& s) {
@@ -250,12 +250,13 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
       // the values exactly as loaded: nothing here may wait on these loads
       // (padding and the fused gate are applied when the set is staged)
       const int tl = min(lane, rem - 1);
+      const int64_t tok = (t0 + tl) * p.hv;
       if constexpr (FUSED) {
-        s.ga = gga[(t0 + tl) * p.hv];
-        s.gbr = ggb[(t0 + tl) * p.hv];
+        s.ga = gga[tok & p.dmask];
+        s.gbr = ggb[tok & p.bmask];
       } else {
-        s.gd = gdec[(t0 + tl) * p.hv];
-        s.bt = gbet[(t0 + tl) * p.hv];
+        s.gd = gdec[tok & p.dmask];
+        s.bt = gbet[tok & p.bmask];
       }
     }
     const __bf16* qb = gq + t0 * p.q_st;
@@ -315,9 +316,9 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
       // 1) and beta 0
       const bool live = lane < (int)min((int64_t)C, end - (start + (int64_t)(c + 1) * C));
       float gd, btl;
-      if constexpr (FUSED) {
-        gd = live ? gate_log_decay_fast(ealog, dtb, (float)s.ga) : 0.f;
-        btl = live ? sigmoid_fast((float)s.gbr) : 0.f;
+      if constexpr (FUSED) {  // an absent input: no decay, beta 1
+        gd = live && p.dmask ? gate_log_decay_fast(ealog, dtb, (float)s.ga) : 0.f;
+        btl = live ? (p.bmask ? sigmoid_fast((float)s.gbr) : 1.f) : 0.f;
       } else {
         gd = live ? s.gd : (p.decay_is_gamma ? 1.f : 0.f);
         btl = live ? s.bt : 0.f;
@@ -346,7 +347,7 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
       const int zlast = __builtin_amdgcn_readlane(z, C - 1);
       sc.F[lane] = F;
       sc.z[lane] = z;
-      sc.bt[lane] = btl;
+      sc.bt[lane] = p.rho * btl;  // beta as it enters A (the retrieval term)
       {
         // F at the first and last lane of this lane's 16-lane row (row_newbcast)
         const float Fb0 = dpp_f<0x150, 0xF>(0.f, F), Fb1 = dpp_f<0x15F, 0xF>(0.f, F);
@@ -366,7 +367,7 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
           const float gam = z < 0 ? __builtin_amdgcn_exp2f(F) : 0.f;
           const float rq = nrm ? B.rqn[lane] : 1.f, rk = nrm ? B.rkn[lane] : 1.f;
           B.bet[lane] = btl;
-          B.gb[lane] = btl * gam * rk;
+          B.gb[lane] = p.rho * btl * gam * rk;
           B.gs[lane] = p.scale * gam * rq;
           B.dc[lane] = zlast <= lane ? __builtin_amdgcn_exp2f(Flast - F) * rk : 0.f;
           if (lane == C - 1) B.gC = gam;
@@ -766,8 +767,9 @@ hipError_t launch_prefill_pair_t(PrefillParams p, hipStream_t stream) {
   p.nsplit = p.dv / 64;
   const int64_t nblk = (int64_t)p.n_seqs * p.hv * p.nsplit;
   const dim3 grid((unsigned)nblk), block(256);
-  if (p.ga && p.qk_norm) hipLaunchKernelGGL((prefill_pair_kernel<DK, true, true>), grid, block, 0, stream, p);
-  else if (p.ga) hipLaunchKernelGGL((prefill_pair_kernel<DK, true, false>), grid, block, 0, stream, p);
+  const bool fused = p.ga || p.gb;
+  if (fused && p.qk_norm) hipLaunchKernelGGL((prefill_pair_kernel<DK, true, true>), grid, block, 0, stream, p);
+  else if (fused) hipLaunchKernelGGL((prefill_pair_kernel<DK, true, false>), grid, block, 0, stream, p);
   else if (p.qk_norm) hipLaunchKernelGGL((prefill_pair_kernel<DK, false, true>), grid, block, 0, stream, p);
   else hipLaunchKernelGGL((prefill_pair_kernel<DK, false, false>), grid, block, 0, stream, p);
   return hipGetLastError();

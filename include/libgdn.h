@@ -51,6 +51,17 @@ typedef enum {
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
+/* update_rule of "com.microsoft.GatedDeltaNet" (Attributes): which terms of
+ *   S_t = exp(g_t) S_{t-1} + k_t (beta_t (v_t - exp(g_t) S_{t-1}^T k_t))^T
+ * survive.  Rules without the decay use g = 0, rules without beta use 1 in
+ * the write, and linear / gated drop the retrieval S^T k. */
+typedef enum {
+  GDN_RULE_GATED_DELTA = 0, /* decay and delta retrieval (the default)         */
+  GDN_RULE_GATED = 1,       /* decay only:     S = exp(g) S + k v^T            */
+  GDN_RULE_DELTA = 2,       /* retrieval only: S = S + k (beta (v - S^T k))^T  */
+  GDN_RULE_LINEAR = 3       /* neither:        S = S + k v^T                   */
+} gdn_update_rule;
+
 /* Meaning of the prefill decay input. */
 typedef enum {
   GDN_DECAY_LOG = 0,   /* log-space decay g, gamma = exp(g); -inf means gamma = 0 */
@@ -91,10 +102,12 @@ gdn_status gdn_gate(const float* A_log, const float* dt_bias,
  * gdn_prefill -- chunked prefill over packed or ragged requests.
  *
  * Contract of "com.microsoft.GatedDeltaNet" (Inputs, Outputs, Attributes) with
- * update_rule gated_delta, gate_activation none and beta_activation none
- * (gates come from gdn_gate or the caller, or from the fused gate fields),
- * qk_l2_norm as the qk_l2norm field says (off: keys arrive normalised, as
- * "Gated DeltaNet State Update" Constraints require):
+ * the update_rule the update_rule field names (gated_delta when zero), the
+ * gates either as given (gate_activation and beta_activation none: they come
+ * from gdn_gate or the caller) or fused (gate_activation qwen and
+ * beta_activation sigmoid, from the gate_a / gate_b fields), and qk_l2_norm
+ * as the qk_l2norm field says (off: keys arrive normalised, as "Gated DeltaNet
+ * State Update" Constraints require):
  *  - request r covers tokens [cu_seqlens[r], cu_seqlens[r+1]), both offsets
  *    clamped to [0, total_tokens]; a decreasing pair is an empty request.
  *    cu_seqlens == NULL means uniform packing, request r = [r*seq_len,
@@ -118,9 +131,18 @@ gdn_status gdn_gate(const float* A_log, const float* dt_bias,
  *                final_state may be the same buffer as initial_state (each
  *                state slice is read completely before it is written) but
  *                must not partially overlap it.
+ * Gate inputs per update_rule, as the card has them "present exactly" for the
+ * rules that use them: the decay source (decay, or gate_a with A_log and
+ * dt_bias) is required for gated_delta and gated and must be absent for delta
+ * and linear; the beta source (beta, or gate_b) is required for gated_delta
+ * and delta and must be absent for gated and linear.  Sources are either all
+ * given (decay / beta) or all fused (gate_a / gate_b); a fused decay with a
+ * given beta (or the reverse) is GDN_ERR_UNSUPPORTED: compute the given one
+ * with gdn_gate instead.
  * Requirements: pointers 16-byte aligned; head and token strides multiples of
- * 8 elements and below 2^25; io_dtype in {GDN_F32, GDN_BF16}.  total_tokens == 0 still
- * writes final_state (copies / zeros).  n_seqs == 0 is a no-op.
+ * 8 elements and below 2^25; total_tokens * hv below 2^31; io_dtype in
+ * {GDN_F32, GDN_BF16}.  total_tokens == 0 still writes final_state (copies /
+ * zeros).  n_seqs == 0 is a no-op.
  * ------------------------------------------------------------------------- */
 typedef struct {
   int32_t n_seqs;
@@ -146,15 +168,16 @@ typedef struct {
    * epsilon is 1e-12); the inputs are not modified. */
   int32_t qk_l2norm;
   float qk_l2norm_eps;     /* >= 0 and finite                                  */
-  /* Fused gate: when gate_a != NULL the gates are computed in the kernel as
-   * gdn_gate computes them -- log-decay -exp(A_log[h]) softplus(a + dt_bias[h])
-   * (threshold 20) and beta = sigmoid(b) -- and decay, beta, decay_kind are
-   * ignored (decay and beta may be NULL).  A_log, dt_bias [hv] fp32;
+  /* Fused gate: the gates are computed in the kernel as gdn_gate computes
+   * them -- log-decay -exp(A_log[h]) softplus(a + dt_bias[h]) (threshold 20)
+   * from gate_a, beta = sigmoid(b) from gate_b; decay and beta must then be
+   * NULL and decay_kind is ignored.  A_log, dt_bias [hv] fp32 (with gate_a);
    * gate_a, gate_b [total_tokens, hv] io_dtype, dense. */
   const float* A_log;
   const float* dt_bias;
   const void* gate_a;
   const void* gate_b;
+  int32_t update_rule;     /* gdn_update_rule; 0 = gated_delta                 */
 } gdn_prefill_args;
 
 gdn_status gdn_prefill(const gdn_prefill_args* args, void* stream);

@@ -95,6 +95,21 @@ PREFILL_ERRORS = [
     (dict(v_stride_token=1 << 25), 4),    # stride too large for 32-bit in-chunk offsets
     (dict(initial_state=FAKE * 7 + 1024), 4),  # partial overlap with final_state
     (dict(n_seqs=-1), 2),
+    # update_rule and the gate inputs it takes
+    (dict(update_rule=4), 3),
+    (dict(update_rule=1), 2),                          # gated takes no beta
+    (dict(update_rule=1, beta=None, decay=None), 1),   # gated needs a decay
+    (dict(update_rule=2), 2),                          # delta takes no decay
+    (dict(update_rule=2, beta=None, decay=None), 1),   # delta needs a beta
+    (dict(update_rule=3, beta=None), 2),               # linear takes no decay
+    (dict(update_rule=3, decay=None), 2),              # ... and no beta
+    (dict(gate_a=FAKE * 8, A_log=FAKE * 9, dt_bias=FAKE * 10), 2),  # decay and gate_a
+    (dict(gate_b=FAKE * 8), 2),                        # beta and gate_b
+    (dict(decay=None, gate_a=FAKE * 8, A_log=FAKE * 9, dt_bias=FAKE * 10), 5),  # fused a, given beta
+    (dict(decay=None, gate_a=FAKE * 8, A_log=None, dt_bias=FAKE * 10, beta=None,
+          gate_b=FAKE * 11), 1),                       # gate_a without A_log
+    (dict(total_tokens=1 << 27, seq_len=1 << 26, hv=16, v_stride_token=1 << 24,
+          out_stride_token=1 << 24), 2),               # total_tokens * hv >= 2^31
 ]
 
 
@@ -103,6 +118,17 @@ def test_prefill_rejects(lib, over, status):
     a = _prefill(**over)
     assert lib.gdn_prefill(ctypes.byref(a), None) == status
     assert lib.gdn_last_error()
+
+
+def test_prefill_rule_inputs_accepted_before_launch(lib):
+    """Each rule with exactly its inputs passes validation: checked with
+    tokens present (so the gate checks run) but n_seqs = 0 through
+    cu_seqlens, where a valid request returns OK without launching."""
+    base = dict(n_seqs=0, seq_len=0, total_tokens=16, cu_seqlens=FAKE * 12)
+    assert lib.gdn_prefill(ctypes.byref(_prefill(**base)), None) == 0
+    for rule, dec, bet in ((1, FAKE * 5, None), (2, None, FAKE * 6), (3, None, None)):
+        a = _prefill(update_rule=rule, decay=dec, beta=bet, **base)
+        assert lib.gdn_prefill(ctypes.byref(a), None) == 0, lib.gdn_last_error()
 
 
 def test_prefill_null_args_and_noop(lib):

@@ -248,3 +248,44 @@ def test_conv1d_rejects_bad_shapes(bad):
         kw["out"] = torch.empty(40, 32, dtype=x.dtype)
     with pytest.raises(ValueError):
         gdn.conv1d_args(x, w, st, sl, off, **kw)
+
+
+@pytest.mark.parametrize("rule,use_d,use_b", [("gated_delta", True, True), ("gated", True, False),
+                                              ("delta", False, True), ("linear", False, False)])
+@pytest.mark.parametrize("fused", [False, True])
+def test_prefill_rule_inputs(rule, use_d, use_b, fused):
+    T, hq, hv, dk, dv = 20, 2, 4, 64, 64
+    q = torch.randn(T, hq, dk).to(torch.bfloat16)
+    k = torch.randn(T, hq, dk).to(torch.bfloat16)
+    v = torch.randn(T, hv, dv).to(torch.bfloat16)
+    kw = dict(update_rule=rule)
+    dec = bet = None
+    if fused:
+        if use_d:
+            kw.update(A_log=torch.zeros(hv), dt_bias=torch.zeros(hv),
+                      a=torch.randn(T, hv).to(torch.bfloat16))
+        if use_b:
+            kw["b"] = torch.randn(T, hv).to(torch.bfloat16)
+    else:
+        dec = -torch.rand(T, hv) if use_d else None
+        bet = torch.rand(T, hv) if use_b else None
+    a, keep, out, fin = gdn.prefill_args(q, k, v, dec, bet, **kw)
+    assert a.update_rule == gdn.RULES[rule]
+    assert bool(a.decay) == (use_d and not fused) and bool(a.beta) == (use_b and not fused)
+    assert bool(a.gate_a) == (use_d and fused) and bool(a.gate_b) == (use_b and fused)
+    assert bool(a.A_log) == bool(a.gate_a) and bool(a.dt_bias) == bool(a.gate_a)
+    # the rule's missing input, or an input it does not take, is refused
+    with pytest.raises(ValueError):
+        gdn.prefill_args(q, k, v, None if use_d else -torch.rand(T, hv), bet if not fused else None,
+                         update_rule=rule)
+
+
+def test_prefill_rejects_mixed_sources_and_unknown_rule():
+    T, hv = 8, 2
+    q = torch.randn(T, 1, 16)
+    v = torch.randn(T, hv, 16)
+    with pytest.raises(ValueError):
+        gdn.prefill_args(q, q, v, None, torch.rand(T, hv), A_log=torch.zeros(hv),
+                         dt_bias=torch.zeros(hv), a=torch.randn(T, hv))
+    with pytest.raises(ValueError):
+        gdn.prefill_args(q, q, v, -torch.rand(T, hv), torch.rand(T, hv), update_rule="mamba")
