@@ -293,6 +293,24 @@ def extra_workloads(torch, gdn, synth, dev):
         "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     del t, o5
 
+    # multi-token decode batches (B64, n1) with 16 and 64 tokens per row: the
+    # decode entry point runs them in the chunked form over the pool
+    for T16 in (16, 64):
+        x = synth.decode_inputs(9, pool_size=256, batch=64, T=T16, n_hh=1, hq=16, hv=32, dk=128,
+                                dv=128, dtype="bf16", write_slots=True)
+        t = {n: x[n].to(dev) for n in ("q", "k", "v", "A_log", "dt_bias", "a", "b", "pool",
+                                       "read_idx", "write_idx")}
+        o6 = torch.zeros(x["batch"], T16, x["hv"], x["dv"], dtype=torch.bfloat16, device=dev)
+        fn = lambda: gdn.decode(t["q"], t["k"], t["v"], t["A_log"], t["dt_bias"], t["a"], t["b"],
+                                t["pool"], t["read_idx"], write_idx=t["write_idx"],
+                                scale=x["scale"], out=o6)
+        ms = _time_launches(torch, fn, flush=flush)
+        by = decode_algorithmic(x)
+        out["mtp_decode_b64_t%d_h32_d128_bf16" % T16] = {
+            "ms": ms, "tokens_per_s": x["batch"] * T16 / (ms * 1e-3), "algorithmic_bytes": by,
+            "gbs": by / (ms * 1e-3) / 1e9, "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del t, o6
+
     # causal conv1d over the QKV rows with the conv-state pool: the prefill
     # batch (B4 x S4096, 8192 channels) and one decode step (256 x 1 row)
     for name, make in (("conv1d_prefill_b4_s4096_c8192_k4_bf16", synth.conv1d_prefill_b4_s4096),

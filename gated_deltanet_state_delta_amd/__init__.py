@@ -130,12 +130,13 @@ def gate(A_log, dt_bias, a=None, b=None, *, want_gamma=False, log_decay_out=None
 def prefill_args(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None,
                  initial_state=None, scale=None, chunk_size=0, out=None, final_state=None,
                  qk_l2norm=False, qk_l2norm_eps=1e-12, A_log=None, dt_bias=None, a=None,
-                 b=None, update_rule="gated_delta"):
+                 b=None, update_rule="gated_delta", state_pool=None, read_slot=None,
+                 write_slot=None):
     """Validate shapes and build the gdn_prefill_args struct (device-agnostic).
 
     Returns (args, keep, out, final_state): `keep` holds every tensor whose
     pointer is in args (converted copies included), `out` is the caller-shaped
-    output tensor.
+    output tensor; with state_pool, final_state is the pool.
     """
     batched = q.dim() == 4
     if batched:
@@ -217,11 +218,24 @@ def prefill_args(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None,
     out3 = out.view(T, hv, dv)  # a view, never a copy: the kernel writes through it
     if out3.stride(-1) != 1 or any(s % 8 for s in out3.stride()[:-1]) or out3.data_ptr() % 16:
         raise ValueError("out must have a dense last dim, 8-aligned strides and a 16-byte base")
-    if final_state is None:
-        final_state = torch.empty((n_seqs, hv, dv, dk), dtype=torch.float32, device=dev)
-    _shape(final_state, "final_state", (n_seqs, hv, dv, dk))
-    if final_state.dtype != torch.float32 or not final_state.is_contiguous():
-        raise ValueError("final_state must be contiguous float32")
+    if state_pool is not None:
+        if initial_state is not None or final_state is not None:
+            raise ValueError("state_pool replaces initial_state and final_state")
+        if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (hv, dv, dk):
+            raise ValueError("state_pool must be [P, hv, dv, dk]")
+        if state_pool.dtype != torch.float32 or state_pool.stride(3) != 1 or \
+                state_pool.stride(2) != dk:
+            raise ValueError("state_pool must be float32 with dense [dv, dk] heads")
+        read_slot = _idx32(read_slot, "read_slot", (n_seqs,))
+        write_slot = _idx32(write_slot, "write_slot", (n_seqs,))
+    elif read_slot is not None or write_slot is not None:
+        raise ValueError("read_slot / write_slot need state_pool")
+    else:
+        if final_state is None:
+            final_state = torch.empty((n_seqs, hv, dv, dk), dtype=torch.float32, device=dev)
+        _shape(final_state, "final_state", (n_seqs, hv, dv, dk))
+        if final_state.dtype != torch.float32 or not final_state.is_contiguous():
+            raise ValueError("final_state must be contiguous float32")
     args = _lib.PrefillArgs()
     args.n_seqs, args.seq_len, args.total_tokens = n_seqs, seq_len, T
     args.hq, args.hv, args.dk, args.dv = hq, hv, dk, dv
@@ -238,7 +252,13 @@ def prefill_args(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None,
     args.beta = None if beta is None else beta.data_ptr()
     args.cu_seqlens = None if cu is None else cu.data_ptr()
     args.initial_state = None if initial_state is None else initial_state.data_ptr()
-    args.final_state = final_state.data_ptr()
+    args.final_state = None if final_state is None else final_state.data_ptr()
+    if state_pool is not None:
+        args.state_pool, args.pool_size = state_pool.data_ptr(), state_pool.shape[0]
+        args.pool_slot_stride, args.pool_head_stride = state_pool.stride(0), state_pool.stride(1)
+        args.read_slot = None if read_slot is None else read_slot.data_ptr()
+        args.write_slot = None if write_slot is None else write_slot.data_ptr()
+        final_state = state_pool
     args.qk_l2norm = 1 if qk_l2norm else 0
     args.qk_l2norm_eps = float(qk_l2norm_eps)
     if ga is not None:
@@ -247,14 +267,15 @@ def prefill_args(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None,
     if gb is not None:
         args.gate_b = gb.data_ptr()
     args.update_rule = RULES[update_rule]
-    keep = (q3, k3, v3, decay, beta, cu, initial_state, out3, final_state, A_log, dt_bias, ga, gb)
+    keep = (q3, k3, v3, decay, beta, cu, initial_state, out3, final_state, A_log, dt_bias, ga, gb,
+            read_slot, write_slot)
     return args, keep, out, final_state
 
 
 def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_state=None,
             scale=None, chunk_size=0, out=None, final_state=None, stream=None,
             qk_l2norm=False, qk_l2norm_eps=1e-12, A_log=None, dt_bias=None, a=None, b=None,
-            update_rule="gated_delta"):
+            update_rule="gated_delta", state_pool=None, read_slot=None, write_slot=None):
     """Chunked prefill.
 
     q, k: [T, hq, dk] (or [B, S, hq, dk], then uniform packing with seq_len S);
@@ -269,6 +290,10 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
     "delta", "linear"; the ONNX card's attribute) selects which terms of the
     recurrence survive; a rule takes exactly the gate inputs it uses (gated:
     decay or a only; delta: beta or b only; linear: neither).
+    state_pool [P, hv, dv, dk] float32 (updated in place) with read_slot /
+    write_slot [N]: the states come from and go to pool slots instead of
+    initial_state / final_state (read slot outside the pool: zeros; write slot
+    None: the read slot; outside the pool: not stored); returns (out, pool).
     Returns (out, final_state [N, hv, dv, dk] float32); out is [T, hv, dv] (or
     [B, S, hv, dv]) in q's dtype.
     """
@@ -276,13 +301,15 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
     for name, t in (("q", q), ("k", k), ("v", v), ("decay", decay), ("beta", beta),
                     ("cu_seqlens", cu_seqlens), ("initial_state", initial_state),
                     ("out", out), ("final_state", final_state), ("A_log", A_log),
-                    ("dt_bias", dt_bias), ("a", a), ("b", b)):
+                    ("dt_bias", dt_bias), ("a", a), ("b", b), ("state_pool", state_pool),
+                    ("read_slot", read_slot), ("write_slot", write_slot)):
         _dev(t, name)
     args, keep, out, final_state = prefill_args(
         q, k, v, decay, beta, decay_kind=decay_kind, cu_seqlens=cu_seqlens,
         initial_state=initial_state, scale=scale, chunk_size=chunk_size, out=out,
         final_state=final_state, qk_l2norm=qk_l2norm, qk_l2norm_eps=qk_l2norm_eps,
-        A_log=A_log, dt_bias=dt_bias, a=a, b=b, update_rule=update_rule)
+        A_log=A_log, dt_bias=dt_bias, a=a, b=b, update_rule=update_rule,
+        state_pool=state_pool, read_slot=read_slot, write_slot=write_slot)
     _lib.check(lib.gdn_prefill(ctypes.byref(args), _stream(stream)))
     del keep
     return out, final_state

@@ -39,6 +39,9 @@ class PrefillArgs(ctypes.Structure):
         ("qk_l2norm", _i32), ("qk_l2norm_eps", _f32),
         ("A_log", _vp), ("dt_bias", _vp), ("gate_a", _vp), ("gate_b", _vp),
         ("update_rule", _i32),
+        ("state_pool", _vp), ("pool_size", _i32),
+        ("pool_slot_stride", _i64), ("pool_head_stride", _i64),
+        ("read_slot", _vp), ("write_slot", _vp),
     ]
 
 

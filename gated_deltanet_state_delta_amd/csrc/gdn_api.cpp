@@ -105,11 +105,25 @@ gdn_status gdn_prefill(const gdn_prefill_args* p, void* stream) {
       return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill: fused and given gate inputs mixed (use gdn_gate for both)");
   }
   if (a.gate_a && (!a.A_log || !a.dt_bias)) return fail(GDN_ERR_NULL, "gdn_prefill: gate_a needs A_log and dt_bias");
+  if (a.state_pool) {
+    if (a.initial_state || a.final_state)
+      return fail(GDN_ERR_SHAPE, "gdn_prefill: state_pool replaces initial_state and final_state (pass NULL)");
+    if (a.pool_size < 0) return fail(GDN_ERR_SHAPE, "gdn_prefill: pool_size=%d", a.pool_size);
+    if (!aligned(a.state_pool, 16) || a.pool_slot_stride % 4 != 0 || a.pool_head_stride % 4 != 0 ||
+        a.pool_slot_stride < 0 || a.pool_head_stride < 0)
+      return fail(GDN_ERR_LAYOUT, "gdn_prefill: state_pool must be 16-byte aligned with strides multiple of 4 elements");
+    if (a.pool_head_stride < (int64_t)a.dv * a.dk ||
+        a.pool_slot_stride < (int64_t)(a.hv - 1) * a.pool_head_stride + (int64_t)a.dv * a.dk)
+      return fail(GDN_ERR_LAYOUT, "gdn_prefill: pool strides smaller than the dense extents");
+  } else if (a.read_slot || a.write_slot) {
+    return fail(GDN_ERR_SHAPE, "gdn_prefill: read_slot / write_slot need state_pool");
+  }
   if (a.n_seqs == 0) return GDN_OK;
-  if (!a.final_state) return fail(GDN_ERR_NULL, "gdn_prefill: final_state is NULL");
+  if (!a.final_state && !a.state_pool) return fail(GDN_ERR_NULL, "gdn_prefill: final_state is NULL");
   if (a.total_tokens > 0 && (!a.q || !a.k || !a.v || !a.out))
     return fail(GDN_ERR_NULL, "gdn_prefill: q, k, v and out are required");
-  const void* ptrs[] = {a.q, a.k, a.v, a.out, a.decay, a.beta, a.initial_state, a.final_state, a.cu_seqlens};
+  const void* ptrs[] = {a.q, a.k, a.v, a.out, a.decay, a.beta, a.initial_state, a.final_state, a.cu_seqlens,
+                        a.state_pool};
   for (const void* q : ptrs)
     if (q && !aligned(q, 16)) return fail(GDN_ERR_LAYOUT, "gdn_prefill: pointers must be 16-byte aligned");
   const int64_t strides[] = {a.q_stride_token, a.q_stride_head, a.k_stride_token, a.k_stride_head,

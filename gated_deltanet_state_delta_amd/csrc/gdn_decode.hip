@@ -230,8 +230,50 @@ static hipError_t dispatch_dk(const DecodeParams& p, int dk, int dv, hipStream_t
   return hipErrorInvalidValue;
 }
 
+// Many tokens per row, one delta step per token, no per-token scatter: the
+// chunked prefill over the pool computes the same recurrence with MFMA
+// instead of one state pass per token.  Measured on B64 x Hv32 x 128x128 bf16:
+// T = 16: 146 -> 132 us, T = 32: 256 -> 155 us, T = 64: 470 -> 181 us (the
+// token loop stays ahead below 16 tokens: 74 vs 144 us at T = 4).  The chunk
+// hint follows T (16, 32, 64).  Every activation must be 16-byte aligned,
+// as the prefill kernels require.
+static bool decode_as_prefill(const gdn_decode_args& a) {
+  if (a.T < 16 || a.n_householder != 1 || a.scatter_idx) return false;
+  if ((int64_t)a.batch * a.T * a.hv >= (int64_t(1) << 31)) return false;
+  const void* ptrs[] = {a.q, a.k, a.v, a.out};
+  for (const void* q : ptrs)
+    if ((uintptr_t)q % 16 != 0) return false;
+  return true;
+}
+
+static hipError_t launch_decode_chunked(const gdn_decode_args& a, hipStream_t stream) {
+  gdn_prefill_args pa = {};
+  pa.n_seqs = a.batch;
+  pa.seq_len = a.T;  // request r = batch row r: tokens [r*T, (r+1)*T)
+  pa.total_tokens = (int64_t)a.batch * a.T;
+  pa.hq = a.hq; pa.hv = a.hv; pa.dk = a.dk; pa.dv = a.dv;
+  pa.io_dtype = a.io_dtype;
+  pa.decay_kind = GDN_DECAY_LOG;
+  pa.chunk_size = a.T < 32 ? 16 : (a.T < 64 ? 32 : 64);
+  pa.scale = a.scale;
+  pa.q = a.q; pa.q_stride_token = (int64_t)a.hq * a.dk; pa.q_stride_head = a.dk;
+  pa.k = a.k; pa.k_stride_token = (int64_t)a.hq * a.dk; pa.k_stride_head = a.dk;  // n = 1
+  pa.v = a.v; pa.v_stride_token = (int64_t)a.hv * a.dv; pa.v_stride_head = a.dv;
+  pa.out = a.out; pa.out_stride_token = (int64_t)a.hv * a.dv; pa.out_stride_head = a.dv;
+  pa.qk_l2norm = a.qk_l2norm; pa.qk_l2norm_eps = a.qk_l2norm_eps;
+  pa.A_log = a.A_log; pa.dt_bias = a.dt_bias; pa.gate_a = a.a; pa.gate_b = a.b;
+  pa.update_rule = GDN_RULE_GATED_DELTA;
+  pa.state_pool = a.pool; pa.pool_size = a.pool_size;
+  pa.pool_slot_stride = a.pool_slot_stride; pa.pool_head_stride = a.pool_head_stride;
+  pa.read_slot = a.read_idx;
+  pa.write_slot = a.write_idx;  // NULL: the read slot, as in the token loop
+  const int flags = kPoolSkipUnread | (a.disable_state_update ? kPoolNoWrite : 0);
+  return launch_prefill(pa, stream, flags);
+}
+
 hipError_t launch_decode(const gdn_decode_args& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
+  if (decode_as_prefill(a)) return launch_decode_chunked(a, stream);
   DecodeParams p;
   p.q = a.q; p.k = a.k; p.v = a.v;
   p.A_log = a.A_log; p.dt_bias = a.dt_bias;

@@ -16,7 +16,12 @@ hipError_t launch_gate(const float* A_log, const float* dt_bias, const void* a, 
 
 hipError_t launch_decode(const gdn_decode_args& args, hipStream_t stream);
 
-hipError_t launch_prefill(const gdn_prefill_args& args, hipStream_t stream);
+// pool_flags (internal): the decode's rules when a multi-token decode runs as
+// a pooled prefill -- kPoolSkipUnread: a request whose read slot is outside
+// the pool is skipped entirely (no output, no state); kPoolNoWrite: no state
+// is stored.
+constexpr int kPoolSkipUnread = 1, kPoolNoWrite = 2;
+hipError_t launch_prefill(const gdn_prefill_args& args, hipStream_t stream, int pool_flags = 0);
 
 hipError_t launch_conv1d(const gdn_conv1d_args& args, hipStream_t stream);
 

@@ -38,8 +38,9 @@ static hipError_t gate_consts(float** out) {
   return hipSuccess;
 }
 
-hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream) {
+hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream, int pool_flags) {
   PrefillParams p;
+  p.pool_flags = pool_flags;
   p.q = a.q; p.k = a.k; p.v = a.v; p.out = a.out;
   p.q_st = a.q_stride_token; p.q_sh = a.q_stride_head;
   p.k_st = a.k_stride_token; p.k_sh = a.k_stride_head;
@@ -47,6 +48,9 @@ hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream) {
   p.o_st = a.out_stride_token; p.o_sh = a.out_stride_head;
   p.decay = a.decay; p.beta = a.beta; p.cu = a.cu_seqlens;
   p.init = a.initial_state; p.fin = a.final_state;
+  p.pool = a.state_pool; p.rslot = a.read_slot; p.wslot = a.write_slot;
+  p.pss = a.pool_slot_stride; p.phs = a.pool_head_stride; p.pool_size = a.pool_size;
+  if (a.state_pool) { p.init = a.state_pool; p.fin = a.state_pool; }
   p.T = a.total_tokens; p.n_seqs = a.n_seqs; p.seq_len = a.seq_len;
   p.hq = a.hq; p.hv = a.hv; p.dv = a.dv; p.nsplit = 1;
   p.decay_is_gamma = a.decay_kind == GDN_DECAY_GAMMA;

@@ -89,7 +89,38 @@ struct PrefillParams {
   // 0 at staging), beta 1 (or b = 0, replaced by 1).
   int64_t dmask, bmask;
   float rho;             // 1: delta retrieval kept; 0: linear / gated rules
+  // State pool: when pool != nullptr the states live in it (init and fin
+  // then point at it too) at slot * pss + head * phs; rslot / wslot pick the
+  // slots per request (see prefill_state_offsets).
+  const float* pool;
+  const int32_t* rslot;
+  const int32_t* wslot;
+  int64_t pss, phs;
+  int pool_size;
+  int pool_flags;        // kPoolSkipUnread | kPoolNoWrite (the decode's rules)
 };
+
+
+// Element offsets of the V-major state slice (request r, value head h, value
+// columns from v0) to read the initial state from and to write the final
+// state to; -1: none (zeros in, nothing out).  Dense states: [r, h] of
+// init / fin.  Pool: the read slot (none when rslot is NULL or the entry is
+// outside [0, pool_size)) and the write slot (the read slot when wslot is
+// NULL; none when outside the pool).
+__device__ __forceinline__ void prefill_state_offsets(const PrefillParams& p, int r, int h, int v0, int dk,
+                                                      int64_t& ibase, int64_t& fbase) {
+  if (p.pool) {
+    const int rs = p.rslot ? p.rslot[r] : -1;
+    const int ws = p.wslot ? p.wslot[r] : rs;
+    const int64_t head = (int64_t)h * p.phs + (int64_t)v0 * dk;
+    ibase = (rs >= 0 && rs < p.pool_size) ? (int64_t)rs * p.pss + head : -1;
+    fbase = (ws >= 0 && ws < p.pool_size && !(p.pool_flags & kPoolNoWrite)) ? (int64_t)ws * p.pss + head : -1;
+  } else {
+    const int64_t st = (((int64_t)r * p.hv + h) * p.dv + v0) * dk;
+    ibase = p.init ? st : -1;
+    fbase = st;
+  }
+}
 
 // LDS layout of one workgroup.
 template <typename E, int DK, int DVS, int C>
@@ -227,7 +258,9 @@ prefill_kernel(const PrefillParams p) {
   E* __restrict__ gout = (E*)p.out + (int64_t)h * p.o_sh + v0;
   const float* __restrict__ gdec = p.decay + (h & p.dmask);
   const float* __restrict__ gbet = p.beta + (h & p.bmask);
-  const int64_t st_base = (((int64_t)r * p.hv + h) * p.dv + v0) * DK;
+  int64_t ibase, fbase;
+  prefill_state_offsets(p, r, h, v0, DK, ibase, fbase);
+  if ((p.pool_flags & kPoolSkipUnread) && ibase < 0) return;  // uniform over the workgroup
 
   // M is only written on and below the diagonal; the readout reads the 16x16
   // blocks just above the diagonal as zeros, so clear M once.
@@ -273,10 +306,10 @@ prefill_kernel(const PrefillParams p) {
       }
     };
     if (active) {
-      if (p.init) {
+      if (ibase >= 0) {
 #pragma unroll
         for (int j = 0; j < NKT; ++j)
-          S[j] = *reinterpret_cast<const f4*>(p.init + st_base + (int64_t)vc * DK + dk_of<NKT>(j, 4 * g));
+          S[j] = *reinterpret_cast<const f4*>(p.init + ibase + (int64_t)vc * DK + dk_of<NKT>(j, 4 * g));
       }
       if (nch > 0) load_v(0);
     }
@@ -442,10 +475,10 @@ prefill_kernel(const PrefillParams p) {
       }
       lds_barrier();
     }
-    if (active) {
+    if (active && fbase >= 0) {
 #pragma unroll
       for (int j = 0; j < NKT; ++j)
-        *reinterpret_cast<f4*>(p.fin + st_base + (int64_t)vc * DK + dk_of<NKT>(j, 4 * g)) = S[j];
+        *reinterpret_cast<f4*>(p.fin + fbase + (int64_t)vc * DK + dk_of<NKT>(j, 4 * g)) = S[j];
     }
     return;
   }

@@ -550,7 +550,9 @@ prefill_pair_kernel(const PrefillParams p) {
   const __bf16* __restrict__ gk = (const __bf16*)p.k + (int64_t)qh * p.k_sh;
   const __bf16* __restrict__ gv = (const __bf16*)p.v + (int64_t)h * p.v_sh + v0;
   __bf16* __restrict__ gout = (__bf16*)p.out + (int64_t)h * p.o_sh + v0;
-  const int64_t st_base = (((int64_t)r * p.hv + h) * p.dv + v0) * DK;
+  int64_t ibase, fbase;
+  prefill_state_offsets(p, r, h, v0, DK, ibase, fbase);
+  if ((p.pool_flags & kPoolSkipUnread) && ibase < 0) return;  // uniform over the workgroup
 
   // The readout pairs each diagonal block of M with the block to its right,
   // which the prep waves never write: clear those two blocks once.
@@ -577,12 +579,12 @@ prefill_pair_kernel(const PrefillParams p) {
   f4 S[NKT][2];
 #pragma unroll
   for (int j = 0; j < NKT; ++j) S[j][0] = S[j][1] = f4{0.f, 0.f, 0.f, 0.f};
-  if (p.init) {
+  if (ibase >= 0) {
 #pragma unroll
     for (int j = 0; j < NKT; ++j)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
-        S[j][ct] = *reinterpret_cast<const f4*>(p.init + st_base + (int64_t)(32 * w + 16 * ct + x) * DK +
+        S[j][ct] = *reinterpret_cast<const f4*>(p.init + ibase + (int64_t)(32 * w + 16 * ct + x) * DK +
                                                 dk_of<NKT>(j, 4 * g));
   }
   const int ost = (int)p.o_st;
@@ -749,12 +751,14 @@ prefill_pair_kernel(const PrefillParams p) {
     }
     lds_barrier();
   }
+  if (fbase >= 0) {
 #pragma unroll
-  for (int j = 0; j < NKT; ++j)
+    for (int j = 0; j < NKT; ++j)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-      *reinterpret_cast<f4*>(p.fin + st_base + (int64_t)(32 * w + 16 * ct + x) * DK + dk_of<NKT>(j, 4 * g)) =
-          S[j][ct];
+      for (int ct = 0; ct < 2; ++ct)
+        *reinterpret_cast<f4*>(p.fin + fbase + (int64_t)(32 * w + 16 * ct + x) * DK + dk_of<NKT>(j, 4 * g)) =
+            S[j][ct];
+  }
 }
 
 // Whether the pair kernel covers a bf16 problem of this shape and chunk hint.

@@ -178,6 +178,23 @@ typedef struct {
   const void* gate_a;
   const void* gate_b;
   int32_t update_rule;     /* gdn_update_rule; 0 = gated_delta                 */
+  /* State pool (optional; appended).  With state_pool != NULL the states live
+   * in a slot-indexed pool laid out as gdn_decode's pool (slot s, head h at
+   * state_pool + s*pool_slot_stride + h*pool_head_stride, a dense [dv][dk]
+   * fp32 block), and initial_state and final_state must be NULL.  Request r
+   * starts from slot read_slot[r] (zeros when read_slot is NULL or the entry
+   * is < 0 or >= pool_size) and its final state is stored to slot
+   * write_slot[r] (read_slot[r] when write_slot is NULL; nothing when the
+   * entry is < 0 or >= pool_size).  A request may read and write one slot; a
+   * slot that one request writes and another reads or writes is undefined
+   * behaviour.  Same alignment and stride rules as gdn_decode's pool.  With
+   * the fused gate and one request per batch row this is a multi-token
+   * (chunked) decode over the decode's pool. */
+  float* state_pool;
+  int32_t pool_size;
+  int64_t pool_slot_stride, pool_head_stride;
+  const int32_t* read_slot;  /* [n_seqs] or NULL                             */
+  const int32_t* write_slot; /* [n_seqs] or NULL                             */
 } gdn_prefill_args;
 
 gdn_status gdn_prefill(const gdn_prefill_args* args, void* stream);
@@ -219,6 +236,10 @@ gdn_status gdn_prefill(const gdn_prefill_args* args, void* stream);
  * Requirements: pool pointer 16-byte aligned and both pool strides multiples
  * of 4 elements; q, k, v, out 8-byte aligned; 1 <= T <= 64;
  * 1 <= n_householder <= 4; batch == 0 is a no-op.
+ * With T >= 16, n_householder == 1, no scatter_idx and q, k, v, out 16-byte
+ * aligned, the call runs the chunked form of the same recurrence (the
+ * prefill kernels over the pool, one request per row): same results up to
+ * rounding order, same skip / write / disable rules.
  * ------------------------------------------------------------------------- */
 typedef struct {
   int32_t batch, T, n_householder;

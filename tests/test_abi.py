@@ -110,6 +110,21 @@ PREFILL_ERRORS = [
           gate_b=FAKE * 11), 1),                       # gate_a without A_log
     (dict(total_tokens=1 << 27, seq_len=1 << 26, hv=16, v_stride_token=1 << 24,
           out_stride_token=1 << 24), 2),               # total_tokens * hv >= 2^31
+    # state pool
+    (dict(final_state=None, state_pool=FAKE * 13, pool_size=10, pool_slot_stride=4 * 64 * 64, pool_head_stride=64 * 64, initial_state=FAKE * 14), 2),            # pool and initial_state
+    (dict(state_pool=FAKE * 13, pool_size=10, pool_slot_stride=4 * 64 * 64,
+          pool_head_stride=64 * 64), 2),                # pool and final_state
+    (dict(final_state=None, state_pool=FAKE * 13, pool_size=-1, pool_slot_stride=4 * 64 * 64,
+          pool_head_stride=64 * 64), 2),
+    (dict(final_state=None, state_pool=FAKE * 13 + 8, pool_size=10, pool_slot_stride=4 * 64 * 64,
+          pool_head_stride=64 * 64), 4),                # misaligned pool
+    (dict(final_state=None, state_pool=FAKE * 13, pool_size=10, pool_slot_stride=4 * 64 * 64,
+          pool_head_stride=64 * 64 - 4), 4),            # heads overlap
+    (dict(final_state=None, state_pool=FAKE * 13, pool_size=10, pool_slot_stride=3 * 64 * 64,
+          pool_head_stride=64 * 64), 4),                # slots overlap
+    (dict(final_state=None, state_pool=FAKE * 13, pool_size=10, pool_slot_stride=4 * 64 * 64 + 2,
+          pool_head_stride=64 * 64), 4),                # stride not a multiple of 4
+    (dict(read_slot=FAKE * 15), 2),                     # slots without a pool
 ]
 
 
@@ -129,6 +144,13 @@ def test_prefill_rule_inputs_accepted_before_launch(lib):
     for rule, dec, bet in ((1, FAKE * 5, None), (2, None, FAKE * 6), (3, None, None)):
         a = _prefill(update_rule=rule, decay=dec, beta=bet, **base)
         assert lib.gdn_prefill(ctypes.byref(a), None) == 0, lib.gdn_last_error()
+
+
+def test_prefill_pool_mode_accepted_before_launch(lib):
+    a = _prefill(n_seqs=0, seq_len=0, total_tokens=16, cu_seqlens=FAKE * 12, final_state=None,
+                 state_pool=FAKE * 13, pool_size=10, pool_slot_stride=4 * 64 * 64 + 64,
+                 pool_head_stride=64 * 64 + 16, read_slot=FAKE * 15, write_slot=FAKE * 16)
+    assert lib.gdn_prefill(ctypes.byref(a), None) == 0, lib.gdn_last_error()
 
 
 def test_prefill_null_args_and_noop(lib):

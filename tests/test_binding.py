@@ -23,7 +23,7 @@ def _span_ok(ptr, max_elem, t):
 
 
 def _check_prefill(a, keep, T):
-    q3, k3, v3, decay, beta, cu, init, out3, fin, A_log, dt_bias, ga, gb = keep
+    q3, k3, v3, decay, beta, cu, init, out3, fin, A_log, dt_bias, ga, gb = keep[:13]
     last_q = (T - 1) * a.q_stride_token + (a.hq - 1) * a.q_stride_head + a.dk - 1
     last_k = (T - 1) * a.k_stride_token + (a.hq - 1) * a.k_stride_head + a.dk - 1
     last_v = (T - 1) * a.v_stride_token + (a.hv - 1) * a.v_stride_head + a.dv - 1
