@@ -11,6 +11,7 @@ because the kernels trust the sizes and strides they are given.
   prefill(q, k, v, decay, beta, ...)    -> (out, final_state)
   decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, ...) -> (out, pool)
   conv1d(x, weight, conv_state, slot_idx, row_offsets, ...) -> out
+  state_update(q, k, v, gamma, beta) -> {"outputs", "final_state"}
 """
 from __future__ import annotations
 
@@ -22,7 +23,7 @@ import torch
 from . import _lib
 from ._lib import GdnError
 
-__all__ = ["gate", "prefill", "decode", "conv1d", "version", "GdnError",
+__all__ = ["gate", "prefill", "decode", "conv1d", "state_update", "version", "GdnError",
            "prefill_args", "decode_args", "conv1d_args"]
 
 _DT = {torch.float32: _lib.GDN_F32, torch.bfloat16: _lib.GDN_BF16}
@@ -313,6 +314,50 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
     _lib.check(lib.gdn_prefill(ctypes.byref(args), _stream(stream)))
     del keep
     return out, final_state
+
+
+_HEAD_SIZES = (16, 32, 64, 128)
+
+
+def _pad_last(t, n):
+    """t with its last dimension zero-padded to n (t itself when already n)."""
+    if t.shape[-1] == n:
+        return t
+    out = torch.zeros(*t.shape[:-1], n, dtype=t.dtype, device=t.device)
+    out[..., :t.shape[-1]] = t
+    return out
+
+
+def state_update(q, k, v, gamma, beta):
+    """The interface of "Gated DeltaNet State Update" (statement, Constraints):
+    q, k [B, S, Dk], v [B, S, Dv] (float32 or bfloat16), gamma, beta [B, S]
+    float32; every batch item starts from a zero state; y_t = q_t^T S_t (no
+    scale).  Returns {"outputs": [B, S, Dv], "final_state": [B, Dk, Dv]} in
+    q's dtype and device.
+
+    The call is one gdn_prefill launch with one head (decay given as gamma,
+    scale 1); its V-major final state is returned transposed, as the
+    statement's (B, Dk, Dv).  Head sizes the kernels do not take (any other
+    than 16, 32, 64, 128, up to 128) are zero-padded to the next one: a zero
+    key or query component adds nothing to any dot product and zero value
+    columns stay zero, so slicing the padding off gives the unpadded result.
+    """
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("q, k must be [B, S, Dk] and v [B, S, Dv]")
+    B, S, dk = q.shape
+    dv = v.shape[2]
+    _shape(gamma, "gamma", (B, S))
+    _shape(beta, "beta", (B, S))
+    pk = next((n for n in _HEAD_SIZES if n >= dk), None)
+    pv = next((n for n in _HEAD_SIZES if n >= dv), None)
+    if pk is None or pv is None:
+        raise ValueError("Dk and Dv up to 128 are supported (got %d, %d)" % (dk, dv))
+    q4, k4 = _pad_last(q, pk).unsqueeze(2), _pad_last(k, pk).unsqueeze(2)
+    v4 = _pad_last(v, pv).unsqueeze(2)
+    out, fin = prefill(q4, k4, v4, gamma.unsqueeze(-1), beta.unsqueeze(-1), decay_kind="gamma",
+                       scale=1.0)
+    return {"outputs": out[:, :, 0, :dv],
+            "final_state": fin[:, 0, :dv, :dk].transpose(1, 2).to(q.dtype)}
 
 
 def decode_args(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None,

@@ -20,7 +20,8 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_
                 4: "GDN_ERR_LAYOUT", 5: "GDN_ERR_UNSUPPORTED", 6: "GDN_ERR_HIP"}
 
 # every extern "C" symbol include/libgdn.h declares
-EXPORTED = ("gdn_last_error", "gdn_version", "gdn_gate", "gdn_prefill", "gdn_decode", "gdn_conv1d")
+EXPORTED = ("gdn_last_error", "gdn_version", "gdn_gate", "gdn_prefill", "gdn_prefill_workspace_size",
+            "gdn_decode", "gdn_conv1d")
 
 _i32, _i64, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 
@@ -42,6 +43,7 @@ class PrefillArgs(ctypes.Structure):
         ("state_pool", _vp), ("pool_size", _i32),
         ("pool_slot_stride", _i64), ("pool_head_stride", _i64),
         ("read_slot", _vp), ("write_slot", _vp),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -92,6 +94,8 @@ def load(path: str | None = None):
         lib.gdn_version.argtypes = []
         lib.gdn_gate.restype = ctypes.c_int
         lib.gdn_gate.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _vp, _vp, _vp, _vp]
+        lib.gdn_prefill_workspace_size.restype = ctypes.c_size_t
+        lib.gdn_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillArgs)]
         lib.gdn_prefill.restype = ctypes.c_int
         lib.gdn_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
         lib.gdn_decode.restype = ctypes.c_int

@@ -62,6 +62,8 @@ gdn_status gdn_gate(const float* A_log, const float* dt_bias, const void* a, con
                   "gdn_gate launch");
 }
 
+size_t gdn_prefill_workspace_size(const gdn_prefill_args* /*args*/) { return 0; }
+
 gdn_status gdn_prefill(const gdn_prefill_args* p, void* stream) {
   g_err[0] = 0;
   if (!p) return fail(GDN_ERR_NULL, "gdn_prefill: args is NULL");

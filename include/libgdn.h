@@ -195,7 +195,15 @@ typedef struct {
   int64_t pool_slot_stride, pool_head_stride;
   const int32_t* read_slot;  /* [n_seqs] or NULL                             */
   const int32_t* write_slot; /* [n_seqs] or NULL                             */
+  /* Caller-provided scratch (appended).  No prefill kernel uses scratch
+   * memory: gdn_prefill_workspace_size() returns 0 and these are ignored. */
+  void* workspace;
+  size_t workspace_bytes;
 } gdn_prefill_args;
+
+/* Device scratch bytes a gdn_prefill call with these arguments needs: always
+ * 0 (every intermediate lives in registers and LDS).  args may be NULL. */
+size_t gdn_prefill_workspace_size(const gdn_prefill_args* args);
 
 gdn_status gdn_prefill(const gdn_prefill_args* args, void* stream);
 

@@ -153,6 +153,11 @@ def test_prefill_pool_mode_accepted_before_launch(lib):
     assert lib.gdn_prefill(ctypes.byref(a), None) == 0, lib.gdn_last_error()
 
 
+def test_prefill_needs_no_workspace(lib):
+    assert lib.gdn_prefill_workspace_size(None) == 0
+    assert lib.gdn_prefill_workspace_size(ctypes.byref(_prefill())) == 0
+
+
 def test_prefill_null_args_and_noop(lib):
     assert lib.gdn_prefill(None, None) == 1
     a = _prefill(n_seqs=0, seq_len=0, total_tokens=0)

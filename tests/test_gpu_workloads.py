@@ -7,7 +7,9 @@ independent, so a sampled unit's oracle result is exact for that unit.
 Bitwise properties (skipped rows, untouched pool slots, empty requests) are
 checked over the whole output.
 """
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -172,3 +174,55 @@ def test_mtp_decode_b64_t4_n2_bf16():
     untouched = torch.ones(512, dtype=torch.bool)
     untouched[sc] = False
     assert torch.equal(pool_after[untouched], x["pool"][untouched])
+
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("idx", [0, 1, 2])
+def test_worked_examples_through_the_kernel(idx, dtype):
+    """The three worked examples of "Gated DeltaNet State Update" (Examples),
+    through gdn.state_update (one prefill launch, head sizes zero-padded to
+    16): the printed outputs and (B, Dk, Dv) final states.  Every printed
+    value is a small integer, exact in bf16 as well."""
+    import gated_deltanet_state_delta_amd as gdn
+    ex = json.load(open(GOLDEN))["examples"][idx]
+    t = {n: torch.tensor(ex[n], dtype=torch.float32, device="cuda")
+         for n in ("q", "k", "v", "gamma", "beta")}
+    res = gdn.state_update(t["q"].to(dtype), t["k"].to(dtype), t["v"].to(dtype), t["gamma"],
+                           t["beta"])
+    torch.cuda.synchronize()
+    assert res["outputs"].dtype == dtype and res["final_state"].dtype == dtype
+    want_o = torch.tensor(ex["outputs"], dtype=torch.float64)
+    want_f = torch.tensor(ex["final_state"], dtype=torch.float64)
+    assert tuple(res["outputs"].shape) == tuple(want_o.shape)
+    assert tuple(res["final_state"].shape) == tuple(want_f.shape)
+    np.testing.assert_allclose(res["outputs"].double().cpu().numpy(), want_o.numpy(), atol=1e-5)
+    np.testing.assert_allclose(res["final_state"].double().cpu().numpy(), want_f.numpy(), atol=1e-5)
+
+
+@pytest.mark.parametrize("dk,dv", [(5, 3), (16, 16), (40, 100)])
+def test_state_update_interface_against_the_oracle(dk, dv):
+    """Random (B, S, D) inputs of the problem statement's interface, odd head
+    sizes included (zero-padded), against the oracle; inputs unmodified."""
+    import gated_deltanet_state_delta_amd as gdn
+    g = torch.Generator().manual_seed(700 + dk + dv)
+    B, S = 3, 77
+    q = torch.randn(B, S, dk, generator=g)
+    k = torch.randn(B, S, dk, generator=g)
+    k = k / k.norm(dim=-1, keepdim=True)
+    v = torch.randn(B, S, dv, generator=g)
+    gam = torch.rand(B, S, generator=g) * 0.2 + 0.8
+    bet = torch.rand(B, S, generator=g)
+    args = [t.cuda() for t in (q, k, v, gam, bet)]
+    copies = [t.clone() for t in args]
+    res = gdn.state_update(*args)
+    torch.cuda.synchronize()
+    for a, c in zip(args, copies):
+        assert torch.equal(a, c), "inputs must not be modified"
+    ro, rf = oracle.prefill(q.reshape(B * S, 1, dk), k.reshape(B * S, 1, dk),
+                            v.reshape(B * S, 1, dv), gam.reshape(B * S, 1), bet.reshape(B * S, 1),
+                            decay_is_gamma=True, n_seqs=B, seq_len=S, scale=1.0)
+    assert_close(res["outputs"], ro.reshape(B, S, dv), "f32", "outputs")
+    assert_close(res["final_state"], rf[:, 0].transpose(0, 2, 1), "f32", "final (B,Dk,Dv)")
