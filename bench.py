@@ -54,15 +54,18 @@ FP32_MATRIX_PEAK_TFLOPS = 157.3  # MI355X fp32 matrix, TFLOP/s
 
 METRIC = "GDN prefill tokens/s (B4×S4096,Hv32,d128) + decode state HBM GB/s % of peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_b4s4096_decode_b256_conv1d_b4s4096.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_prefill_b4s4096.json")
 CALIB_BYTES = 2 * (1 << 30)   # the calibration copy reads 1 GiB and writes 1 GiB
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the HIP/C++ sources of libgdn (any change invalidates traffic)."""
+    """sha256 over the kernel sources of libgdn (.hip, .hpp; the host-only
+    argument validation in .cpp does not change a kernel).  Any change
+    invalidates the stored counter figures."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_deltanet_state_delta_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".cpp")):
+        if f.endswith((".hip", ".hpp")):
             h.update(f.encode())
             h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
@@ -123,6 +126,27 @@ def summarize_traffic(fetch_csv, write_csv):
         res["kernels"]["conv1d"] = {n: sum(p[n] for p in parts)
                                     for n in ("read_bytes", "write_bytes", "bytes")}
     return res
+
+
+def summarize_mfma(csv_path):
+    """MfmaUtil (% of SIMD cycles the MFMA unit is busy) and MfmaFlopsBF16 of
+    the prefill kernel, averaged over its dispatches."""
+    vals = {}
+    for r in csv.DictReader(open(csv_path)):
+        if _kernel_key(r["Kernel_Name"]) == "prefill":
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {"source_hash": kernel_source_hash(), "kernel": "prefill_pair_kernel<128,false,false>",
+            "dispatches": len(vals.get("MfmaUtil", [])),
+            "mfma_util_pct": statistics.mean(vals["MfmaUtil"]),
+            "mfma_flops_bf16": statistics.mean(vals["MfmaFlopsBF16"])}
+
+
+def load_mfma():
+    try:
+        m = json.load(open(MFMA_FILE))
+    except (OSError, ValueError):
+        return None
+    return m if m.get("source_hash") == kernel_source_hash() else None
 
 
 def load_traffic(kernel):
@@ -341,11 +365,15 @@ def main():
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-mfma", metavar="MFMA_CSV")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the single-head, ragged-fp32 and multi-token-decode timings")
     args = ap.parse_args()
     if args.summarize_traffic:
         print(json.dumps(summarize_traffic(*args.summarize_traffic), indent=1))
+        return
+    if args.summarize_mfma:
+        print(json.dumps(summarize_mfma(args.summarize_mfma), indent=1))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -475,6 +503,11 @@ def main():
                            "algorithmic_bytes": pb, "algorithmic_flops": pf,
                            "mfma_tflops": tfl, "mfma_peak_tflops": BF16_PEAK_TFLOPS,
                            "mfma_frac": tfl / BF16_PEAK_TFLOPS, "avg_ms": pm}
+        mf = load_mfma()
+        # counter view of the same kernel (rocprofv3 MfmaUtil / MfmaFlopsBF16), or
+        # null once the kernels have changed since it was taken
+        res["roofline"]["mfma_util_counter_pct"] = None if mf is None else mf["mfma_util_pct"]
+        res["roofline"]["mfma_flops_executed"] = None if mf is None else mf["mfma_flops_bf16"]
         res["prefill"] = {"gate_ms": statistics.median(gate_ms), "prefill_ms": pm,
                           "prefill_ms_min": min(pre_ms), "tokens_per_s": res["value"]}
     if do_decode:
@@ -510,6 +543,11 @@ def main():
         del pool, flush
         torch.cuda.empty_cache()
         res["extra"] = extra_workloads(torch, gdn, synth, dev)
+        # rates against the measured plain-copy bandwidth of this machine
+        copy_gbs = res["extra"]["copy_1gib"]["gbs"]
+        for part in ("roofline", "decode", "conv1d"):
+            if part in res and res[part].get("unit") == "GB/s":
+                res[part]["frac_of_measured_copy"] = res[part]["achieved"] / copy_gbs
 
     if not args.no_cpu_baseline and do_prefill:
         res["cpu_baseline"] = cpu_baseline_prefill(px)
