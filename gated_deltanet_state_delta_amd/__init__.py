@@ -287,7 +287,9 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
     x / sqrt(sum x^2 + qk_l2norm_eps) (the ONNX card's qk_l2_norm).  a, b
     ([T, hv] or [B, S, hv] in q's dtype): the fused gate, computed in the
     kernel -- the qwen decay from a with A_log, dt_bias [hv], beta = sigmoid(b)
-    (pass decay and beta as None then).  update_rule ("gated_delta", "gated",
+    (pass decay and beta as None then).  Head sizes other than 16, 32, 64, 128
+    (up to 128) run zero-padded to the next kernel size, with dense states
+    only; the results are exact.  update_rule ("gated_delta", "gated",
     "delta", "linear"; the ONNX card's attribute) selects which terms of the
     recurrence survive; a rule takes exactly the gate inputs it uses (gated:
     decay or a only; delta: beta or b only; linear: neither).
@@ -305,6 +307,15 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
                     ("dt_bias", dt_bias), ("a", a), ("b", b), ("state_pool", state_pool),
                     ("read_slot", read_slot), ("write_slot", write_slot)):
         _dev(t, name)
+    dk, dv = q.shape[-1], v.shape[-1]
+    pk, pv = _head_pad(dk), _head_pad(dv)
+    if (pk, pv) != (dk, dv):
+        return _prefill_padded(q, k, v, decay, beta, pk, pv, decay_kind=decay_kind,
+                               cu_seqlens=cu_seqlens, initial_state=initial_state, scale=scale,
+                               chunk_size=chunk_size, out=out, final_state=final_state,
+                               stream=stream, qk_l2norm=qk_l2norm, qk_l2norm_eps=qk_l2norm_eps,
+                               A_log=A_log, dt_bias=dt_bias, a=a, b=b, update_rule=update_rule,
+                               state_pool=state_pool)
     args, keep, out, final_state = prefill_args(
         q, k, v, decay, beta, decay_kind=decay_kind, cu_seqlens=cu_seqlens,
         initial_state=initial_state, scale=scale, chunk_size=chunk_size, out=out,
@@ -319,6 +330,12 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
 _HEAD_SIZES = (16, 32, 64, 128)
 
 
+def _head_pad(d):
+    """The kernel head size a head of size d runs at: the next of 16, 32, 64,
+    128 (d itself when it is one; d above 128 is refused by the C ABI)."""
+    return next((n for n in _HEAD_SIZES if n >= d), d)
+
+
 def _pad_last(t, n):
     """t with its last dimension zero-padded to n (t itself when already n)."""
     if t.shape[-1] == n:
@@ -326,6 +343,40 @@ def _pad_last(t, n):
     out = torch.zeros(*t.shape[:-1], n, dtype=t.dtype, device=t.device)
     out[..., :t.shape[-1]] = t
     return out
+
+
+def _prefill_padded(q, k, v, decay, beta, pk, pv, *, out, final_state, initial_state,
+                    state_pool, **kw):
+    """prefill for head sizes the kernels do not take (the ONNX card's head
+    sizes are free, e.g. its JS example's 12 and 9): q, k and v are
+    zero-padded to the kernel sizes pk, pv, the initial state likewise, and
+    the results are sliced back.  This is exact: a zero key or query
+    component adds nothing to any dot product, and a value row that starts at
+    zero with zero values stays zero."""
+    if state_pool is not None:
+        raise ValueError("head sizes other than 16, 32, 64, 128 need dense states "
+                         "(a pool slot cannot be padded in place)")
+    dk, dv = q.shape[-1], v.shape[-1]
+    if kw.get("scale") is None:
+        kw["scale"] = 1.0 / math.sqrt(dk)  # the caller's head size, not the padded one
+    init = None
+    if initial_state is not None:
+        init = torch.zeros(*initial_state.shape[:-2], pv, pk, dtype=torch.float32,
+                           device=initial_state.device)
+        init[..., :dv, :dk] = initial_state
+    o_p, f_p = prefill(_pad_last(q, pk), _pad_last(k, pk), _pad_last(v, pv), decay, beta,
+                       initial_state=init, **kw)
+    o = o_p[..., :dv]
+    f = f_p[..., :dv, :dk]
+    if out is not None:
+        out.copy_(o)
+    else:
+        out = o.contiguous()
+    if final_state is not None:
+        final_state.copy_(f)
+    else:
+        final_state = f.contiguous()
+    return out, final_state
 
 
 def state_update(q, k, v, gamma, beta):
@@ -336,11 +387,9 @@ def state_update(q, k, v, gamma, beta):
     q's dtype and device.
 
     The call is one gdn_prefill launch with one head (decay given as gamma,
-    scale 1); its V-major final state is returned transposed, as the
-    statement's (B, Dk, Dv).  Head sizes the kernels do not take (any other
-    than 16, 32, 64, 128, up to 128) are zero-padded to the next one: a zero
-    key or query component adds nothing to any dot product and zero value
-    columns stay zero, so slicing the padding off gives the unpadded result.
+    scale 1; head sizes the kernels do not take are zero-padded by prefill);
+    its V-major final state is returned transposed, as the statement's
+    (B, Dk, Dv).
     """
     if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
         raise ValueError("q, k must be [B, S, Dk] and v [B, S, Dv]")
@@ -348,16 +397,11 @@ def state_update(q, k, v, gamma, beta):
     dv = v.shape[2]
     _shape(gamma, "gamma", (B, S))
     _shape(beta, "beta", (B, S))
-    pk = next((n for n in _HEAD_SIZES if n >= dk), None)
-    pv = next((n for n in _HEAD_SIZES if n >= dv), None)
-    if pk is None or pv is None:
+    if dk > 128 or dv > 128:
         raise ValueError("Dk and Dv up to 128 are supported (got %d, %d)" % (dk, dv))
-    q4, k4 = _pad_last(q, pk).unsqueeze(2), _pad_last(k, pk).unsqueeze(2)
-    v4 = _pad_last(v, pv).unsqueeze(2)
-    out, fin = prefill(q4, k4, v4, gamma.unsqueeze(-1), beta.unsqueeze(-1), decay_kind="gamma",
-                       scale=1.0)
-    return {"outputs": out[:, :, 0, :dv],
-            "final_state": fin[:, 0, :dv, :dk].transpose(1, 2).to(q.dtype)}
+    out, fin = prefill(q.unsqueeze(2), k.unsqueeze(2), v.unsqueeze(2), gamma.unsqueeze(-1),
+                       beta.unsqueeze(-1), decay_kind="gamma", scale=1.0)
+    return {"outputs": out[:, :, 0], "final_state": fin[:, 0].transpose(1, 2).to(q.dtype)}
 
 
 def decode_args(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None,

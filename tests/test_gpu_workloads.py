@@ -226,3 +226,28 @@ def test_state_update_interface_against_the_oracle(dk, dv):
                             decay_is_gamma=True, n_seqs=B, seq_len=S, scale=1.0)
     assert_close(res["outputs"], ro.reshape(B, S, dv), "f32", "outputs")
     assert_close(res["final_state"], rf[:, 0].transpose(0, 2, 1), "f32", "final (B,Dk,Dv)")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_onnx_js_example_shapes(dtype):
+    """The shapes of the ONNX card's JS usage example ("Use with
+    @huggingface/kernels": 4 tokens, one query head of 12, two value heads
+    of 9, an initial state [1, 2, 9, 12]; the page gives no values): seeded
+    values, head sizes zero-padded in the binding, against the oracle."""
+    import gated_deltanet_state_delta_amd as gdn
+    g = torch.Generator().manual_seed(710)
+    dt = synth.DTYPES[dtype]
+    q = torch.randn(4, 1, 12, generator=g).to(dt)
+    k = torch.nn.functional.normalize(torch.randn(4, 1, 12, generator=g), dim=-1).to(dt)
+    v = torch.randn(4, 2, 9, generator=g).to(dt)
+    decay = -torch.rand(4, 2, generator=g)
+    beta = torch.rand(4, 2, generator=g)
+    init = torch.randn(1, 2, 9, 12, generator=g) * 0.1
+    o, f = gdn.prefill(q.cuda(), k.cuda(), v.cuda(), decay.cuda(), beta.cuda(),
+                       initial_state=init.cuda())
+    torch.cuda.synchronize()
+    assert tuple(o.shape) == (4, 2, 9) and tuple(f.shape) == (1, 2, 9, 12)
+    ro, rf = oracle.prefill(q, k, v, decay, beta, initial_state=init, n_seqs=1, seq_len=4,
+                            scale=1.0 / math.sqrt(12))
+    assert_close(o, ro, dtype, "outputs")
+    assert_close(f, rf, dtype, "final state")
