@@ -64,14 +64,15 @@ def _load():
                 ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                 _dp, _dp, _dp, _dp, ctypes.c_int32, _dp, _ip, _dp, ctypes.c_double,
-                _dp, _dp, ctypes.c_int32, ctypes.c_double, _dp, _dp, _dp, _dp, ctypes.c_int32]
+                _dp, _dp, ctypes.c_int32, ctypes.c_double, _dp, _dp, _dp, _dp, ctypes.c_int32,
+                ctypes.c_int32]
             lib.gdno_decode.restype = ctypes.c_int
             lib.gdno_decode.argtypes = [
                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                 ctypes.c_int32, ctypes.c_int32,
                 _dp, _dp, _dp, _dp, _dp, _dp, _dp,
                 _dp, ctypes.c_int32, _ip, _ip, _ip, ctypes.c_int32, ctypes.c_double,
-                _dp, ctypes.c_int32, ctypes.c_double]
+                _dp, ctypes.c_int32, ctypes.c_double, _dp]
             lib.gdno_conv1d.restype = ctypes.c_int
             lib.gdno_conv1d.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, _dp, _dp, _dp, ctypes.c_int64, _ip,
@@ -145,7 +146,7 @@ RULES = {"gated_delta": 0, "gated": 1, "delta": 2, "linear": 3}
 def prefill(q, k, v, decay, beta, *, decay_is_gamma=False, cu_seqlens=None,
             n_seqs=None, seq_len=None, initial_state=None, scale=1.0,
             out_init=None, nthreads=None, qk_l2norm_eps=None, A_log=None, dt_bias=None,
-            a=None, b=None, update_rule="gated_delta"):
+            a=None, b=None, update_rule="gated_delta", decay_per_key=False):
     """Sequential fp64 prefill.
 
     q, k: [T, hq, dk]; v: [T, hv, dv]; decay, beta: [T, hv];
@@ -156,7 +157,8 @@ def prefill(q, k, v, decay, beta, *, decay_is_gamma=False, cu_seqlens=None,
     fused qwen decay (decay is then ignored); b [T, hv]: beta = sigmoid(b)
     (beta is then ignored).  update_rule: "gated_delta", "gated", "delta" or
     "linear" (the ONNX card's update_rule); rules without the decay ignore
-    decay / a, rules without beta ignore beta / b.
+    decay / a, rules without beta ignore beta / b.  decay_per_key: decay is
+    [T, hv, dk], one decay per key dimension (given, not fused).
     Returns (out [T, hv, dv], final_state [N, hv, dv, dk]) as float64 arrays.
     out rows no request covers hold out_init (default NaN).
     """
@@ -186,7 +188,8 @@ def prefill(q, k, v, decay, beta, *, decay_is_gamma=False, cu_seqlens=None,
                           _p(init), float(scale), _p(out), _p(fin),
                           nthreads or default_threads(),
                           -1.0 if qk_l2norm_eps is None else float(qk_l2norm_eps),
-                          *[_p(x) for x in fused], RULES[update_rule])
+                          *[_p(x) for x in fused], RULES[update_rule],
+                          1 if decay_per_key else 0)
     if rc != 0:
         raise ValueError("gdno_prefill rejected its arguments")
     return out, fin
@@ -194,14 +197,15 @@ def prefill(q, k, v, decay, beta, *, decay_is_gamma=False, cu_seqlens=None,
 
 def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None,
            scatter_idx=None, disable_state_update=False, scale=1.0, out_init=None,
-           nthreads=None, qk_l2norm_eps=None):
+           nthreads=None, qk_l2norm_eps=None, decay_per_key=None):
     """fp64 slot-pool decode.
 
     q [B,T,hq,dk]; k [B,T,n,hq,dk]; v [B,T,n,hv,dv]; A_log, dt_bias [hv];
     a [B,T,hv]; b [B,T,n,hv]; pool [P,hv,dv,dk] (not modified: a float64 copy is
     updated and returned); read_idx [B]; write_idx [B] or None;
     scatter_idx [B,T] or None; qk_l2norm_eps: None or the epsilon of the
-    in-kernel L2 norm of q and k (use_qk_l2norm).
+    in-kernel L2 norm of q and k (use_qk_l2norm); decay_per_key [B,T,hv,dk]
+    log-decay per key dimension or None (then the fused gate on a).
     Returns (out [B,T,hv,dv], pool_after [P,hv,dv,dk]) as float64 arrays;
     out rows of skipped batch rows hold out_init (default zeros).
     """
@@ -218,7 +222,8 @@ def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None,
                          _p(pool64), P, _p(_i64(read_idx), _ip), _p(_i64(write_idx), _ip),
                          _p(_i64(scatter_idx), _ip), 1 if disable_state_update else 0,
                          float(scale), _p(out), nthreads or default_threads(),
-                         -1.0 if qk_l2norm_eps is None else float(qk_l2norm_eps))
+                         -1.0 if qk_l2norm_eps is None else float(qk_l2norm_eps),
+                         _p(_f64(decay_per_key)))
     if rc != 0:
         raise ValueError("gdno_decode rejected its arguments")
     return out, pool64

@@ -93,6 +93,15 @@ static void rule_step(int dk, int dv, double* S, const double* k, const double* 
     for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += k[i] * tmp[j];
 }
 
+/* Decay of each key row of S by its own factor: the ONNX card's per-key-
+ * dimension decay (Inputs, decay (..., num_heads_v, head_size_qk)) read in
+ * its recurrence, where exp(g_t) multiplies S_{t-1} elementwise over the
+ * key dimension: S <- diag(alpha) S. */
+static void decay_rows(int dk, int dv, double* S, const double* alpha) {
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= alpha[i];
+}
+
 /* Readout y = scale * q^T S (a dv-vector), taken after the update. */
 static void readout(int dk, int dv, const double* S, const double* q, double scale,
                     double* y) {
@@ -175,6 +184,7 @@ typedef struct {
   double qk_eps;                      /* < 0: no in-kernel L2 norm */
   const double *A_log, *dt_bias, *a, *b;  /* fused decay when a != NULL, fused beta when b != NULL */
   int32_t rule;                       /* GDNO_RULE_* */
+  int32_t per_key;                    /* decay is [T, hv, dk] */
 } prefill_ctx;
 
 static int64_t clamp64(int64_t x, int64_t lo, int64_t hi) {
@@ -205,6 +215,7 @@ static void prefill_unit(void* vctx, int64_t unit) {
   double* tmp = (double*)malloc(sizeof(double) * (size_t)dv);
   double* qn = (double*)malloc(sizeof(double) * (size_t)dk);
   double* kn = (double*)malloc(sizeof(double) * (size_t)dk);
+  double* alpha = (double*)malloc(sizeof(double) * (size_t)dk);
   const size_t st_off = ((size_t)r * c->hv + h) * (size_t)dv * dk;
   if (c->init) vmajor_to_kmajor(dk, dv, c->init + st_off, S);
 
@@ -222,17 +233,27 @@ static void prefill_unit(void* vctx, int64_t unit) {
     const int has_decay = c->rule == GDNO_RULE_GATED_DELTA || c->rule == GDNO_RULE_GATED;
     const int has_beta = c->rule == GDNO_RULE_GATED_DELTA || c->rule == GDNO_RULE_DELTA;
     double gamma = 1.0, beta = 1.0;
+    if (has_beta) /* fused: a sigmoid of b */
+      beta = c->b ? sigmoid(c->b[e]) : c->beta[e];
+    if (c->per_key) {
+      /* per-key decay: decay the key rows, then the step without decay */
+      const double* d = c->decay + e * (size_t)dk;
+      for (int i = 0; i < dk; ++i) alpha[i] = c->decay_is_gamma ? d[i] : exp(d[i]);
+      decay_rows(dk, dv, S, alpha);
+      rule_step(dk, dv, S, k, v, 1.0, beta, c->rule == GDNO_RULE_GATED_DELTA, tmp);
+      readout(dk, dv, S, q, c->scale, c->out + ((size_t)t * c->hv + h) * dv);
+      continue;
+    }
     if (has_decay) /* fused: the qwen gate on a */
       gamma = c->a ? exp(gate_log_decay(c->A_log[h], c->dt_bias[h], c->a[e]))
                    : (c->decay_is_gamma ? c->decay[e] : exp(c->decay[e]));
-    if (has_beta) /* fused: a sigmoid of b */
-      beta = c->b ? sigmoid(c->b[e]) : c->beta[e];
     if (c->rule == GDNO_RULE_GATED_DELTA)
       gd_step(dk, dv, S, k, v, gamma, beta, tmp);
     else
       rule_step(dk, dv, S, k, v, gamma, beta, c->rule == GDNO_RULE_DELTA, tmp);
     readout(dk, dv, S, q, c->scale, c->out + ((size_t)t * c->hv + h) * dv);
   }
+  free(alpha);
   free(kn);
   free(qn);
   /* final state after the request's last token; an empty request copies its
@@ -249,7 +270,7 @@ int gdno_prefill(int32_t n_seqs, int64_t total_tokens, int32_t seq_len,
                  const int64_t* cu, const double* init, double scale,
                  double* out, double* final_state, int32_t nthreads,
                  double qk_l2norm_eps, const double* A_log, const double* dt_bias,
-                 const double* a, const double* b, int32_t update_rule) {
+                 const double* a, const double* b, int32_t update_rule, int32_t decay_per_key) {
   if (n_seqs < 0 || total_tokens < 0 || hq <= 0 || hv <= 0 || dk <= 0 || dv <= 0)
     return -1;
   if (hv % hq != 0) return -1;
@@ -258,11 +279,12 @@ int gdno_prefill(int32_t n_seqs, int64_t total_tokens, int32_t seq_len,
   const int has_decay = update_rule == GDNO_RULE_GATED_DELTA || update_rule == GDNO_RULE_GATED;
   const int has_beta = update_rule == GDNO_RULE_GATED_DELTA || update_rule == GDNO_RULE_DELTA;
   if (a && (!A_log || !dt_bias)) return -1;
+  if (decay_per_key && (a || !has_decay)) return -1; /* per-key decay: given, rules with a decay */
   if (total_tokens > 0 && has_decay && !a && !decay) return -1;
   if (total_tokens > 0 && has_beta && !b && !beta) return -1;
   prefill_ctx c = {n_seqs, seq_len, hq, hv, dk, dv, decay_is_gamma, total_tokens,
                    q, k, v, decay, beta, init, cu, scale, out, final_state,
-                   qk_l2norm_eps, A_log, dt_bias, a, b, update_rule};
+                   qk_l2norm_eps, A_log, dt_bias, a, b, update_rule, decay_per_key};
   run_units(prefill_unit, &c, (int64_t)n_seqs * hv, nthreads);
   return 0;
 }
@@ -278,6 +300,7 @@ typedef struct {
   double scale;
   double* out;
   double qk_eps; /* < 0: no in-kernel L2 norm */
+  const double* pk_decay; /* [B, T, hv, dk] log-decay per key, or NULL (fused gate) */
 } decode_ctx;
 
 static int slot_ok(int64_t s, int32_t P) { return s >= 0 && s < P; }
@@ -303,14 +326,21 @@ static void decode_unit(void* vctx, int64_t unit) {
   double* tmp = (double*)malloc(sizeof(double) * (size_t)dv);
   double* qn = (double*)malloc(sizeof(double) * (size_t)dk);
   double* kn = (double*)malloc(sizeof(double) * (size_t)dk);
+  double* alpha = (double*)malloc(sizeof(double) * (size_t)dk);
   vmajor_to_kmajor(dk, dv, c->pool0 + (size_t)rd * slot_elems + head_off, S);
 
   for (int32_t t = 0; t < c->T; ++t) {
     const size_t bt = (size_t)bi * c->T + t;
-    const double g = gate_log_decay(c->A_log[h], c->dt_bias[h], c->a[bt * c->hv + h]);
-    const double gamma = exp(g);
     /* decay once per token (gatedDeltaStep: scale the state first) */
-    for (size_t e = 0; e < (size_t)dk * dv; ++e) S[e] *= gamma;
+    if (c->pk_decay) {
+      const double* d = c->pk_decay + (bt * c->hv + h) * (size_t)dk;
+      for (int i = 0; i < dk; ++i) alpha[i] = exp(d[i]);
+      decay_rows(dk, dv, S, alpha);
+    } else {
+      const double g = gate_log_decay(c->A_log[h], c->dt_bias[h], c->a[bt * c->hv + h]);
+      const double gamma = exp(g);
+      for (size_t e = 0; e < (size_t)dk * dv; ++e) S[e] *= gamma;
+    }
     for (int32_t j = 0; j < c->n_hh; ++j) {
       const size_t btj = bt * c->n_hh + j;
       const double* k = c->k + (btj * c->hq + qh) * dk;
@@ -335,6 +365,7 @@ static void decode_unit(void* vctx, int64_t unit) {
   }
   if (!c->scatter && !c->disable && slot_ok(wr, c->P))
     kmajor_to_vmajor(dk, dv, S, c->pool + (size_t)wr * slot_elems + head_off);
+  free(alpha);
   free(kn);
   free(qn);
   free(tmp);
@@ -349,7 +380,8 @@ int gdno_decode(int32_t B, int32_t T, int32_t n_hh, int32_t hq, int32_t hv,
                 double* pool, int32_t P,
                 const int64_t* read, const int64_t* write, const int64_t* scatter,
                 int32_t disable_state_update, double scale,
-                double* out, int32_t nthreads, double qk_l2norm_eps) {
+                double* out, int32_t nthreads, double qk_l2norm_eps,
+                const double* decay_per_key) {
   if (B < 0 || T <= 0 || n_hh <= 0 || hq <= 0 || hv <= 0 || dk <= 0 || dv <= 0 || P < 0)
     return -1;
   if (hv % hq != 0) return -1;
@@ -360,7 +392,7 @@ int gdno_decode(int32_t B, int32_t T, int32_t n_hh, int32_t hq, int32_t hv,
   memcpy(pool0, pool, sizeof(double) * pool_elems);
   decode_ctx c = {B, T, n_hh, hq, hv, dk, dv, P, disable_state_update,
                   q, k, v, A_log, dt_bias, a, b, pool0, pool,
-                  read, write, scatter, scale, out, qk_l2norm_eps};
+                  read, write, scatter, scale, out, qk_l2norm_eps, decay_per_key};
   run_units(decode_unit, &c, (int64_t)B * hv, nthreads);
   free(pool0);
   return 0;

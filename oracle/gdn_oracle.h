@@ -67,6 +67,11 @@ void gdno_gate(int64_t n, int32_t hv, const double* A_log, const double* dt_bias
  *                             A_log and dt_bias; decay is then not read), b
  *                             != NULL gives beta = sigmoid(b) (beta is then
  *                             not read)
+ *   decay_per_key             != 0: decay is [T, hv, dk], one decay per key
+ *                             dimension (the ONNX card's per-key spelling):
+ *                             each step first scales key row i of the state
+ *                             by its own factor; rules with a decay only, and
+ *                             the decay given (a == NULL)
  *   update_rule               GDNO_RULE_*: which terms of the recurrence
  *                             survive (the ONNX card's update_rule).  Rules
  *                             without the decay read no decay (gamma = 1),
@@ -86,7 +91,8 @@ int gdno_prefill(int32_t n_seqs, int64_t total_tokens, int32_t seq_len,
                  const int64_t* cu, const double* init, double scale,
                  double* out, double* final_state, int32_t nthreads,
                  double qk_l2norm_eps, const double* A_log, const double* dt_bias,
-                 const double* a, const double* b, int32_t update_rule);
+                 const double* a, const double* b, int32_t update_rule,
+                 int32_t decay_per_key);
 
 /* Slot-pool decode with n_hh Householder sub-steps per token.  With
  * qk_l2norm_eps >= 0 every q and k head vector is first replaced by
@@ -97,6 +103,9 @@ int gdno_prefill(int32_t n_seqs, int64_t total_tokens, int32_t seq_len,
  *                         row reads the pool as it was on entry)
  *   read [B]; write [B] or NULL (= read); scatter [B, T] or NULL
  *   out  [B, T, hv, dv]  rows of skipped batch rows are left as given
+ *   decay_per_key [B, T, hv, dk] log-decay per key dimension, or NULL: when
+ *                         given it replaces the fused gate's decay (each
+ *                         token scales key row i of the state by its factor)
  * Returns 0, or -1 on an argument error (includes scatter with disable). */
 int gdno_decode(int32_t B, int32_t T, int32_t n_hh, int32_t hq, int32_t hv,
                 int32_t dk, int32_t dv,
@@ -106,7 +115,8 @@ int gdno_decode(int32_t B, int32_t T, int32_t n_hh, int32_t hq, int32_t hv,
                 double* pool, int32_t P,
                 const int64_t* read, const int64_t* write, const int64_t* scatter,
                 int32_t disable_state_update, double scale,
-                double* out, int32_t nthreads, double qk_l2norm_eps);
+                double* out, int32_t nthreads, double qk_l2norm_eps,
+                const double* decay_per_key);
 
 /* Causal depthwise conv1d over a ragged batch with a slot-indexed conv-state
  * pool ("gated_delta_conv1d_fwd").

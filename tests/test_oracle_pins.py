@@ -775,3 +775,115 @@ def test_rules_ignore_the_inputs_they_drop_and_fuse_per_input():
         oracle.prefill(*args, None, gb, **kw)
     with pytest.raises(ValueError):
         oracle.prefill(*args, gd, None, update_rule="delta", **kw)
+
+
+# ---------------------------------------------------------------------------
+# per-key decay ("com.microsoft.GatedDeltaNet", decay input: the per-key-
+# dimension spelling (..., num_heads_v, head_size_qk)): exp(g_t) scales the
+# key rows of S elementwise in the card's recurrence
+
+
+def _pk_inputs(seed, T=23, dk=5, dv=4, hv=2):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(T, 1, dk, generator=g, dtype=torch.float64).numpy()
+    k = torch.randn(T, 1, dk, generator=g, dtype=torch.float64).numpy()
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = torch.randn(T, hv, dv, generator=g, dtype=torch.float64).numpy()
+    gk = -torch.rand(T, hv, dk, generator=g, dtype=torch.float64).numpy() * 0.6
+    beta = torch.rand(T, hv, generator=g, dtype=torch.float64).numpy()
+    init = torch.randn(1, hv, dv, dk, generator=g, dtype=torch.float64).numpy()
+    return q, k, v, gk, beta, init
+
+
+def test_per_key_decay_equal_across_keys_is_scalar_decay():
+    q, k, v, gk, beta, init = _pk_inputs(120)
+    gs = gk[:, :, 0]
+    gk_eq = np.repeat(gs[:, :, None], gk.shape[2], axis=2)
+    T = q.shape[0]
+    for rule in ("gated_delta", "gated"):
+        bet = beta if rule == "gated_delta" else None
+        o1, f1 = oracle.prefill(q, k, v, gk_eq, bet, n_seqs=1, seq_len=T, initial_state=init,
+                                scale=0.8, update_rule=rule, decay_per_key=True)
+        o2, f2 = oracle.prefill(q, k, v, gs, bet, n_seqs=1, seq_len=T, initial_state=init,
+                                scale=0.8, update_rule=rule)
+        np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(f1, f2, rtol=1e-12, atol=1e-12)
+
+
+def test_per_key_decay_brute_force_matrices():
+    """S_t = (I - beta k k^T) diag(alpha_t) S_{t-1} + beta k v^T with explicit
+    dk x dk matrices, y_t = scale S_t^T q_t."""
+    q, k, v, gk, beta, init = _pk_inputs(121)
+    T, hv = v.shape[0], v.shape[1]
+    out, fin = oracle.prefill(q, k, v, gk, beta, n_seqs=1, seq_len=T, initial_state=init,
+                              scale=0.5, decay_per_key=True)
+    for h in range(hv):
+        S = init[0, h].T.copy()
+        for t in range(T):
+            kt = k[t, 0][:, None]
+            M = (np.eye(kt.shape[0]) - beta[t, h] * kt @ kt.T) @ np.diag(np.exp(gk[t, h]))
+            S = M @ S + beta[t, h] * kt @ v[t, h][None, :]
+            np.testing.assert_allclose(out[t, h], 0.5 * S.T @ q[t, 0], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(fin[0, h], S.T, rtol=1e-12, atol=1e-12)
+
+
+def test_per_key_decay_one_hot_keys_closed_form():
+    """One-hot keys e_i: key row i is written, (1 - beta) alpha_i S[i] + beta v;
+    every other row only decays by its own factor."""
+    g = torch.Generator().manual_seed(122)
+    T, dk, dv = 40, 6, 3
+    idx = torch.randint(0, dk, (T,), generator=g).numpy()
+    k = np.zeros((T, 1, dk))
+    k[np.arange(T), 0, idx] = 1.0
+    q = torch.randn(T, 1, dk, generator=g, dtype=torch.float64).numpy()
+    v = torch.randn(T, 1, dv, generator=g, dtype=torch.float64).numpy()
+    gk = -torch.rand(T, 1, dk, generator=g, dtype=torch.float64).numpy()
+    beta = torch.rand(T, 1, generator=g, dtype=torch.float64).numpy()
+    init = torch.randn(1, 1, dv, dk, generator=g, dtype=torch.float64).numpy()
+    out, fin = oracle.prefill(q, k, v, gk, beta, n_seqs=1, seq_len=T, initial_state=init,
+                              scale=1.0, decay_per_key=True)
+    S = init[0, 0].T.copy()
+    for t in range(T):
+        a = np.exp(gk[t, 0])
+        S = a[:, None] * S
+        i = idx[t]
+        S[i] = (1.0 - beta[t, 0]) * S[i] + beta[t, 0] * v[t, 0]
+        np.testing.assert_allclose(out[t, 0], q[t, 0] @ S, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(fin[0, 0], S.T, rtol=1e-13, atol=1e-13)
+
+
+def test_per_key_gated_rule_masked_form():
+    """gated rule with per-key decay: y_t = (q_t o Gam_t)^T S0 +
+    sum_{s<=t} ((q_t o Gam_t / Gam_s) . k_s) v_s with Gam_t the running
+    product of the per-key factors (no retrieval term)."""
+    q, k, v, gk, beta, init = _pk_inputs(123)
+    T, hv = v.shape[0], v.shape[1]
+    out, fin = oracle.prefill(q, k, v, gk, None, n_seqs=1, seq_len=T, initial_state=init,
+                              scale=1.0, update_rule="gated", decay_per_key=True)
+    for h in range(hv):
+        G = np.cumsum(gk[:, h], axis=0)          # [T, dk]
+        S0 = init[0, h].T                        # [dk, dv]
+        for t in range(T):
+            y = (q[t, 0] * np.exp(G[t])) @ S0
+            for s in range(t + 1):
+                y = y + ((q[t, 0] * np.exp(G[t] - G[s])) @ k[s, 0]) * v[s, h]
+            np.testing.assert_allclose(out[t, h], y, rtol=1e-11, atol=1e-11)
+        S = np.exp(G[-1])[:, None] * S0 + sum(np.outer(k[s, 0] * np.exp(G[-1] - G[s]), v[s, h])
+                                              for s in range(T))
+        np.testing.assert_allclose(fin[0, h], S.T, rtol=1e-11, atol=1e-11)
+
+
+def test_per_key_decay_decode_equals_prefill_from_the_slot():
+    q, k, v, gk, beta_raw, init = _pk_inputs(124, T=6)
+    T, hv, dv, dk = v.shape[0], v.shape[1], v.shape[2], k.shape[2]
+    g = torch.Generator().manual_seed(125)
+    b = torch.randn(T, hv, generator=g, dtype=torch.float64).numpy()
+    beta = 1.0 / (1.0 + np.exp(-b))
+    pool = np.concatenate([np.zeros((1, hv, dv, dk)), init])  # slot 1 holds the state
+    ro, rp = oracle.decode(q[None], k[None, :, None], v[None, :, None], np.zeros(hv), np.zeros(hv),
+                           np.zeros((1, T, hv)), b[None, :, None], pool, np.array([1]),
+                           scale=0.7, decay_per_key=gk[None])
+    po, pf = oracle.prefill(q, k, v, gk, beta, n_seqs=1, seq_len=T, initial_state=init, scale=0.7,
+                            decay_per_key=True)
+    np.testing.assert_allclose(ro[0], po, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(rp[1], pf[0], rtol=1e-12, atol=1e-12)
