@@ -335,6 +335,27 @@ def extra_workloads(torch, gdn, synth, dev):
             "gbs": by / (ms * 1e-3) / 1e9, "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         del t, o6
 
+    # the chunked-prefill shape with a per-key decay ([T, hv, dk] log-decay,
+    # the separate 16-token-chunk kernel)
+    px = synth.chunked_prefill_b4_s4096()
+    g = torch.Generator().manual_seed(12)
+    q, k, v = (px[n].to(dev) for n in ("q", "k", "v"))
+    T, hv, dk = px["T"], px["hv"], px["dk"]
+    dec = (-torch.rand(T, hv, dk, generator=g) * 0.5).to(dev)
+    bet = torch.rand(T, hv, generator=g).to(dev)
+    cu = torch.arange(px["n_seqs"] + 1, dtype=torch.int32, device=dev) * px["seq_len"]
+    o8 = torch.empty_like(v)
+    f8 = torch.empty(px["n_seqs"], hv, px["dv"], dk, device=dev)
+    fn = lambda: gdn.prefill(q, k, v, dec, bet, cu_seqlens=cu, scale=px["scale"], out=o8,
+                             final_state=f8, decay_per_key=True)
+    ms = _time_launches(torch, fn, flush=flush, runs=5)
+    nb, _ = prefill_algorithmic(T, px["hq"], hv, dk, px["dv"], px["n_seqs"], 16)
+    nb += T * hv * dk * 4 - T * hv * 4  # the decay is per key
+    out["chunked_prefill_per_key_decay_b4_s4096_bf16"] = {
+        "ms": ms, "tokens_per_s": T / (ms * 1e-3), "algorithmic_bytes": nb,
+        "gbs": nb / (ms * 1e-3) / 1e9, "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del q, k, v, dec, bet, o8, f8
+
     # causal conv1d over the QKV rows with the conv-state pool: the prefill
     # batch (B4 x S4096, 8192 channels) and one decode step (256 x 1 row)
     for name, make in (("conv1d_prefill_b4_s4096_c8192_k4_bf16", synth.conv1d_prefill_b4_s4096),

@@ -132,7 +132,7 @@ def prefill_args(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None,
                  initial_state=None, scale=None, chunk_size=0, out=None, final_state=None,
                  qk_l2norm=False, qk_l2norm_eps=1e-12, A_log=None, dt_bias=None, a=None,
                  b=None, update_rule="gated_delta", state_pool=None, read_slot=None,
-                 write_slot=None):
+                 write_slot=None, decay_per_key=False):
     """Validate shapes and build the gdn_prefill_args struct (device-agnostic).
 
     Returns (args, keep, out, final_state): `keep` holds every tensor whose
@@ -194,7 +194,12 @@ def prefill_args(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None,
         if gb.dtype != q3.dtype:
             raise ValueError("b must have q's dtype")
         gb = gb.contiguous()
-    if decay is not None:
+    if decay_per_key and (a is not None or b is not None):
+        raise ValueError("decay_per_key takes the decay and beta as given inputs (not a, b)")
+    if decay is not None and decay_per_key:
+        decay = _f32c(decay.reshape(-1, hv, dk) if decay.dim() == 4 else decay, "decay",
+                      (T, hv, dk))
+    elif decay is not None:
         decay = _f32c(decay.reshape(-1, hv) if decay.dim() == 3 else decay, "decay", (T, hv))
     if beta is not None:
         beta = _f32c(beta.reshape(-1, hv) if beta.dim() == 3 else beta, "beta", (T, hv))
@@ -268,6 +273,7 @@ def prefill_args(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None,
     if gb is not None:
         args.gate_b = gb.data_ptr()
     args.update_rule = RULES[update_rule]
+    args.decay_per_key = 1 if decay_per_key else 0
     keep = (q3, k3, v3, decay, beta, cu, initial_state, out3, final_state, A_log, dt_bias, ga, gb,
             read_slot, write_slot)
     return args, keep, out, final_state
@@ -276,7 +282,8 @@ def prefill_args(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None,
 def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_state=None,
             scale=None, chunk_size=0, out=None, final_state=None, stream=None,
             qk_l2norm=False, qk_l2norm_eps=1e-12, A_log=None, dt_bias=None, a=None, b=None,
-            update_rule="gated_delta", state_pool=None, read_slot=None, write_slot=None):
+            update_rule="gated_delta", state_pool=None, read_slot=None, write_slot=None,
+            decay_per_key=False):
     """Chunked prefill.
 
     q, k: [T, hq, dk] (or [B, S, hq, dk], then uniform packing with seq_len S);
@@ -297,6 +304,9 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
     write_slot [N]: the states come from and go to pool slots instead of
     initial_state / final_state (read slot outside the pool: zeros; write slot
     None: the read slot; outside the pool: not stored); returns (out, pool).
+    decay_per_key: decay is [T, hv, dk] (or [B, S, hv, dk]), one decay per
+    key dimension (the ONNX card's per-key spelling; given decay and beta
+    only); it runs a separate, slower kernel.
     Returns (out, final_state [N, hv, dv, dk] float32); out is [T, hv, dv] (or
     [B, S, hv, dv]) in q's dtype.
     """
@@ -315,13 +325,14 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
                                chunk_size=chunk_size, out=out, final_state=final_state,
                                stream=stream, qk_l2norm=qk_l2norm, qk_l2norm_eps=qk_l2norm_eps,
                                A_log=A_log, dt_bias=dt_bias, a=a, b=b, update_rule=update_rule,
-                               state_pool=state_pool)
+                               state_pool=state_pool, decay_per_key=decay_per_key)
     args, keep, out, final_state = prefill_args(
         q, k, v, decay, beta, decay_kind=decay_kind, cu_seqlens=cu_seqlens,
         initial_state=initial_state, scale=scale, chunk_size=chunk_size, out=out,
         final_state=final_state, qk_l2norm=qk_l2norm, qk_l2norm_eps=qk_l2norm_eps,
         A_log=A_log, dt_bias=dt_bias, a=a, b=b, update_rule=update_rule,
-        state_pool=state_pool, read_slot=read_slot, write_slot=write_slot)
+        state_pool=state_pool, read_slot=read_slot, write_slot=write_slot,
+        decay_per_key=decay_per_key)
     _lib.check(lib.gdn_prefill(ctypes.byref(args), _stream(stream)))
     del keep
     return out, final_state
@@ -346,7 +357,7 @@ def _pad_last(t, n):
 
 
 def _prefill_padded(q, k, v, decay, beta, pk, pv, *, out, final_state, initial_state,
-                    state_pool, **kw):
+                    state_pool, decay_per_key=False, **kw):
     """prefill for head sizes the kernels do not take (the ONNX card's head
     sizes are free, e.g. its JS example's 12 and 9): q, k and v are
     zero-padded to the kernel sizes pk, pv, the initial state likewise, and
@@ -364,8 +375,10 @@ def _prefill_padded(q, k, v, decay, beta, pk, pv, *, out, final_state, initial_s
         init = torch.zeros(*initial_state.shape[:-2], pv, pk, dtype=torch.float32,
                            device=initial_state.device)
         init[..., :dv, :dk] = initial_state
+    if decay_per_key and decay is not None:
+        decay = _pad_last(decay, pk)  # padded keys: zero k, q and state; their decay is moot
     o_p, f_p = prefill(_pad_last(q, pk), _pad_last(k, pk), _pad_last(v, pv), decay, beta,
-                       initial_state=init, **kw)
+                       initial_state=init, decay_per_key=decay_per_key, **kw)
     o = o_p[..., :dv]
     f = f_p[..., :dv, :dk]
     if out is not None:
@@ -406,7 +419,7 @@ def state_update(q, k, v, gamma, beta):
 
 def decode_args(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None,
                 scatter_idx=None, disable_state_update=False, scale=None, out=None,
-                use_qk_l2norm=False, qk_l2norm_eps=1e-6):
+                use_qk_l2norm=False, qk_l2norm_eps=1e-6, decay_per_key=None):
     """Validate shapes and build the gdn_decode_args struct (device-agnostic).
 
     Returns (args, keep, out)."""
@@ -417,14 +430,20 @@ def decode_args(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None
     hv, dv = v.shape[3], v.shape[4]
     _shape(k, "k", (B, T, n, hq, dk))
     _shape(v, "v", (B, T, n, hv, dv))
-    _shape(a, "a", (B, T, hv))
     _shape(b, "b", (B, T, n, hv))
     dt = _io_dtype(q)
-    if any(t.dtype != q.dtype for t in (k, v, a, b)):
+    if decay_per_key is not None:
+        # the per-key decay replaces the fused gate's decay: a, A_log, dt_bias unused
+        decay_per_key = _f32c(decay_per_key, "decay_per_key", (B, T, hv, dk))
+        a = A_log = dt_bias = None
+    else:
+        _shape(a, "a", (B, T, hv))
+        A_log = _f32c(A_log, "A_log", (hv,))
+        dt_bias = _f32c(dt_bias, "dt_bias", (hv,))
+    if any(t.dtype != q.dtype for t in (k, v, b) + ((a,) if a is not None else ())):
         raise ValueError("q, k, v, a and b must share one dtype")
-    q, k, v, a, b = (t.contiguous() for t in (q, k, v, a, b))
-    A_log = _f32c(A_log, "A_log", (hv,))
-    dt_bias = _f32c(dt_bias, "dt_bias", (hv,))
+    q, k, v, b = (t.contiguous() for t in (q, k, v, b))
+    a = None if a is None else a.contiguous()
     if pool.dim() != 4 or tuple(pool.shape[1:]) != (hv, dv, dk):
         raise ValueError("pool must be [P, %d, %d, %d], got %s" % (hv, dv, dk, tuple(pool.shape)))
     if pool.dtype != torch.float32 or pool.stride(-1) != 1 or pool.stride(-2) != dk:
@@ -444,8 +463,11 @@ def decode_args(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None
     d.disable_state_update = 1 if disable_state_update else 0
     d.scale = (1.0 / math.sqrt(dk)) if scale is None else float(scale)
     d.q, d.k, d.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
-    d.A_log, d.dt_bias = A_log.data_ptr(), dt_bias.data_ptr()
-    d.a, d.b = a.data_ptr(), b.data_ptr()
+    d.A_log = None if A_log is None else A_log.data_ptr()
+    d.dt_bias = None if dt_bias is None else dt_bias.data_ptr()
+    d.a = None if a is None else a.data_ptr()
+    d.b = b.data_ptr()
+    d.decay_per_key = None if decay_per_key is None else decay_per_key.data_ptr()
     d.pool, d.pool_size = pool.data_ptr(), pool.shape[0]
     d.pool_slot_stride, d.pool_head_stride = pool.stride(0), pool.stride(1)
     d.read_idx = read_idx.data_ptr()
@@ -454,13 +476,13 @@ def decode_args(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None
     d.out = out.data_ptr()
     d.qk_l2norm = 1 if use_qk_l2norm else 0
     d.qk_l2norm_eps = float(qk_l2norm_eps)
-    keep = (q, k, v, a, b, A_log, dt_bias, read_idx, write_idx, scatter_idx)
+    keep = (q, k, v, a, b, A_log, dt_bias, read_idx, write_idx, scatter_idx, decay_per_key)
     return d, keep, out
 
 
 def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None, scatter_idx=None,
            disable_state_update=False, scale=None, out=None, stream=None, use_qk_l2norm=False,
-           qk_l2norm_eps=1e-6):
+           qk_l2norm_eps=1e-6, decay_per_key=None):
     """Slot-pool decode with Householder sub-steps (one fused launch).
 
     q [B, T, hq, dk]; k [B, T, n, hq, dk]; v [B, T, n, hv, dv]; A_log, dt_bias
@@ -468,19 +490,22 @@ def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None, sca
     (updated in place); read_idx [B]; write_idx [B] or None; scatter_idx [B, T]
     or None.  scale None means 1/sqrt(dk).  use_qk_l2norm: use every q and k
     head vector as x / sqrt(sum x^2 + qk_l2norm_eps) (the FlashInfer page's
-    use_qk_l2norm; off by default here).  Returns (out [B, T, hv, dv], pool);
-    rows of skipped batch rows keep out's previous contents (zeros when out is
-    None).
+    use_qk_l2norm; off by default here).  decay_per_key [B, T, hv, dk] float32
+    log-decay per key dimension: replaces the gate's decay (a, A_log, dt_bias
+    may then be None).  Returns (out [B, T, hv, dv], pool); rows of skipped
+    batch rows keep out's previous contents (zeros when out is None).
     """
     lib = _lib.load()
     for name, t in (("q", q), ("k", k), ("v", v), ("A_log", A_log), ("dt_bias", dt_bias),
                     ("a", a), ("b", b), ("pool", pool), ("read_idx", read_idx),
-                    ("write_idx", write_idx), ("scatter_idx", scatter_idx), ("out", out)):
+                    ("write_idx", write_idx), ("scatter_idx", scatter_idx), ("out", out),
+                    ("decay_per_key", decay_per_key)):
         _dev(t, name)
     d, keep, out = decode_args(q, k, v, A_log, dt_bias, a, b, pool, read_idx,
                                write_idx=write_idx, scatter_idx=scatter_idx,
                                disable_state_update=disable_state_update, scale=scale, out=out,
-                               use_qk_l2norm=use_qk_l2norm, qk_l2norm_eps=qk_l2norm_eps)
+                               use_qk_l2norm=use_qk_l2norm, qk_l2norm_eps=qk_l2norm_eps,
+                               decay_per_key=decay_per_key)
     _lib.check(lib.gdn_decode(ctypes.byref(d), _stream(stream)))
     del keep
     return out, pool

@@ -44,6 +44,7 @@ class PrefillArgs(ctypes.Structure):
         ("pool_slot_stride", _i64), ("pool_head_stride", _i64),
         ("read_slot", _vp), ("write_slot", _vp),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+        ("decay_per_key", _i32),
     ]
 
 
@@ -59,6 +60,7 @@ class DecodeArgs(ctypes.Structure):
         ("read_idx", _vp), ("write_idx", _vp), ("scatter_idx", _vp),
         ("out", _vp),
         ("qk_l2norm", _i32), ("qk_l2norm_eps", _f32),
+        ("decay_per_key", _vp),
     ]
 
 

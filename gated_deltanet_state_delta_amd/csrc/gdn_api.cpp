@@ -107,6 +107,8 @@ gdn_status gdn_prefill(const gdn_prefill_args* p, void* stream) {
       return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill: fused and given gate inputs mixed (use gdn_gate for both)");
   }
   if (a.gate_a && (!a.A_log || !a.dt_bias)) return fail(GDN_ERR_NULL, "gdn_prefill: gate_a needs A_log and dt_bias");
+  if (a.decay_per_key && (a.gate_a || a.gate_b))
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill: decay_per_key takes the decay and beta as given inputs");
   if (a.state_pool) {
     if (a.initial_state || a.final_state)
       return fail(GDN_ERR_SHAPE, "gdn_prefill: state_pool replaces initial_state and final_state (pass NULL)");
@@ -168,8 +170,12 @@ gdn_status gdn_decode(const gdn_decode_args* p, void* stream) {
   if (a.scatter_idx && a.disable_state_update)
     return fail(GDN_ERR_UNSUPPORTED, "gdn_decode: scatter_idx requires disable_state_update == 0");
   if (a.batch == 0) return GDN_OK;
-  if (!a.q || !a.k || !a.v || !a.A_log || !a.dt_bias || !a.a || !a.b || !a.pool || !a.read_idx || !a.out)
-    return fail(GDN_ERR_NULL, "gdn_decode: q, k, v, A_log, dt_bias, a, b, pool, read_idx and out are required");
+  if (!a.q || !a.k || !a.v || !a.b || !a.pool || !a.read_idx || !a.out)
+    return fail(GDN_ERR_NULL, "gdn_decode: q, k, v, b, pool, read_idx and out are required");
+  if (!a.decay_per_key && (!a.A_log || !a.dt_bias || !a.a))
+    return fail(GDN_ERR_NULL, "gdn_decode: A_log, dt_bias and a are required (or decay_per_key)");
+  if (a.decay_per_key && !aligned(a.decay_per_key, 16))
+    return fail(GDN_ERR_LAYOUT, "gdn_decode: decay_per_key must be 16-byte aligned");
   if (!aligned(a.pool, 16) || a.pool_slot_stride % 4 != 0 || a.pool_head_stride % 4 != 0 ||
       a.pool_slot_stride < 0 || a.pool_head_stride < 0)
     return fail(GDN_ERR_LAYOUT, "gdn_decode: pool must be 16-byte aligned with strides multiple of 4 elements");

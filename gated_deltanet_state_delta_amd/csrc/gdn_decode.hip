@@ -41,6 +41,7 @@ struct DecodeParams {
   float scale;
   int qk_norm;    // q, k used as x * rsqrt(sum x^2 + qk_eps) (use_qk_l2norm)
   float qk_eps;
+  const float* decay_pk;  // [B, T, hv, DK] log-decay per key, or nullptr (fused gate)
 };
 
 // Four io elements moved as one word group (8 bytes for bf16, 16 for fp32).
@@ -60,6 +61,7 @@ decode_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(16))) IO sq[TT * DK];         // [t][DK]
   __shared__ __attribute__((aligned(16))) IO sv[TT * NJ * ROWS];  // [t][j][rows of this block]
   __shared__ float sgam[TT], sbet[TT * NJ];
+  __shared__ __attribute__((aligned(16))) float spk[TT * DK];       // per-key log-decay [t][DK]
   const int blk = blockIdx.x;
   const int rb = blk % NRB;
   const int h = (blk / NRB) % p.hv;
@@ -88,8 +90,9 @@ decode_kernel(const DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = ld_nt(src + i * 4 * L);
   }
-  const float A_log = p.A_log[h];
-  const float dt_bias = p.dt_bias[h];
+  const bool per_key = p.decay_pk != nullptr;  // uniform: the per-key decay replaces the gate's
+  const float A_log = per_key ? 0.f : p.A_log[h];
+  const float dt_bias = per_key ? 0.f : p.dt_bias[h];
 
   // One token: decay, the sub-steps, the readout and the optional scatter.
   // kp(j): this lane's k of sub-step j; vj(j), beta(j): the row's v and beta;
@@ -106,10 +109,21 @@ decode_kernel(const DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) v4[i] *= r;
   };
-  auto token = [&](int t, float gamma, auto kp, auto vj, auto beta, const IO* qp) {
+  // gp: this lane's per-key log-decays (used when per_key)
+  auto token = [&](int t, float gamma, const float* gp, auto kp, auto vj, auto beta, const IO* qp) {
     const int64_t bt = (int64_t)b * p.T + t;
+    if (per_key) {
+      // key column i*4L + 4o + e of this lane decays by its own factor
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] *= gamma;
+      for (int i = 0; i < 4; ++i) {
+        const f4 gi = *reinterpret_cast<const f4*>(gp + i * 4 * L);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[i][e] *= __builtin_amdgcn_exp2f(gi[e] * 1.4426950408889634f);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] *= gamma;
+    }
     for (int j = 0; j < p.nhh; ++j) {
       const IO* kj = kp(j);
       f4 kf[4];
@@ -148,8 +162,9 @@ decode_kernel(const DecodeParams p) {
     // a single step: its inputs straight from global memory, issued beside
     // the state loads (staging would only add a round trip)
     const int64_t bt = (int64_t)b;
-    const float gamma = expf(gate_log_decay(A_log, dt_bias, to_f32(ga[bt * p.hv + h])));
-    token(0, gamma, [&](int) { return k + (bt * p.hq + qh) * DK + 4 * o; },
+    const float gamma = per_key ? 1.f : expf(gate_log_decay(A_log, dt_bias, to_f32(ga[bt * p.hv + h])));
+    const float* gp = per_key ? p.decay_pk + (bt * p.hv + h) * DK + 4 * o : nullptr;
+    token(0, gamma, gp, [&](int) { return k + (bt * p.hq + qh) * DK + 4 * o; },
           [&](int) { return to_f32(v[(bt * p.hv + h) * DV + row]); },
           [&](int) { return sigmoidf(to_f32(gb[bt * p.hv + h])); }, q + (bt * p.hq + qh) * DK + 4 * o);
   } else {
@@ -177,15 +192,24 @@ decode_kernel(const DecodeParams p) {
         reinterpret_cast<Q4*>(sv)[(t * NJ + j) * (ROWS / 4) + c] =
             reinterpret_cast<const Q4*>(v + ((bt0 * p.nhh + tj) * p.hv + h) * DV + rb * ROWS)[c];
       }
-      for (int idx = tid; idx < nt; idx += NT)
-        sgam[idx] = expf(gate_log_decay(A_log, dt_bias, to_f32(ga[(bt0 + idx) * p.hv + h])));
+      if (per_key) {
+        for (int idx = tid; idx < nt * (DK / 4); idx += NT) {
+          const int t = idx / (DK / 4), c = idx % (DK / 4);
+          reinterpret_cast<f4*>(spk)[t * (DK / 4) + c] =
+              reinterpret_cast<const f4*>(p.decay_pk + ((bt0 + t) * p.hv + h) * DK)[c];
+        }
+      } else {
+        for (int idx = tid; idx < nt; idx += NT)
+          sgam[idx] = expf(gate_log_decay(A_log, dt_bias, to_f32(ga[(bt0 + idx) * p.hv + h])));
+      }
       for (int idx = tid; idx < ntj; idx += NT) {
         const int t = idx / p.nhh, j = idx % p.nhh;
         sbet[t * NJ + j] = sigmoidf(to_f32(gb[(bt0 * p.nhh + idx) * p.hv + h]));
       }
       __syncthreads();
       for (int tl = 0; tl < nt; ++tl)
-        token(t0 + tl, sgam[tl], [&](int j) -> const IO* { return sk + (tl * NJ + j) * DK + 4 * o; },
+        token(t0 + tl, per_key ? 1.f : sgam[tl], spk + tl * DK + 4 * o,
+              [&](int j) -> const IO* { return sk + (tl * NJ + j) * DK + 4 * o; },
               [&](int j) { return to_f32(sv[(tl * NJ + j) * ROWS + (row - rb * ROWS)]); },
               [&](int j) { return sbet[tl * NJ + j]; }, sq + tl * DK + 4 * o);
     }
@@ -238,7 +262,7 @@ static hipError_t dispatch_dk(const DecodeParams& p, int dk, int dv, hipStream_t
 // hint follows T (16, 32, 64).  Every activation must be 16-byte aligned,
 // as the prefill kernels require.
 static bool decode_as_prefill(const gdn_decode_args& a) {
-  if (a.T < 16 || a.n_householder != 1 || a.scatter_idx) return false;
+  if (a.T < 16 || a.n_householder != 1 || a.scatter_idx || a.decay_per_key) return false;
   if ((int64_t)a.batch * a.T * a.hv >= (int64_t(1) << 31)) return false;
   const void* ptrs[] = {a.q, a.k, a.v, a.out};
   for (const void* q : ptrs)
@@ -285,6 +309,7 @@ hipError_t launch_decode(const gdn_decode_args& a, hipStream_t stream) {
   p.batch = a.batch; p.T = a.T; p.nhh = a.n_householder; p.hq = a.hq; p.hv = a.hv;
   p.pool_size = a.pool_size; p.disable = a.disable_state_update; p.scale = a.scale;
   p.qk_norm = a.qk_l2norm != 0; p.qk_eps = a.qk_l2norm_eps;
+  p.decay_pk = a.decay_per_key;
   if (a.io_dtype == GDN_BF16) return dispatch_dk<__bf16>(p, a.dk, a.dv, stream);
   return dispatch_dk<float>(p, a.dk, a.dv, stream);
 }

@@ -78,6 +78,7 @@ hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream, int poo
     }
   }
   const bool bf = a.io_dtype == GDN_BF16;
+  if (a.decay_per_key) return launch_prefill_pk(p, a.dk, a.dv, bf, stream);
   if (bf && prefill_pair_supported(a.dk, a.dv, a.chunk_size)) return prefill_pair_bf16(p, a.dk, stream);
   const int hint = a.chunk_size != 0 ? a.chunk_size : 64;
   const int c = bf ? prefill_chunk_for<__bf16>(a.dk, a.dv, hint)

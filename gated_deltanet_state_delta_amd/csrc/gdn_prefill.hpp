@@ -101,6 +101,9 @@ struct PrefillParams {
 };
 
 
+// The per-key-decay prefill (gdn_prefill_pk.hip).
+hipError_t launch_prefill_pk(const PrefillParams& p, int dk, int dv, bool bf16, hipStream_t s);
+
 // Element offsets of the V-major state slice (request r, value head h, value
 // columns from v0) to read the initial state from and to write the final
 // state to; -1: none (zeros in, nothing out).  Dense states: [r, h] of

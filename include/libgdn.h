@@ -199,6 +199,14 @@ typedef struct {
    * memory: gdn_prefill_workspace_size() returns 0 and these are ignored. */
   void* workspace;
   size_t workspace_bytes;
+  /* Per-key decay (appended): with decay_per_key != 0, decay is
+   * [total_tokens, hv, dk] fp32 dense, one decay per key dimension (the ONNX
+   * card's per-key-dimension spelling, in decay_kind's meaning), read in the
+   * card's recurrence: each token first scales key column i of the V-major
+   * state by its own factor.  Needs a given decay (not gate_a) and given
+   * beta; any update_rule with a decay; runs a separate 16-token-chunk kernel
+   * (fp32 arithmetic), slower than the scalar-decay kernels. */
+  int32_t decay_per_key;
 } gdn_prefill_args;
 
 /* Device scratch bytes a gdn_prefill call with these arguments needs: always
@@ -274,6 +282,13 @@ typedef struct {
    * x / sqrt(sum(x^2) + qk_l2norm_eps) (the page's epsilon is 1e-6). */
   int32_t qk_l2norm;
   float qk_l2norm_eps;     /* >= 0 and finite                                  */
+  /* Per-key decay (optional, appended): [batch, T, hv, dk] fp32 log-decay,
+   * one per key dimension (the ONNX card's per-key-dimension decay spelling).
+   * When given it replaces the fused gate's decay -- each token first scales
+   * key column i of the V-major state by exp(decay_per_key[b,t,h,i]) -- and a,
+   * A_log, dt_bias are not read (may be NULL); beta still comes from b.
+   * 16-byte aligned. */
+  const float* decay_per_key;
 } gdn_decode_args;
 
 gdn_status gdn_decode(const gdn_decode_args* args, void* stream);

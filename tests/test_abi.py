@@ -125,6 +125,8 @@ PREFILL_ERRORS = [
     (dict(final_state=None, state_pool=FAKE * 13, pool_size=10, pool_slot_stride=4 * 64 * 64 + 2,
           pool_head_stride=64 * 64), 4),                # stride not a multiple of 4
     (dict(read_slot=FAKE * 15), 2),                     # slots without a pool
+    (dict(decay_per_key=1, decay=None, beta=None, gate_a=FAKE * 8, A_log=FAKE * 9,
+          dt_bias=FAKE * 10, gate_b=FAKE * 11), 5),      # per-key decay takes given inputs
 ]
 
 
