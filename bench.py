@@ -161,7 +161,10 @@ def load_traffic(kernel):
 
 
 def prefill_algorithmic(T, hq, hv, dk, dv, n_seqs, chunk, io_bytes=2):
-    """Bytes and flops one prefill launch must move / compute."""
+    """Bytes and flops one prefill launch must move / compute: q, k, v, out and
+    the fp32 gates once per token, the final states once; per q/k head the
+    chunk's Gram products (4 C dk per token), per value head the state pass
+    (6 dk dv per token) and the intra-chunk M U / U products (4 C dv)."""
     per_token_bytes = (hq * dk * io_bytes * 2          # q, k
                        + hv * dv * io_bytes * 2        # v, out
                        + hv * 4 * 2)                   # log-decay, beta (fp32)
@@ -397,7 +400,7 @@ def main():
         print(json.dumps(summarize_mfma(args.summarize_mfma), indent=1))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 

@@ -45,7 +45,7 @@ typedef enum {
   GDN_ERR_SHAPE = 2,       /* a size is <= 0, inconsistent, or hv % hq != 0        */
   GDN_ERR_DTYPE = 3,       /* unknown dtype or decay kind                          */
   GDN_ERR_LAYOUT = 4,      /* misaligned pointer / stride, or a partial overlap    */
-  GDN_ERR_UNSUPPORTED = 5, /* valid request this build does not implement          */
+  GDN_ERR_UNSUPPORTED = 5, /* valid request the library does not implement           */
   GDN_ERR_HIP = 6          /* a HIP launch failed; gdn_last_error() has the text   */
 } gdn_status;
 
