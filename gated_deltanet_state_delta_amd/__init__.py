@@ -307,6 +307,8 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
     decay_per_key: decay is [T, hv, dk] (or [B, S, hv, dk]), one decay per
     key dimension (the ONNX card's per-key spelling; given decay and beta
     only); it runs a separate, slower kernel.
+    float16 q, k, v (the ONNX card's T includes f16) run the float32 path on
+    exact widenings and the output is rounded back to float16.
     Returns (out, final_state [N, hv, dv, dk] float32); out is [T, hv, dv] (or
     [B, S, hv, dv]) in q's dtype.
     """
@@ -317,6 +319,21 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
                     ("dt_bias", dt_bias), ("a", a), ("b", b), ("state_pool", state_pool),
                     ("read_slot", read_slot), ("write_slot", write_slot)):
         _dev(t, name)
+    if q.dtype == torch.float16:
+        if out is not None and out.dtype != torch.float16:
+            raise ValueError("out must have q's dtype")
+        w = lambda t: None if t is None else t.float()
+        o32, fin = prefill(w(q), w(k), w(v), decay, beta, decay_kind=decay_kind,
+                           cu_seqlens=cu_seqlens, initial_state=initial_state, scale=scale,
+                           chunk_size=chunk_size, final_state=final_state, stream=stream,
+                           qk_l2norm=qk_l2norm, qk_l2norm_eps=qk_l2norm_eps, A_log=A_log,
+                           dt_bias=dt_bias, a=w(a), b=w(b), update_rule=update_rule,
+                           state_pool=state_pool, read_slot=read_slot, write_slot=write_slot,
+                           decay_per_key=decay_per_key)
+        if out is None:
+            return o32.half(), fin
+        out.copy_(o32)
+        return out, fin
     dk, dv = q.shape[-1], v.shape[-1]
     pk, pv = _head_pad(dk), _head_pad(dv)
     if (pk, pv) != (dk, dv):
@@ -492,8 +509,11 @@ def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None, sca
     head vector as x / sqrt(sum x^2 + qk_l2norm_eps) (the FlashInfer page's
     use_qk_l2norm; off by default here).  decay_per_key [B, T, hv, dk] float32
     log-decay per key dimension: replaces the gate's decay (a, A_log, dt_bias
-    may then be None).  Returns (out [B, T, hv, dv], pool); rows of skipped
-    batch rows keep out's previous contents (zeros when out is None).
+    may then be None).  float16 q, k, v, a, b are converted to bfloat16 for
+    the kernel and the output is copied into a float16 buffer (skipped rows
+    keep their values through a bfloat16 round trip), as the FlashInfer page
+    describes.  Returns (out [B, T, hv, dv], pool); rows of skipped batch rows
+    keep out's previous contents (zeros when out is None).
     """
     lib = _lib.load()
     for name, t in (("q", q), ("k", k), ("v", v), ("A_log", A_log), ("dt_bias", dt_bias),
@@ -501,6 +521,18 @@ def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None, sca
                     ("write_idx", write_idx), ("scatter_idx", scatter_idx), ("out", out),
                     ("decay_per_key", decay_per_key)):
         _dev(t, name)
+    if q.dtype == torch.float16:
+        c = lambda t: None if t is None else t.to(torch.bfloat16)
+        o16 = None if out is None else out.to(torch.bfloat16)
+        o, pool = decode(c(q), c(k), c(v), A_log, dt_bias, c(a), c(b), pool, read_idx,
+                         write_idx=write_idx, scatter_idx=scatter_idx,
+                         disable_state_update=disable_state_update, scale=scale, out=o16,
+                         stream=stream, use_qk_l2norm=use_qk_l2norm, qk_l2norm_eps=qk_l2norm_eps,
+                         decay_per_key=decay_per_key)
+        if out is None:
+            return o.half(), pool
+        out.copy_(o)
+        return out, pool
     d, keep, out = decode_args(q, k, v, A_log, dt_bias, a, b, pool, read_idx,
                                write_idx=write_idx, scatter_idx=scatter_idx,
                                disable_state_update=disable_state_update, scale=scale, out=out,

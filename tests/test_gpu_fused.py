@@ -157,3 +157,53 @@ def test_decode_use_qk_l2norm(T, n, dtype):
                            x["pool"], x["read_idx"], write_idx=x["write_idx"],
                            scatter_idx=x["scatter_idx"], scale=x["scale"])
     assert np.abs(ro2 - ro).max() > 1e-2 * np.abs(ro).max()
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_prefill_float16_inputs(fused):
+    """float16 q, k, v (the ONNX card's T includes f16): the float32 path on
+    exact widenings, the output rounded to float16 once."""
+    x = synth.prefill_inputs(760, lengths=[70, 0, 33], hq=2, hv=4, dk=64, dv=64, dtype="f32",
+                             gate="qwen", init_std=0.05)
+    q, k, v = (x[n].half() for n in ("q", "k", "v"))
+    kw = dict(cu_seqlens=to_dev(x["cu_seqlens"]), initial_state=to_dev(x["initial_state"]),
+              scale=x["scale"])
+    okw = dict(cu_seqlens=x["cu_seqlens"], initial_state=x["initial_state"], scale=x["scale"])
+    if fused:
+        a, b = x["a"].half(), x["b"].half()
+        o, f = gdn.prefill(q.cuda(), k.cuda(), v.cuda(), None, None, A_log=to_dev(x["A_log"]),
+                           dt_bias=to_dev(x["dt_bias"]), a=a.cuda(), b=b.cuda(), **kw)
+        ro, rf = oracle.prefill(q, k, v, None, None, A_log=x["A_log"], dt_bias=x["dt_bias"], a=a,
+                                b=b, **okw)
+    else:
+        g, _, beta = oracle.gate(x["A_log"], x["dt_bias"], x["a"], x["b"])
+        dec, bet = torch.from_numpy(g).float(), torch.from_numpy(beta).float()
+        o, f = gdn.prefill(q.cuda(), k.cuda(), v.cuda(), dec.cuda(), bet.cuda(), **kw)
+        ro, rf = oracle.prefill(q, k, v, dec, bet, **okw)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float16
+    e = np.abs(o.double().cpu().numpy() - ro).max() / np.abs(ro).max()
+    assert e <= 2e-3, e  # float32 arithmetic, one float16 rounding (2^-11 relative)
+    assert_close(f, rf, "f32", "final state")
+
+
+def test_decode_float16_inputs_go_through_bfloat16():
+    x = synth.decode_inputs(761, pool_size=20, batch=5, T=3, n_hh=2, hq=2, hv=4, dk=64, dv=64,
+                            dtype="f32", skip_rows=1)
+    h = {n: x[n].half() for n in ("q", "k", "v", "a", "b")}
+    pool = to_dev(x["pool"].clone())
+    out = torch.full((5, 3, 4, 64), 3.0, dtype=torch.float16, device="cuda")
+    o, _ = gdn.decode(h["q"].cuda(), h["k"].cuda(), h["v"].cuda(), to_dev(x["A_log"]),
+                      to_dev(x["dt_bias"]), h["a"].cuda(), h["b"].cuda(), pool,
+                      to_dev(x["read_idx"]), write_idx=to_dev(x["write_idx"]), scale=x["scale"],
+                      out=out)
+    # the oracle on the bfloat16 values the kernel saw
+    bf = {n: t.to(torch.bfloat16) for n, t in h.items()}
+    ro, rp = oracle.decode(bf["q"], bf["k"], bf["v"], x["A_log"], x["dt_bias"], bf["a"], bf["b"],
+                           x["pool"], x["read_idx"], write_idx=x["write_idx"], scale=x["scale"])
+    torch.cuda.synchronize()
+    assert o is out and out.dtype == torch.float16
+    act = (x["read_idx"] >= 0).numpy()
+    assert_close(out[torch.from_numpy(act).cuda()], ro[act], "bf16", "out")
+    assert torch.all(out[torch.from_numpy(~act).cuda()] == 3.0)
+    assert_close(pool, rp, "bf16", "pool")
