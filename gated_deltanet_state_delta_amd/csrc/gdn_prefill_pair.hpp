@@ -15,7 +15,10 @@
 //    i = 2w, 2w+1, of chunk c (right-looking, one lane pair per row) and
 //    shares them through LDS (a counter tells when both halves are there);
 //    both then run [Q; K] S0, the block forward substitution, Y += M U and
-//    the state update, and write the outputs through LDS as 16-byte rows;
+//    the state update; they accumulate the outputs transposed (Y^T, the
+//    MFMA operands swapped), so each lane holds 4 columns of one token and,
+//    after a lane swap between 16-lane rows, stores 16-byte row pieces
+//    straight to memory;
 //  * prep waves 2 and 3 prepare chunk c+1 meanwhile.  Each loads half of the
 //    chunk's Q, K and V rows (two chunks ahead: token-strided loads have a
 //    long latency) and stages them in LDS; after an LDS counter shows both
@@ -30,8 +33,8 @@
 //    a and b when they stage a chunk) and the in-kernel q/k L2 norm (1/|q_t|
 //    and 1/|k_t| from the diagonals of the diagonal Gram tiles, folded into
 //    the per-token factors and the -A and M blocks; q and k stay as given).
-// K^T fragments for the state update, V in accumulator layout and the output
-// rows come from LDS through the gfx950 transposing LDS read
+// K^T fragments for the state update and V in accumulator layout come from
+// LDS through the gfx950 transposing LDS read
 // (ds_read_b64_tr_b16): lane 4a+b of a 16-lane group receives element b of
 // the 8-byte block addressed by lane a+4e as its element e.
 //
@@ -82,9 +85,6 @@ struct PairSmem {
   // (I + A_ii)^-1 of the current chunk, bf16 (blocks 2w, 2w+1 written by
   // state wave w)
   alignas(16) __bf16 tinv[NT][16][LDT];
-  // outputs of state wave w, transposed: column c (of its 32), token t at
-  // yt[w][64 c + 4 ((t / 4) ^ f(c)) + t % 4]
-  alignas(16) __bf16 yt[2][32 * 64];
   int prep_cnt;  // staging halves written by the prep waves so far
   int nrm_cnt;   // norm halves written by the prep waves so far (L2 norm only)
   int inv_cnt;   // inverse halves written by the state waves so far
@@ -94,8 +94,6 @@ struct PairSmem {
 __device__ __forceinline__ int pair_swz(int row, int slot) {
   return slot ^ (((row & 1) << 2) | ((row >> 1) & 3));
 }
-// 8-byte block permutation of an output column (4 tokens per block).
-__device__ __forceinline__ int yt_swz(int col) { return ((col & 3) << 2) | ((col >> 2) & 3); }
 
 typedef __attribute__((address_space(3))) s4 lds_s4;
 
@@ -588,7 +586,6 @@ prefill_pair_kernel(const PrefillParams p) {
                                                 dk_of<NKT>(j, 4 * g));
   }
   const int ost = (int)p.o_st;
-  __bf16* yt = sm.yt[w];
 
   for (int c = -1; c < nch; ++c) {
     if (c >= 0) {
@@ -596,7 +593,8 @@ prefill_pair_kernel(const PrefillParams p) {
       // ---- (I + A_ii)^-1 for blocks 2w, 2w+1; the other wave does the rest
       pair_tri_inverse<Sm::LDT>(sm.adiag[c & 1], sm.tinv, 2 * w, lane);
       if (lane == 0) __hip_atomic_fetch_add(&sm.inv_cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      // ---- R = [Q; K] S0 (state rounded to bf16 as the B operand)
+      // ---- R_K = K S0 and R_Q^T = S0^T Q^T (the state rounded to bf16; the
+      // same fragments serve as B operand for R_K and as A operand for R_Q^T)
       bf8 Sb[NPP][2];
 #pragma unroll
       for (int pp = 0; pp < NPP; ++pp)
@@ -618,17 +616,17 @@ prefill_pair_kernel(const PrefillParams p) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct) {
-            rq[i][ct] = mfma32(rq[i][ct], aq[i], Sb[pp][ct]);
+            rq[i][ct] = mfma32(rq[i][ct], Sb[pp][ct], aq[i]);
             rk[i][ct] = mfma32(rk[i][ct], ak[i], Sb[pp][ct]);
           }
       }
-      // ---- X = beta V - beta Gam R_K ; Y = scale Gam R_Q
+      // ---- X = beta V - beta Gam R_K ; Y^T = scale R_Q^T Gam
       f4 X[4][2], Y[4][2];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const f4 bt = *reinterpret_cast<const f4*>(&B.bet[16 * i + 4 * g]);
         const f4 gb = *reinterpret_cast<const f4*>(&B.gb[16 * i + 4 * g]);
-        const f4 gs = *reinterpret_cast<const f4*>(&B.gs[16 * i + 4 * g]);
+        const float gs = B.gs[16 * i + x];
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           const f4 vv = bf4_to_f4(lds_tr(&B.v[16 * i + 4 * g + te][32 * w + 16 * ct + 4 * ta]));
@@ -703,7 +701,7 @@ prefill_pair_kernel(const PrefillParams p) {
             const bf8 a = cat8(lds_b64(&B.m[16 * i + x][16 * m0 + 4 * g]),
                                lds_b64(&B.m[16 * i + x][16 * m + 4 * g]));
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) Y[i][ct] = mfma32(Y[i][ct], a, cat8(Ub[m0][ct], Ub[m][ct]));
+            for (int ct = 0; ct < 2; ++ct) Y[i][ct] = mfma32(Y[i][ct], cat8(Ub[m0][ct], Ub[m][ct]), a);
           }
 #pragma unroll
           for (int j = 0; j < NKT; ++j) {
@@ -718,35 +716,29 @@ prefill_pair_kernel(const PrefillParams p) {
       const int nvalid = (int)min((int64_t)C, end - tok0);
       __bf16* ob = gout + tok0 * p.o_st + 32 * w;
       if (nvalid == C) {
-        // transpose through LDS: each lane writes 4 tokens of one column,
-        // then reads 16-byte rows (token 16i + x, columns 8g .. 8g+7)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            const int col = 16 * ct + x;
-            *reinterpret_cast<bf4*>(&yt[64 * col + 4 * ((4 * i + g) ^ yt_swz(col))]) = to_bf4(Y[i][ct]);
-          }
+        // Y^T tiles: lane (x, g) holds columns 16 ct + 4 g .. +3 of token
+        // 16 i + x.  Swapping rows 1, 3 of the ct = 0 tile with rows 0, 2 of
+        // the ct = 1 tile (v_permlane16_swap) leaves each lane 8 consecutive
+        // columns, 16 ct' + 8 g' .. +7 with ct' = g & 1, g' = g >> 1.
         const __amdgpu_buffer_rsrc_t rs = buf_rsrc(ob);
-        const uint32_t o_lane = (uint32_t)((x * ost + 8 * g) * 2);
+        const uint32_t o_lane = (uint32_t)((x * ost + 16 * (g & 1) + 8 * (g >> 1)) * 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int c0 = 8 * g + te, c1 = 8 * g + 4 + te;
-          const bf4 lo = lds_tr(&yt[64 * c0 + 4 * ((4 * i + ta) ^ yt_swz(c0))]);
-          const bf4 hi = lds_tr(&yt[64 * c1 + 4 * ((4 * i + ta) ^ yt_swz(c1))]);
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, cat8(lo, hi)), rs, o_lane,
+          const u32x2 p0 = __builtin_bit_cast(u32x2, to_bf4(Y[i][0]));
+          const u32x2 p1 = __builtin_bit_cast(u32x2, to_bf4(Y[i][1]));
+          const auto s0 = __builtin_amdgcn_permlane16_swap(p0[0], p1[0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane16_swap(p0[1], p1[1], false, false);
+          __builtin_amdgcn_raw_buffer_store_b128((u32x4){s0[0], s1[0], s0[1], s1[1]}, rs, o_lane,
                                                  (uint32_t)(16 * i * ost * 2), 0);
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int t = 16 * i + 4 * g + e;
-              if (t < nvalid) ob[(int64_t)t * ost + 16 * ct + x] = (__bf16)Y[i][ct][e];
-            }
+          for (int ct = 0; ct < 2; ++ct) {
+            const int t = 16 * i + x;
+            if (t < nvalid) *reinterpret_cast<bf4*>(ob + (int64_t)t * ost + 16 * ct + 4 * g) = to_bf4(Y[i][ct]);
+          }
       }
     }
     lds_barrier();
