@@ -109,6 +109,8 @@ gdn_status gdn_prefill(const gdn_prefill_args* p, void* stream) {
   if (a.gate_a && (!a.A_log || !a.dt_bias)) return fail(GDN_ERR_NULL, "gdn_prefill: gate_a needs A_log and dt_bias");
   if (a.decay_per_key && (a.gate_a || a.gate_b))
     return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill: decay_per_key takes the decay and beta as given inputs");
+  if (a.decay_per_key && a.update_rule != GDN_RULE_GATED_DELTA && a.update_rule != GDN_RULE_GATED)
+    return fail(GDN_ERR_SHAPE, "gdn_prefill: decay_per_key needs an update_rule with a decay (gated_delta, gated)");
   if (a.state_pool) {
     if (a.initial_state || a.final_state)
       return fail(GDN_ERR_SHAPE, "gdn_prefill: state_pool replaces initial_state and final_state (pass NULL)");

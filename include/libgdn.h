@@ -204,8 +204,9 @@ typedef struct {
    * card's per-key-dimension spelling, in decay_kind's meaning), read in the
    * card's recurrence: each token first scales key column i of the V-major
    * state by its own factor.  Needs a given decay (not gate_a) and given
-   * beta; any update_rule with a decay; runs a separate 16-token-chunk kernel
-   * (fp32 arithmetic), slower than the scalar-decay kernels. */
+   * beta, and an update_rule with a decay (gated_delta or gated; others
+   * return GDN_ERR_SHAPE); runs a separate 16-token-chunk MFMA kernel,
+   * slower than the scalar-decay kernels. */
   int32_t decay_per_key;
 } gdn_prefill_args;
 

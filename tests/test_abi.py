@@ -127,6 +127,8 @@ PREFILL_ERRORS = [
     (dict(read_slot=FAKE * 15), 2),                     # slots without a pool
     (dict(decay_per_key=1, decay=None, beta=None, gate_a=FAKE * 8, A_log=FAKE * 9,
           dt_bias=FAKE * 10, gate_b=FAKE * 11), 5),      # per-key decay takes given inputs
+    (dict(decay_per_key=1, update_rule=2, decay=None), 2),  # per-key decay with a rule without decay
+    (dict(decay_per_key=1, update_rule=3, decay=None, beta=None), 2),
 ]
 
 
