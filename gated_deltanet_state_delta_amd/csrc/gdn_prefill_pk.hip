@@ -55,37 +55,45 @@ namespace gdn {
 // Exceptional-key bound: Gam_{C-1} below 2^-96 (log2 below -96).
 constexpr float kPkLog2Floor = -96.f;
 
+typedef float pk_f2 __attribute__((ext_vector_type(2)));
+
 template <typename E, int DK>
 struct PkSmem {
   static constexpr int C = 16;
   static constexpr int PAD = 16 / sizeof(E);  // 16-byte row skew
   static constexpr int LDK = DK + PAD;        // Qd, Kd rows
   static constexpr int LDC = C + PAD;         // K~^T, M and inverse rows
-  struct Raw {       // one chunk's decayed operands
+  struct Raw {       // one chunk's decayed operands (prepared two chunks ahead)
     E q[C][LDK];     // Qd
     E k[C][LDK];     // Kd
     E kt[DK][LDC];   // K~^T
+    alignas(16) float lam[DK];  // Gam_{C-1} per key
+    alignas(16) float bet[C];   // beta_t (0 on padded tokens)
   };
-  struct Der {       // one chunk's prep results
+  struct Der {       // one chunk's finished Gram results (one chunk ahead)
     E m[C][LDC];     // M (scale and norms folded in), lower triangle
     E tinv[C][LDC];  // (I + A)^-1
-    alignas(16) float bet[C];   // beta_t (0 on padded tokens)
     alignas(16) float gb[C];    // rho beta_t / |k_t|
     alignas(16) float gs[C];    // scale / |q_t|
     alignas(16) float dc[C];    // 1 / |k_t|
-    alignas(16) float lam[DK];  // Gam_{C-1} per key
   };
-  Raw raw[2];
+  struct Part {      // one chunk's per-prep-wave results, for its finishing
+    alignas(16) float gp[4][2][C][C];  // partial tiles [wave][KK | QK][t][s]
+    alignas(16) float np[4][2][C];     // partial |q_t|^2, |k_t|^2
+    uint32_t xmask[4];                 // exceptional keys: bit 8g + e of wave w's word
+  };
+  Raw raw[3];
   Der der[2];
-  // single-buffered: written in part 1, read in part 2 of the same chunk
-  alignas(16) float gp[4][2][C][C];  // partial tiles [wave][KK | QK][t][s]
-  alignas(16) float np[4][2][C];     // partial |q_t|^2, |k_t|^2
-  alignas(16) float adT[C][20];      // A transposed: adT[s][t] = A[t][s]
-  alignas(16) float xq[C][DK];       // exceptional keys: q, k, P, n
+  Part part[2];
+  // the finishing wave's rows of A, split by column parity:
+  // ad[20 r + 8 h + jj] = A[r][2 jj + h]
+  alignas(16) float ad[C * 20];
+  // exceptional keys' q, k, P, n of the chunk being finished (one buffer:
+  // a chunk that has any is finished before the next is prepared)
+  alignas(16) float xq[C][DK];
   alignas(16) float xk[C][DK];
   alignas(16) float xP[C][DK];
   alignas(16) float xn[C][DK];
-  uint32_t xmask[4];                 // exceptional keys: bit 8g + e of wave w's word
 };
 
 // DPP move inside 16-lane rows; lanes without a source lane receive `fill`.
@@ -94,21 +102,18 @@ __device__ __forceinline__ float pk_dpp(float fill, float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// Eight consecutive io elements (16 or 32 bytes) from global memory, as fp32.
-__device__ __forceinline__ void load8(const __bf16* p, float* o) {
-  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+// Eight consecutive io elements: 16 bytes of bf16 or 32 bytes of fp32, kept
+// as loaded (NV 16-byte vectors) and widened to fp32 when used.
+template <typename E> struct Raw8 { static constexpr int NV = sizeof(E) / 2; u32x4 v[NV]; };
+template <typename E>
+__device__ __forceinline__ void load8(const E* p, Raw8<E>& r) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    o[e] = bf16_bits_to_float((uint16_t)((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu)));
+  for (int i = 0; i < Raw8<E>::NV; ++i) r.v[i] = reinterpret_cast<const u32x4*>(p)[i];
 }
-__device__ __forceinline__ void load8(const float* p, float* o) {
-  const f4 a = *reinterpret_cast<const f4*>(p), b = *reinterpret_cast<const f4*>(p + 4);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    o[e] = a[e];
-    o[4 + e] = b[e];
-  }
+__device__ __forceinline__ float elem8(const Raw8<__bf16>& r, int e) {
+  return bf16_bits_to_float((uint16_t)((e & 1) ? (r.v[0][e >> 1] >> 16) : (r.v[0][e >> 1] & 0xffffu)));
 }
+__device__ __forceinline__ float elem8(const Raw8<float>& r, int e) { return __uint_as_float(r.v[e >> 2][e & 3]); }
 
 // Eight fp32 values -> io elements, stored as one row piece (16 or 32 bytes).
 __device__ __forceinline__ void store8(__bf16* p, const float* v) {
@@ -136,6 +141,52 @@ __device__ __forceinline__ f4 mma_k32v(f4 acc, const float* a, const float* b, _
 __device__ __forceinline__ f4 mma_k32v(f4 acc, const float* a, const float* b, float) {
   return mma_k32(acc, f4{a[0], a[1], a[2], a[3]}, f4{a[4], a[5], a[6], a[7]}, f4{b[0], b[1], b[2], b[3]},
                  f4{b[4], b[5], b[6], b[7]});
+}
+
+// (I + A)^-1 of a unit-lower 16x16 block (A strictly lower, in `ad` as laid
+// out above), right-looking: the lane pair (2r, 2r+1) owns row r, lane parity
+// h keeps T[r][j] for j = h mod 2, and T[r][j] = [j == r] - sum_{k > j}
+// T[r][k] A[k][j].  Once T[r][k] is final (its owner passes it to the
+// partner) it updates every j < k; A is strictly lower, so updates of entries
+// j >= k add zero.  Lanes 32..63 repeat lanes 0..31 and store nothing.
+template <typename E, int LDC>
+__device__ __forceinline__ void pk_tri_inverse(const float* ad, E (*tout)[LDC], int lane) {
+  const int r = (lane >> 1) & 15, h = lane & 1;
+  const float* arow = ad + 8 * h;
+  float acc[8];
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) acc[jj] = 2 * jj + h == r ? 1.f : 0.f;
+  // row k of A: entries 2 jj + h for jj < (k + 1) / 2 can be nonzero
+  f4 a[16][2];
+#pragma unroll
+  for (int k = 1; k < 16; ++k) {
+    a[k][0] = *reinterpret_cast<const f4*>(arow + 20 * k);
+    if (k > 8) a[k][1] = *reinterpret_cast<const f4*>(arow + 20 * k + 4);
+  }
+#pragma unroll
+  for (int k = 15; k >= 1; --k) {
+    const float mine = acc[k >> 1];
+    const float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mine), 0xB1, 0xF, 0xF, false));
+    const float tk = (k & 1) == h ? mine : other;
+    auto ak = [&](int jj) -> float { return jj < 4 ? a[k][0][jj] : a[k][1][jj - 4]; };
+    acc[(k - 1) >> 1] -= tk * ak((k - 1) >> 1);  // the entry the next step reads first
+#pragma unroll
+    for (int jj = 0; jj < ((k - 1) >> 1); ++jj) acc[jj] -= tk * ak(jj);
+  }
+  // row r, columns 8h .. 8h+7: even columns from parity 0, odd from parity 1
+  float o[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float lo = acc[q], hi = acc[4 + q];
+    const float sw_lo = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(lo), 0xB1, 0xF, 0xF, false));
+    const float sw_hi = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(hi), 0xB1, 0xF, 0xF, false));
+    o[2 * q] = h == 0 ? lo : sw_hi;
+    o[2 * q + 1] = h == 0 ? sw_lo : hi;
+  }
+  if (lane < 32) {
+    *reinterpret_cast<typename pack4<E>::type*>(&tout[r][8 * h]) = to_pack4<E>(f4{o[0], o[1], o[2], o[3]});
+    *reinterpret_cast<typename pack4<E>::type*>(&tout[r][8 * h + 4]) = to_pack4<E>(f4{o[4], o[5], o[6], o[7]});
+  }
 }
 
 template <typename E, int DK, int DVS>
@@ -186,10 +237,24 @@ prefill_pk_kernel(const PrefillParams p) {
   E* __restrict__ gout = (E*)p.out + (int64_t)h * p.o_sh + v0;
   const float* __restrict__ gdec = p.decay + (int64_t)h * DK;  // [T, hv, DK]
   const float* __restrict__ gbet = p.beta + (h & p.bmask);
+  const bool nrm = p.qk_norm != 0;
+
+  // Whether chunk jc holds exceptional keys (read after the barrier that
+  // follows its preparation; the same in every wave).
+  auto has_exc = [&](int jc) -> bool {
+    if (jc < 0 || jc >= nch) return false;
+    uint32_t any = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) any |= sm.part[jc & 1].xmask[w];
+    return any != 0;
+  };
 
   // ------------------------------------------------------------ state waves
+  // Iteration j: the state pass of chunk j (state waves below NVT) and, on
+  // state wave 3, the finishing of chunk j+1: its partial tiles summed, the
+  // exceptional keys' terms added, -A and M formed, (I + A) inverted.
   if (wave < 4) {
-    const bool active = wave < NVT;  // waves beyond the slice only keep the barriers
+    const bool active = wave < NVT;  // waves beyond the slice only finish and keep the barriers
     const int vc = 16 * wave + x;    // value column inside the slice
     const int vst = (int)p.v_st, ost = (int)p.o_st;
     const int v_lane = 4 * g * vst + x, o_lane = 4 * g * ost + x;
@@ -216,256 +281,91 @@ prefill_pk_kernel(const PrefillParams p) {
         }
       }
     };
-    if (active) {
-      if (ibase >= 0) {
+    // The state pass of chunk c.
+    auto state_pass = [&](int c) {
+      const typename Sm::Raw& R = sm.raw[c % 3];
+      const typename Sm::Der& Dd = sm.der[c & 1];
+      // R = [Qd; Kd] S0; X = beta V - rho beta R_K / |k|; Y = scale R_Q / |q|
+      Fr Sb[NKT];
 #pragma unroll
-        for (int j = 0; j < NKT; ++j)
-          S[j] = *reinterpret_cast<const f4*>(p.init + ibase + (int64_t)vc * DK + dk_of<NKT>(j, 4 * g));
-      }
-      if (nch > 0) load_v(0);
-    }
-    f4 X, Y;
-    for (int c = -1; c < nch; ++c) {
-      const int cur = c & 1;
-      const bool work = active && c >= 0;
-      // ---- part 1: R = [Qd; Kd] S0, X = beta V - rho beta R_K / |k|, Y = scale R_Q / |q|
-      if (work) {
-        const typename Sm::Raw& R = sm.raw[cur];
-        const typename Sm::Der& Dd = sm.der[cur];
-        Fr Sb[NKT];
+      for (int j = 0; j < NKT; ++j) cvt_frag(S[j], Sb[j]);
+      f4 rq = f4{0.f, 0.f, 0.f, 0.f}, rk = rq;
+      if constexpr (NKT % 2 == 0) {
 #pragma unroll
-        for (int j = 0; j < NKT; ++j) cvt_frag(S[j], Sb[j]);
-        f4 rq = f4{0.f, 0.f, 0.f, 0.f}, rk = rq;
-        if constexpr (NKT % 2 == 0) {
-#pragma unroll
-          for (int pp = 0; pp < NKT / 2; ++pp) {
-            Fr aq0, aq1, ak0, ak1;
-            lds_frag8(&R.q[x][32 * pp + 8 * g], aq0, aq1);
-            lds_frag8(&R.k[x][32 * pp + 8 * g], ak0, ak1);
-            rq = mma_k32(rq, aq0, aq1, Sb[2 * pp], Sb[2 * pp + 1]);
-            rk = mma_k32(rk, ak0, ak1, Sb[2 * pp], Sb[2 * pp + 1]);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < NKT; ++j) {
-            Fr aq, ak;
-            lds_frag(&R.q[x][16 * j + 4 * g], aq);
-            lds_frag(&R.k[x][16 * j + 4 * g], ak);
-            rq = mma_k16(rq, aq, Sb[j]);
-            rk = mma_k16(rk, ak, Sb[j]);
-          }
+        for (int pp = 0; pp < NKT / 2; ++pp) {
+          Fr aq0, aq1, ak0, ak1;
+          lds_frag8(&R.q[x][32 * pp + 8 * g], aq0, aq1);
+          lds_frag8(&R.k[x][32 * pp + 8 * g], ak0, ak1);
+          rq = mma_k32(rq, aq0, aq1, Sb[2 * pp], Sb[2 * pp + 1]);
+          rk = mma_k32(rk, ak0, ak1, Sb[2 * pp], Sb[2 * pp + 1]);
         }
-        const f4 bt = *reinterpret_cast<const f4*>(&Dd.bet[4 * g]);
-        const f4 gb = *reinterpret_cast<const f4*>(&Dd.gb[4 * g]);
-        const f4 gs = *reinterpret_cast<const f4*>(&Dd.gs[4 * g]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          X[e] = bt[e] * to_f32(vreg[e]) - gb[e] * rk[e];
-          Y[e] = gs[e] * rq[e];
-        }
-        if (c + 1 < nch) load_v(c + 1);
-      }
-      lds_barrier();
-      // ---- part 2: S <- Gam_{C-1} S; U = (I + A)^-1 X; Y += M U; S += K~^T U / |k|
-      if (work) {
-        const typename Sm::Raw& R = sm.raw[cur];
-        const typename Sm::Der& Dd = sm.der[cur];
-#pragma unroll
-        for (int j = 0; j < NKT; ++j) S[j] = S[j] * *reinterpret_cast<const f4*>(&Dd.lam[dk_of<NKT>(j, 4 * g)]);
-        Fr Pb, ti, Ub, DU, a;
-        cvt_frag(X, Pb);
-        lds_frag(&Dd.tinv[x][4 * g], ti);
-        const f4 U = mma_k16(f4{0.f, 0.f, 0.f, 0.f}, ti, Pb);
-        cvt_frag(U, Ub);
-        cvt_frag(*reinterpret_cast<const f4*>(&Dd.dc[4 * g]) * U, DU);
-        lds_frag(&Dd.m[x][4 * g], a);
-        Y = mma_k16(Y, a, Ub);
+      } else {
 #pragma unroll
         for (int j = 0; j < NKT; ++j) {
-          lds_frag(&R.kt[dk_of<NKT>(j, x)][4 * g], a);
-          S[j] = mma_k16(S[j], a, DU);
-        }
-        const int64_t tok0 = start + (int64_t)c * C;
-        const int nvalid = (int)min((int64_t)C, end - tok0);
-        E* ob = gout + tok0 * p.o_st + 16 * wave;
-        if (nvalid == C) {
-          const __amdgpu_buffer_rsrc_t rs = buf_rsrc(ob);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            buf_store(rs, o_lane * (uint32_t)sizeof(E), e * ost * (uint32_t)sizeof(E), from_f32<E>(Y[e]));
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (4 * g + e < nvalid) ob[(4 * g + e) * ost + x] = from_f32<E>(Y[e]);
+          Fr aq, ak;
+          lds_frag(&R.q[x][16 * j + 4 * g], aq);
+          lds_frag(&R.k[x][16 * j + 4 * g], ak);
+          rq = mma_k16(rq, aq, Sb[j]);
+          rk = mma_k16(rk, ak, Sb[j]);
         }
       }
-      lds_barrier();
-    }
-    if (active && fbase >= 0) {
-#pragma unroll
-      for (int j = 0; j < NKT; ++j)
-        *reinterpret_cast<f4*>(p.fin + fbase + (int64_t)vc * DK + dk_of<NKT>(j, 4 * g)) = S[j];
-    }
-    return;
-  }
-
-  // ------------------------------------------------------------- prep waves
-  const int pw = wave - 4;
-  const int kb = 32 * pw + 8 * g;  // first of this lane's 8 keys
-  const bool keys = kb < DK;       // lanes past the head size hold zeros
-  const bool nrm = p.qk_norm != 0;
-  // the next chunk as loaded (converted when it is used)
-  float pq[8], pk[8], pd[8], pbt = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) pq[e] = pk[e] = pd[e] = 0.f;
-  int prem = 0;
-  auto prefetch = [&](int c) {
-    const int64_t t0 = start + (int64_t)c * C;
-    prem = (int)min((int64_t)C, end - t0);      // >= 1
-    const int64_t tok = t0 + min(x, prem - 1);  // clamped: inside the request
-    if (keys) {
-      load8(gq + tok * p.q_st + kb, pq);
-      load8(gk + tok * p.k_st + kb, pk);
-      const float* dp = gdec + tok * (int64_t)p.hv * DK + kb;
-      const f4 d0 = *reinterpret_cast<const f4*>(dp), d1 = *reinterpret_cast<const f4*>(dp + 4);
+      const f4 bt = *reinterpret_cast<const f4*>(&R.bet[4 * g]);
+      const f4 gb = *reinterpret_cast<const f4*>(&Dd.gb[4 * g]);
+      const f4 gs = *reinterpret_cast<const f4*>(&Dd.gs[4 * g]);
+      f4 X, Y;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pd[e] = d0[e];
-        pd[4 + e] = d1[e];
+        X[e] = bt[e] * to_f32(vreg[e]) - gb[e] * rk[e];
+        Y[e] = gs[e] * rq[e];
       }
-    }
-    if (pw == 0) pbt = gbet[(tok * p.hv) & p.bmask];
-  };
-
-  if (nch > 0 && pw < NW) prefetch(0);
-  for (int c = -1; c < nch; ++c) {
-    const int nxt = (c + 1) & 1;
-    const bool work = c + 1 < nch;
-    float bt = 0.f;  // beta of token x of chunk c+1 (prep wave 4)
-    // ---- part 1: scan, decayed operands, partial Gram tiles and norms
-    if (work && pw < NW) {
-      typename Sm::Raw& R = sm.raw[nxt];
-      typename Sm::Der& Dd = sm.der[nxt];
-      const bool live = x < prem && keys;
-      bt = x < prem ? pbt : 0.f;
-      float P[8], n[8], qf[8], kf[8];
+      if (c + 1 < nch) load_v(c + 1);
+      // S <- Gam_{C-1} S; U = (I + A)^-1 X; Y += M U; S += K~^T U / |k|
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float d = pd[e];
-        bool zero;
-        float l;
-        if (p.decay_is_gamma) {
-          zero = !(d > 0.f);
-          l = zero ? 0.f : __log2f(d);
-        } else {
-          zero = !(d > -INFINITY);
-          l = zero ? 0.f : d * 1.4426950408889634f;
-        }
-        P[e] = live ? l : 0.f;  // padded tokens: no decay
-        n[e] = zero && live ? 1.f : 0.f;
-        qf[e] = live ? pq[e] : 0.f;
-        kf[e] = live ? pk[e] : 0.f;
-      }
-      if (c + 2 < nch) prefetch(c + 2);
-      // segmented inclusive scan over the 16 tokens (the lanes x of a row):
-      // (P, n) of an earlier span and (P', n') of the later one combine to
-      // (n' > 0 ? P' : P + P', n + n')
+      for (int j = 0; j < NKT; ++j) S[j] = S[j] * *reinterpret_cast<const f4*>(&R.lam[dk_of<NKT>(j, 4 * g)]);
+      Fr Pb, ti, Ub, DU, a;
+      cvt_frag(X, Pb);
+      lds_frag(&Dd.tinv[x][4 * g], ti);
+      const f4 U = mma_k16(f4{0.f, 0.f, 0.f, 0.f}, ti, Pb);
+      cvt_frag(U, Ub);
+      cvt_frag(*reinterpret_cast<const f4*>(&Dd.dc[4 * g]) * U, DU);
+      lds_frag(&Dd.m[x][4 * g], a);
+      Y = mma_k16(Y, a, Ub);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float pv = P[e], nv = n[e], pl, nl;
-        pl = pk_dpp<0x111>(0.f, pv);  // row_shr:1
-        nl = pk_dpp<0x111>(0.f, nv);
-        pv = nv > 0.f ? pv : pv + pl;
-        nv += nl;
-        pl = pk_dpp<0x112>(0.f, pv);  // row_shr:2
-        nl = pk_dpp<0x112>(0.f, nv);
-        pv = nv > 0.f ? pv : pv + pl;
-        nv += nl;
-        pl = pk_dpp<0x114>(0.f, pv);  // row_shr:4
-        nl = pk_dpp<0x114>(0.f, nv);
-        pv = nv > 0.f ? pv : pv + pl;
-        nv += nl;
-        pl = pk_dpp<0x118>(0.f, pv);  // row_shr:8
-        nl = pk_dpp<0x118>(0.f, nv);
-        pv = nv > 0.f ? pv : pv + pl;
-        nv += nl;
-        P[e] = pv;
-        n[e] = nv;
+      for (int j = 0; j < NKT; ++j) {
+        lds_frag(&R.kt[dk_of<NKT>(j, x)][4 * g], a);
+        S[j] = mma_k16(S[j], a, DU);
       }
-      float qd[8], kd[8], kt[8], kc[8];
-      uint32_t xbits = 0;
+      const int64_t tok0 = start + (int64_t)c * C;
+      const int nvalid = (int)min((int64_t)C, end - tok0);
+      E* ob = gout + tok0 * p.o_st + 16 * wave;
+      if (nvalid == C) {
+        const __amdgpu_buffer_rsrc_t rs = buf_rsrc(ob);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float PL = pk_dpp<0x15F>(0.f, P[e]), nL = pk_dpp<0x15F>(0.f, n[e]);  // token 15 (row_newbcast)
-        const float gam = n[e] == 0.f ? __builtin_amdgcn_exp2f(P[e]) : 0.f;        // Gam_t
-        const float gct = n[e] == nL ? __builtin_amdgcn_exp2f(PL - P[e]) : 0.f;    // Gam_{C-1/t}
-        const bool exc = nL > 0.f || PL < kPkLog2Floor;                            // same for all tokens
-        const float inv = exc ? 0.f : __builtin_amdgcn_exp2f(-P[e]);               // 1 / Gam_t
-        qd[e] = qf[e] * gam;
-        kd[e] = kf[e] * gam;
-        kt[e] = kf[e] * gct;
-        kc[e] = kf[e] * inv;
-        if (exc) {
-          xbits |= 1u << e;
-          sm.xq[x][kb + e] = qf[e];
-          sm.xk[x][kb + e] = kf[e];
-          sm.xP[x][kb + e] = P[e];
-          sm.xn[x][kb + e] = n[e];
-        }
-        if (keys && x == 0) Dd.lam[kb + e] = nL == 0.f ? __builtin_amdgcn_exp2f(PL) : 0.f;
-      }
-      if (keys) {
-        store8(&R.q[x][kb], qd);
-        store8(&R.k[x][kb], kd);
+        for (int e = 0; e < 4; ++e)
+          buf_store(rs, o_lane * (uint32_t)sizeof(E), e * ost * (uint32_t)sizeof(E), from_f32<E>(Y[e]));
+      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) R.kt[kb + e][x] = from_f32<E>(kt[e]);
+        for (int e = 0; e < 4; ++e)
+          if (4 * g + e < nvalid) ob[(4 * g + e) * ost + x] = from_f32<E>(Y[e]);
       }
-      // exceptional keys of this wave: byte g of the word (the same in every
-      // lane of a row)
-      const uint32_t word = (uint32_t)__builtin_amdgcn_readlane((int)xbits, 0) |
-                            ((uint32_t)__builtin_amdgcn_readlane((int)xbits, 16) << 8) |
-                            ((uint32_t)__builtin_amdgcn_readlane((int)xbits, 32) << 16) |
-                            ((uint32_t)__builtin_amdgcn_readlane((int)xbits, 48) << 24);
-      if (lane == 0) sm.xmask[pw] = word;
-      // partial Gram tiles: lane (x, g) gets rows s = 4g .. 4g+3 of column t = x
-      const f4 zero4 = f4{0.f, 0.f, 0.f, 0.f};
-      const f4 kk = mma_k32v(zero4, kc, kd, E{});
-      const f4 qk = mma_k32v(zero4, kc, qd, E{});
-      *reinterpret_cast<f4*>(&sm.gp[pw][0][x][4 * g]) = kk;
-      *reinterpret_cast<f4*>(&sm.gp[pw][1][x][4 * g]) = qk;
-      if (nrm) {
-        float sq = 0.f, sk = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          sq += qf[e] * qf[e];
-          sk += kf[e] * kf[e];
-        }
-        sq += __shfl_xor(sq, 16);
-        sk += __shfl_xor(sk, 16);
-        sq += __shfl_xor(sq, 32);
-        sk += __shfl_xor(sk, 32);
-        if (g == 0) {
-          sm.np[pw][0][x] = sq;
-          sm.np[pw][1][x] = sk;
-        }
-      }
-    }
-    lds_barrier();
-    // ---- part 2 (prep wave 4): -A, M, the exceptional terms and the inverse
-    if (work && pw == 0) {
-      typename Sm::Der& Dd = sm.der[nxt];
+    };
+    // Finishing of chunk c (state wave 3, all 64 lanes).
+    auto finish = [&](int c) {
+      const typename Sm::Part& Pa = sm.part[c & 1];
+      const typename Sm::Raw& R = sm.raw[c % 3];
+      typename Sm::Der& Dd = sm.der[c & 1];
       const int t = x;
-      f4 kk = *reinterpret_cast<const f4*>(&sm.gp[0][0][t][4 * g]);
-      f4 qk = *reinterpret_cast<const f4*>(&sm.gp[0][1][t][4 * g]);
+      f4 kk = *reinterpret_cast<const f4*>(&Pa.gp[0][0][t][4 * g]);
+      f4 qk = *reinterpret_cast<const f4*>(&Pa.gp[0][1][t][4 * g]);
 #pragma unroll
       for (int w = 1; w < NW; ++w) {
-        kk += *reinterpret_cast<const f4*>(&sm.gp[w][0][t][4 * g]);
-        qk += *reinterpret_cast<const f4*>(&sm.gp[w][1][t][4 * g]);
+        kk += *reinterpret_cast<const f4*>(&Pa.gp[w][0][t][4 * g]);
+        qk += *reinterpret_cast<const f4*>(&Pa.gp[w][1][t][4 * g]);
       }
       // exceptional keys, term by term (s <= t only)
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        uint32_t mk = sm.xmask[w];  // uniform over the wave
+        uint32_t mk = Pa.xmask[w];  // uniform over the wave
         while (mk) {
           const int b = __builtin_ctz(mk);
           mk &= mk - 1;
@@ -489,7 +389,7 @@ prefill_pk_kernel(const PrefillParams p) {
         auto inv_norm = [&](int which, int tt) {
           float s2 = 0.f;
 #pragma unroll
-          for (int w = 0; w < NW; ++w) s2 += sm.np[w][which][tt];
+          for (int w = 0; w < NW; ++w) s2 += Pa.np[w][which][tt];
           s2 += p.qk_eps;
           return s2 > 0.f ? 1.f / sqrtf(s2) : 0.f;
         };
@@ -498,35 +398,231 @@ prefill_pk_kernel(const PrefillParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) rks[e] = inv_norm(1, 4 * g + e);
       }
-      f4 mrow;
+      const float bt = R.bet[t];
+      f4 arow, mrow;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int s = 4 * g + e;
-        sm.adT[s][t] = s < t ? p.rho * bt * rkt * rks[e] * kk[e] : 0.f;
+        arow[e] = s < t ? p.rho * bt * rkt * rks[e] * kk[e] : 0.f;
         mrow[e] = s <= t ? p.scale * rqt * rks[e] * qk[e] : 0.f;
       }
+      // columns 4g, 4g+2 (parity 0) and 4g+1, 4g+3 (parity 1) of row t
+      *reinterpret_cast<pk_f2*>(&sm.ad[20 * t + 2 * g]) = pk_f2{arow[0], arow[2]};
+      *reinterpret_cast<pk_f2*>(&sm.ad[20 * t + 8 + 2 * g]) = pk_f2{arow[1], arow[3]};
       *reinterpret_cast<typename pack4<E>::type*>(&Dd.m[t][4 * g]) = to_pack4<E>(mrow);
       if (g == 0) {
-        Dd.bet[t] = bt;
         Dd.gb[t] = p.rho * bt * rkt;
         Dd.gs[t] = p.scale * rqt;
         Dd.dc[t] = rkt;
-        // row t of (I + A)^-1 by back substitution on the transposed block:
-        // T[t][j] = [j == t] - sum_{k > j} A[k][j] T[t][k], j = 15 .. 0
-        float row[16];
+      }
+      pk_tri_inverse<E, Sm::LDC>(sm.ad, Dd.tinv, lane);
+    };
+
+    if (active) {
+      if (ibase >= 0) {
 #pragma unroll
-        for (int j = 15; j >= 0; --j) {
-          float acc = j == t ? 1.f : 0.f;
+        for (int j = 0; j < NKT; ++j)
+          S[j] = *reinterpret_cast<const f4*>(p.init + ibase + (int64_t)vc * DK + dk_of<NKT>(j, 4 * g));
+      }
+      if (nch > 0) load_v(0);
+    }
+    for (int j = -2; j < nch; ++j) {
+      const bool fin = wave == 3 && j + 1 >= 0 && j + 1 < nch;
+      if (has_exc(j + 1)) {
+        // the prep waves overwrite the exceptional keys' values only after
+        // chunk j+1 has been finished
+        if (fin) finish(j + 1);
+        lds_barrier();
+        if (active && j >= 0) state_pass(j);
+      } else {
+        if (active && j >= 0) state_pass(j);
+        if (fin) finish(j + 1);
+      }
+      lds_barrier();
+    }
+    if (active && fbase >= 0) {
 #pragma unroll
-          for (int k = j + 1; k < 16; ++k) acc -= sm.adT[j][k] * row[k];
-          row[j] = acc;
-        }
+      for (int j = 0; j < NKT; ++j)
+        *reinterpret_cast<f4*>(p.fin + fbase + (int64_t)vc * DK + dk_of<NKT>(j, 4 * g)) = S[j];
+    }
+    return;
+  }
+
+  // ------------------------------------------------------------- prep waves
+  // Iteration j prepares chunk j+2.
+  const int pw = wave - 4;
+  const int kb = 32 * pw + 8 * g;  // first of this lane's 8 keys
+  const bool keys = kb < DK;       // lanes past the head size hold zeros
+  // the next chunk exactly as loaded: nothing here may wait on these loads
+  // (they are converted when the chunk is prepared, an iteration later)
+  Raw8<E> pq, pk;
+  Raw8<float> pd;
+  float pbt = 0.f;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<typename pack4<E>::type*>(&Dd.tinv[t][4 * q4]) =
-              to_pack4<E>(f4{row[4 * q4], row[4 * q4 + 1], row[4 * q4 + 2], row[4 * q4 + 3]});
+  for (int i = 0; i < Raw8<E>::NV; ++i) pq.v[i] = pk.v[i] = u32x4{0u, 0u, 0u, 0u};
+  pd.v[0] = pd.v[1] = u32x4{0u, 0u, 0u, 0u};
+  int prem = 0;
+  auto prefetch = [&](int c) {
+    const int64_t t0 = start + (int64_t)c * C;
+    prem = (int)min((int64_t)C, end - t0);      // >= 1
+    const int64_t tok = t0 + min(x, prem - 1);  // clamped: inside the request
+    if (keys) {
+      load8(gq + tok * p.q_st + kb, pq);
+      load8(gk + tok * p.k_st + kb, pk);
+      load8(gdec + tok * (int64_t)p.hv * DK + kb, pd);
+    }
+    if (pw == 0) pbt = gbet[(tok * p.hv) & p.bmask];
+  };
+  // Preparation of chunk c from the prefetched registers.
+  auto prepare = [&](int c) {
+    typename Sm::Raw& R = sm.raw[c % 3];
+    typename Sm::Part& Pa = sm.part[c & 1];
+    const bool live = x < prem && keys;
+    if (pw == 0 && g == 0) R.bet[x] = x < prem ? pbt : 0.f;
+    float P[8], n[8], qf[8], kf[8];
+    if (p.decay_is_gamma) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = elem8(pd, e);
+        const bool zero = !(d > 0.f);
+        P[e] = live && !zero ? __log2f(d) : 0.f;  // padded tokens: no decay
+        n[e] = live && zero ? 1.f : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = elem8(pd, e);
+        const bool zero = !(d > -INFINITY);
+        P[e] = live && !zero ? d * 1.4426950408889634f : 0.f;
+        n[e] = live && zero ? 1.f : 0.f;
       }
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qf[e] = live ? elem8(pq, e) : 0.f;
+      kf[e] = live ? elem8(pk, e) : 0.f;
+    }
+    if (c + 1 < nch) prefetch(c + 1);
+    // inclusive scan over the 16 tokens (the lanes x of a row).  With a zero
+    // decay in the wave it is segmented: (P, n) of an earlier span and
+    // (P', n') of the later one combine to (n' > 0 ? P' : P + P', n + n').
+    bool lz = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lz = lz || n[e] > 0.f;
+    if (__builtin_amdgcn_ballot_w64(lz) != 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float pv = P[e], nv = n[e], pl, nl;
+        pl = pk_dpp<0x111>(0.f, pv);  // row_shr:1
+        nl = pk_dpp<0x111>(0.f, nv);
+        pv = nv > 0.f ? pv : pv + pl;
+        nv += nl;
+        pl = pk_dpp<0x112>(0.f, pv);  // row_shr:2
+        nl = pk_dpp<0x112>(0.f, nv);
+        pv = nv > 0.f ? pv : pv + pl;
+        nv += nl;
+        pl = pk_dpp<0x114>(0.f, pv);  // row_shr:4
+        nl = pk_dpp<0x114>(0.f, nv);
+        pv = nv > 0.f ? pv : pv + pl;
+        nv += nl;
+        pl = pk_dpp<0x118>(0.f, pv);  // row_shr:8
+        nl = pk_dpp<0x118>(0.f, nv);
+        pv = nv > 0.f ? pv : pv + pl;
+        nv += nl;
+        P[e] = pv;
+        n[e] = nv;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float pv = P[e];
+        pv += pk_dpp<0x111>(0.f, pv);
+        pv += pk_dpp<0x112>(0.f, pv);
+        pv += pk_dpp<0x114>(0.f, pv);
+        pv += pk_dpp<0x118>(0.f, pv);
+        P[e] = pv;
+      }
+    }
+    // factors (token 15's values broadcast along the row, row_newbcast)
+    float qd[8], kd[8], kt[8], kc[8], PL[8], nL[8];
+    bool exc_l = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      PL[e] = pk_dpp<0x15F>(0.f, P[e]);
+      nL[e] = pk_dpp<0x15F>(0.f, n[e]);
+      const float gam = n[e] == 0.f ? __builtin_amdgcn_exp2f(P[e]) : 0.f;  // Gam_t
+      qd[e] = qf[e] * gam;
+      kd[e] = kf[e] * gam;
+      if (keys && x == C - 1) R.lam[kb + e] = gam;  // Gam_{C-1}
+      kt[e] = gam;
+      exc_l = exc_l || nL[e] > 0.f || PL[e] < kPkLog2Floor;  // the same for all tokens
+    }
+    uint32_t xbits = 0;
+    if (__builtin_amdgcn_ballot_w64(exc_l) == 0) {
+      // no exceptional key: Gam_{C-1/t} = Gam_{C-1} / Gam_t
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float inv = __builtin_amdgcn_exp2f(-P[e]);  // 1 / Gam_t
+        kc[e] = kf[e] * inv;
+        kt[e] = kf[e] * (pk_dpp<0x15F>(0.f, kt[e]) * inv);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool exc = nL[e] > 0.f || PL[e] < kPkLog2Floor;
+        const float gct = n[e] == nL[e] ? __builtin_amdgcn_exp2f(PL[e] - P[e]) : 0.f;  // Gam_{C-1/t}
+        kc[e] = exc ? 0.f : kf[e] * __builtin_amdgcn_exp2f(-P[e]);
+        kt[e] = kf[e] * gct;
+        if (exc) {
+          xbits |= 1u << e;
+          sm.xq[x][kb + e] = qf[e];
+          sm.xk[x][kb + e] = kf[e];
+          sm.xP[x][kb + e] = P[e];
+          sm.xn[x][kb + e] = n[e];
+        }
+      }
+    }
+    if (keys) {
+      store8(&R.q[x][kb], qd);
+      store8(&R.k[x][kb], kd);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) R.kt[kb + e][x] = from_f32<E>(kt[e]);
+    }
+    // exceptional keys of this wave: byte g of the word (the same in every
+    // lane of a row)
+    const uint32_t word = (uint32_t)__builtin_amdgcn_readlane((int)xbits, 0) |
+                          ((uint32_t)__builtin_amdgcn_readlane((int)xbits, 16) << 8) |
+                          ((uint32_t)__builtin_amdgcn_readlane((int)xbits, 32) << 16) |
+                          ((uint32_t)__builtin_amdgcn_readlane((int)xbits, 48) << 24);
+    if (lane == 0) Pa.xmask[pw] = word;
+    // partial Gram tiles: lane (x, g) gets rows s = 4g .. 4g+3 of column t = x
+    const f4 zero4 = f4{0.f, 0.f, 0.f, 0.f};
+    const f4 kk = mma_k32v(zero4, kc, kd, E{});
+    const f4 qk = mma_k32v(zero4, kc, qd, E{});
+    *reinterpret_cast<f4*>(&Pa.gp[pw][0][x][4 * g]) = kk;
+    *reinterpret_cast<f4*>(&Pa.gp[pw][1][x][4 * g]) = qk;
+    if (nrm) {
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sq += qf[e] * qf[e];
+        sk += kf[e] * kf[e];
+      }
+      sq += __shfl_xor(sq, 16);
+      sk += __shfl_xor(sk, 16);
+      sq += __shfl_xor(sq, 32);
+      sk += __shfl_xor(sk, 32);
+      if (g == 0) {
+        Pa.np[pw][0][x] = sq;
+        Pa.np[pw][1][x] = sk;
+      }
+    }
+  };
+
+  if (nch > 0 && pw < NW) prefetch(0);
+  for (int j = -2; j < nch; ++j) {
+    if (has_exc(j + 1)) lds_barrier();  // see the state waves' loop
+    if (j + 2 < nch && pw < NW) prepare(j + 2);
     lds_barrier();
   }
 }
