@@ -2,7 +2,9 @@
 scales the key rows of the state) through the C ABI, against the fp64
 oracle: the prefill's per-key kernel (ragged requests with empty, one-token
 and partial-chunk requests, initial states, both rules with a decay, exact
-zero decays, gamma input, in-kernel L2 norm, pooled states, odd head sizes)
+zero decays and decays below 2^-96 per chunk -- the keys the kernel sums
+term by term --, gamma input, in-kernel L2 norm, pooled states, odd head
+sizes)
 and the decode's token loop (single step, staged multi-token with sub-steps,
 per-token scatter), and decode against prefill from the same slot.
 """
@@ -83,6 +85,25 @@ def test_prefill_per_key_edge_cases(mode):
     torch.cuda.synchronize()
     assert_close(o, ro, "f32", "out %s" % mode)
     assert_close(f, rf, "f32", "final %s" % mode)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_per_key_extreme_decays(dtype):
+    """Keys whose decay over a 16-token chunk falls below 2^-96 (no zero
+    among them) mixed with ordinary keys: the kernel adds the former term by
+    term instead of through the factored Gram tile, and must match."""
+    x, dec = _pk_case(1150, dtype, 128, 64)
+    g = torch.Generator().manual_seed(1151)
+    wild = torch.rand(dec.shape[1:], generator=g) < 0.3          # per (head, key)
+    dec = torch.where(wild, -torch.rand(dec.shape, generator=g) * 14.0, dec)
+    o, f = gdn.prefill(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(dec), to_dev(x["beta"]),
+                       cu_seqlens=to_dev(x["cu_seqlens"]), initial_state=to_dev(x["initial_state"]),
+                       scale=x["scale"], decay_per_key=True)
+    ro, rf = oracle.prefill(x["q"], x["k"], x["v"], dec, x["beta"], cu_seqlens=x["cu_seqlens"],
+                            initial_state=x["initial_state"], scale=x["scale"], decay_per_key=True)
+    torch.cuda.synchronize()
+    assert_close(o, ro, dtype, "out")
+    assert_close(f, rf, dtype, "final state")
 
 
 def test_prefill_per_key_pool_and_odd_head_sizes():
