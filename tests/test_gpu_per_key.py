@@ -191,3 +191,70 @@ def test_decode_per_key_equals_prefill_from_the_slot():
     active = (x["read_idx"] >= 0).cuda()
     assert_close(op.view(B, T, 4, 64)[active], od[active].double().cpu().numpy(), "f32", "out")
     assert_close(pool_b, pool_a.double().cpu().numpy(), "f32", "pool")
+
+
+def _pk_random(i):
+    import random
+    r = random.Random(7000 + i)
+    dtype = r.choice(["bf16", "f32"])
+    dk, dv = r.choice([16, 32, 64, 128]), r.choice([16, 32, 64, 128])
+    hq = r.choice([1, 2])
+    hv = hq * r.choice([1, 2])
+    lengths = [r.choice([0, 1, r.randint(2, 40), r.randint(41, 120)]) for _ in range(r.randint(1, 4))]
+    if sum(lengths) == 0:
+        lengths[0] = 9
+    return dict(dtype=dtype, dk=dk, dv=dv, hq=hq, hv=hv, lengths=lengths,
+                rule=r.choice(["gated_delta", "gated"]), norm=r.random() < 0.3, pool=r.random() < 0.4,
+                gamma=r.random() < 0.3, zeros=r.choice([0.0, 0.0, 0.02, 0.2]),
+                wild=r.choice([0.0, 0.0, 0.1, 0.5]))
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_prefill_per_key_random_configuration(i):
+    """Seeded cross-feature per-key configurations: io dtype, head sizes, GVA,
+    ragged lengths, rule, in-kernel L2 norm, pooled or dense states, log or
+    gamma decays, exact zero decays and keys decaying below 2^-96 per chunk."""
+    c = _pk_random(i)
+    x = synth.prefill_inputs(7100 + i, lengths=c["lengths"], hq=c["hq"], hv=c["hv"], dk=c["dk"], dv=c["dv"],
+                             dtype=c["dtype"], gate="log", init_std=0.05)
+    g = torch.Generator().manual_seed(7200 + i)
+    T, hv, dk, dv, n = x["T"], c["hv"], c["dk"], c["dv"], len(c["lengths"])
+    dec = -torch.rand(T, hv, dk, generator=g) * 0.6
+    wild = torch.rand(hv, dk, generator=g) < c["wild"]
+    dec = torch.where(wild, -torch.rand(T, hv, dk, generator=g) * 12.0, dec)
+    dec[torch.rand(T, hv, dk, generator=g) < c["zeros"]] = -float("inf")
+    kw, okw = {}, {}
+    if c["gamma"]:
+        dec = torch.exp(dec)
+        kw["decay_kind"] = "gamma"
+        okw["decay_is_gamma"] = True
+    if c["norm"]:
+        x["q"] = (x["q"].float() * (torch.rand(T, c["hq"], 1, generator=g) * 3 + 0.3)).to(x["q"].dtype)
+        x["k"] = (x["k"].float() * (torch.rand(T, c["hq"], 1, generator=g) * 3 + 0.3)).to(x["k"].dtype)
+        kw["qk_l2norm"] = True
+        okw["qk_l2norm_eps"] = 1e-12
+    bet = x["beta"] if c["rule"] == "gated_delta" else None
+    args = (to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(dec), to_dev(bet))
+    oargs = (x["q"], x["k"], x["v"], dec, bet)
+    common = dict(scale=x["scale"], update_rule=c["rule"], decay_per_key=True)
+    if c["pool"]:
+        P = n + 3
+        pool0 = torch.randn(P, hv, dv, dk, generator=g) * 0.05
+        slots = torch.randperm(P, generator=g)[:n].to(torch.int32)
+        pool = to_dev(pool0.clone())
+        o, _ = gdn.prefill(*args, cu_seqlens=to_dev(x["cu_seqlens"]), state_pool=pool,
+                           read_slot=to_dev(slots), **common, **kw)
+        init = np.stack([pool0[s].numpy() for s in slots.tolist()])
+        ro, rf = oracle.prefill(*oargs, cu_seqlens=x["cu_seqlens"], initial_state=init, **common, **okw)
+        torch.cuda.synchronize()
+        assert_close(o, ro, c["dtype"], "out %s" % c)
+        for r_, s_ in enumerate(slots.tolist()):
+            assert_close(pool[s_], rf[r_], c["dtype"], "slot %d %s" % (s_, c))
+    else:
+        o, f = gdn.prefill(*args, cu_seqlens=to_dev(x["cu_seqlens"]), initial_state=to_dev(x["initial_state"]),
+                           **common, **kw)
+        ro, rf = oracle.prefill(*oargs, cu_seqlens=x["cu_seqlens"], initial_state=x["initial_state"],
+                                **common, **okw)
+        torch.cuda.synchronize()
+        assert_close(o, ro, c["dtype"], "out %s" % c)
+        assert_close(f, rf, c["dtype"], "final %s" % c)
