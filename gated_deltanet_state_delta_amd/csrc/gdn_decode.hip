@@ -262,7 +262,7 @@ static hipError_t dispatch_dk(const DecodeParams& p, int dk, int dv, hipStream_t
 // hint follows T (16, 32, 64).  Every activation must be 16-byte aligned,
 // as the prefill kernels require.
 static bool decode_as_prefill(const gdn_decode_args& a) {
-  if (a.T < 16 || a.n_householder != 1 || a.scatter_idx || a.decay_per_key) return false;
+  if (a.T < 16 || a.n_householder != 1 || a.scatter_idx) return false;
   if ((int64_t)a.batch * a.T * a.hv >= (int64_t(1) << 31)) return false;
   const void* ptrs[] = {a.q, a.k, a.v, a.out};
   for (const void* q : ptrs)
@@ -285,7 +285,14 @@ static hipError_t launch_decode_chunked(const gdn_decode_args& a, hipStream_t st
   pa.v = a.v; pa.v_stride_token = (int64_t)a.hv * a.dv; pa.v_stride_head = a.dv;
   pa.out = a.out; pa.out_stride_token = (int64_t)a.hv * a.dv; pa.out_stride_head = a.dv;
   pa.qk_l2norm = a.qk_l2norm; pa.qk_l2norm_eps = a.qk_l2norm_eps;
-  pa.A_log = a.A_log; pa.dt_bias = a.dt_bias; pa.gate_a = a.a; pa.gate_b = a.b;
+  if (a.decay_per_key) {
+    // per-key decay: given (log space, [batch * T, hv, dk]), beta fused from b
+    pa.decay = a.decay_per_key;
+    pa.decay_per_key = 1;
+    pa.gate_b = a.b;
+  } else {
+    pa.A_log = a.A_log; pa.dt_bias = a.dt_bias; pa.gate_a = a.a; pa.gate_b = a.b;
+  }
   pa.update_rule = GDN_RULE_GATED_DELTA;
   pa.state_pool = a.pool; pa.pool_size = a.pool_size;
   pa.pool_slot_stride = a.pool_slot_stride; pa.pool_head_stride = a.pool_head_stride;

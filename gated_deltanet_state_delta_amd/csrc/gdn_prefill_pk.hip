@@ -236,7 +236,11 @@ prefill_pk_kernel(const PrefillParams p) {
   const E* __restrict__ gv = (const E*)p.v + (int64_t)h * p.v_sh + v0;
   E* __restrict__ gout = (E*)p.out + (int64_t)h * p.o_sh + v0;
   const float* __restrict__ gdec = p.decay + (int64_t)h * DK;  // [T, hv, DK]
-  const float* __restrict__ gbet = p.beta + (h & p.bmask);
+  // beta given, or fused as sigmoid(b) from the raw b (the multi-token
+  // decode's gate, which runs this kernel over its state pool)
+  const bool fused_b = p.gb != nullptr;
+  const float* __restrict__ gbet = fused_b ? nullptr : p.beta + (h & p.bmask);
+  const E* __restrict__ ggb = fused_b ? (const E*)p.gb + (h & p.bmask) : nullptr;
   const bool nrm = p.qk_norm != 0;
 
   // Whether chunk jc holds exceptional keys (read after the barrier that
@@ -458,6 +462,7 @@ prefill_pk_kernel(const PrefillParams p) {
   Raw8<E> pq, pk;
   Raw8<float> pd;
   float pbt = 0.f;
+  E pbr = from_f32<E>(0.f);
 #pragma unroll
   for (int i = 0; i < Raw8<E>::NV; ++i) pq.v[i] = pk.v[i] = u32x4{0u, 0u, 0u, 0u};
   pd.v[0] = pd.v[1] = u32x4{0u, 0u, 0u, 0u};
@@ -471,14 +476,17 @@ prefill_pk_kernel(const PrefillParams p) {
       load8(gk + tok * p.k_st + kb, pk);
       load8(gdec + tok * (int64_t)p.hv * DK + kb, pd);
     }
-    if (pw == 0) pbt = gbet[(tok * p.hv) & p.bmask];
+    if (pw == 0) {
+      if (fused_b) pbr = ggb[(tok * p.hv) & p.bmask];
+      else pbt = gbet[(tok * p.hv) & p.bmask];
+    }
   };
   // Preparation of chunk c from the prefetched registers.
   auto prepare = [&](int c) {
     typename Sm::Raw& R = sm.raw[c % 3];
     typename Sm::Part& Pa = sm.part[c & 1];
     const bool live = x < prem && keys;
-    if (pw == 0 && g == 0) R.bet[x] = x < prem ? pbt : 0.f;
+    if (pw == 0 && g == 0) R.bet[x] = x < prem ? (fused_b ? sigmoid_fast(to_f32(pbr)) : pbt) : 0.f;
     float P[8], n[8], qf[8], kf[8];
     if (p.decay_is_gamma) {
 #pragma unroll

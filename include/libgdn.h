@@ -255,8 +255,9 @@ gdn_status gdn_prefill(const gdn_prefill_args* args, void* stream);
  * 1 <= n_householder <= 4; batch == 0 is a no-op.
  * With T >= 16, n_householder == 1, no scatter_idx and q, k, v, out 16-byte
  * aligned, the call runs the chunked form of the same recurrence (the
- * prefill kernels over the pool, one request per row): same results up to
- * rounding order, same skip / write / disable rules.
+ * prefill kernels over the pool, one request per row; the per-key prefill
+ * kernel when decay_per_key is given): same results up to rounding order,
+ * same skip / write / disable rules.
  * ------------------------------------------------------------------------- */
 typedef struct {
   int32_t batch, T, n_householder;

@@ -5,8 +5,10 @@ and partial-chunk requests, initial states, both rules with a decay, exact
 zero decays and decays below 2^-96 per chunk -- the keys the kernel sums
 term by term --, gamma input, in-kernel L2 norm, pooled states, odd head
 sizes)
-and the decode's token loop (single step, staged multi-token with sub-steps,
-per-token scatter), and decode against prefill from the same slot.
+and the decode (single step, staged multi-token with sub-steps, per-token
+scatter in the token loop; 16 or more tokens per row in the chunked form,
+with and without write-back and with the L2 norm), and decode against
+prefill from the same slot.
 """
 import numpy as np
 import pytest
@@ -153,7 +155,8 @@ def _decode_pk(seed, dtype, T, n, scatter, dk=128, dv=64):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("T,n,scatter", [(1, 1, False), (3, 2, False), (4, 1, True), (20, 1, False)])
+@pytest.mark.parametrize("T,n,scatter", [(1, 1, False), (3, 2, False), (4, 1, True), (20, 1, False),
+                                         (16, 1, False), (33, 1, False), (64, 1, False)])
 def test_decode_per_key_matches_oracle(dtype, T, n, scatter):
     x, dec = _decode_pk(1300 + T * 10 + n, dtype, T, n, scatter)
     pool = to_dev(x["pool"].clone())
@@ -171,6 +174,32 @@ def test_decode_per_key_matches_oracle(dtype, T, n, scatter):
     assert_close(pool, rp, dtype, "decode pool")
     skipped = torch.from_numpy(~active).cuda()
     assert torch.all(out[skipped] == 0)
+
+
+@pytest.mark.parametrize("mode", ["disable", "qk_l2norm"])
+def test_decode_per_key_chunked_modes(mode):
+    """The multi-token decode with a per-key decay in its chunked form (T >= 16):
+    no state write-back, and the in-kernel q/k L2 norm."""
+    x, dec = _decode_pk(1500 + len(mode), "bf16", 24, 1, False)
+    kw = dict(disable_state_update=True) if mode == "disable" else dict(use_qk_l2norm=True, qk_l2norm_eps=1e-12)
+    okw = dict(disable_state_update=True) if mode == "disable" else dict(qk_l2norm_eps=1e-12)
+    if mode == "qk_l2norm":
+        x["q"] = x["q"] * 2.5
+        x["k"] = x["k"] * 0.5
+    pool = to_dev(x["pool"].clone())
+    out = torch.zeros(6, 24, 4, 64, dtype=torch.bfloat16, device="cuda")
+    gdn.decode(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), None, None, None, to_dev(x["b"]),
+               pool, to_dev(x["read_idx"]), write_idx=to_dev(x["write_idx"]), scale=x["scale"], out=out,
+               decay_per_key=to_dev(dec), **kw)
+    ro, rp = oracle.decode(x["q"], x["k"], x["v"], None, None, None, x["b"], x["pool"], x["read_idx"],
+                           write_idx=x["write_idx"], scale=x["scale"], decay_per_key=dec, **okw)
+    torch.cuda.synchronize()
+    active = (x["read_idx"] >= 0).numpy()
+    assert_close(out[torch.from_numpy(active).cuda()], ro[active], "bf16", "decode out")
+    if mode == "disable":
+        assert torch.equal(pool.cpu(), x["pool"])
+    else:
+        assert_close(pool, rp, "bf16", "decode pool")
 
 
 def test_decode_per_key_equals_prefill_from_the_slot():
