@@ -31,19 +31,25 @@
 // -inf - (-inf) is ever formed.
 //
 // Mapping.  One workgroup of 8 waves per (request, value head, slice of DVS
-// <= 64 value columns), walking the request's chunks in order with two
-// workgroup barriers per chunk:
-//  * state waves 0..3 each own one 16-column tile of the slice and keep the
-//    state in MFMA accumulators.  Part 1: R = [Qd; Kd] S0, X, Y.  Part 2: the
-//    per-key row scale, U = (I + A)^-1 X, Y += M U, S += K~^T U, the outputs;
-//  * prep waves 4..7 prepare the next chunk.  Prep wave w holds keys
-//    32w .. 32w+31 of all 16 tokens in MFMA fragment layout (lane (x, g):
-//    token x, keys 32w + 8g .. +7), so the per-key scan over tokens is a DPP
-//    scan inside 16-lane rows.  Part 1: the scan, the decayed operands (Qd,
-//    Kd and K~^T to LDS), the wave's partial Gram tiles Kc Kd^T and Kc Qd^T
-//    (one MFMA each: rows s, columns t), the raw values of exceptional keys
-//    and partial row norms.  Part 2 (prep wave 4): the partial tiles summed,
-//    the exceptional keys' terms added, -A and M formed, (I + A) inverted.
+// <= 64 value columns) walks the request's chunks in order, one workgroup
+// barrier per chunk; in iteration j:
+//  * prep waves 4..7 prepare chunk j+2.  Prep wave w holds keys 32w .. 32w+31
+//    of all 16 tokens in MFMA fragment layout (lane (x, g): token x, keys
+//    32w + 8g .. +7), so the per-key scan over tokens is a DPP scan inside
+//    16-lane rows.  It writes the decayed operands (Qd, Kd, K~^T, Gam_{C-1})
+//    to one of three LDS buffers and its partial Gram tiles Kc Kd^T and
+//    Kc Qd^T (one MFMA each: rows s, columns t), row norms and the raw values
+//    of exceptional keys for the finishing step;
+//  * state wave 3 finishes chunk j+1: the partial tiles summed, the
+//    exceptional keys' terms added, -A and M formed, (I + A) inverted;
+//  * state waves 0..3 each own one 16-column tile of the slice, keep the
+//    state in MFMA accumulators and run the state pass of chunk j:
+//    R = [Qd; Kd] S0, X, Y, the per-key row scale, U = (I + A)^-1 X,
+//    Y += M U, S += K~^T U, the outputs.
+// A chunk with exceptional keys adds one barrier, so that the next chunk's
+// raw values (one LDS buffer) are written only after it has been finished.
+// The same kernel runs the multi-token decode's chunked form over its state
+// pool, with beta formed here as sigmoid(b) from the raw b.
 // Operand precision: bf16 inputs use bf16 MFMA operands (the decayed q and k
 // are rounded once to bf16); the state, accumulators, decays and the inverse
 // are fp32.  fp32 inputs use fp32 MFMA.
