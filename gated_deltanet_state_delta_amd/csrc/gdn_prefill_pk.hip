@@ -195,7 +195,8 @@ __device__ __forceinline__ void pk_tri_inverse(const float* ad, E (*tout)[LDC], 
   }
 }
 
-template <typename E, int DK, int DVS>
+// FB: beta fused as sigmoid(b) from the raw b (p.gb), else given (p.beta).
+template <typename E, int DK, int DVS, bool FB>
 __global__ void __launch_bounds__(512)
 prefill_pk_kernel(const PrefillParams p) {
   typedef typename frag_of<E>::type Fr;
@@ -244,9 +245,8 @@ prefill_pk_kernel(const PrefillParams p) {
   const float* __restrict__ gdec = p.decay + (int64_t)h * DK;  // [T, hv, DK]
   // beta given, or fused as sigmoid(b) from the raw b (the multi-token
   // decode's gate, which runs this kernel over its state pool)
-  const bool fused_b = p.gb != nullptr;
-  const float* __restrict__ gbet = fused_b ? nullptr : p.beta + (h & p.bmask);
-  const E* __restrict__ ggb = fused_b ? (const E*)p.gb + (h & p.bmask) : nullptr;
+  const float* __restrict__ gbet = FB ? nullptr : p.beta + (h & p.bmask);
+  const E* __restrict__ ggb = FB ? (const E*)p.gb + (h & p.bmask) : nullptr;
   const bool nrm = p.qk_norm != 0;
 
   // Whether chunk jc holds exceptional keys (read after the barrier that
@@ -483,7 +483,7 @@ prefill_pk_kernel(const PrefillParams p) {
       load8(gdec + tok * (int64_t)p.hv * DK + kb, pd);
     }
     if (pw == 0) {
-      if (fused_b) pbr = ggb[(tok * p.hv) & p.bmask];
+      if constexpr (FB) pbr = ggb[(tok * p.hv) & p.bmask];
       else pbt = gbet[(tok * p.hv) & p.bmask];
     }
   };
@@ -492,7 +492,7 @@ prefill_pk_kernel(const PrefillParams p) {
     typename Sm::Raw& R = sm.raw[c % 3];
     typename Sm::Part& Pa = sm.part[c & 1];
     const bool live = x < prem && keys;
-    if (pw == 0 && g == 0) R.bet[x] = x < prem ? (fused_b ? sigmoid_fast(to_f32(pbr)) : pbt) : 0.f;
+    if (pw == 0 && g == 0) R.bet[x] = x < prem ? (FB ? sigmoid_fast(to_f32(pbr)) : pbt) : 0.f;
     float P[8], n[8], qf[8], kf[8];
     if (p.decay_is_gamma) {
 #pragma unroll
@@ -645,7 +645,8 @@ template <typename E, int DK, int DVS>
 static hipError_t launch_pk_t(PrefillParams p, hipStream_t stream) {
   p.nsplit = p.dv / DVS;
   const int64_t nblk = (int64_t)p.n_seqs * p.hv * p.nsplit;
-  hipLaunchKernelGGL((prefill_pk_kernel<E, DK, DVS>), dim3((unsigned)nblk), dim3(512), 0, stream, p);
+  if (p.gb) hipLaunchKernelGGL((prefill_pk_kernel<E, DK, DVS, true>), dim3((unsigned)nblk), dim3(512), 0, stream, p);
+  else hipLaunchKernelGGL((prefill_pk_kernel<E, DK, DVS, false>), dim3((unsigned)nblk), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
