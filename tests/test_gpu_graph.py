@@ -1,9 +1,10 @@
 """Every libgdn call can be captured in a HIP graph: no call reads device data
-on the host, synchronises or allocates.  The calls (gate, prefill with the
+on the host, synchronises or allocates.  The calls (gate; prefill with the
 pair-role and general kernels and an update_rule that reads the per-device
-gate constant, decode with the token loop and the chunked form, conv1d) are
-captured once into a torch CUDA graph and replayed three times, with eager
-work in between; every replay must reproduce the eager results bit for bit.
+gate constant; decode with the token loop and the chunked form; conv1d; the
+per-key prefill and the chunked per-key decode) are captured once into a
+torch CUDA graph and replayed three times, with eager work in between; every
+replay must reproduce the eager results bit for bit.
 States updated in place (pools) are reset eagerly before each replay.
 """
 import pytest
@@ -33,6 +34,11 @@ def _inputs():
                               dtype="bf16", skip_rows=1, write_slots=True)
     cx = synth.conv1d_inputs(804, lengths=[40, 1, 77], conv_dim=256, kernel_size=4, max_slots=8,
                              dtype="bf16")
+    pk = synth.prefill_inputs(805, lengths=[45, 0, 20], hq=1, hv=2, dk=64, dv=64, dtype="bf16", gate="log",
+                              init_std=0.05)
+    dpk = synth.decode_inputs(806, pool_size=24, batch=6, T=16, n_hh=1, hq=2, hv=4, dk=64, dv=64,
+                              dtype="bf16", skip_rows=1, write_slots=True)
+    g = torch.Generator().manual_seed(807)
     t = {}
     for name, x in (("p", px), ("f", pf)):
         for k in ("q", "k", "v", "A_log", "dt_bias", "a", "b", "cu_seqlens", "initial_state"):
@@ -44,6 +50,14 @@ def _inputs():
         t[name + "scale"] = x["scale"]
     for k in ("x", "weight", "conv_state"):
         t["c" + k] = cx[k].to(dev)
+    for k in ("q", "k", "v", "beta", "cu_seqlens", "initial_state"):
+        t["k" + k] = pk[k].to(dev)
+    t["kdec"] = (-torch.rand(pk["T"], 2, 64, generator=g) * 0.5).to(dev)
+    t["kscale"] = pk["scale"]
+    for k in ("q", "k", "v", "b", "read_idx", "write_idx", "pool"):
+        t["e" + k] = dpk[k].to(dev)
+    t["edec"] = (-torch.rand(6, 16, 4, 64, generator=g) * 0.5).to(dev)
+    t["escale"] = dpk["scale"]
     t["cslot"] = cx["slot_idx"].to(torch.int32).to(dev)
     t["coff"] = cx["row_offsets"].to(torch.int32).to(dev)
     T, hv = px["T"], px["hv"]
@@ -54,7 +68,10 @@ def _inputs():
         fo=torch.empty(pf["T"], 2, 32, device=dev), ffin=torch.empty(2, 2, 32, 64, device=dev),
         d1o=torch.zeros(6, 1, 4, 64, dtype=torch.bfloat16, device=dev),
         d16o=torch.zeros(6, 16, 4, 64, dtype=torch.bfloat16, device=dev),
-        co=torch.zeros(cx["T"], 256, dtype=torch.bfloat16, device=dev))
+        co=torch.zeros(cx["T"], 256, dtype=torch.bfloat16, device=dev),
+        ko=torch.empty(pk["T"], 2, 64, dtype=torch.bfloat16, device=dev),
+        kfin=torch.empty(3, 2, 64, 64, device=dev),
+        eo=torch.zeros(6, 16, 4, 64, dtype=torch.bfloat16, device=dev))
     return t, out, px["scale"], pf["scale"]
 
 
@@ -71,9 +88,15 @@ def _calls(t, o, ps, fs):
                    t[n + "b"], t[n + "pool"], t[n + "read_idx"], write_idx=t[n + "write_idx"],
                    scale=t[n + "scale"], out=o[n + "o"])
     gdn.conv1d(t["cx"], t["cweight"], t["cconv_state"], t["cslot"], t["coff"], out=o["co"])
+    # per-key decay: prefill, and the chunked multi-token decode over a pool
+    gdn.prefill(t["kq"], t["kk"], t["kv"], t["kdec"], t["kbeta"], cu_seqlens=t["kcu_seqlens"],
+                initial_state=t["kinitial_state"], scale=t["kscale"], out=o["ko"], final_state=o["kfin"],
+                decay_per_key=True)
+    gdn.decode(t["eq"], t["ek"], t["ev"], None, None, None, t["eb"], t["epool"], t["eread_idx"],
+               write_idx=t["ewrite_idx"], scale=t["escale"], out=o["eo"], decay_per_key=t["edec"])
 
 
-STATEFUL = ("d1pool", "d16pool", "cconv_state")
+STATEFUL = ("d1pool", "d16pool", "cconv_state", "epool")
 
 
 def test_all_calls_replay_from_a_graph():
