@@ -477,15 +477,18 @@ prefill_pk_kernel(const PrefillParams p) {
     const int64_t t0 = start + (int64_t)c * C;
     prem = (int)min((int64_t)C, end - t0);      // >= 1
     const int64_t tok = t0 + min(x, prem - 1);  // clamped: inside the request
-    if (keys) {
-      load8(gq + tok * p.q_st + kb, pq);
-      load8(gk + tok * p.k_st + kb, pk);
-      load8(gdec + tok * (int64_t)p.hv * DK + kb, pd);
-    }
+    // beta first: a wait the compiler places for its register must not also
+    // wait for the row loads (the wait counter is in order)
     if (pw == 0) {
       if constexpr (FB) pbr = ggb[(tok * p.hv) & p.bmask];
       else pbt = gbet[(tok * p.hv) & p.bmask];
     }
+    // lanes past the head size read the last keys (in bounds) and are masked
+    // when used, so the loads take no branch
+    const int kl = min(kb, DK - 8);
+    load8(gq + tok * p.q_st + kl, pq);
+    load8(gk + tok * p.k_st + kl, pk);
+    load8(gdec + tok * (int64_t)p.hv * DK + kl, pd);
   };
   // Preparation of chunk c from the prefetched registers.
   auto prepare = [&](int c) {
