@@ -499,9 +499,27 @@ prefill_kernel(const PrefillParams p) {
   const float ealog = fused ? expf(p.A_log[h & p.dmask]) : 0.f, dtb = fused ? p.dt_bias[h & p.dmask] : 0.f;
   const bool nrm = EXT && p.qk_norm != 0;
 
+  int prem = 0;  // rows of the prefetched chunk
   auto prefetch = [&](int c) {
     const int64_t t0 = start + (int64_t)c * C;
     const int rem = (int)min((int64_t)C, end - t0);  // >= 1
+    prem = rem;
+    // the gates first: a wait the compiler places for their registers must
+    // not also wait for the row loads (the wait counter is in order)
+    {
+      pvalid = lane < rem;
+      const int tl = min(lane, rem - 1);
+      const int64_t tok = (t0 + tl) * p.hv;
+      if (fused) {
+        // raw a and b as loaded (the gates are computed in the scan, so that
+        // nothing waits on these loads here)
+        pga = gga[tok & p.dmask];
+        pgb = ggb[tok & p.bmask];
+      } else {
+        pg = gdec[tok & p.dmask];
+        pb = gbet[tok & p.bmask];
+      }
+    }
     const E* qb = gq + t0 * p.q_st;
     const E* kb = gk + t0 * p.k_st;
     const int qst = (int)p.q_st, kst = (int)p.k_st;
@@ -510,37 +528,16 @@ prefill_kernel(const PrefillParams p) {
       const int pr = ptid + 256 * u;
       const int quad = pr / NOCT, oct = pr % NOCT;
       if (pr < NPAIR) {
+        // rows past the end of the request read its last row (in bounds) and
+        // are zeroed when staged, so the loads take no branch
         const __amdgpu_buffer_rsrc_t rq = buf_rsrc(qb), rk = buf_rsrc(kb);
-        const uint32_t lq = (uint32_t)((4 * quad * qst + oct * VE) * sizeof(E));
-        const uint32_t lk = (uint32_t)((4 * quad * kst + oct * VE) * sizeof(E));
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const int t = 4 * quad + w;
-          if (rem == C) {
-            pq[u][w] = buf_load16(rq, lq, w * qst * (uint32_t)sizeof(E));
-            pk[u][w] = buf_load16(rk, lk, w * kst * (uint32_t)sizeof(E));
-          } else {
-            const int tc = min(t, rem - 1);  // clamped: always inside the request
-            const u32x4 vq = *reinterpret_cast<const u32x4*>(qb + tc * qst + oct * VE);
-            const u32x4 vk = *reinterpret_cast<const u32x4*>(kb + tc * kst + oct * VE);
-            const uint32_t keep = t < rem ? 0xffffffffu : 0u;
-            pq[u][w] = vq & keep;
-            pk[u][w] = vk & keep;
-          }
+          const int tc = min(4 * quad + w, rem - 1);
+          pq[u][w] = buf_load16(rq, (uint32_t)((tc * qst + oct * VE) * sizeof(E)), 0);
+          pk[u][w] = buf_load16(rk, (uint32_t)((tc * kst + oct * VE) * sizeof(E)), 0);
         }
       }
-    }
-    pvalid = lane < rem;
-    const int tl = min(lane, rem - 1);
-    const int64_t tok = (t0 + tl) * p.hv;
-    if (fused) {
-      // raw a and b as loaded (the gates are computed in the scan, so that
-      // nothing waits on these loads here)
-      pga = gga[tok & p.dmask];
-      pgb = ggb[tok & p.bmask];
-    } else {
-      pg = gdec[tok & p.dmask];
-      pb = gbet[tok & p.bmask];
     }
   };
 
@@ -555,7 +552,7 @@ prefill_kernel(const PrefillParams p) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         float sq = 0.f, sk = 0.f;
-        if (pr < NPAIR) {
+        if (pr < NPAIR && 4 * quad + w < prem) {
 #pragma unroll
           for (int e = 0; e < VE; ++e) {
             const float a = to_f32(elem16<E>(pq[u][w], e)), b = to_f32(elem16<E>(pk[u][w], e));
@@ -585,10 +582,14 @@ prefill_kernel(const PrefillParams p) {
       const int pr = ptid + 256 * u;
       if (pr < NPAIR) {
         const int quad = pr / NOCT, oct = pr % NOCT;
+        u32x4 kq[4], kk[4];  // padded rows zeroed
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          *reinterpret_cast<u32x4*>(&R.q[4 * quad + w][oct * VE]) = pq[u][w];
-          *reinterpret_cast<u32x4*>(&R.k[4 * quad + w][oct * VE]) = pk[u][w];
+          const uint32_t keep = 4 * quad + w < prem ? 0xffffffffu : 0u;
+          kq[w] = pq[u][w] & keep;
+          kk[w] = pk[u][w] & keep;
+          *reinterpret_cast<u32x4*>(&R.q[4 * quad + w][oct * VE]) = kq[w];
+          *reinterpret_cast<u32x4*>(&R.k[4 * quad + w][oct * VE]) = kk[w];
         }
         // transposed K: for each key of the vector, 4 consecutive tokens
 #pragma unroll
@@ -596,7 +597,7 @@ prefill_kernel(const PrefillParams p) {
           const int krow = oct * VE + e;
           typename pack4<E>::type col;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) col[w] = elem16<E>(pk[u][w], e);
+          for (int w = 0; w < 4; ++w) col[w] = elem16<E>(kk[w], e);
           *reinterpret_cast<typename pack4<E>::type*>(&R.kt[krow][(4 * quad) ^ kt_swz(krow)]) = col;
         }
       }
