@@ -56,6 +56,7 @@ METRIC = "GDN prefill tokens/s (B4×S4096,Hv32,d128) + decode state HBM GB/s % o
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_b4s4096_decode_b256_conv1d_b4s4096.json")
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_prefill_b4s4096.json")
 CALIB_BYTES = 2 * (1 << 30)   # the calibration copy reads 1 GiB and writes 1 GiB
+PREFILL_KERNEL = "prefill_pair_kernel<128,false,false>"
 
 
 def kernel_source_hash() -> str:
@@ -135,7 +136,7 @@ def summarize_mfma(csv_path):
     for r in csv.DictReader(open(csv_path)):
         if _kernel_key(r["Kernel_Name"]) == "prefill":
             vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-    return {"source_hash": kernel_source_hash(), "kernel": "prefill_pair_kernel<128,false,false>",
+    return {"source_hash": kernel_source_hash(), "kernel": PREFILL_KERNEL,
             "dispatches": len(vals.get("MfmaUtil", [])),
             "mfma_util_pct": statistics.mean(vals["MfmaUtil"]),
             "mfma_flops_bf16": statistics.mean(vals["MfmaFlopsBF16"])}
@@ -161,17 +162,28 @@ def load_traffic(kernel):
 
 
 def prefill_algorithmic(T, hq, hv, dk, dv, n_seqs, chunk, io_bytes=2):
-    """Bytes and flops one prefill launch must move / compute: q, k, v, out and
-    the fp32 gates once per token, the final states once; per q/k head the
-    chunk's Gram products (4 C dk per token), per value head the state pass
-    (6 dk dv per token) and the intra-chunk M U / U products (4 C dv)."""
+    """Bytes and flops one prefill launch must move / compute.
+
+    Bytes: q, k, v, out and the fp32 gates once per token, the final states
+    once.  Flops: the GEMM work of the chunked WY form, per token -- per q/k
+    head the chunk's Gram products K K^T and Q K^T (4 C dk); per value head
+    the WY transform W = T diag(beta Gam) K (2 C dk), U~ = T diag(beta) V and
+    the intra-chunk (M o Q K^T) U (4 C dv), and the state pass [Q; W] S0 plus
+    the state update K^T U (6 dk dv)."""
     per_token_bytes = (hq * dk * io_bytes * 2          # q, k
                        + hv * dv * io_bytes * 2        # v, out
                        + hv * 4 * 2)                   # log-decay, beta (fp32)
     state_bytes = n_seqs * hv * dv * dk * 4            # final state (no initial state)
     bytes_ = T * per_token_bytes + state_bytes
-    flops_per_token = hq * 4 * chunk * dk + hv * (6 * dk * dv + 4 * chunk * dv)
+    flops_per_token = hq * 4 * chunk * dk + hv * (2 * chunk * dk + 4 * chunk * dv + 6 * dk * dv)
     return bytes_, T * flops_per_token
+
+
+def prefill_flops_substitution_form(T, hq, hv, dk, dv, chunk):
+    """Flops of the same chunk in the substitution form, which never forms W:
+    X = beta (V - Gam K S0) is solved for U by block forward substitution,
+    so the 2 C dk per value head of the WY transform of K drop out."""
+    return T * (hq * 4 * chunk * dk + hv * (6 * dk * dv + 4 * chunk * dv))
 
 
 def decode_algorithmic(x):
@@ -521,12 +533,16 @@ def main():
         res["unit"] = "tokens/s"
         gbs = pb / (pm * 1e-3) / 1e9
         tfl = pf / (pm * 1e-3) / 1e12
-        res["roofline"] = {"kernel": "prefill_pair_kernel<128,false,false>", "bound": "hbm",
+        pf_sub = prefill_flops_substitution_form(px["T"], px["hq"], px["hv"], px["dk"], px["dv"], 64)
+        res["roofline"] = {"kernel": PREFILL_KERNEL, "bound": "hbm",
                            "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic("prefill"),
                            "algorithmic_bytes": pb, "algorithmic_flops": pf,
                            "mfma_tflops": tfl, "mfma_peak_tflops": BF16_PEAK_TFLOPS,
-                           "mfma_frac": tfl / BF16_PEAK_TFLOPS, "avg_ms": pm}
+                           "mfma_frac": tfl / BF16_PEAK_TFLOPS,
+                           "algorithmic_flops_substitution_form": pf_sub,
+                           "mfma_frac_substitution_form": pf_sub / (pm * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                           "avg_ms": pm}
         mf = load_mfma()
         # counter view of the same kernel (rocprofv3 MfmaUtil / MfmaFlopsBF16), or
         # null once the kernels have changed since it was taken

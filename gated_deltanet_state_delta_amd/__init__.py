@@ -62,12 +62,27 @@ def _shape(t, name, shape):
     return t
 
 
-def _idx32(t, name, shape):
+_I32_MIN, _I32_MAX = -(1 << 31), (1 << 31) - 1
+
+
+def _idx32(t, name, shape, offsets=False):
+    """An int32 or int64 index tensor as the int32 table the C ABI reads.
+
+    int64 entries outside the int32 range never wrap onto a valid index:
+    slot indices (offsets=False) become -1, which every slot rule reads as
+    "skip" exactly as it reads the original out-of-range value; offsets
+    (cu_seqlens) are clamped to the int32 range, which the kernels' clamp to
+    [0, total_tokens] maps to the same request bounds."""
     if t is None:
         return None
     if t.dtype not in (torch.int32, torch.int64):
         raise ValueError("%s must be int32 or int64" % name)
     _shape(t, name, shape)
+    if t.dtype == torch.int64:
+        if offsets:
+            t = t.clamp(_I32_MIN, _I32_MAX)
+        else:
+            t = torch.where((t < _I32_MIN) | (t > _I32_MAX), torch.full_like(t, -1), t)
     return t.to(torch.int32).contiguous()
 
 
@@ -165,10 +180,10 @@ def prefill_args(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None,
         raise ValueError("update_rule must be one of %s" % sorted(RULES))
     uses_decay = update_rule in ("gated_delta", "gated")
     uses_beta = update_rule in ("gated_delta", "delta")
-    fused = a is not None or b is not None
-    if fused and (decay is not None or beta is not None):
-        raise ValueError("give the gates either fused (a, b) or as decay / beta, not both "
-                         "(gdn.gate computes either one)")
+    if a is not None and decay is not None:
+        raise ValueError("give the decay either fused (a) or given (decay), not both")
+    if b is not None and beta is not None:
+        raise ValueError("give beta either fused (b) or given (beta), not both")
     if (a is not None or (decay is not None)) != uses_decay:
         raise ValueError("update_rule %s %s a decay input (decay or a)"
                          % (update_rule, "needs" if uses_decay else "takes no"))
@@ -194,8 +209,8 @@ def prefill_args(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None,
         if gb.dtype != q3.dtype:
             raise ValueError("b must have q's dtype")
         gb = gb.contiguous()
-    if decay_per_key and (a is not None or b is not None):
-        raise ValueError("decay_per_key takes the decay and beta as given inputs (not a, b)")
+    if decay_per_key and a is not None:
+        raise ValueError("decay_per_key takes the decay as a given input (not a)")
     if decay is not None and decay_per_key:
         decay = _f32c(decay.reshape(-1, hv, dk) if decay.dim() == 4 else decay, "decay",
                       (T, hv, dk))
@@ -206,7 +221,7 @@ def prefill_args(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None,
     if cu_seqlens is not None:
         if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
             raise ValueError("cu_seqlens must be [N + 1]")
-        cu = _idx32(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),))
+        cu = _idx32(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), offsets=True)
         n_seqs, seq_len = cu.numel() - 1, 0
     else:
         cu = None
@@ -293,8 +308,10 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
     scale None means 1/sqrt(dk).  qk_l2norm: use every q and k head vector as
     x / sqrt(sum x^2 + qk_l2norm_eps) (the ONNX card's qk_l2_norm).  a, b
     ([T, hv] or [B, S, hv] in q's dtype): the fused gate, computed in the
-    kernel -- the qwen decay from a with A_log, dt_bias [hv], beta = sigmoid(b)
-    (pass decay and beta as None then).  Head sizes other than 16, 32, 64, 128
+    kernel -- the qwen decay from a with A_log, dt_bias [hv], beta = sigmoid(b);
+    each gate input is given or fused on its own (the ONNX card's separate
+    gate_activation and beta_activation), so a with beta, or decay with b,
+    is accepted too.  Head sizes other than 16, 32, 64, 128
     (up to 128) run zero-padded to the next kernel size, with dense states
     only; the results are exact.  update_rule ("gated_delta", "gated",
     "delta", "linear"; the ONNX card's attribute) selects which terms of the
@@ -305,8 +322,8 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
     initial_state / final_state (read slot outside the pool: zeros; write slot
     None: the read slot; outside the pool: not stored); returns (out, pool).
     decay_per_key: decay is [T, hv, dk] (or [B, S, hv, dk]), one decay per
-    key dimension (the ONNX card's per-key spelling; given decay and beta
-    only); it runs a separate, slower kernel.
+    key dimension (the ONNX card's per-key spelling; a given decay, with a
+    given beta or a fused b); it runs a separate, slower kernel.
     float16 q, k, v (the ONNX card's T includes f16) run the float32 path on
     exact widenings and the output is rounded back to float16.
     Returns (out, final_state [N, hv, dv, dk] float32); out is [T, hv, dv] (or
@@ -512,8 +529,11 @@ def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None, sca
     may then be None).  float16 q, k, v, a, b are converted to bfloat16 for
     the kernel and the output is copied into a float16 buffer (skipped rows
     keep their values through a bfloat16 round trip), as the FlashInfer page
-    describes.  Returns (out [B, T, hv, dv], pool); rows of skipped batch rows
-    keep out's previous contents (zeros when out is None).
+    describes.  out may be any [B, T, hv, dv] tensor of q's dtype: a
+    non-contiguous (or unaligned) one receives a copy of the kernel's dense
+    output after the launch, as the FlashInfer page's output parameter says.
+    Returns (out [B, T, hv, dv], pool); rows of skipped batch rows keep out's
+    previous contents (zeros when out is None).
     """
     lib = _lib.load()
     for name, t in (("q", q), ("k", k), ("v", v), ("A_log", A_log), ("dt_bias", dt_bias),
@@ -532,6 +552,19 @@ def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None, sca
         if out is None:
             return o.half(), pool
         out.copy_(o)
+        return out, pool
+    if out is not None and out.dtype == q.dtype and out.dim() == 4 and \
+            (not out.is_contiguous() or out.data_ptr() % 16):
+        # "flashinfer...cake_gated_delta_product_mtp", Parameters (output): the
+        # kernel writes a dense buffer and any other buffer receives a copy
+        # after the launch.  The dense buffer starts as a copy of out, so rows
+        # the call skips keep their previous contents.
+        dense = out.clone(memory_format=torch.contiguous_format)
+        _, pool = decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, write_idx=write_idx,
+                         scatter_idx=scatter_idx, disable_state_update=disable_state_update,
+                         scale=scale, out=dense, stream=stream, use_qk_l2norm=use_qk_l2norm,
+                         qk_l2norm_eps=qk_l2norm_eps, decay_per_key=decay_per_key)
+        out.copy_(dense)
         return out, pool
     d, keep, out = decode_args(q, k, v, A_log, dt_bias, a, b, pool, read_idx,
                                write_idx=write_idx, scatter_idx=scatter_idx,

@@ -94,7 +94,6 @@ gdn_status gdn_prefill(const gdn_prefill_args* p, void* stream) {
     const bool uses_decay = a.update_rule == GDN_RULE_GATED_DELTA || a.update_rule == GDN_RULE_GATED;
     const bool uses_beta = a.update_rule == GDN_RULE_GATED_DELTA || a.update_rule == GDN_RULE_DELTA;
     const bool has_decay = a.decay || a.gate_a, has_beta = a.beta || a.gate_b;
-    const bool fused = a.gate_a || a.gate_b, given = a.decay || a.beta;
     if (a.decay && a.gate_a) return fail(GDN_ERR_SHAPE, "gdn_prefill: decay and gate_a are both given");
     if (a.beta && a.gate_b) return fail(GDN_ERR_SHAPE, "gdn_prefill: beta and gate_b are both given");
     if (has_decay != uses_decay)
@@ -103,12 +102,10 @@ gdn_status gdn_prefill(const gdn_prefill_args* p, void* stream) {
     if (has_beta != uses_beta)
       return fail(uses_beta ? GDN_ERR_NULL : GDN_ERR_SHAPE, "gdn_prefill: update_rule %d %s a beta input",
                   a.update_rule, uses_beta ? "needs" : "takes no");
-    if (fused && given)
-      return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill: fused and given gate inputs mixed (use gdn_gate for both)");
   }
   if (a.gate_a && (!a.A_log || !a.dt_bias)) return fail(GDN_ERR_NULL, "gdn_prefill: gate_a needs A_log and dt_bias");
-  if (a.decay_per_key && (a.gate_a || a.gate_b))
-    return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill: decay_per_key takes the decay and beta as given inputs");
+  if (a.decay_per_key && a.gate_a)
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill: decay_per_key takes the decay as a given input (not gate_a)");
   if (a.decay_per_key && a.update_rule != GDN_RULE_GATED_DELTA && a.update_rule != GDN_RULE_GATED)
     return fail(GDN_ERR_SHAPE, "gdn_prefill: decay_per_key needs an update_rule with a decay (gated_delta, gated)");
   if (a.state_pool) {
@@ -134,9 +131,12 @@ gdn_status gdn_prefill(const gdn_prefill_args* p, void* stream) {
     if (q && !aligned(q, 16)) return fail(GDN_ERR_LAYOUT, "gdn_prefill: pointers must be 16-byte aligned");
   const int64_t strides[] = {a.q_stride_token, a.q_stride_head, a.k_stride_token, a.k_stride_head,
                              a.v_stride_token, a.v_stride_head, a.out_stride_token, a.out_stride_head};
+  // The kernels form in-chunk row offsets (up to 63 rows of a stride, in bytes
+  // of fp32 at most) in 32-bit arithmetic: strides below 2^23 elements keep
+  // 63 * stride * 4 plus a row's extent below 2^31.
   for (int64_t s : strides)
-    if (s < 0 || s % 8 != 0 || s >= (int64_t(1) << 25))
-      return fail(GDN_ERR_LAYOUT, "gdn_prefill: strides must be non-negative multiples of 8 elements below 2^25");
+    if (s < 0 || s % 8 != 0 || s >= (int64_t(1) << 23))
+      return fail(GDN_ERR_LAYOUT, "gdn_prefill: strides must be non-negative multiples of 8 elements below 2^23");
   if (a.total_tokens > 0) {
     if (a.q_stride_head < a.dk || a.k_stride_head < a.dk || a.v_stride_head < a.dv || a.out_stride_head < a.dv ||
         a.q_stride_token < (int64_t)a.hq * a.dk || a.k_stride_token < (int64_t)a.hq * a.dk ||

@@ -61,10 +61,14 @@ hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream, int poo
   // update_rule: the delta retrieval is kept by gated_delta and delta
   p.rho = (a.update_rule == GDN_RULE_GATED_DELTA || a.update_rule == GDN_RULE_DELTA) ? 1.f : 0.f;
   p.dmask = p.bmask = ~int64_t(0);
+  // Each gate input is given or fused on its own ("com.microsoft.GatedDeltaNet",
+  // Attributes: gate_activation and beta_activation).  One fused and one given
+  // input ("mixed") runs on the general kernel, which chooses per input.
   const bool fused = a.gate_a || a.gate_b;
-  if (fused) p.decay_is_gamma = 0;  // the fused gate yields log-space decay
+  const bool mixed = (a.gate_a && a.beta) || (a.gate_b && a.decay);
+  if (a.gate_a) p.decay_is_gamma = 0;  // the fused gate yields log-space decay
   const bool absent = fused ? (!a.gate_a || !a.gate_b) : (!a.decay || !a.beta);
-  if (absent) {
+  if (absent && !mixed) {
     // a rule without decay or beta: the missing source reads the constants
     float* c = nullptr;
     const hipError_t e = gate_consts(&c);
@@ -79,7 +83,7 @@ hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream, int poo
   }
   const bool bf = a.io_dtype == GDN_BF16;
   if (a.decay_per_key) return launch_prefill_pk(p, a.dk, a.dv, bf, stream);
-  if (bf && prefill_pair_supported(a.dk, a.dv, a.chunk_size)) return prefill_pair_bf16(p, a.dk, stream);
+  if (bf && !mixed && prefill_pair_supported(a.dk, a.dv, a.chunk_size)) return prefill_pair_bf16(p, a.dk, stream);
   const int hint = a.chunk_size != 0 ? a.chunk_size : 64;
   const int c = bf ? prefill_chunk_for<__bf16>(a.dk, a.dv, hint)
                    : prefill_chunk_for<float>(a.dk, a.dv, hint);

@@ -491,12 +491,13 @@ prefill_kernel(const PrefillParams p) {
   float pg = 0.f, pb = 0.f;     // prefetched decay/beta of token `lane`
   E pga = from_f32<E>(0.f), pgb = from_f32<E>(0.f);  // or the fused gate's raw a, b
   bool pvalid = false;
-  // gates: given (decay, beta) or fused (the qwen gate and a sigmoid beta
-  // from A_log, dt_bias, a, b, computed here per token)
-  const bool fused = EXT && (p.ga != nullptr || p.gb != nullptr);
+  // gates, each input on its own: given (decay, beta) or fused (the qwen
+  // gate from A_log, dt_bias, a; a sigmoid beta from b), computed here per
+  // token
+  const bool fd = EXT && p.ga != nullptr, fb = EXT && p.gb != nullptr;
   const E* gga = (const E*)p.ga + (h & p.dmask);
   const E* ggb = (const E*)p.gb + (h & p.bmask);
-  const float ealog = fused ? expf(p.A_log[h & p.dmask]) : 0.f, dtb = fused ? p.dt_bias[h & p.dmask] : 0.f;
+  const float ealog = fd ? expf(p.A_log[h & p.dmask]) : 0.f, dtb = fd ? p.dt_bias[h & p.dmask] : 0.f;
   const bool nrm = EXT && p.qk_norm != 0;
 
   int prem = 0;  // rows of the prefetched chunk
@@ -510,15 +511,12 @@ prefill_kernel(const PrefillParams p) {
       pvalid = lane < rem;
       const int tl = min(lane, rem - 1);
       const int64_t tok = (t0 + tl) * p.hv;
-      if (fused) {
-        // raw a and b as loaded (the gates are computed in the scan, so that
-        // nothing waits on these loads here)
-        pga = gga[tok & p.dmask];
-        pgb = ggb[tok & p.bmask];
-      } else {
-        pg = gdec[tok & p.dmask];
-        pb = gbet[tok & p.bmask];
-      }
+      // raw a and b as loaded (the gates are computed in the scan, so that
+      // nothing waits on these loads here)
+      if (fd) pga = gga[tok & p.dmask];
+      else pg = gdec[tok & p.dmask];
+      if (fb) pgb = ggb[tok & p.bmask];
+      else pb = gbet[tok & p.bmask];
     }
     const E* qb = gq + t0 * p.q_st;
     const E* kb = gk + t0 * p.k_st;
@@ -608,10 +606,9 @@ prefill_kernel(const PrefillParams p) {
   auto scan = [&](typename Sm::Derived& Dd) {
     float lg = 0.f;
     bool reset = false;
-    if (fused) {  // an absent input: no decay, beta 1
-      pg = p.dmask ? gate_log_decay_fast(ealog, dtb, to_f32(pga)) : 0.f;
-      pb = p.bmask ? sigmoid_fast(to_f32(pgb)) : 1.f;
-    }
+    // an absent fused input: no decay, beta 1
+    if (fd) pg = p.dmask ? gate_log_decay_fast(ealog, dtb, to_f32(pga)) : 0.f;
+    if (fb) pb = p.bmask ? sigmoid_fast(to_f32(pgb)) : 1.f;
     if (pvalid) {
       if (p.decay_is_gamma) {
         reset = !(pg > 0.f);

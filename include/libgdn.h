@@ -135,12 +135,13 @@ gdn_status gdn_gate(const float* A_log, const float* dt_bias,
  * rules that use them: the decay source (decay, or gate_a with A_log and
  * dt_bias) is required for gated_delta and gated and must be absent for delta
  * and linear; the beta source (beta, or gate_b) is required for gated_delta
- * and delta and must be absent for gated and linear.  Sources are either all
- * given (decay / beta) or all fused (gate_a / gate_b); a fused decay with a
- * given beta (or the reverse) is GDN_ERR_UNSUPPORTED: compute the given one
- * with gdn_gate instead.
+ * and delta and must be absent for gated and linear.  Each source is given
+ * or fused on its own, as the card's gate_activation and beta_activation are
+ * separate attributes: a fused decay with a given beta, or a given decay with
+ * a fused beta, is accepted (it runs on the general kernel, which picks the
+ * form per input).
  * Requirements: pointers 16-byte aligned; head and token strides multiples of
- * 8 elements and below 2^25; total_tokens * hv below 2^31; io_dtype in
+ * 8 elements and below 2^23 (in-chunk offsets are 32-bit); total_tokens * hv below 2^31; io_dtype in
  * {GDN_F32, GDN_BF16}.  total_tokens == 0 still writes final_state (copies /
  * zeros).  n_seqs == 0 is a no-op.
  * ------------------------------------------------------------------------- */
@@ -203,8 +204,8 @@ typedef struct {
    * [total_tokens, hv, dk] fp32 dense, one decay per key dimension (the ONNX
    * card's per-key-dimension spelling, in decay_kind's meaning), read in the
    * card's recurrence: each token first scales key column i of the V-major
-   * state by its own factor.  Needs a given decay (not gate_a) and given
-   * beta, and an update_rule with a decay (gated_delta or gated; others
+   * state by its own factor.  Needs a given decay (not gate_a), a given
+   * beta or a fused one (gate_b), and an update_rule with a decay (gated_delta or gated; others
    * return GDN_ERR_SHAPE); runs a separate 16-token-chunk MFMA kernel,
    * slower than the scalar-decay kernels. */
   int32_t decay_per_key;

@@ -93,6 +93,8 @@ PREFILL_ERRORS = [
     (dict(v_stride_head=68), 4),          # stride not a multiple of 8
     (dict(q_stride_token=64), 4),         # token stride smaller than heads * dk
     (dict(v_stride_token=1 << 25), 4),    # stride too large for 32-bit in-chunk offsets
+    (dict(q_stride_token=1 << 23), 4),    # the first stride past the 32-bit offset range
+    (dict(out_stride_head=1 << 23), 4),
     (dict(initial_state=FAKE * 7 + 1024), 4),  # partial overlap with final_state
     (dict(n_seqs=-1), 2),
     # update_rule and the gate inputs it takes
@@ -105,7 +107,6 @@ PREFILL_ERRORS = [
     (dict(update_rule=3, decay=None), 2),              # ... and no beta
     (dict(gate_a=FAKE * 8, A_log=FAKE * 9, dt_bias=FAKE * 10), 2),  # decay and gate_a
     (dict(gate_b=FAKE * 8), 2),                        # beta and gate_b
-    (dict(decay=None, gate_a=FAKE * 8, A_log=FAKE * 9, dt_bias=FAKE * 10), 5),  # fused a, given beta
     (dict(decay=None, gate_a=FAKE * 8, A_log=None, dt_bias=FAKE * 10, beta=None,
           gate_b=FAKE * 11), 1),                       # gate_a without A_log
     (dict(total_tokens=1 << 27, seq_len=1 << 26, hv=16, v_stride_token=1 << 24,
@@ -126,7 +127,8 @@ PREFILL_ERRORS = [
           pool_head_stride=64 * 64), 4),                # stride not a multiple of 4
     (dict(read_slot=FAKE * 15), 2),                     # slots without a pool
     (dict(decay_per_key=1, decay=None, beta=None, gate_a=FAKE * 8, A_log=FAKE * 9,
-          dt_bias=FAKE * 10, gate_b=FAKE * 11), 5),      # per-key decay takes given inputs
+          dt_bias=FAKE * 10, gate_b=FAKE * 11), 5),      # per-key decay takes a given decay
+    (dict(decay_per_key=1, decay=None, gate_a=FAKE * 8, A_log=FAKE * 9, dt_bias=FAKE * 10), 5),
     (dict(decay_per_key=1, update_rule=2, decay=None), 2),  # per-key decay with a rule without decay
     (dict(decay_per_key=1, update_rule=3, decay=None, beta=None), 2),
 ]
@@ -139,6 +141,26 @@ def test_prefill_rejects(lib, over, status):
     assert lib.gdn_last_error()
 
 
+def test_prefill_stride_limit_matches_the_kernel_offset_range(lib):
+    """The kernels form a row's byte offset inside a chunk (up to 63 rows of
+    one stride, elements of at most 4 bytes, plus the row's own extent) in
+    32-bit signed arithmetic.  The validator's limit must keep that below
+    2^31: the largest stride it accepts passes validation (on a host without
+    a GPU the call then fails at the launch, GDN_ERR_HIP), the next multiple
+    of 8 is refused, and the worst offset at the accepted stride fits."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("an accepted call would launch on the fake pointers of this test")
+    limit = 1 << 23
+    for field in ("q_stride_token", "k_stride_token", "v_stride_token", "out_stride_token",
+                  "q_stride_head", "out_stride_head"):
+        assert lib.gdn_prefill(ctypes.byref(_prefill(**{field: limit})), None) == 4
+        st = lib.gdn_prefill(ctypes.byref(_prefill(**{field: limit - 8})), None)
+        assert st in (0, 6), (field, st, lib.gdn_last_error())
+    worst = 63 * (limit - 8) * 4 + 128 * 4
+    assert worst < (1 << 31)
+
+
 def test_prefill_rule_inputs_accepted_before_launch(lib):
     """Each rule with exactly its inputs passes validation: checked with
     tokens present (so the gate checks run) but n_seqs = 0 through
@@ -148,6 +170,21 @@ def test_prefill_rule_inputs_accepted_before_launch(lib):
     for rule, dec, bet in ((1, FAKE * 5, None), (2, None, FAKE * 6), (3, None, None)):
         a = _prefill(update_rule=rule, decay=dec, beta=bet, **base)
         assert lib.gdn_prefill(ctypes.byref(a), None) == 0, lib.gdn_last_error()
+
+
+def test_prefill_mixed_gate_sources_accepted_before_launch(lib):
+    """"com.microsoft.GatedDeltaNet", Attributes: gate_activation and
+    beta_activation are separate, so a fused decay with a given beta and a
+    given decay with a fused beta both pass validation (n_seqs = 0 through
+    cu_seqlens: nothing is launched); so does a per-key decay with a fused
+    beta."""
+    base = dict(n_seqs=0, seq_len=0, total_tokens=16, cu_seqlens=FAKE * 12)
+    a = _prefill(decay=None, gate_a=FAKE * 8, A_log=FAKE * 9, dt_bias=FAKE * 10, **base)
+    assert lib.gdn_prefill(ctypes.byref(a), None) == 0, lib.gdn_last_error()
+    a = _prefill(beta=None, gate_b=FAKE * 8, **base)
+    assert lib.gdn_prefill(ctypes.byref(a), None) == 0, lib.gdn_last_error()
+    a = _prefill(beta=None, gate_b=FAKE * 8, decay_per_key=1, **base)
+    assert lib.gdn_prefill(ctypes.byref(a), None) == 0, lib.gdn_last_error()
 
 
 def test_prefill_pool_mode_accepted_before_launch(lib):

@@ -19,11 +19,16 @@ def test_prefill_algorithmic_bytes_and_flops():
     final = n * hv * dv * dk * 4           # fp32 final states, written once
     assert by == q_k + v_out + gates + final == 415236096
     # Gram tiles K K^T and Q K^T (2 C dk flops each per token and q/k head),
-    # and per value head: [Q; K] S0 (4 dk dv), the state update (2 dk dv),
-    # M U and the substitution (4 C dv)
+    # and per value head: W = T diag(beta Gam) K (2 C dk), U~ = T diag(beta) V
+    # and (M o Q K^T) U (2 C dv each), [Q; W] S0 (4 dk dv) and the state
+    # update K^T U (2 dk dv): 5 242 880 flops per token, 85.9 GFLOP in all
     gram = T * hq * 4 * C * dk
+    wy = T * hv * 2 * C * dk
     state = T * hv * (6 * dk * dv + 4 * C * dv)
-    assert fl == gram + state == 77309411328
+    assert fl == gram + wy + state == 85899345920
+    assert fl // T == 5242880
+    # the substitution form (no explicit W) drops the WY term of K
+    assert bench.prefill_flops_substitution_form(T, hq, hv, dk, dv, C) == gram + state == 77309411328
 
 
 def test_decode_algorithmic_bytes():

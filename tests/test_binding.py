@@ -280,12 +280,58 @@ def test_prefill_rule_inputs(rule, use_d, use_b, fused):
                          update_rule=rule)
 
 
-def test_prefill_rejects_mixed_sources_and_unknown_rule():
+def test_prefill_mixed_sources_and_unknown_rule():
+    """Each gate input is given or fused on its own ("com.microsoft.GatedDeltaNet",
+    Attributes): a with beta, and decay with b, build the struct with one
+    fused and one given pointer; one input given both ways is refused."""
     T, hv = 8, 2
     q = torch.randn(T, 1, 16)
     v = torch.randn(T, hv, 16)
+    args, *_ = gdn.prefill_args(q, q, v, None, torch.rand(T, hv), A_log=torch.zeros(hv),
+                                dt_bias=torch.zeros(hv), a=torch.randn(T, hv))
+    assert args.gate_a and args.beta and not args.decay and not args.gate_b
+    args, *_ = gdn.prefill_args(q, q, v, -torch.rand(T, hv), None, b=torch.randn(T, hv))
+    assert args.decay and args.gate_b and not args.beta and not args.gate_a
     with pytest.raises(ValueError):
-        gdn.prefill_args(q, q, v, None, torch.rand(T, hv), A_log=torch.zeros(hv),
+        gdn.prefill_args(q, q, v, -torch.rand(T, hv), torch.rand(T, hv), A_log=torch.zeros(hv),
                          dt_bias=torch.zeros(hv), a=torch.randn(T, hv))
     with pytest.raises(ValueError):
+        gdn.prefill_args(q, q, v, -torch.rand(T, hv), torch.rand(T, hv), b=torch.randn(T, hv))
+    with pytest.raises(ValueError):
         gdn.prefill_args(q, q, v, -torch.rand(T, hv), torch.rand(T, hv), update_rule="mamba")
+
+
+def test_int64_slot_and_offset_narrowing():
+    """int64 slot indices outside the int32 range must not wrap onto a valid
+    slot (2^32 + 3 would become 3 under a plain cast): they reach the C ABI as
+    -1, which the slot rules ("flashinfer...cake_gated_delta_product_mtp",
+    Parameters) read as skip, as they read the original value.  int64
+    cu_seqlens are clamped to the int32 range, which the kernels' clamp to
+    [0, total_tokens] ("com.microsoft.GatedDeltaNet", Inputs) maps to the
+    same request bounds."""
+    x = _dec(B=6)
+    rd = torch.tensor([2**32 + 3, 5, -2**33 + 1, 2**31, 2**31 - 1, -1], dtype=torch.int64)
+    wr = torch.tensor([1, 2**40, 3, 4, 2**32, 0], dtype=torch.int64)
+    d, keep, _ = gdn.decode_args(x["q"], x["k"], x["v"], x["A_log"], x["dt_bias"], x["a"],
+                                 x["b"], x["pool"], rd, write_idx=wr)
+    rd32, wr32 = keep[7], keep[8]
+    assert rd32.dtype == torch.int32 and wr32.dtype == torch.int32
+    assert rd32.tolist() == [-1, 5, -1, -1, 2**31 - 1, -1]
+    assert wr32.tolist() == [1, -1, 3, 4, -1, 0]
+    sc = torch.tensor([[2**32 + 1, 7]] * 6, dtype=torch.int64)
+    _, keep, _ = gdn.decode_args(x["q"], x["k"], x["v"], x["A_log"], x["dt_bias"], x["a"],
+                                 x["b"], x["pool"], rd, scatter_idx=sc)
+    assert keep[9].tolist() == [[-1, 7]] * 6
+    T, hq, hv, dk, dv = 96, 2, 4, 64, 32
+    cu = torch.tensor([-2**40, 10, 2**35, 2**31 - 1], dtype=torch.int64)
+    args, keep, _, _ = gdn.prefill_args(torch.zeros(T, hq, dk), torch.zeros(T, hq, dk),
+                                        torch.zeros(T, hv, dv), torch.zeros(T, hv),
+                                        torch.zeros(T, hv), cu_seqlens=cu)
+    assert keep[5].tolist() == [-2**31, 10, 2**31 - 1, 2**31 - 1]
+    pool = torch.zeros(8, hv, dv, dk)
+    args, keep, _, _ = gdn.prefill_args(torch.zeros(T, hq, dk), torch.zeros(T, hq, dk),
+                                        torch.zeros(T, hv, dv), torch.zeros(T, hv),
+                                        torch.zeros(T, hv), state_pool=pool,
+                                        read_slot=torch.tensor([2**32 + 2], dtype=torch.int64),
+                                        write_slot=torch.tensor([2**33], dtype=torch.int64))
+    assert keep[13].tolist() == [-1] and keep[14].tolist() == [-1]

@@ -134,6 +134,38 @@ def test_decode_write_slots_disable_and_skips():
     assert torch.equal(pool_d.cpu(), x["pool"])
 
 
+@pytest.mark.parametrize("layout", ["transposed", "strided", "offset"])
+def test_decode_into_a_non_contiguous_output(layout):
+    """"flashinfer...cake_gated_delta_product_mtp", Parameters (output): the
+    kernel writes a dense buffer and any other caller buffer receives a copy
+    after the launch.  A transposed view, a strided slice of a larger buffer
+    and an unaligned offset view all end bitwise equal to the dense output,
+    and rows the call skips keep their previous contents."""
+    x = synth.decode_inputs(420, pool_size=40, batch=10, T=3, n_hh=2, hq=2, hv=4, dk=64, dv=64,
+                            dtype="bf16", skip_rows=3)
+    sentinel = torch.full((10, 3, 4, 64), 5.0, dtype=torch.bfloat16)
+    ref_out, ref_pool = _gpu_decode(x, out=sentinel.cuda().clone())
+    if layout == "transposed":
+        base = torch.full((10, 4, 3, 64), 5.0, dtype=torch.bfloat16, device="cuda")
+        out = base.transpose(1, 2)
+    elif layout == "strided":
+        base = torch.full((10, 3, 4, 128), 5.0, dtype=torch.bfloat16, device="cuda")
+        out = base[..., 32:96]
+    else:
+        base = torch.full((10 * 3 * 4 * 64 + 1,), 5.0, dtype=torch.bfloat16, device="cuda")
+        out = base[1:].view(10, 3, 4, 64)
+    assert not (out.is_contiguous() and out.data_ptr() % 16 == 0)
+    o, pool = _gpu_decode(x, out=out)
+    torch.cuda.synchronize()
+    assert o is out
+    assert torch.equal(out, ref_out)
+    assert torch.equal(pool, ref_pool)
+    skipped = (x["read_idx"] < 0).cuda()
+    assert torch.all(out[skipped] == 5.0)
+    if layout == "strided":
+        assert torch.all(base[..., :32] == 5.0) and torch.all(base[..., 96:] == 5.0)
+
+
 def test_decode_in_place_default_write_slot_and_padded_pool():
     """write_idx None writes back to the read slot; a pool with padding between
     heads and slots is used as is."""

@@ -60,6 +60,25 @@ def test_prefill_per_key_matches_oracle(dtype, dk, dv, rule):
     assert_close(f, rf, dtype, "final state")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128)])
+def test_prefill_per_key_with_fused_beta(dtype, dk, dv):
+    """A given per-key decay with beta fused from the raw b (beta_activation
+    sigmoid of "com.microsoft.GatedDeltaNet", Attributes, taken on its own)."""
+    x, dec = _pk_case(1100 + dk + dv, dtype, dk, dv)
+    g = torch.Generator().manual_seed(1101)
+    b = torch.randn(x["T"], 2, generator=g).to(synth.DTYPES[dtype])
+    o, f = gdn.prefill(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(dec), None,
+                       b=to_dev(b), cu_seqlens=to_dev(x["cu_seqlens"]),
+                       initial_state=to_dev(x["initial_state"]), scale=x["scale"],
+                       decay_per_key=True)
+    ro, rf = oracle.prefill(x["q"], x["k"], x["v"], dec, None, b=b, cu_seqlens=x["cu_seqlens"],
+                            initial_state=x["initial_state"], scale=x["scale"], decay_per_key=True)
+    torch.cuda.synchronize()
+    assert_close(o, ro, dtype, "out")
+    assert_close(f, rf, dtype, "final state")
+
+
 @pytest.mark.parametrize("mode", ["zeros", "strong", "gamma", "qk_l2norm", "gva"])
 def test_prefill_per_key_edge_cases(mode):
     kw = dict(zeros=mode == "zeros", strong=mode == "strong")

@@ -106,3 +106,37 @@ def test_gated_delta_default_is_unchanged_bitwise():
     o2, f2 = gdn.prefill(q, k, v, g, beta, cu_seqlens=cu, update_rule="gated_delta")
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("mix", ["fused_decay_given_beta", "given_log_decay_fused_beta",
+                                 "given_gamma_fused_beta"])
+@pytest.mark.parametrize("cfg", CONFIGS, ids=[c[0] for c in CONFIGS])
+def test_mixed_gate_sources(mix, cfg):
+    """"com.microsoft.GatedDeltaNet", Attributes: gate_activation and
+    beta_activation are separate attributes, so one input may be fused while
+    the other is given (already activated, fp32).  Each mix against the
+    oracle, which takes each source on its own, on every kernel shape
+    (mixed problems run on the general kernel)."""
+    name, dt, dk, dv, chunk = cfg
+    x = synth.prefill_inputs(360 + CONFIGS.index(cfg), lengths=LENGTHS, hq=2, hv=4, dk=dk, dv=dv,
+                             dtype=dt, gate="qwen", init_std=0.05)
+    g, gam, beta = oracle.gate(x["A_log"], x["dt_bias"], x["a"], x["b"])
+    kw = dict(cu_seqlens=to_dev(x["cu_seqlens"]), initial_state=to_dev(x["initial_state"]),
+              scale=x["scale"], chunk_size=chunk)
+    okw = dict(cu_seqlens=x["cu_seqlens"], initial_state=x["initial_state"], scale=x["scale"])
+    q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+    if mix == "fused_decay_given_beta":
+        bet = torch.from_numpy(beta).float()
+        fa = dict(A_log=x["A_log"], dt_bias=x["dt_bias"], a=x["a"])
+        o, f = gdn.prefill(q, k, v, None, to_dev(bet), **{n: to_dev(t) for n, t in fa.items()}, **kw)
+        ro, rf = oracle.prefill(x["q"], x["k"], x["v"], None, bet, **fa, **okw)
+    else:
+        is_gamma = mix == "given_gamma_fused_beta"
+        dec = torch.from_numpy(gam if is_gamma else g).float()
+        o, f = gdn.prefill(q, k, v, to_dev(dec), None, b=to_dev(x["b"]),
+                           decay_kind="gamma" if is_gamma else "log", **kw)
+        ro, rf = oracle.prefill(x["q"], x["k"], x["v"], dec, None, b=x["b"],
+                                decay_is_gamma=is_gamma, **okw)
+    torch.cuda.synchronize()
+    assert_close(o, ro, dt, "%s %s out" % (mix, name))
+    assert_close(f, rf, dt, "%s %s final state" % (mix, name))
