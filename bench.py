@@ -371,6 +371,30 @@ def extra_workloads(torch, gdn, synth, dev):
         "gbs": nb / (ms * 1e-3) / 1e9, "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     del q, k, v, dec, bet, o8, f8
 
+    # one long request with few heads (1 x 65536 tokens, Hq 2, Hv 4, d 128):
+    # the scan over segment maps (local pass, combine, rerun, with a
+    # preallocated workspace) against the serial walk of the same call
+    x = synth.long_request_b1_s65536_hv4()
+    q, k, v, cu = (x[n].to(dev) for n in ("q", "k", "v", "cu_seqlens"))
+    g9, _, b9 = gdn.gate(x["A_log"].to(dev), x["dt_bias"].to(dev), x["a"].to(dev), x["b"].to(dev))
+    o9 = torch.empty_like(v)
+    f9 = torch.empty(1, x["hv"], x["dv"], x["dk"], device=dev)
+    need = gdn.prefill_workspace_size(q, k, v, g9, b9, cu_seqlens=cu)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    fn_scan = lambda: gdn.prefill(q, k, v, g9, b9, cu_seqlens=cu, scale=x["scale"], out=o9,
+                                  final_state=f9, workspace=ws)
+    fn_serial = lambda: gdn.prefill(q, k, v, g9, b9, cu_seqlens=cu, scale=x["scale"], out=o9,
+                                    final_state=f9, scan=False)
+    ms_scan = _time_launches(torch, fn_scan, flush=flush)
+    ms_serial = _time_launches(torch, fn_serial, flush=flush, runs=5)
+    T = x["T"]
+    out["long_request_b1_s65536_hq2_hv4_d128_bf16"] = {
+        "ms_scan": ms_scan, "ms_serial": ms_serial, "speedup": ms_serial / ms_scan,
+        "segments": need // (x["hv"] * x["dk"] * (2 * x["dv"] + x["dk"]) * 4),
+        "workspace_bytes": need, "tokens_per_s_scan": T / (ms_scan * 1e-3),
+        "tokens_per_s_serial": T / (ms_serial * 1e-3)}
+    del q, k, v, g9, b9, o9, f9, ws
+
     # causal conv1d over the QKV rows with the conv-state pool: the prefill
     # batch (B4 x S4096, 8192 channels) and one decode step (256 x 1 row)
     for name, make in (("conv1d_prefill_b4_s4096_c8192_k4_bf16", synth.conv1d_prefill_b4_s4096),

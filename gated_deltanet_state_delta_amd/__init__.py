@@ -24,7 +24,7 @@ from . import _lib
 from ._lib import GdnError
 
 __all__ = ["gate", "prefill", "decode", "conv1d", "state_update", "version", "GdnError",
-           "prefill_args", "decode_args", "conv1d_args"]
+           "prefill_args", "decode_args", "conv1d_args", "prefill_workspace_size"]
 
 _DT = {torch.float32: _lib.GDN_F32, torch.bfloat16: _lib.GDN_BF16}
 # update_rule of the ONNX card -> gdn_update_rule
@@ -298,7 +298,7 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
             scale=None, chunk_size=0, out=None, final_state=None, stream=None,
             qk_l2norm=False, qk_l2norm_eps=1e-12, A_log=None, dt_bias=None, a=None, b=None,
             update_rule="gated_delta", state_pool=None, read_slot=None, write_slot=None,
-            decay_per_key=False):
+            decay_per_key=False, scan=True, workspace=None):
     """Chunked prefill.
 
     q, k: [T, hq, dk] (or [B, S, hq, dk], then uniform packing with seq_len S);
@@ -326,6 +326,12 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
     given beta or a fused b); it runs a separate, slower kernel.
     float16 q, k, v (the ONNX card's T includes f16) run the float32 path on
     exact widenings and the output is rounded back to float16.
+    scan: calls with few (request, head) units and long requests may run as a
+    scan over request segments (gdn_prefill_workspace_size > 0), which needs a
+    device workspace: `workspace` (a uint8 CUDA tensor of at least that many
+    bytes) or, when None, one allocated here; scan=False runs the serial
+    walk instead (no workspace).  Both compute the same recurrence; only the
+    rounding order differs.
     Returns (out, final_state [N, hv, dv, dk] float32); out is [T, hv, dv] (or
     [B, S, hv, dv]) in q's dtype.
     """
@@ -367,9 +373,29 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
         A_log=A_log, dt_bias=dt_bias, a=a, b=b, update_rule=update_rule,
         state_pool=state_pool, read_slot=read_slot, write_slot=write_slot,
         decay_per_key=decay_per_key)
+    ws = None
+    if scan:
+        need = lib.gdn_prefill_workspace_size(ctypes.byref(args))
+        if need > 0:
+            if workspace is None:
+                ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+            else:
+                _dev(workspace, "workspace")
+                if workspace.numel() * workspace.element_size() < need or not workspace.is_contiguous():
+                    raise ValueError("workspace must be a contiguous buffer of at least %d bytes" % need)
+                ws = workspace
+            args.workspace, args.workspace_bytes = ws.data_ptr(), need
     _lib.check(lib.gdn_prefill(ctypes.byref(args), _stream(stream)))
-    del keep
+    del keep, ws
     return out, final_state
+
+
+def prefill_workspace_size(q, k, v, decay, beta, **kw) -> int:
+    """Bytes of device workspace a prefill call with these arguments would use
+    (gdn_prefill_workspace_size): 0 unless the call runs as the scan over
+    request segments."""
+    args, keep, _, _ = prefill_args(q, k, v, decay, beta, **kw)
+    return int(_lib.load().gdn_prefill_workspace_size(ctypes.byref(args)))
 
 
 _HEAD_SIZES = (16, 32, 64, 128)

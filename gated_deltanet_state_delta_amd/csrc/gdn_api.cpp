@@ -62,7 +62,9 @@ gdn_status gdn_gate(const float* A_log, const float* dt_bias, const void* a, con
                   "gdn_gate launch");
 }
 
-size_t gdn_prefill_workspace_size(const gdn_prefill_args* /*args*/) { return 0; }
+size_t gdn_prefill_workspace_size(const gdn_prefill_args* args) {
+  return args ? gdn::prefill_workspace_bytes(*args) : 0;
+}
 
 gdn_status gdn_prefill(const gdn_prefill_args* p, void* stream) {
   g_err[0] = 0;

@@ -23,6 +23,10 @@ hipError_t launch_decode(const gdn_decode_args& args, hipStream_t stream);
 constexpr int kPoolSkipUnread = 1, kPoolNoWrite = 2;
 hipError_t launch_prefill(const gdn_prefill_args& args, hipStream_t stream, int pool_flags = 0);
 
+// Scratch bytes launch_prefill uses for these arguments when the workspace
+// holds at least that many (the scan over segment maps); 0 when it needs none.
+size_t prefill_workspace_bytes(const gdn_prefill_args& args);
+
 hipError_t launch_conv1d(const gdn_conv1d_args& args, hipStream_t stream);
 
 }  // namespace gdn

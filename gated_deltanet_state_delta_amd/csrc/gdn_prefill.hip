@@ -7,6 +7,7 @@
 // and a hint is lowered to the largest chunk whose double-buffered working
 // set fits one workgroup's LDS (for fp32 operands with dk = 128 that is 32)
 // -- and the (dk, dv) instantiation.
+#include <algorithm>
 #include <atomic>
 
 #include "gdn_prefill.hpp"
@@ -14,28 +15,99 @@
 
 namespace gdn {
 
-// What an absent gate input reads: log-decay 0 (or a raw gate input 0) at
-// [0], beta 1 at [1].  Each device holds its own copy; its address comes
-// from hipGetSymbolAddress on that device.
+// Read-only device constants.  kGateConst: what an absent gate input reads,
+// log-decay 0 (or a raw gate input 0) at [0], beta 1 at [1].  kZeroRow: the
+// zero V rows of the scan's transition slices.  Each device holds its own
+// copies; their addresses come from hipGetSymbolAddress on that device.
 __device__ float kGateConst[2] = {0.f, 1.f};
+__device__ __align__(16) float kZeroRow[32] = {};
 
-static hipError_t gate_consts(float** out) {
+static hipError_t device_consts(float** gate, const void** zero) {
   constexpr int kMaxDevices = 64;
-  static std::atomic<float*> cache[kMaxDevices];
+  static std::atomic<float*> cache_g[kMaxDevices];
+  static std::atomic<float*> cache_z[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  float* c = cache[dev].load(std::memory_order_acquire);
-  if (!c) {
+  float* c = cache_g[dev].load(std::memory_order_acquire);
+  float* z = cache_z[dev].load(std::memory_order_acquire);
+  if (!c || !z) {
     void* addr = nullptr;
     e = hipGetSymbolAddress(&addr, HIP_SYMBOL(kGateConst));
     if (e != hipSuccess) return e;
     c = static_cast<float*>(addr);
-    cache[dev].store(c, std::memory_order_release);
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(kZeroRow));
+    if (e != hipSuccess) return e;
+    z = static_cast<float*>(addr);
+    cache_g[dev].store(c, std::memory_order_release);
+    cache_z[dev].store(z, std::memory_order_release);
   }
-  *out = c;
+  if (gate) *gate = c;
+  if (zero) *zero = z;
   return hipSuccess;
+}
+
+// Whether one fused and one given gate input are combined.
+static bool gates_mixed(const gdn_prefill_args& a) {
+  return (a.gate_a && a.beta) || (a.gate_b && a.decay);
+}
+
+// Segments per request for the scan over segment maps (gdn_prefill_scan.hip),
+// or 1 when the call runs as one serial walk per (request, head, slice).
+// The scan takes the pair kernel's problems (bf16, dk and dv in {64, 128},
+// the default chunk, scalar decay, not called from the decode) when the
+// serial walk would fill at most a quarter of a 256-CU chip (64 units):
+// enough segments that the local pass has about 512 workgroups, each
+// segment on average at least 16 chunks long, at most 64 segments, and at
+// least 4 (fewer cannot repay the three passes).  Only sizes decide, so a
+// call's result does not depend on the device.
+int prefill_scan_segments(const gdn_prefill_args& a, int pool_flags) {
+  if (pool_flags || a.decay_per_key || a.io_dtype != GDN_BF16 || gates_mixed(a) ||
+      !prefill_pair_supported(a.dk, a.dv, a.chunk_size) || a.n_seqs <= 0 || a.total_tokens <= 0)
+    return 1;
+  const int64_t seg_wgs = (int64_t)a.n_seqs * a.hv * ((a.dv + a.dk) / 64);
+  int64_t nseg = 512 / seg_wgs;
+  nseg = std::min<int64_t>(nseg, (a.total_tokens / a.n_seqs) / 64 / 16);
+  nseg = std::min<int64_t>(nseg, 64);
+  return nseg >= 4 ? (int)nseg : 1;
+}
+
+size_t prefill_workspace_bytes(const gdn_prefill_args& a) {
+  const int nseg = prefill_scan_segments(a, 0);
+  if (nseg <= 1) return 0;
+  return (size_t)a.n_seqs * nseg * a.hv * a.dk * (2 * (size_t)a.dv + a.dk) * sizeof(float);
+}
+
+// The three launches of the scan (see gdn_prefill_scan.hip); the workspace
+// holds the segment maps, then every segment's incoming state.
+static hipError_t launch_prefill_scan(const PrefillParams& p, const gdn_prefill_args& a, int nseg,
+                                      hipStream_t stream) {
+  const void* zero = nullptr;
+  hipError_t e = device_consts(nullptr, &zero);
+  if (e != hipSuccess) return e;
+  float* ws_map = static_cast<float*>(a.workspace);
+  float* ws_in = ws_map + (size_t)a.n_seqs * nseg * a.hv * (a.dv + a.dk) * a.dk;
+  PrefillParams pa = p;
+  pa.nseg = nseg;
+  pa.seg_mode = 1;
+  pa.vzero = zero;
+  pa.init = nullptr;
+  pa.fin = ws_map;
+  pa.pool = nullptr;
+  pa.rslot = pa.wslot = nullptr;
+  e = prefill_pair_bf16(pa, a.dk, stream);
+  if (e != hipSuccess) return e;
+  e = launch_scan_combine(p, nseg, a.dk, ws_map, ws_in, stream);
+  if (e != hipSuccess) return e;
+  PrefillParams pb = p;
+  pb.nseg = nseg;
+  pb.seg_mode = 2;
+  pb.init = ws_in;
+  pb.fin = nullptr;
+  pb.pool = nullptr;
+  pb.rslot = pb.wslot = nullptr;
+  return prefill_pair_bf16(pb, a.dk, stream);
 }
 
 hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream, int pool_flags) {
@@ -53,6 +125,7 @@ hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream, int poo
   if (a.state_pool) { p.init = a.state_pool; p.fin = a.state_pool; }
   p.T = a.total_tokens; p.n_seqs = a.n_seqs; p.seq_len = a.seq_len;
   p.hq = a.hq; p.hv = a.hv; p.dv = a.dv; p.nsplit = 1;
+  p.nseg = 1; p.nsv = 1; p.seg_mode = 0; p.vzero = nullptr;
   p.decay_is_gamma = a.decay_kind == GDN_DECAY_GAMMA;
   p.scale = a.scale;
   p.qk_norm = a.qk_l2norm != 0;
@@ -65,13 +138,13 @@ hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream, int poo
   // Attributes: gate_activation and beta_activation).  One fused and one given
   // input ("mixed") runs on the general kernel, which chooses per input.
   const bool fused = a.gate_a || a.gate_b;
-  const bool mixed = (a.gate_a && a.beta) || (a.gate_b && a.decay);
+  const bool mixed = gates_mixed(a);
   if (a.gate_a) p.decay_is_gamma = 0;  // the fused gate yields log-space decay
   const bool absent = fused ? (!a.gate_a || !a.gate_b) : (!a.decay || !a.beta);
   if (absent && !mixed) {
     // a rule without decay or beta: the missing source reads the constants
     float* c = nullptr;
-    const hipError_t e = gate_consts(&c);
+    const hipError_t e = device_consts(&c, nullptr);
     if (e != hipSuccess) return e;
     if (fused) {
       if (!a.gate_a) { p.ga = c; p.A_log = c; p.dt_bias = c; p.dmask = 0; }
@@ -83,6 +156,9 @@ hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream, int poo
   }
   const bool bf = a.io_dtype == GDN_BF16;
   if (a.decay_per_key) return launch_prefill_pk(p, a.dk, a.dv, bf, stream);
+  const int nseg = prefill_scan_segments(a, pool_flags);
+  if (nseg > 1 && a.workspace && a.workspace_bytes >= prefill_workspace_bytes(a))
+    return launch_prefill_scan(p, a, nseg, stream);
   if (bf && !mixed && prefill_pair_supported(a.dk, a.dv, a.chunk_size)) return prefill_pair_bf16(p, a.dk, stream);
   const int hint = a.chunk_size != 0 ? a.chunk_size : 64;
   const int c = bf ? prefill_chunk_for<__bf16>(a.dk, a.dv, hint)

@@ -98,11 +98,55 @@ struct PrefillParams {
   int64_t pss, phs;
   int pool_size;
   int pool_flags;        // kPoolSkipUnread | kPoolNoWrite (the decode's rules)
+  // Segmented scan over chunk affine maps (pair kernel only).  seg_mode 0:
+  // off (nseg 1, nsv = nsplit).  Otherwise request r is cut into nseg
+  // segments of whole chunks (prefill_segment_bounds) and a workgroup runs
+  // unit (r, j, h, slice) on segment j:
+  //  * seg_mode 1 (local pass): value slices (slice < nsv) start from a zero
+  //    state, transition slices (slice >= nsv, nsplit - nsv of them) from the
+  //    key identity -- row i of their V-major state is e_i -- and read V from
+  //    vzero (zeros), so their final rows are the columns of the segment's
+  //    state transition P.  No outputs.  The final states go to fin as
+  //    [r * nseg + j, h, dv + dk, dk]: rows < dv the segment's own state
+  //    (V-major), then P itself as dk rows of dk (K-major: row k holds
+  //    P[k][0 .. dk-1]).
+  //  * seg_mode 2 (rerun pass): segment j starts from init
+  //    [r * nseg + j, h, dv, dk]; outputs as usual; no final state.
+  int nseg, nsv, seg_mode;
+  const void* vzero;     // >= 128 zero bytes
 };
+
+// Token range [start, end) of request r: cu_seqlens clamped to [0, T] (a
+// decreasing pair is empty), or uniform packing.
+__device__ __forceinline__ void prefill_request_bounds(const PrefillParams& p, int r, int64_t& start,
+                                                       int64_t& end) {
+  if (p.cu) {
+    start = min(max((int64_t)p.cu[r], (int64_t)0), p.T);
+    end = min(max((int64_t)p.cu[r + 1], (int64_t)0), p.T);
+  } else {
+    start = (int64_t)r * p.seq_len;
+    end = start + p.seq_len;
+  }
+  if (end < start) end = start;
+}
+
+// Segment j of nseg of a request's range: ceil(chunks / nseg) whole chunks of
+// C tokens each (the last segments may be shorter or empty).
+__device__ __forceinline__ void prefill_segment_bounds(int nseg, int j, int C, int64_t& start, int64_t& end) {
+  const int64_t nch = (end - start + C - 1) / C;
+  const int64_t L = (nch + nseg - 1) / nseg;
+  const int64_t s0 = min(end, start + (int64_t)j * L * C);
+  end = min(end, start + (int64_t)(j + 1) * L * C);
+  start = s0;
+}
 
 
 // The per-key-decay prefill (gdn_prefill_pk.hip).
 hipError_t launch_prefill_pk(const PrefillParams& p, int dk, int dv, bool bf16, hipStream_t s);
+
+// The combine launch of the scan over segment maps (gdn_prefill_scan.hip).
+hipError_t launch_scan_combine(const PrefillParams& p, int nseg, int dk, const float* ws_map, float* ws_in,
+                               hipStream_t stream);
 
 // Element offsets of the V-major state slice (request r, value head h, value
 // columns from v0) to read the initial state from and to write the final

@@ -227,7 +227,7 @@ __device__ __forceinline__ void pair_tri_inverse(const float (*ad)[16 * 20 + 4],
 template <int DK, int PW, bool FUSED, bool NORM>
 __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& sm, int64_t start,
                                           int64_t end, int nch, const __bf16* gq, const __bf16* gk,
-                                          const __bf16* gv, int h) {
+                                          const __bf16* gv, int v_st, int h) {
   typedef PairSmem<DK> Sm;
   constexpr int C = 64, NPP = DK / 32;
   const int lane = threadIdx.x & 63, x = lane & 15, g = lane >> 4;
@@ -259,8 +259,8 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
     }
     const __bf16* qb = gq + t0 * p.q_st;
     const __bf16* kb = gk + t0 * p.k_st;
-    const __bf16* vb = gv + t0 * p.v_st;
-    const int qst = (int)p.q_st, kst = (int)p.k_st, vst = (int)p.v_st;
+    const __bf16* vb = gv + t0 * v_st;
+    const int qst = (int)p.q_st, kst = (int)p.k_st, vst = v_st;
     if (rem == C) {
       const __amdgpu_buffer_rsrc_t rq = buf_rsrc(qb), rk = buf_rsrc(kb), rv = buf_rsrc(vb);
       const uint32_t lq = (uint32_t)((x * qst + 8 * g) * 2), lk = (uint32_t)((x * kst + 8 * g) * 2);
@@ -511,7 +511,7 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
   }
 }
 
-template <int DK, bool FUSED, bool NORM>
+template <int DK, bool FUSED, bool NORM, bool SEG>
 __global__ void __launch_bounds__(256, 1)
 prefill_pair_kernel(const PrefillParams p) {
   typedef PairSmem<DK> Sm;
@@ -527,29 +527,39 @@ prefill_pair_kernel(const PrefillParams p) {
   int blk = blockIdx.x;
   const int nblk = gridDim.x;
   if ((nblk & 31) == 0) blk = (blk & 7) * (nblk >> 3) + (blk >> 3);
+  // unit (request r, segment j, value head h, slice); without segments (SEG
+  // false, an instantiation of its own) j = 0 and every slice is a value slice
   const int split = blk % p.nsplit;
   const int h = (blk / p.nsplit) % p.hv;
-  const int r = blk / (p.nsplit * p.hv);
+  const int rj = blk / (p.nsplit * p.hv);
+  const int r = SEG ? rj / p.nseg : rj, j = SEG ? rj % p.nseg : 0;
   const int qh = (int)(((int64_t)h * p.hq) / p.hv);
-  const int v0 = split * 64;
+  const bool trans = SEG && split >= p.nsv;  // transition slice of a local pass
+  const int v0 = (trans ? split - p.nsv : split) * 64;
 
   int64_t start, end;
-  if (p.cu) {
-    start = min(max((int64_t)p.cu[r], (int64_t)0), p.T);
-    end = min(max((int64_t)p.cu[r + 1], (int64_t)0), p.T);
-  } else {
-    start = (int64_t)r * p.seq_len;
-    end = start + p.seq_len;
-  }
-  if (end < start) end = start;
+  prefill_request_bounds(p, r, start, end);
+  if constexpr (SEG) prefill_segment_bounds(p.nseg, j, C, start, end);
   const int nch = (int)((end - start + C - 1) / C);
 
   const __bf16* __restrict__ gq = (const __bf16*)p.q + (int64_t)qh * p.q_sh;
   const __bf16* __restrict__ gk = (const __bf16*)p.k + (int64_t)qh * p.k_sh;
-  const __bf16* __restrict__ gv = (const __bf16*)p.v + (int64_t)h * p.v_sh + v0;
+  // a transition slice reads V as zeros: every row from the same 128 zero bytes
+  const __bf16* __restrict__ gv = trans ? (const __bf16*)p.vzero : (const __bf16*)p.v + (int64_t)h * p.v_sh + v0;
+  const int v_st = trans ? 0 : (int)p.v_st;
   __bf16* __restrict__ gout = (__bf16*)p.out + (int64_t)h * p.o_sh + v0;
   int64_t ibase, fbase;
-  prefill_state_offsets(p, r, h, v0, DK, ibase, fbase);
+  if (SEG && p.seg_mode == 1) {
+    // value slices: V-major rows v0.. of the segment's state; transition
+    // slices: the dk x dk transition block, stored K-major (see below)
+    ibase = -1;
+    fbase = (((int64_t)rj * p.hv + h) * (p.dv + DK) + (trans ? p.dv : v0)) * DK;
+  } else if (SEG) {  // seg_mode 2
+    ibase = (((int64_t)rj * p.hv + h) * p.dv + v0) * DK;
+    fbase = -1;
+  } else {
+    prefill_state_offsets(p, r, h, v0, DK, ibase, fbase);
+  }
   if ((p.pool_flags & kPoolSkipUnread) && ibase < 0) return;  // uniform over the workgroup
 
   // The readout pairs each diagonal block of M with the block to its right,
@@ -566,8 +576,8 @@ prefill_pair_kernel(const PrefillParams p) {
   lds_barrier();
 
   if (wave >= 2) {
-    if (wave == 2) pair_prep<DK, 0, FUSED, NORM>(p, sm, start, end, nch, gq, gk, gv, h);
-    else pair_prep<DK, 1, FUSED, NORM>(p, sm, start, end, nch, gq, gk, gv, h);
+    if (wave == 2) pair_prep<DK, 0, FUSED, NORM>(p, sm, start, end, nch, gq, gk, gv, v_st, h);
+    else pair_prep<DK, 1, FUSED, NORM>(p, sm, start, end, nch, gq, gk, gv, v_st, h);
     return;
   }
 
@@ -584,7 +594,17 @@ prefill_pair_kernel(const PrefillParams p) {
       for (int ct = 0; ct < 2; ++ct)
         S[j][ct] = *reinterpret_cast<const f4*>(p.init + ibase + (int64_t)(32 * w + 16 * ct + x) * DK +
                                                 dk_of<NKT>(j, 4 * g));
+  } else if (trans) {
+    // the key identity: row i = v0 + column of the V-major state is e_i
+#pragma unroll
+    for (int j = 0; j < NKT; ++j)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          S[j][ct][e] = dk_of<NKT>(j, 4 * g) + e == v0 + 32 * w + 16 * ct + x ? 1.f : 0.f;
   }
+  const bool store_out = !SEG || p.seg_mode != 1;
   const int ost = (int)p.o_st;
 
   for (int c = -1; c < nch; ++c) {
@@ -713,7 +733,7 @@ prefill_pair_kernel(const PrefillParams p) {
       }
       // ---- outputs (scale is folded into Gam and M)
       const int64_t tok0 = start + (int64_t)c * C;
-      const int nvalid = (int)min((int64_t)C, end - tok0);
+      const int nvalid = store_out ? (int)min((int64_t)C, end - tok0) : 0;
       __bf16* ob = gout + tok0 * p.o_st + 32 * w;
       if (nvalid == C) {
         // Y^T tiles: lane (x, g) holds columns 16 ct + 4 g .. +3 of token
@@ -743,7 +763,17 @@ prefill_pair_kernel(const PrefillParams p) {
     }
     lds_barrier();
   }
-  if (fbase >= 0) {
+  if (SEG && fbase >= 0 && trans) {
+    // transition slice: element (key k, column i) of the K-major state is
+    // P[k][i]; stored at k * DK + i, so a row of the block is a key's row of P
+#pragma unroll
+    for (int j = 0; j < NKT; ++j)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          p.fin[fbase + (int64_t)(dk_of<NKT>(j, 4 * g) + e) * DK + v0 + 32 * w + 16 * ct + x] = S[j][ct][e];
+  } else if (fbase >= 0) {
 #pragma unroll
     for (int j = 0; j < NKT; ++j)
 #pragma unroll
@@ -760,14 +790,22 @@ inline bool prefill_pair_supported(int dk, int dv, int chunk_hint) {
 
 template <int DK>
 hipError_t launch_prefill_pair_t(PrefillParams p, hipStream_t stream) {
-  p.nsplit = p.dv / 64;
-  const int64_t nblk = (int64_t)p.n_seqs * p.hv * p.nsplit;
+  p.nsv = p.dv / 64;
+  p.nsplit = p.nsv + (p.seg_mode == 1 ? DK / 64 : 0);
+  const int64_t nblk = (int64_t)p.n_seqs * p.nseg * p.hv * p.nsplit;
   const dim3 grid((unsigned)nblk), block(256);
   const bool fused = p.ga || p.gb;
-  if (fused && p.qk_norm) hipLaunchKernelGGL((prefill_pair_kernel<DK, true, true>), grid, block, 0, stream, p);
-  else if (fused) hipLaunchKernelGGL((prefill_pair_kernel<DK, true, false>), grid, block, 0, stream, p);
-  else if (p.qk_norm) hipLaunchKernelGGL((prefill_pair_kernel<DK, false, true>), grid, block, 0, stream, p);
-  else hipLaunchKernelGGL((prefill_pair_kernel<DK, false, false>), grid, block, 0, stream, p);
+#define GDN_PAIR_LAUNCH(SEG)                                                                                   \
+  if (fused && p.qk_norm) hipLaunchKernelGGL((prefill_pair_kernel<DK, true, true, SEG>), grid, block, 0, stream, p); \
+  else if (fused) hipLaunchKernelGGL((prefill_pair_kernel<DK, true, false, SEG>), grid, block, 0, stream, p);       \
+  else if (p.qk_norm) hipLaunchKernelGGL((prefill_pair_kernel<DK, false, true, SEG>), grid, block, 0, stream, p);   \
+  else hipLaunchKernelGGL((prefill_pair_kernel<DK, false, false, SEG>), grid, block, 0, stream, p);
+  if (p.seg_mode) {
+    GDN_PAIR_LAUNCH(true)
+  } else {
+    GDN_PAIR_LAUNCH(false)
+  }
+#undef GDN_PAIR_LAUNCH
   return hipGetLastError();
 }
 

@@ -196,8 +196,14 @@ typedef struct {
   int64_t pool_slot_stride, pool_head_stride;
   const int32_t* read_slot;  /* [n_seqs] or NULL                             */
   const int32_t* write_slot; /* [n_seqs] or NULL                             */
-  /* Caller-provided scratch (appended).  No prefill kernel uses scratch
-   * memory: gdn_prefill_workspace_size() returns 0 and these are ignored. */
+  /* Caller-provided device scratch (appended), 256-byte aligned.  With
+   * workspace_bytes >= gdn_prefill_workspace_size(args) > 0 the call runs as
+   * a scan over the affine maps of request segments (three launches; see
+   * gdn_prefill_workspace_size); otherwise, and whenever that size is 0, the
+   * workspace is ignored and every (request, head) is one serial walk over
+   * its chunks.  Both compute the same result up to rounding order.  The
+   * library neither allocates nor keeps the workspace; calls that share one
+   * workspace on overlapping streams race. */
   void* workspace;
   size_t workspace_bytes;
   /* Per-key decay (appended): with decay_per_key != 0, decay is
@@ -211,8 +217,23 @@ typedef struct {
   int32_t decay_per_key;
 } gdn_prefill_args;
 
-/* Device scratch bytes a gdn_prefill call with these arguments needs: always
- * 0 (every intermediate lives in registers and LDS).  args may be NULL. */
+/* Device scratch bytes a gdn_prefill call with these arguments can use; 0
+ * when it needs none (args may be NULL: 0).
+ *
+ * Over any run of tokens the recurrence maps the state entering the run to
+ * the state leaving it by an affine map S_out = P S_in + R ("Gated DeltaNet
+ * State Update", statement: every step is affine in S), and the chunk is a
+ * scheduling choice ("com.microsoft.GatedDeltaNet", Attributes, chunk_size).
+ * A call with few (request, value head) units and long requests -- bf16,
+ * dk and dv in {64, 128}, the default chunk, scalar decay, gates not mixed,
+ * and a serial walk that would fill at most 64 workgroups -- is cut into
+ * nseg segments per request (nseg between 4 and 64, chosen from the sizes
+ * alone: about 512 workgroups in the first launch, segments of 16 chunks or
+ * more on average).  The size is
+ *     n_seqs * nseg * hv * dk * (2 dv + dk) * 4 bytes
+ * (each segment's map, then each segment's incoming state), at most about
+ * 25 MiB for such calls.  Sizes only decide it: the same arguments give the
+ * same size on every device. */
 size_t gdn_prefill_workspace_size(const gdn_prefill_args* args);
 
 gdn_status gdn_prefill(const gdn_prefill_args* args, void* stream);

@@ -183,6 +183,15 @@ def mtp_decode_b64_t4():
                          dv=64, dtype="bf16", scatter=True)
 
 
+def long_request_b1_s65536_hv4():
+    """One request of 65536 tokens with few heads: Hq=2, Hv=4, Dk=Dv=128,
+    bf16 q/k/v, qwen gates drawn as for the chunked-prefill workload, zero
+    initial state, scale 1/sqrt(128).  Its serial walk fills only 8
+    workgroups; it is the case the scan over segment maps is for."""
+    return prefill_inputs(13, lengths=[65536], hq=2, hv=4, dk=128, dv=128, dtype="bf16",
+                          gate="qwen")
+
+
 def conv1d_inputs(seed: int, *, lengths, conv_dim, kernel_size=4, max_slots=8, dtype="bf16",
                   slots=None, state_std=1.0, x_std=1.0):
     """Inputs for one conv1d call (all CPU tensors), after the page example of

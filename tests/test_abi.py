@@ -194,9 +194,48 @@ def test_prefill_pool_mode_accepted_before_launch(lib):
     assert lib.gdn_prefill(ctypes.byref(a), None) == 0, lib.gdn_last_error()
 
 
-def test_prefill_needs_no_workspace(lib):
+def test_prefill_workspace_size(lib):
+    """0 for calls that run as serial walks; for one long request with few
+    heads the scan's workspace n_seqs * nseg * hv * dk * (2 dv + dk) * 4 bytes,
+    with nseg from the sizes alone (about 512 local-pass workgroups, segments
+    of 16 chunks or more, 4 <= nseg <= 64)."""
     assert lib.gdn_prefill_workspace_size(None) == 0
     assert lib.gdn_prefill_workspace_size(ctypes.byref(_prefill())) == 0
+    def one_long(**over):
+        kw = dict(n_seqs=1, seq_len=65536, total_tokens=65536, hq=2, hv=4, dk=128, dv=128,
+                  q_stride_token=256, k_stride_token=256, q_stride_head=128, k_stride_head=128,
+                  v_stride_token=512, out_stride_token=512, v_stride_head=128, out_stride_head=128)
+        kw.update(over)
+        return lib.gdn_prefill_workspace_size(ctypes.byref(_prefill(**kw)))
+    # 512 / (1 * 4 * (256 / 64)) = 32 segments of 32 chunks
+    assert one_long() == 1 * 32 * 4 * 128 * (2 * 128 + 128) * 4
+    # dk = dv = 64: 512 / (4 * 2) = 64 segments
+    assert one_long(dk=64, dv=64) == 1 * 64 * 4 * 64 * (2 * 64 + 64) * 4
+    # shorter request: segments of at least 16 chunks -> 8192 / 64 / 16 = 8
+    assert one_long(seq_len=8192, total_tokens=8192) == 8 * 4 * 128 * 384 * 4
+    # too short for 4 segments, too many heads, fp32, per-key decay, a chunk hint,
+    # mixed gates: serial walks, no workspace
+    assert one_long(seq_len=2048, total_tokens=2048) == 0
+    # Hv = 32: the serial walk fills 64 workgroups, 4 segments still pay;
+    # Hv = 64 fills 128 and keeps the serial walk
+    assert one_long(hv=32, hq=16, q_stride_token=2048, k_stride_token=2048,
+                    v_stride_token=4096, out_stride_token=4096) == 4 * 32 * 128 * 384 * 4
+    assert one_long(hv=64, hq=16, q_stride_token=2048, k_stride_token=2048,
+                    v_stride_token=8192, out_stride_token=8192) == 0
+    assert one_long(io_dtype=L.GDN_F32) == 0
+    assert one_long(decay_per_key=1) == 0
+    assert one_long(chunk_size=32) == 0
+    assert one_long(beta=None, gate_b=FAKE * 8) == 0
+    # the size is at most about 25 MiB whenever it is not 0
+    for hv in (1, 2, 4, 8):
+        for d in (64, 128):
+            for n in (1, 2):
+                sz = one_long(hv=hv, dk=d, dv=d, n_seqs=n, seq_len=65536 // n,
+                              q_stride_token=hv * d, k_stride_token=hv * d,
+                              q_stride_head=d, k_stride_head=d, hq=hv,
+                              v_stride_token=hv * d, out_stride_token=hv * d,
+                              v_stride_head=d, out_stride_head=d)
+                assert sz <= 26 * 1024 * 1024
 
 
 def test_prefill_null_args_and_noop(lib):
