@@ -24,7 +24,8 @@ from . import _lib
 from ._lib import GdnError
 
 __all__ = ["gate", "prefill", "decode", "conv1d", "state_update", "version", "GdnError",
-           "prefill_args", "decode_args", "conv1d_args", "prefill_workspace_size"]
+           "prefill_args", "decode_args", "conv1d_args", "prefill_workspace_size",
+           "prefill_noalloc"]
 
 _DT = {torch.float32: _lib.GDN_F32, torch.bfloat16: _lib.GDN_BF16}
 # update_rule of the ONNX card -> gdn_update_rule
@@ -387,6 +388,27 @@ def prefill(q, k, v, decay, beta, *, decay_kind="log", cu_seqlens=None, initial_
             args.workspace, args.workspace_bytes = ws.data_ptr(), need
     _lib.check(lib.gdn_prefill(ctypes.byref(args), _stream(stream)))
     del keep, ws
+    return out, final_state
+
+
+def prefill_noalloc(q, k, v, decay, beta, *, stream=None, **kw):
+    """prefill through gdn_prefill_noalloc: the same call and result as
+    prefill, with any scratch taken from the library's static per-device
+    array instead of an allocated workspace (for callers that cannot
+    allocate; calls that overlap on one device race).  q, k, v in float32 or
+    bfloat16 with head sizes of 16, 32, 64 or 128; out and final_state are
+    allocated here when not given.  Returns (out, final_state)."""
+    for name in ("scan", "workspace"):
+        if name in kw:
+            raise ValueError("prefill_noalloc takes no %s argument" % name)
+    for name, t in (("q", q), ("k", k), ("v", v), ("decay", decay), ("beta", beta)):
+        _dev(t, name)
+    for name, t in kw.items():
+        if isinstance(t, torch.Tensor):
+            _dev(t, name)
+    args, keep, out, final_state = prefill_args(q, k, v, decay, beta, **kw)
+    _lib.check(_lib.load().gdn_prefill_noalloc(ctypes.byref(args), _stream(stream)))
+    del keep
     return out, final_state
 
 

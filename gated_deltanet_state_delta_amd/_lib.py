@@ -21,7 +21,8 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_
 
 # every extern "C" symbol include/libgdn.h declares
 EXPORTED = ("gdn_last_error", "gdn_version", "gdn_gate", "gdn_prefill", "gdn_prefill_workspace_size",
-            "gdn_decode", "gdn_conv1d")
+            "gdn_prefill_noalloc", "gdn_decode", "gdn_conv1d")
+NOALLOC_SCRATCH_BYTES = 32 << 20  # GDN_NOALLOC_SCRATCH_BYTES
 
 _i32, _i64, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 
@@ -100,6 +101,8 @@ def load(path: str | None = None):
         lib.gdn_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillArgs)]
         lib.gdn_prefill.restype = ctypes.c_int
         lib.gdn_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
+        lib.gdn_prefill_noalloc.restype = ctypes.c_int
+        lib.gdn_prefill_noalloc.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
         lib.gdn_decode.restype = ctypes.c_int
         lib.gdn_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
         lib.gdn_conv1d.restype = ctypes.c_int

@@ -7,6 +7,7 @@
 // prescribe: clamping and skipping, never faulting.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -29,6 +30,32 @@ gdn_status fail(gdn_status s, const char* fmt, ...) {
 gdn_status from_hip(hipError_t e, const char* what) {
   if (e == hipSuccess) return GDN_OK;
   return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Static device scratch of gdn_prefill_noalloc: one copy per device, held
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: only the address hipGetSymbolAddress returns for the
+// current device is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+// The current device's address of `scratch`, looked up once per device (with
+// that device current) and kept.
+hipError_t noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> cache[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* ptr = cache[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    cache[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return hipSuccess;
 }
 
 bool head_size_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
@@ -66,10 +93,10 @@ size_t gdn_prefill_workspace_size(const gdn_prefill_args* args) {
   return args ? gdn::prefill_workspace_bytes(*args) : 0;
 }
 
-gdn_status gdn_prefill(const gdn_prefill_args* p, void* stream) {
-  g_err[0] = 0;
-  if (!p) return fail(GDN_ERR_NULL, "gdn_prefill: args is NULL");
-  const gdn_prefill_args& a = *p;
+// Every host-visible check of a gdn_prefill call, in order; *noop is set
+// when the call is valid and has nothing to do (n_seqs == 0).
+static gdn_status prefill_check(const gdn_prefill_args& a, bool* noop) {
+  *noop = false;
   if (a.io_dtype != GDN_F32 && a.io_dtype != GDN_BF16) return fail(GDN_ERR_DTYPE, "gdn_prefill: io_dtype %d", a.io_dtype);
   if (a.decay_kind != GDN_DECAY_LOG && a.decay_kind != GDN_DECAY_GAMMA)
     return fail(GDN_ERR_DTYPE, "gdn_prefill: decay_kind %d", a.decay_kind);
@@ -123,7 +150,10 @@ gdn_status gdn_prefill(const gdn_prefill_args* p, void* stream) {
   } else if (a.read_slot || a.write_slot) {
     return fail(GDN_ERR_SHAPE, "gdn_prefill: read_slot / write_slot need state_pool");
   }
-  if (a.n_seqs == 0) return GDN_OK;
+  if (a.n_seqs == 0) {
+    *noop = true;
+    return GDN_OK;
+  }
   if (!a.final_state && !a.state_pool) return fail(GDN_ERR_NULL, "gdn_prefill: final_state is NULL");
   if (a.total_tokens > 0 && (!a.q || !a.k || !a.v || !a.out))
     return fail(GDN_ERR_NULL, "gdn_prefill: q, k, v and out are required");
@@ -152,7 +182,41 @@ gdn_status gdn_prefill(const gdn_prefill_args* p, void* stream) {
     if (i0 < f0 + bytes && f0 < i0 + bytes)
       return fail(GDN_ERR_LAYOUT, "gdn_prefill: initial_state and final_state partially overlap");
   }
-  return from_hip(gdn::launch_prefill(a, (hipStream_t)stream), "gdn_prefill launch");
+  return GDN_OK;
+}
+
+gdn_status gdn_prefill(const gdn_prefill_args* p, void* stream) {
+  g_err[0] = 0;
+  if (!p) return fail(GDN_ERR_NULL, "gdn_prefill: args is NULL");
+  bool noop = false;
+  const gdn_status st = prefill_check(*p, &noop);
+  if (st != GDN_OK || noop) return st;
+  return from_hip(gdn::launch_prefill(*p, (hipStream_t)stream), "gdn_prefill launch");
+}
+
+gdn_status gdn_prefill_noalloc(const gdn_prefill_args* p, void* stream) {
+  g_err[0] = 0;
+  if (!p) return fail(GDN_ERR_NULL, "gdn_prefill_noalloc: args is NULL");
+  bool noop = false;
+  const gdn_status st = prefill_check(*p, &noop);
+  if (st != GDN_OK || noop) return st;
+  const size_t need = gdn::prefill_workspace_bytes(*p);
+  if (need > (size_t)GDN_NOALLOC_SCRATCH_BYTES)
+    return fail(GDN_ERR_UNSUPPORTED,
+                "gdn_prefill_noalloc: the call needs %zu bytes of scratch, more than the %zu of the static array "
+                "(use gdn_prefill with a workspace)",
+                need, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+  gdn_prefill_args a = *p;
+  a.workspace = nullptr;
+  a.workspace_bytes = 0;
+  if (need > 0) {
+    void* ptr = nullptr;
+    const hipError_t e = noalloc_scratch(&ptr);
+    if (e != hipSuccess) return from_hip(e, "gdn_prefill_noalloc: static scratch address");
+    a.workspace = ptr;
+    a.workspace_bytes = GDN_NOALLOC_SCRATCH_BYTES;
+  }
+  return from_hip(gdn::launch_prefill(a, (hipStream_t)stream), "gdn_prefill_noalloc launch");
 }
 
 gdn_status gdn_decode(const gdn_decode_args* p, void* stream) {

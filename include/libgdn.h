@@ -239,6 +239,27 @@ size_t gdn_prefill_workspace_size(const gdn_prefill_args* args);
 gdn_status gdn_prefill(const gdn_prefill_args* args, void* stream);
 
 /* ----------------------------------------------------------------------------
+ * gdn_prefill_noalloc -- gdn_prefill for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.
+ *
+ * Runs exactly what gdn_prefill runs with a workspace of
+ * gdn_prefill_workspace_size(args) bytes, taking that workspace from a static
+ * device array of GDN_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on
+ * every device it runs on until the process ends; args->workspace and
+ * args->workspace_bytes are ignored.  It allocates and frees nothing.  A call
+ * whose workspace size exceeds the array returns GDN_ERR_UNSUPPORTED (the
+ * segment choice keeps every call within about 25 MiB).  Argument errors and
+ * results are those of gdn_prefill.
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents: calls that overlap on one device (other streams, other
+ * threads) race and must be serialised by the caller.  The array needs no
+ * clearing -- each call writes every scratch byte it reads.
+ * ------------------------------------------------------------------------- */
+#define GDN_NOALLOC_SCRATCH_BYTES (32u << 20)
+gdn_status gdn_prefill_noalloc(const gdn_prefill_args* args, void* stream);
+
+/* ----------------------------------------------------------------------------
  * gdn_decode -- one fused launch over a slot-indexed fp32 state pool.
  *
  * Contract of "flashinfer.cake_gdp.cake_gated_delta_product_mtp" (parameters

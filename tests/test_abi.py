@@ -238,6 +238,25 @@ def test_prefill_workspace_size(lib):
                 assert sz <= 26 * 1024 * 1024
 
 
+def test_prefill_noalloc_host_checks(lib):
+    """gdn_prefill_noalloc refuses what gdn_prefill refuses, before any
+    launch, and every call the scan plan can choose fits its static array."""
+    assert lib.gdn_prefill_noalloc(None, None) == 1
+    assert b"gdn_prefill_noalloc" in lib.gdn_last_error()
+    for over, status in PREFILL_ERRORS:
+        assert lib.gdn_prefill_noalloc(ctypes.byref(_prefill(**over)), None) == status
+    a = _prefill(n_seqs=0, seq_len=0, total_tokens=0)
+    assert lib.gdn_prefill_noalloc(ctypes.byref(a), None) == 0
+    for hv in (1, 2, 4, 8, 16, 32):
+        for d in (64, 128):
+            for n in (1, 2, 3):
+                a = _prefill(n_seqs=n, seq_len=(1 << 20) // n, total_tokens=((1 << 20) // n) * n,
+                             hq=hv, hv=hv, dk=d, dv=d, q_stride_token=hv * d, k_stride_token=hv * d,
+                             q_stride_head=d, k_stride_head=d, v_stride_token=hv * d,
+                             out_stride_token=hv * d, v_stride_head=d, out_stride_head=d)
+                assert lib.gdn_prefill_workspace_size(ctypes.byref(a)) <= L.NOALLOC_SCRATCH_BYTES
+
+
 def test_prefill_null_args_and_noop(lib):
     assert lib.gdn_prefill(None, None) == 1
     a = _prefill(n_seqs=0, seq_len=0, total_tokens=0)
