@@ -85,6 +85,17 @@ __device__ __forceinline__ void st_nt(float* p, f4 v) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
 }
+// A resource covering `bytes` bytes from `base` (accesses past them read
+// zeros and touch no memory), its fields taken through readfirstlane so the
+// compiler keeps it in SGPRs (a resource it cannot prove uniform makes it
+// loop over the lanes' distinct values).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc_n(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, (int)n, 0x00020000);
+}
 template <typename E> __device__ __forceinline__ E buf_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
 template <> __device__ __forceinline__ __bf16 buf_load<__bf16>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(__bf16, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));

@@ -82,12 +82,11 @@ struct PairSmem {
   // A_ii[r][2 jj + h]; padded rows and blocks keep the row reads of the four
   // blocks on distinct banks)
   alignas(16) float adiag[2][NT][16 * 20 + 4];
-  // (I + A_ii)^-1 of the current chunk, bf16 (blocks 2w, 2w+1 written by
-  // state wave w)
-  alignas(16) __bf16 tinv[NT][16][LDT];
+  // (I + A_ii)^-1 of the current chunk, bf16: one copy per state wave, each
+  // computed by that wave alone
+  alignas(16) __bf16 tinv[2][NT][16][LDT];
   int prep_cnt;  // staging halves written by the prep waves so far
   int nrm_cnt;   // norm halves written by the prep waves so far (L2 norm only)
-  int inv_cnt;   // inverse halves written by the state waves so far
 };
 
 // 16-byte slot permutation of a Q/K row.
@@ -155,16 +154,17 @@ __device__ __forceinline__ int wave_scan_max(int v) {
   return v;
 }
 
-// One prep wave's half of a chunk, as loaded from global memory: Q and K
-// tiles 2pw and 2pw+1 (16-byte fragment rows: row 16i + x, keys 32pp + 8g
-// .. +7), V rows 32pw .. 32pw+31 (row 32pw + 8u + lane/8, columns 8 (lane % 8)
-// .. +7), and the gate of token `lane`.  (Loads of 16 rows x 64 bytes measured
-// faster here than loads of 4 rows x 256 bytes.)
+// One prep wave's half of a chunk, as loaded from global memory: Q and K rows
+// 32pw .. 32pw+31 as whole rows, DK/8 lanes per row (load u: row 32pw +
+// RPL u + lane / (DK/8), 16-byte slot lane % (DK/8), RPL = 512 / DK rows per
+// load), so each load covers whole 128-byte lines; V rows 32pw .. 32pw+31
+// (row 32pw + 8u + lane/8, columns 8 (lane % 8) .. +7); the gate of token
+// `lane`.
 template <int DK>
 struct PairPrepSet {
-  static constexpr int NPP = DK / 32;
-  u32x4 q[2][NPP];
-  u32x4 k[2][NPP];
+  static constexpr int NLD = DK / 16;  // loads of whole rows per operand
+  u32x4 q[NLD];
+  u32x4 k[NLD];
   u32x4 v[4];
   float gd, bt;      // decay and beta of token `lane` as loaded (clamped to the chunk)
   __bf16 ga, gbr;    // or the fused gate's raw a and b
@@ -220,6 +220,51 @@ __device__ __forceinline__ void pair_tri_inverse(const float (*ad)[16 * 20 + 4],
   *reinterpret_cast<bf4*>(&tout[i][r][8 * h + 4]) = to_bf4(f4{o[4], o[5], o[6], o[7]});
 }
 
+// One right-looking step of pair_tri_inverse4 and the steps below it: with
+// t = T[r][K] final, T[r][j] -= t A[K][j] for every j < K, where A[K][j] is
+// row K's value held by lane K of this lane's 16-lane row, broadcast with
+// DPP row_newbcast:K.  The entry step K-1 reads first is updated first.
+template <int K>
+__device__ __forceinline__ void tri_inverse_steps(float (&acc)[16], const float (&arow)[16]) {
+  const float t = acc[K];
+  acc[K - 1] -= t * dpp_f<0x150 + K, 0xF>(0.f, arow[K - 1]);
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) acc[j] -= t * dpp_f<0x150 + K, 0xF>(0.f, arow[j]);
+  if constexpr (K > 1) tri_inverse_steps<K - 1>(acc, arow);
+}
+
+// Inverses of the four unit-lower diagonal blocks I + A_i of a chunk (A_i
+// strictly lower, fp32 rows in `ad` as the prep waves lay them out: row k of
+// block i at ad[i][20 k ..], A_i[k][j] at 20 k + 8 (j & 1) + (j >> 1)).
+// Lane l owns row r = l % 16 of block i = l / 16 -- block i is DPP row i --
+// holding row r of A_i and row r of T_i = (I + A_i)^-1 in registers.
+// Right-looking: T[r][j] = [j == r] - sum_{k > j} T[r][k] A[k][j]; with k
+// falling from 15, T[r][k] is final when step k reads it (entries k > r
+// stay 0: T is lower triangular), and row k of A comes from lane k by a DPP
+// broadcast, so the steps touch neither LDS nor other rows' registers.
+// Writes row r of T_i in bf16 to tout[i][r][0..15].
+template <int LDT>
+__device__ __forceinline__ void pair_tri_inverse4(const float (*ad)[16 * 20 + 4], __bf16 (*tout)[16][LDT],
+                                                  int lane) {
+  const int i = lane >> 4, r = lane & 15;
+  const float* a = &ad[i][20 * r];
+  const f4 e0 = *reinterpret_cast<const f4*>(a);       // A[r][0, 2, 4, 6]
+  const f4 e1 = *reinterpret_cast<const f4*>(a + 4);   // A[r][8, 10, 12, 14]
+  const f4 o0 = *reinterpret_cast<const f4*>(a + 8);   // A[r][1, 3, 5, 7]
+  const f4 o1 = *reinterpret_cast<const f4*>(a + 12);  // A[r][9, 11, 13, 15]
+  float arow[16], acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int jj = j >> 1;
+    arow[j] = (j & 1) ? (jj < 4 ? o0[jj] : o1[jj - 4]) : (jj < 4 ? e0[jj] : e1[jj - 4]);
+    acc[j] = j == r ? 1.f : 0.f;
+  }
+  tri_inverse_steps<15>(acc, arow);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<bf4*>(&tout[i][r][4 * q]) = to_bf4(f4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]});
+}
+
 // Prep wave PW of the pair kernel (see the header comment).  FUSED: the gates
 // come from A_log, dt_bias, a, b (computed here); NORM: the in-kernel q/k L2
 // norm.  Each combination is its own instantiation, so none carries branches
@@ -241,79 +286,76 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
   const float ealog = fused ? expf(p.A_log[h & p.dmask]) : 0.f, dtb = fused ? p.dt_bias[h & p.dmask] : 0.f;
   constexpr bool nrm = NORM;
 
-  auto prefetch = [&](int c, PairPrepSet<DK>& s) {
-    const int64_t t0 = start + (int64_t)c * C;
-    const int rem = (int)min((int64_t)C, end - t0);  // >= 1
-    {
-      // the values exactly as loaded: nothing here may wait on these loads
-      // (padding and the fused gate are applied when the set is staged)
-      const int tl = min(lane, rem - 1);
-      const int64_t tok = (t0 + tl) * p.hv;
+  // Loads chunk c into `s`: always the same 22 buffer loads, whether or not
+  // the chunk exists, so that the compiler counts the loads in flight
+  // exactly -- a branch around them makes that count conservative, and then
+  // every iteration waits for the other set's loads too.  Every offset is in
+  // the VGPR offset, which the buffer range check covers: rows past the
+  // chunk's last token, and every row of a chunk past the request
+  // (num_records 0), read zeros without touching memory.  The values are
+  // kept exactly as loaded: nothing here may wait on these loads (padding
+  // and the fused gate are applied when the set is staged).
+  auto prefetch = [&](int c, PairPrepSet<DK>& s, int part) {
+    const bool have = c < nch;
+    const int64_t t0 = start + (int64_t)(have ? c : 0) * C;
+    const int rem = have ? (int)min((int64_t)C, end - t0) : 1;  // rows of the chunk
+    const int qst = (int)p.q_st, kst = (int)p.k_st, vst = v_st;
+    auto rsrc = [&](const void* base, int bytes) { return buf_rsrc_n(base, have ? (uint32_t)bytes : 0u); };
+    if (part == 0) {
+      const uint32_t toff = (uint32_t)(min(lane, rem - 1) * p.hv);  // token `lane`, clamped to the chunk
       if constexpr (FUSED) {
-        s.ga = gga[tok & p.dmask];
-        s.gbr = ggb[tok & p.bmask];
+        s.ga = buf_load<__bf16>(rsrc(gga + ((t0 * p.hv) & p.dmask), -1), (toff & (uint32_t)p.dmask) * 2, 0);
+        s.gbr = buf_load<__bf16>(rsrc(ggb + ((t0 * p.hv) & p.bmask), -1), (toff & (uint32_t)p.bmask) * 2, 0);
       } else {
-        s.gd = gdec[tok & p.dmask];
-        s.bt = gbet[tok & p.bmask];
+        s.gd = buf_load<float>(rsrc(gdec + ((t0 * p.hv) & p.dmask), -1), (toff & (uint32_t)p.dmask) * 4, 0);
+        s.bt = buf_load<float>(rsrc(gbet + ((t0 * p.hv) & p.bmask), -1), (toff & (uint32_t)p.bmask) * 4, 0);
       }
     }
-    const __bf16* qb = gq + t0 * p.q_st;
-    const __bf16* kb = gk + t0 * p.k_st;
-    const __bf16* vb = gv + t0 * v_st;
-    const int qst = (int)p.q_st, kst = (int)p.k_st, vst = v_st;
-    if (rem == C) {
-      const __amdgpu_buffer_rsrc_t rq = buf_rsrc(qb), rk = buf_rsrc(kb), rv = buf_rsrc(vb);
-      const uint32_t lq = (uint32_t)((x * qst + 8 * g) * 2), lk = (uint32_t)((x * kst + 8 * g) * 2);
+    // in range: the bytes up to the end of row rem - 1
+    const __amdgpu_buffer_rsrc_t rq = rsrc(gq + t0 * p.q_st, ((rem - 1) * qst + DK) * 2);
+    const __amdgpu_buffer_rsrc_t rk = rsrc(gk + t0 * p.k_st, ((rem - 1) * kst + DK) * 2);
+    const __amdgpu_buffer_rsrc_t rv = rsrc(gv + t0 * v_st, ((rem - 1) * vst + 64) * 2);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int pp = 0; pp < NPP; ++pp) {
-          s.q[i][pp] = buf_load16(rq, lq, (uint32_t)((16 * (2 * PW + i) * qst + 32 * pp) * 2));
-          s.k[i][pp] = buf_load16(rk, lk, (uint32_t)((16 * (2 * PW + i) * kst + 32 * pp) * 2));
-        }
-      const uint32_t lv = (uint32_t)(((lane >> 3) * vst + 8 * (lane & 7)) * 2);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) s.v[u] = buf_load16(rv, lv, (uint32_t)((32 * PW + 8 * u) * vst * 2));
-    } else {
-      auto ld = [&](const __bf16* base, int st, int row, int col) -> u32x4 {
-        const u32x4 val = *reinterpret_cast<const u32x4*>(base + (int64_t)min(row, rem - 1) * st + col);
-        return val & (row < rem ? 0xffffffffu : 0u);
-      };
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int pp = 0; pp < NPP; ++pp) {
-          s.q[i][pp] = ld(qb, qst, 16 * (2 * PW + i) + x, 32 * pp + 8 * g);
-          s.k[i][pp] = ld(kb, kst, 16 * (2 * PW + i) + x, 32 * pp + 8 * g);
-        }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) s.v[u] = ld(vb, vst, 32 * PW + 8 * u + (lane >> 3), 8 * (lane & 7));
+    for (int u = 0; u < DK / 16; ++u) {
+      const int row = 32 * PW + (512 / DK) * u + lane / (DK / 8), slot = lane % (DK / 8);
+      if (part == 1) s.q[u] = buf_load16(rq, (uint32_t)((row * qst + 8 * slot) * 2), 0);
+      if (part == 2) s.k[u] = buf_load16(rk, (uint32_t)((row * kst + 8 * slot) * 2), 0);
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (part == 0)
+        s.v[u] = buf_load16(rv, (uint32_t)(((32 * PW + 8 * u + (lane >> 3)) * vst + 8 * (lane & 7)) * 2), 0);
   };
 
   auto frag_col = [&](int row, int pp) -> int { return 8 * pair_swz(row, 4 * pp + g); };
 
   int staged = 0;  // chunks staged by this wave so far
-  // One iteration: prepare chunk c+1 from `s`, then refill `s` with chunk c+3.
+  // One iteration: prepare chunk c+1 from `s`, and refill `s` with chunk c+3
+  // in three batches spread over the iteration (gates and V, then Q, then K),
+  // so that each batch finds the memory pipeline with room and the wave does
+  // not stall issuing 22 loads at once.  The iteration has no branches: past
+  // the request's last chunk it runs on zeros (the loads of a missing chunk
+  // read zeros) into the buffer no state wave reads any more.  Loads behind a
+  // branch make the compiler's count of loads in flight conservative (every
+  // iteration would then wait for the other set's loads too), and loads on
+  // two paths get different registers and copies that wait for them.
   auto iter = [&](int c, PairPrepSet<DK>& s) {
-    if (c + 1 < nch) {
+    float gd = 0.f, btl = 0.f;
+    {
       typename Sm::Buf& B = sm.buf[(c + 1) & 1];
       // ---- stage this wave's half
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int pp = 0; pp < NPP; ++pp) {
-          const int r = 16 * (2 * PW + i) + x;
-          *reinterpret_cast<u32x4*>(&B.q[r][frag_col(r, pp)]) = s.q[i][pp];
-          *reinterpret_cast<u32x4*>(&B.k[r][frag_col(r, pp)]) = s.k[i][pp];
-        }
+      for (int u = 0; u < DK / 16; ++u) {
+        const int r = 32 * PW + (512 / DK) * u + lane / (DK / 8), slot = lane % (DK / 8);
+        *reinterpret_cast<u32x4*>(&B.q[r][8 * pair_swz(r, slot)]) = s.q[u];
+        *reinterpret_cast<u32x4*>(&B.k[r][8 * pair_swz(r, slot)]) = s.k[u];
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         *reinterpret_cast<u32x4*>(&B.v[32 * PW + 8 * u + (lane >> 3)][8 * (lane & 7)]) = s.v[u];
       // gates of token `lane`; padded tokens: no decay (log-decay 0 / gamma
       // 1) and beta 0
       const bool live = lane < (int)min((int64_t)C, end - (start + (int64_t)(c + 1) * C));
-      float gd, btl;
       if constexpr (FUSED) {  // an absent input: no decay, beta 1
         gd = live && p.dmask ? gate_log_decay_fast(ealog, dtb, (float)s.ga) : 0.f;
         btl = live ? (p.bmask ? sigmoid_fast((float)s.gbr) : 1.f) : 0.f;
@@ -321,13 +363,16 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
         gd = live ? s.gd : (p.decay_is_gamma ? 1.f : 0.f);
         btl = live ? s.bt : 0.f;
       }
-      // ---- signal this half written and refill the registers; the wait for
-      // the other prep wave's half comes after the scan.  Both prep waves
-      // stage every chunk, so that wait ends; its bound only guards against a
-      // wave that never arrives.
+      // ---- signal this half written; the wait for the other prep wave's
+      // half comes after the scan.  Both prep waves stage every chunk, so
+      // that wait ends; its bound only guards against a wave that never
+      // arrives.
       ++staged;
       if (lane == 0) __hip_atomic_fetch_add(&sm.prep_cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      if (c + 3 < nch) prefetch(c + 3, s);
+    }
+    prefetch(c + 3, s, 0);
+    {
+      typename Sm::Buf& B = sm.buf[(c + 1) & 1];
       // ---- decay scan (lane = token)
       typename Sm::Scan& sc = sm.scan[PW];
       bool reset;
@@ -352,6 +397,7 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
         sc.E[lane] = __builtin_amdgcn_exp2f(F - Fb0);
         sc.Fx[lane] = __builtin_amdgcn_exp2f(Fb1 - F);
       }
+      prefetch(c + 3, s, 1);
       for (int spin = 0; spin < (1 << 22); ++spin) {
         if (__hip_atomic_load(&sm.prep_cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= 2 * staged) break;
         __builtin_amdgcn_s_sleep(1);
@@ -409,6 +455,7 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
           qko[n] = mfma32(qko[n], kf[TM[n]], qf[TI[n]]);
         }
       }
+      prefetch(c + 3, s, 2);
       if constexpr (NORM) {
         // ---- in-kernel L2 norm: |k_t|^2 and |q_t|^2 are the diagonals of this
         // wave's diagonal tiles K K^T and Q Q^T (token t = 16i + x sits on lane
@@ -502,12 +549,17 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
     lds_barrier();
   };
 
+  // Two iterations per trip, both always run: (nch + 2) & ~1 barriers in all,
+  // matched by the state waves.
+  // The two first sets load in the loop's order (no instruction scheduled
+  // across), so the loop head's wait for `sa` leaves `sb` in flight.
   PairPrepSet<DK> sa, sb;
-  if (nch > 0) prefetch(0, sa);
-  if (nch > 1) prefetch(1, sb);
+  for (int part = 0; part < 3; ++part) prefetch(0, sa, part);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int part = 0; part < 3; ++part) prefetch(1, sb, part);
   for (int c = -1; c < nch; c += 2) {
     iter(c, sa);
-    if (c + 1 < nch) iter(c + 1, sb);
+    iter(c + 1, sb);
   }
 }
 
@@ -570,7 +622,6 @@ prefill_pair_kernel(const PrefillParams p) {
   }
   if (tid == 0) {
     sm.prep_cnt = 0;
-    sm.inv_cnt = 0;
     sm.nrm_cnt = 0;
   }
   lds_barrier();
@@ -607,12 +658,13 @@ prefill_pair_kernel(const PrefillParams p) {
   const bool store_out = !SEG || p.seg_mode != 1;
   const int ost = (int)p.o_st;
 
-  for (int c = -1; c < nch; ++c) {
-    if (c >= 0) {
+  // (nch + 2) & ~1 barriers, as the prep waves run them in pairs
+  const int nbar = (nch + 2) & ~1;
+  for (int c = -1; c < nbar - 1; ++c) {
+    if (c >= 0 && c < nch) {
       const typename Sm::Buf& B = sm.buf[c & 1];
-      // ---- (I + A_ii)^-1 for blocks 2w, 2w+1; the other wave does the rest
-      pair_tri_inverse<Sm::LDT>(sm.adiag[c & 1], sm.tinv, 2 * w, lane);
-      if (lane == 0) __hip_atomic_fetch_add(&sm.inv_cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      // ---- (I + A_ii)^-1 of the four diagonal blocks, this wave's own copy
+      pair_tri_inverse4<Sm::LDT>(sm.adiag[c & 1], sm.tinv[w], lane);
       // ---- R_K = K S0 and R_Q^T = S0^T Q^T (the state rounded to bf16; the
       // same fragments serve as B operand for R_K and as A operand for R_Q^T)
       bf8 Sb[NPP][2];
@@ -662,18 +714,12 @@ prefill_pair_kernel(const PrefillParams p) {
         S[j][1] = gC * S[j][1];
       }
       const bf4 zero4 = bf4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
-      // operands of the substitution chain, read before it starts (the
-      // other state wave inverts every chunk too, so the wait for its
-      // blocks ends; its bound only guards against a wave that never arrives)
-      for (int spin = 0; spin < (1 << 22); ++spin) {
-        if (__hip_atomic_load(&sm.inv_cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= 2 * (c + 1)) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
+      // operands of the substitution chain, read before it starts
       bf4 tiv[4], na[4][4];
       f4 dcs[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        tiv[m] = lds_b64(&sm.tinv[m][x][4 * g]);
+        tiv[m] = lds_b64(&sm.tinv[w][m][x][4 * g]);
         dcs[m] = *reinterpret_cast<const f4*>(&B.dc[16 * m + 4 * g]);
 #pragma unroll
         for (int i = m + 1; i < 4; ++i) na[i][m] = lds_b64(&B.negA[16 * i + x][16 * m + 4 * g]);
