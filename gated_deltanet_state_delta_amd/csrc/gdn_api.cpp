@@ -231,6 +231,7 @@ gdn_status gdn_decode(const gdn_decode_args* p, void* stream) {
   if (a.n_householder < 1 || a.n_householder > 4)
     return fail(GDN_ERR_UNSUPPORTED, "gdn_decode: n_householder=%d (supported 1..4)", a.n_householder);
   if (a.hv % a.hq != 0) return fail(GDN_ERR_SHAPE, "gdn_decode: hv=%d is not a multiple of hq=%d", a.hv, a.hq);
+  if (a.hv > 65536) return fail(GDN_ERR_UNSUPPORTED, "gdn_decode: hv=%d (supported up to 65536)", a.hv);
   if (a.qk_l2norm && !(a.qk_l2norm_eps >= 0.f && a.qk_l2norm_eps <= 3.0e38f))
     return fail(GDN_ERR_SHAPE, "gdn_decode: qk_l2norm_eps must be finite and >= 0");
   if (!head_size_ok(a.dk) || !head_size_ok(a.dv))

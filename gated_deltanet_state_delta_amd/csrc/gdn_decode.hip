@@ -61,6 +61,7 @@ decode_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(16))) IO sq[TT * DK];         // [t][DK]
   __shared__ __attribute__((aligned(16))) IO sv[TT * NJ * ROWS];  // [t][j][rows of this block]
   __shared__ float sgam[TT], sbet[TT * NJ];
+  __shared__ int ssc[TT];  // scatter slots of the pass's tokens
   __shared__ __attribute__((aligned(16))) float spk[TT * DK];       // per-key log-decay [t][DK]
   const int blk = blockIdx.x;
   const int rb = blk % NRB;
@@ -95,8 +96,8 @@ decode_kernel(const DecodeParams p) {
   const float dt_bias = per_key ? 0.f : p.dt_bias[h];
 
   // One token: decay, the sub-steps, the readout and the optional scatter.
-  // kp(j): this lane's k of sub-step j; vj(j), beta(j): the row's v and beta;
-  // qp: this lane's q.
+  // kp(j, kf): this lane's k of sub-step j into kf[4]; vj(j), beta(j): the
+  // row's v and beta; qp(qf): this lane's q into qf[4].
   // in-kernel L2 norm of a vector spread over the row's L lanes (16 elements
   // each); an all-zero vector stays zero
   auto l2n = [&](f4* v4) {
@@ -109,8 +110,11 @@ decode_kernel(const DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) v4[i] *= r;
   };
-  // gp: this lane's per-key log-decays (used when per_key)
-  auto token = [&](int t, float gamma, const float* gp, auto kp, auto vj, auto beta, const IO* qp) {
+  // gp: this lane's per-key log-decays (used when per_key); scatter_slot(t):
+  // token t's scatter slot (read before the token loop: a load inside it
+  // would wait for the previous tokens' stores)
+  auto token = [&](int t, float gamma, const float* gp, auto kp, auto vj, auto beta, auto qp,
+                   auto scatter_slot) {
     const int64_t bt = (int64_t)b * p.T + t;
     if (per_key) {
       // key column i*4L + 4o + e of this lane decays by its own factor
@@ -125,10 +129,8 @@ decode_kernel(const DecodeParams p) {
       for (int i = 0; i < 4; ++i) x[i] *= gamma;
     }
     for (int j = 0; j < p.nhh; ++j) {
-      const IO* kj = kp(j);
       f4 kf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kf[i] = load4(kj + i * 4 * L);
+      kp(j, kf);
       l2n(kf);
       float r = 0.0f;
 #pragma unroll
@@ -140,8 +142,7 @@ decode_kernel(const DecodeParams p) {
       for (int i = 0; i < 4; ++i) x[i] += u * kf[i];
     }
     f4 qf[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qf[i] = load4(qp + i * 4 * L);
+    qp(qf);
     l2n(qf);
     float y = 0.0f;
 #pragma unroll
@@ -149,7 +150,7 @@ decode_kernel(const DecodeParams p) {
     y = group_sum<L>(y);
     if (o == 0) out[(bt * p.hv + h) * DV + row] = from_f32<IO>(p.scale * y);
     if (p.scatter_idx) {
-      const int s = p.scatter_idx[bt];
+      const int s = scatter_slot(t);
       if (s >= 0 && s < p.pool_size) {
         float* dst = p.pool + (int64_t)s * p.slot_stride + head_off;
 #pragma unroll
@@ -164,54 +165,119 @@ decode_kernel(const DecodeParams p) {
     const int64_t bt = (int64_t)b;
     const float gamma = per_key ? 1.f : expf(gate_log_decay(A_log, dt_bias, to_f32(ga[bt * p.hv + h])));
     const float* gp = per_key ? p.decay_pk + (bt * p.hv + h) * DK + 4 * o : nullptr;
-    token(0, gamma, gp, [&](int) { return k + (bt * p.hq + qh) * DK + 4 * o; },
+    const int sc0 = p.scatter_idx ? p.scatter_idx[bt] : -1;
+    const IO* kq = k + (bt * p.hq + qh) * DK + 4 * o;
+    const IO* qq = q + (bt * p.hq + qh) * DK + 4 * o;
+    token(0, gamma, gp,
+          [&](int, f4* kf) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kf[i] = load4(kq + i * 4 * L);
+          },
           [&](int) { return to_f32(v[(bt * p.hv + h) * DV + row]); },
-          [&](int) { return sigmoidf(to_f32(gb[bt * p.hv + h])); }, q + (bt * p.hq + qh) * DK + 4 * o);
+          [&](int) { return sigmoidf(to_f32(gb[bt * p.hv + h])); },
+          [&](f4* qf) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qf[i] = load4(qq + i * 4 * L);
+          },
+          [&](int) { return sc0; });
   } else {
     for (int t0 = 0; t0 < p.T; t0 += TT) {
       const int nt = min(TT, p.T - t0);
       const int ntj = nt * p.nhh;
-      if (t0 > 0) __syncthreads();  // the previous pass has read the staging area
-      // stage k rows [t][j], q rows [t], v slices [t][j] (4-element groups)
-      // and the gates of this pass
+      // stage k rows [t][j], q rows [t], v slices [t][j] (4-element groups),
+      // the gates and the scatter slots of this pass: every thread issues
+      // all of its loads before it writes any of them to LDS, so the pass
+      // waits for its loads once (a load-then-store loop waits per element)
+      constexpr int MK = (TT * NJ * (DK / 4) + NT - 1) / NT;
+      constexpr int MQ = (TT * (DK / 4) + NT - 1) / NT;
+      constexpr int MV = (TT * NJ * (ROWS / 4) + NT - 1) / NT;
+      constexpr int MP = (TT * (DK / 4) + NT - 1) / NT;
       const int64_t bt0 = (int64_t)b * p.T + t0;
-      for (int idx = tid; idx < ntj * (DK / 4); idx += NT) {
-        const int tj = idx / (DK / 4), c = idx % (DK / 4);
-        const int t = tj / p.nhh, j = tj % p.nhh;
-        reinterpret_cast<Q4*>(sk)[(t * NJ + j) * (DK / 4) + c] =
-            reinterpret_cast<const Q4*>(k + ((bt0 * p.nhh + tj) * p.hq + qh) * DK)[c];
+      // the loads run unconditionally (indices clamped into the pass, values
+      // past it are not stored): guarded loads compile to branches whose
+      // register reuse makes every load wait for the previous one
+      Q4 rk[MK], rq[MQ], rv[MV];
+      f4 rp[MP];
+      // uniform bases of the pass; lane offsets stay 32-bit (a pass spans at
+      // most TT tokens of one batch row)
+      const Q4* kb = reinterpret_cast<const Q4*>(k + (bt0 * p.nhh * p.hq + qh) * DK);
+      const Q4* qb = reinterpret_cast<const Q4*>(q + (bt0 * p.hq + qh) * DK);
+      const Q4* vb = reinterpret_cast<const Q4*>(v + (bt0 * p.nhh * p.hv + h) * DV + rb * ROWS);
+      const int ks = p.hq * (DK / 4), vs = p.hv * (DV / 4);  // token(-step) strides in Q4
+#pragma unroll
+      for (int u = 0; u < MK; ++u) {
+        const int idx = min(tid + u * NT, ntj * (DK / 4) - 1), tj = idx / (DK / 4), c = idx % (DK / 4);
+        rk[u] = kb[tj * ks + c];
       }
-      for (int idx = tid; idx < nt * (DK / 4); idx += NT) {
-        const int t = idx / (DK / 4), c = idx % (DK / 4);
-        reinterpret_cast<Q4*>(sq)[t * (DK / 4) + c] =
-            reinterpret_cast<const Q4*>(q + ((bt0 + t) * p.hq + qh) * DK)[c];
+#pragma unroll
+      for (int u = 0; u < MQ; ++u) {
+        const int idx = min(tid + u * NT, nt * (DK / 4) - 1), t = idx / (DK / 4), c = idx % (DK / 4);
+        rq[u] = qb[t * ks + c];
       }
-      for (int idx = tid; idx < ntj * (ROWS / 4); idx += NT) {
-        const int tj = idx / (ROWS / 4), c = idx % (ROWS / 4);
-        const int t = tj / p.nhh, j = tj % p.nhh;
-        reinterpret_cast<Q4*>(sv)[(t * NJ + j) * (ROWS / 4) + c] =
-            reinterpret_cast<const Q4*>(v + ((bt0 * p.nhh + tj) * p.hv + h) * DV + rb * ROWS)[c];
+#pragma unroll
+      for (int u = 0; u < MV; ++u) {
+        const int idx = min(tid + u * NT, ntj * (ROWS / 4) - 1), tj = idx / (ROWS / 4), c = idx % (ROWS / 4);
+        rv[u] = vb[tj * vs + c];
       }
       if (per_key) {
-        for (int idx = tid; idx < nt * (DK / 4); idx += NT) {
-          const int t = idx / (DK / 4), c = idx % (DK / 4);
-          reinterpret_cast<f4*>(spk)[t * (DK / 4) + c] =
-              reinterpret_cast<const f4*>(p.decay_pk + ((bt0 + t) * p.hv + h) * DK)[c];
+        const f4* pb = reinterpret_cast<const f4*>(p.decay_pk + (bt0 * p.hv + h) * DK);
+#pragma unroll
+        for (int u = 0; u < MP; ++u) {
+          const int idx = min(tid + u * NT, nt * (DK / 4) - 1), t = idx / (DK / 4), c = idx % (DK / 4);
+          rp[u] = pb[t * (p.hv * (DK / 4)) + c];
         }
-      } else {
-        for (int idx = tid; idx < nt; idx += NT)
-          sgam[idx] = expf(gate_log_decay(A_log, dt_bias, to_f32(ga[(bt0 + idx) * p.hv + h])));
       }
-      for (int idx = tid; idx < ntj; idx += NT) {
-        const int t = idx / p.nhh, j = idx % p.nhh;
-        sbet[t * NJ + j] = sigmoidf(to_f32(gb[(bt0 * p.nhh + idx) * p.hv + h]));
+      // one thread per token (gate, scatter slot) and per (token, sub-step) (beta)
+      // (with a per-key decay the raw gate a is absent: b, which holds at
+      // least as many entries, stands in and its value is not used)
+      const IO raw_a = (per_key ? gb : ga)[(bt0 + min(tid, nt - 1)) * p.hv + h];
+      const float rbv = to_f32(gb[(bt0 * p.nhh + min(tid, ntj - 1)) * p.hv + h]);
+      const int rsc = p.scatter_idx ? p.scatter_idx[bt0 + min(tid, nt - 1)] : -1;
+      if (t0 > 0) __syncthreads();  // the previous pass has read the staging area
+#pragma unroll
+      for (int u = 0; u < MK; ++u) {
+        const int idx = tid + u * NT, tj = idx / (DK / 4), c = idx % (DK / 4);
+        const int t = tj / p.nhh, j = tj % p.nhh;
+        if (idx < ntj * (DK / 4)) reinterpret_cast<Q4*>(sk)[(t * NJ + j) * (DK / 4) + c] = rk[u];
       }
+#pragma unroll
+      for (int u = 0; u < MQ; ++u) {
+        const int idx = tid + u * NT, t = idx / (DK / 4), c = idx % (DK / 4);
+        if (idx < nt * (DK / 4)) reinterpret_cast<Q4*>(sq)[t * (DK / 4) + c] = rq[u];
+      }
+#pragma unroll
+      for (int u = 0; u < MV; ++u) {
+        const int idx = tid + u * NT, tj = idx / (ROWS / 4), c = idx % (ROWS / 4);
+        const int t = tj / p.nhh, j = tj % p.nhh;
+        if (idx < ntj * (ROWS / 4)) reinterpret_cast<Q4*>(sv)[(t * NJ + j) * (ROWS / 4) + c] = rv[u];
+      }
+      if (per_key) {
+#pragma unroll
+        for (int u = 0; u < MP; ++u) {
+          const int idx = tid + u * NT, t = idx / (DK / 4), c = idx % (DK / 4);
+          if (idx < nt * (DK / 4)) reinterpret_cast<f4*>(spk)[t * (DK / 4) + c] = rp[u];
+        }
+      } else if (tid < nt) {
+        sgam[tid] = expf(gate_log_decay(A_log, dt_bias, to_f32(raw_a)));
+      }
+      if (tid < ntj) sbet[(tid / p.nhh) * NJ + tid % p.nhh] = sigmoidf(rbv);
+      if (tid < nt) ssc[tid] = rsc;
       __syncthreads();
       for (int tl = 0; tl < nt; ++tl)
         token(t0 + tl, per_key ? 1.f : sgam[tl], spk + tl * DK + 4 * o,
-              [&](int j) -> const IO* { return sk + (tl * NJ + j) * DK + 4 * o; },
+              [&](int j, f4* kf) {
+                const IO* kj = sk + (tl * NJ + j) * DK + 4 * o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) kf[i] = load4(kj + i * 4 * L);
+              },
               [&](int j) { return to_f32(sv[(tl * NJ + j) * ROWS + (row - rb * ROWS)]); },
-              [&](int j) { return sbet[tl * NJ + j]; }, sq + tl * DK + 4 * o);
+              [&](int j) { return sbet[tl * NJ + j]; },
+              [&](f4* qf) {
+                const IO* qj = sq + tl * DK + 4 * o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) qf[i] = load4(qj + i * 4 * L);
+              },
+              [&](int) { return ssc[tl]; });
     }
   }
   if (!p.scatter_idx && !p.disable && wr >= 0 && wr < p.pool_size) {

@@ -295,7 +295,8 @@ gdn_status gdn_prefill_noalloc(const gdn_prefill_args* args, void* stream);
  *       previous contents
  * Requirements: pool pointer 16-byte aligned and both pool strides multiples
  * of 4 elements; q, k, v, out 8-byte aligned; 1 <= T <= 64;
- * 1 <= n_householder <= 4; batch == 0 is a no-op.
+ * 1 <= n_householder <= 4; hv <= 65536 (GDN_ERR_UNSUPPORTED above);
+ * batch == 0 is a no-op.
  * With T >= 16, n_householder == 1, no scatter_idx and q, k, v, out 16-byte
  * aligned, the call runs the chunked form of the same recurrence (the
  * prefill kernels over the pool, one request per row; the per-key prefill

@@ -270,6 +270,7 @@ DECODE_ERRORS = [
     (dict(n_householder=0), 5),
     (dict(n_householder=5), 5),
     (dict(hq=3), 2),
+    (dict(hq=1, hv=65537), 5),   # in-kernel offsets of a pass stay 32-bit
     (dict(dk=96), 5),
     (dict(scatter_idx=FAKE * 11, disable_state_update=1), 5),
     (dict(pool=None), 1),
