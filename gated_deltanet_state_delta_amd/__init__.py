@@ -25,7 +25,7 @@ from ._lib import GdnError
 
 __all__ = ["gate", "prefill", "decode", "conv1d", "state_update", "version", "GdnError",
            "prefill_args", "decode_args", "conv1d_args", "prefill_workspace_size",
-           "prefill_noalloc"]
+           "prefill_noalloc", "wait_timeouts"]
 
 _DT = {torch.float32: _lib.GDN_F32, torch.bfloat16: _lib.GDN_BF16}
 # update_rule of the ONNX card -> gdn_update_rule
@@ -418,6 +418,15 @@ def prefill_workspace_size(q, k, v, decay, beta, **kw) -> int:
     request segments."""
     args, keep, _, _ = prefill_args(q, k, v, decay, beta, **kw)
     return int(_lib.load().gdn_prefill_workspace_size(ctypes.byref(args)))
+
+
+def wait_timeouts(clear=True) -> int:
+    """The current device's count of in-kernel waits that ran out of polls
+    (gdn_wait_timeouts): 0 in every correct run.  clear resets it.  Waits
+    for all work on the device."""
+    n = ctypes.c_uint32(0)
+    _lib.check(_lib.load().gdn_wait_timeouts(ctypes.byref(n), 1 if clear else 0))
+    return int(n.value)
 
 
 _HEAD_SIZES = (16, 32, 64, 128)

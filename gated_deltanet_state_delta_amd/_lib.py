@@ -21,7 +21,7 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_
 
 # every extern "C" symbol include/libgdn.h declares
 EXPORTED = ("gdn_last_error", "gdn_version", "gdn_gate", "gdn_prefill", "gdn_prefill_workspace_size",
-            "gdn_prefill_noalloc", "gdn_decode", "gdn_conv1d")
+            "gdn_prefill_noalloc", "gdn_decode", "gdn_conv1d", "gdn_wait_timeouts")
 NOALLOC_SCRATCH_BYTES = 32 << 20  # GDN_NOALLOC_SCRATCH_BYTES
 
 _i32, _i64, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
@@ -105,6 +105,8 @@ def load(path: str | None = None):
         lib.gdn_prefill_noalloc.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
         lib.gdn_decode.restype = ctypes.c_int
         lib.gdn_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
+        lib.gdn_wait_timeouts.restype = ctypes.c_int
+        lib.gdn_wait_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint32), _i32]
         lib.gdn_conv1d.restype = ctypes.c_int
         lib.gdn_conv1d.argtypes = [ctypes.POINTER(Conv1dArgs), _vp]
         if path is None:

@@ -89,6 +89,12 @@ gdn_status gdn_gate(const float* A_log, const float* dt_bias, const void* a, con
                   "gdn_gate launch");
 }
 
+gdn_status gdn_wait_timeouts(uint32_t* count, int32_t clear) {
+  g_err[0] = 0;
+  if (!count) return fail(GDN_ERR_NULL, "gdn_wait_timeouts: count is NULL");
+  return from_hip(gdn::wait_timeouts(count, clear != 0), "gdn_wait_timeouts");
+}
+
 size_t gdn_prefill_workspace_size(const gdn_prefill_args* args) {
   return args ? gdn::prefill_workspace_bytes(*args) : 0;
 }

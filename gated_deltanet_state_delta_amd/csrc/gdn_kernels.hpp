@@ -26,6 +26,9 @@ hipError_t launch_prefill(const gdn_prefill_args& args, hipStream_t stream, int 
 // Scratch bytes launch_prefill uses for these arguments when the workspace
 // holds at least that many (the scan over segment maps); 0 when it needs none.
 size_t prefill_workspace_bytes(const gdn_prefill_args& args);
+// Reads (and optionally clears) the current device's count of expired
+// in-kernel waits; synchronous.
+hipError_t wait_timeouts(uint32_t* count, bool clear);
 
 hipError_t launch_conv1d(const gdn_conv1d_args& args, hipStream_t stream);
 

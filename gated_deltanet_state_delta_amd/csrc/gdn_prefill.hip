@@ -15,24 +15,35 @@
 
 namespace gdn {
 
-// Read-only device constants.  kGateConst: what an absent gate input reads,
-// log-decay 0 (or a raw gate input 0) at [0], beta 1 at [1].  kZeroRow: the
-// zero V rows of the scan's transition slices.  Each device holds its own
+// Device globals.  kGateConst (read-only): what an absent gate input reads,
+// log-decay 0 (or a raw gate input 0) at [0], beta 1 at [1].  kZeroRow
+// (read-only): the zero V rows of the scan's transition slices.
+// kWaitExpired: the number of in-kernel waits that ran out of polls since
+// the last clear (0 unless a schedule is broken).  Each device holds its own
 // copies; their addresses come from hipGetSymbolAddress on that device.
 __device__ float kGateConst[2] = {0.f, 1.f};
 __device__ __align__(16) float kZeroRow[32] = {};
+__device__ unsigned int kWaitExpired = 0;
 
-static hipError_t device_consts(float** gate, const void** zero) {
+struct DeviceSyms {
+  float* gate;
+  const void* zero;
+  unsigned int* wait_err;
+};
+
+static hipError_t device_syms(DeviceSyms* out) {
   constexpr int kMaxDevices = 64;
   static std::atomic<float*> cache_g[kMaxDevices];
   static std::atomic<float*> cache_z[kMaxDevices];
+  static std::atomic<unsigned int*> cache_w[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   float* c = cache_g[dev].load(std::memory_order_acquire);
   float* z = cache_z[dev].load(std::memory_order_acquire);
-  if (!c || !z) {
+  unsigned int* w = cache_w[dev].load(std::memory_order_acquire);
+  if (!c || !z || !w) {
     void* addr = nullptr;
     e = hipGetSymbolAddress(&addr, HIP_SYMBOL(kGateConst));
     if (e != hipSuccess) return e;
@@ -40,12 +51,32 @@ static hipError_t device_consts(float** gate, const void** zero) {
     e = hipGetSymbolAddress(&addr, HIP_SYMBOL(kZeroRow));
     if (e != hipSuccess) return e;
     z = static_cast<float*>(addr);
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(kWaitExpired));
+    if (e != hipSuccess) return e;
+    w = static_cast<unsigned int*>(addr);
     cache_g[dev].store(c, std::memory_order_release);
     cache_z[dev].store(z, std::memory_order_release);
+    cache_w[dev].store(w, std::memory_order_release);
   }
-  if (gate) *gate = c;
-  if (zero) *zero = z;
+  out->gate = c;
+  out->zero = z;
+  out->wait_err = w;
   return hipSuccess;
+}
+
+hipError_t wait_timeouts(uint32_t* count, bool clear) {
+  DeviceSyms d;
+  hipError_t e = device_syms(&d);
+  if (e != hipSuccess) return e;
+  unsigned int v = 0;
+  e = hipMemcpy(&v, d.wait_err, sizeof(v), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  if (count) *count = v;
+  if (clear) {
+    const unsigned int zero = 0;
+    e = hipMemcpy(d.wait_err, &zero, sizeof(zero), hipMemcpyHostToDevice);
+  }
+  return e;
 }
 
 // Whether one fused and one given gate input are combined.
@@ -83,9 +114,10 @@ size_t prefill_workspace_bytes(const gdn_prefill_args& a) {
 // holds the segment maps, then every segment's incoming state.
 static hipError_t launch_prefill_scan(const PrefillParams& p, const gdn_prefill_args& a, int nseg,
                                       hipStream_t stream) {
-  const void* zero = nullptr;
-  hipError_t e = device_consts(nullptr, &zero);
+  DeviceSyms d;
+  hipError_t e = device_syms(&d);
   if (e != hipSuccess) return e;
+  const void* zero = d.zero;
   float* ws_map = static_cast<float*>(a.workspace);
   float* ws_in = ws_map + (size_t)a.n_seqs * nseg * a.hv * (a.dv + a.dk) * a.dk;
   PrefillParams pa = p;
@@ -111,7 +143,11 @@ static hipError_t launch_prefill_scan(const PrefillParams& p, const gdn_prefill_
 }
 
 hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream, int pool_flags) {
+  DeviceSyms syms;
+  const hipError_t se = device_syms(&syms);
+  if (se != hipSuccess) return se;
   PrefillParams p;
+  p.wait_err = syms.wait_err;
   p.pool_flags = pool_flags;
   p.q = a.q; p.k = a.k; p.v = a.v; p.out = a.out;
   p.q_st = a.q_stride_token; p.q_sh = a.q_stride_head;
@@ -143,9 +179,7 @@ hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream, int poo
   const bool absent = fused ? (!a.gate_a || !a.gate_b) : (!a.decay || !a.beta);
   if (absent && !mixed) {
     // a rule without decay or beta: the missing source reads the constants
-    float* c = nullptr;
-    const hipError_t e = device_consts(&c, nullptr);
-    if (e != hipSuccess) return e;
+    float* c = syms.gate;
     if (fused) {
       if (!a.gate_a) { p.ga = c; p.A_log = c; p.dt_bias = c; p.dmask = 0; }
       if (!a.gate_b) { p.gb = c; p.bmask = 0; }

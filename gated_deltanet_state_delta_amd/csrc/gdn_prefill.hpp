@@ -114,6 +114,8 @@ struct PrefillParams {
   //    [r * nseg + j, h, dv, dk]; outputs as usual; no final state.
   int nseg, nsv, seg_mode;
   const void* vzero;     // >= 128 zero bytes
+  // count of in-kernel waits that ran out of polls (see gdn_wait_timeouts)
+  unsigned int* wait_err;
 };
 
 // Token range [start, end) of request r: cu_seqlens clamped to [0, T] (a

@@ -11,17 +11,22 @@
 //    registers -- per (request, value head, 64-column slice of the state);
 //  * state waves 0 and 1 each own 32 value columns (two 16-column MFMA
 //    tiles), so every Q, K and K^T fragment read from LDS feeds two MFMAs;
-//    state wave w inverts the unit-lower diagonal blocks I + A_ii,
-//    i = 2w, 2w+1, of chunk c (right-looking, one lane pair per row) and
-//    shares them through LDS (a counter tells when both halves are there);
-//    both then run [Q; K] S0, the block forward substitution, Y += M U and
+//    each state wave inverts all four unit-lower diagonal blocks I + A_ii
+//    of chunk c itself (right-looking, one lane per row, row k of A_ii
+//    broadcast from its owner lane by DPP), so the two waves never wait
+//    for each other; both then run [Q; K] S0, the block forward
+//    substitution, Y += M U and
 //    the state update; they accumulate the outputs transposed (Y^T, the
 //    MFMA operands swapped), so each lane holds 4 columns of one token and,
 //    after a lane swap between 16-lane rows, stores 16-byte row pieces
 //    straight to memory;
 //  * prep waves 2 and 3 prepare chunk c+1 meanwhile.  Each loads half of the
 //    chunk's Q, K and V rows (two chunks ahead: token-strided loads have a
-//    long latency) and stages them in LDS; after an LDS counter shows both
+//    long latency; whole 16-byte row pieces, unconditionally, through buffer
+//    loads whose range check zeroes rows past the request, in three batches
+//    -- gates and V, Q, K -- placed between the wave's compute phases so the
+//    waits for one batch never stall the next) and stages them in LDS;
+//    after an LDS counter shows both
 //    halves written, each computes two diagonal and three off-diagonal
 //    16x16 Gram tiles, their M and -A blocks (the decay D(t,s) of an
 //    off-diagonal tile factored into three per-tile factors <= 1 unless the
@@ -88,6 +93,18 @@ struct PairSmem {
   int prep_cnt;  // staging halves written by the prep waves so far
   int nrm_cnt;   // norm halves written by the prep waves so far (L2 norm only)
 };
+
+// Polls an LDS counter until it reaches `target`, at most 2^22 times (far
+// beyond any wait of a working schedule); when the polls run out, lane 0
+// adds 1 to the call's wait-expiry word and the wave goes on, so a broken
+// schedule is reported instead of hanging the GPU.
+__device__ __forceinline__ void pair_wait_count(int* cnt, int target, unsigned int* wait_err) {
+  for (int spin = 0; spin < (1 << 22); ++spin) {
+    if (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (__lane_id() == 0) __hip_atomic_fetch_add(wait_err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // 16-byte slot permutation of a Q/K row.
 __device__ __forceinline__ int pair_swz(int row, int slot) {
@@ -169,56 +186,6 @@ struct PairPrepSet {
   float gd, bt;      // decay and beta of token `lane` as loaded (clamped to the chunk)
   __bf16 ga, gbr;    // or the fused gate's raw a and b
 };
-
-// Inverse of the unit-lower block I + A_i (A_i strictly lower, fp32 rows in
-// `ad` as laid out by the prep waves), right-looking: a lane pair owns row
-// r = (lane / 2) % 16 of block i = i0 + lane / 32; lane parity h keeps
-// T[r][j] for j = h mod 2.  T[r][j] = [j == r] - sum_{k > j} T[r][k] A[k][j];
-// once T[r][k] is final (its owner lane passes it to the partner) it updates
-// every j < k.  A is strictly lower, so updates of entries j >= k add zero.
-// Writes row r of T_i in bf16 to tout[i][r][0..15].
-template <int LDT>
-__device__ __forceinline__ void pair_tri_inverse(const float (*ad)[16 * 20 + 4], __bf16 (*tout)[16][LDT], int i0,
-                                                 int lane) {
-  const int i = i0 + (lane >> 5), r = (lane >> 1) & 15, h = lane & 1;
-  const float* arow = &ad[i][8 * h];
-  float acc[8];
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) acc[jj] = 2 * jj + h == r ? 1.f : 0.f;
-  // row k of A: entries 2 jj + h for jj < (k + 1) / 2 can be nonzero
-  f4 a[16][2];
-#pragma unroll
-  for (int k = 1; k < 16; ++k) {
-    a[k][0] = *reinterpret_cast<const f4*>(arow + 20 * k);
-    if (k > 8) a[k][1] = *reinterpret_cast<const f4*>(arow + 20 * k + 4);
-  }
-#pragma unroll
-  for (int k = 15; k >= 1; --k) {
-    const float mine = acc[k >> 1];
-    const float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mine), 0xB1, 0xF, 0xF, false));
-    const float tk = (k & 1) == h ? mine : other;
-    auto ak = [&](int jj) -> float { return jj < 4 ? a[k][0][jj] : a[k][1][jj - 4]; };
-    // the entry the next step reads first, then the rest
-    acc[(k - 1) >> 1] -= tk * ak((k - 1) >> 1);
-#pragma unroll
-    for (int jj = 0; jj < ((k - 1) >> 1); ++jj) acc[jj] -= tk * ak(jj);
-  }
-  // row r, columns 8 h .. 8 h + 7: even entries from lane parity 0, odd ones
-  // from parity 1
-  float o[8];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float even_lo = acc[q], even_hi = acc[4 + q];  // my parity's values
-    const float sw_lo = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(even_lo), 0xB1, 0xF, 0xF, false));
-    const float sw_hi = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(even_hi), 0xB1, 0xF, 0xF, false));
-    // h == 0 assembles columns 0..7: T[r][2q] (mine, jj = q), T[r][2q+1] (partner's jj = q)
-    // h == 1 assembles columns 8..15: T[r][8+2q] (partner's jj = 4+q), T[r][9+2q] (mine, jj = 4+q)
-    o[2 * q] = h == 0 ? even_lo : sw_hi;
-    o[2 * q + 1] = h == 0 ? sw_lo : even_hi;
-  }
-  *reinterpret_cast<bf4*>(&tout[i][r][8 * h]) = to_bf4(f4{o[0], o[1], o[2], o[3]});
-  *reinterpret_cast<bf4*>(&tout[i][r][8 * h + 4]) = to_bf4(f4{o[4], o[5], o[6], o[7]});
-}
 
 // One right-looking step of pair_tri_inverse4 and the steps below it: with
 // t = T[r][K] final, T[r][j] -= t A[K][j] for every j < K, where A[K][j] is
@@ -398,10 +365,7 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
         sc.Fx[lane] = __builtin_amdgcn_exp2f(Fb1 - F);
       }
       prefetch(c + 3, s, 1);
-      for (int spin = 0; spin < (1 << 22); ++spin) {
-        if (__hip_atomic_load(&sm.prep_cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= 2 * staged) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
+      pair_wait_count(&sm.prep_cnt, 2 * staged, p.wait_err);
       const bool any_zero = zlast >= 0;  // wave-uniform
 
       // ---- per-token factors of the state waves (wave 2), after the norms
@@ -504,10 +468,7 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
         *reinterpret_cast<f2*>(&ad[20 * x + 8 + 2 * g]) = f2{arow[1], arow[3]};
       }
       if constexpr (NORM) {
-        for (int spin = 0; spin < (1 << 22); ++spin) {
-          if (__hip_atomic_load(&sm.nrm_cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= 2 * staged) break;
-          __builtin_amdgcn_s_sleep(1);
-        }
+        pair_wait_count(&sm.nrm_cnt, 2 * staged, p.wait_err);
         factors();
       }
       // ---- off-diagonal tiles: -A and M blocks.  D(t, s) = e_t c_im f_s for

@@ -74,6 +74,20 @@ const char* gdn_last_error(void);
 /* Library version as "major.minor.patch". */
 const char* gdn_version(void);
 
+/* gdn_wait_timeouts -- health check of the in-kernel waits.
+ *
+ * The bf16 pair prefill kernel (and the scan's passes, which run it) hands
+ * each chunk from its preparing waves to its state waves through counters
+ * in workgroup memory; every wait on such a counter is bounded (2^22 polls,
+ * far beyond any working schedule).  A wait that runs out adds 1 to a
+ * per-device word and the kernel finishes normally, with results that are
+ * then not to be trusted.  This call stores the current device's word in
+ * *count (0 in every correct run) and sets it back to 0 when clear != 0.
+ * Synchronous: it waits for all work on the current device.  Returns
+ * GDN_ERR_NULL for a NULL count, GDN_ERR_HIP when the copy fails.
+ */
+gdn_status gdn_wait_timeouts(uint32_t* count, int32_t clear);
+
 /* ----------------------------------------------------------------------------
  * gdn_gate -- fused gates, elementwise over n_tokens rows of hv heads.
  *

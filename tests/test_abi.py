@@ -257,6 +257,12 @@ def test_prefill_noalloc_host_checks(lib):
                 assert lib.gdn_prefill_workspace_size(ctypes.byref(a)) <= L.NOALLOC_SCRATCH_BYTES
 
 
+def test_wait_timeouts_null(lib):
+    """gdn_wait_timeouts refuses a NULL count before touching the device."""
+    assert lib.gdn_wait_timeouts(None, 0) == 1
+    assert b"gdn_wait_timeouts" in lib.gdn_last_error()
+
+
 def test_prefill_null_args_and_noop(lib):
     assert lib.gdn_prefill(None, None) == 1
     a = _prefill(n_seqs=0, seq_len=0, total_tokens=0)
