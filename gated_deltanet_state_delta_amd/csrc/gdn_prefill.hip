@@ -162,6 +162,8 @@ hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream, int poo
   p.T = a.total_tokens; p.n_seqs = a.n_seqs; p.seq_len = a.seq_len;
   p.hq = a.hq; p.hv = a.hv; p.dv = a.dv; p.nsplit = 1;
   p.nseg = 1; p.nsv = 1; p.seg_mode = 0; p.vzero = nullptr;
+  p.lpt = a.cu_seqlens && a.n_seqs >= 2 && a.n_seqs <= kLptMax &&
+          a.total_tokens >= (int64_t)kLptMinTokens * a.n_seqs;
   p.decay_is_gamma = a.decay_kind == GDN_DECAY_GAMMA;
   p.scale = a.scale;
   p.qk_norm = a.qk_l2norm != 0;

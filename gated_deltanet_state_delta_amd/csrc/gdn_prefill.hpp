@@ -116,6 +116,7 @@ struct PrefillParams {
   const void* vzero;     // >= 128 zero bytes
   // count of in-kernel waits that ran out of polls (see gdn_wait_timeouts)
   unsigned int* wait_err;
+  int lpt;  // take requests longest first (prefill_request_of_rank)
 };
 
 // Token range [start, end) of request r: cu_seqlens clamped to [0, T] (a
@@ -130,6 +131,57 @@ __device__ __forceinline__ void prefill_request_bounds(const PrefillParams& p, i
     end = start + p.seq_len;
   }
   if (end < start) end = start;
+}
+
+// Work unit of workgroup b of a prefill grid of nblk workgroups, as an index
+// blk = (rank * hv + h) * nsplit + split (the scan's passes put the segment
+// between rank and h).  Workgroups are dealt to the 8 XCDs round-robin by
+// block index, and the `group` consecutive units that read one query/key
+// head (group = nsplit * hv / hq) always stay on one XCD, where they share
+// its L2.  spread (requests of different lengths, taken longest first):
+// consecutive groups go to different XCDs, so every request is spread over
+// the whole chip -- one request's workgroups on one XCD would leave the
+// others idle when it is the long one.  Otherwise each XCD takes a
+// contiguous eighth of the units (measured faster for many short, equal
+// requests).  Identity when nblk does not divide evenly.
+__device__ __forceinline__ int prefill_block_unit(int b, int nblk, int group, bool spread) {
+  const int x = b & 7, l = b >> 3;
+  if (spread) {
+    if (group > 0 && nblk % (8 * group) == 0) return ((l / group) * 8 + x) * group + l % group;
+  } else if ((nblk & 31) == 0) {
+    return x * (nblk >> 3) + l;
+  }
+  return b;
+}
+
+// Requests are taken longest first (list scheduling): the units of rank k
+// belong to the k-th longest request (ties: lower index first), so the
+// workgroups that run longest start in the first dispatch round and short
+// ones fill the CUs that free up.  Done on the device from cu_seqlens when
+// the host set lpt (2 to kLptMax requests averaging at least kLptMinTokens
+// tokens: below that a workgroup's few chunks do not repay the extra round
+// trip); identity otherwise.  Every thread of the workgroup calls it (two
+// workgroup barriers when ordering); tmp is LDS scratch of kLptMax + 2 ints
+// that nothing else uses until a later barrier.  The result is wave-uniform.
+constexpr int kLptMax = 64;
+constexpr int kLptMinTokens = 256;
+__device__ __forceinline__ int prefill_request_of_rank(const PrefillParams& p, int k, int* tmp) {
+  const int n = p.n_seqs;
+  if (!p.lpt) return k;
+  const int tid = threadIdx.x;
+  if (tid <= n) tmp[tid] = (int)min(max((int64_t)p.cu[tid], (int64_t)0), p.T);
+  __syncthreads();
+  if (tid < n) {
+    const int li = max(tmp[tid + 1] - tmp[tid], 0);
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+      const int lj = max(tmp[j + 1] - tmp[j], 0);
+      rank += (lj > li) || (lj == li && j < tid);
+    }
+    if (rank == k) tmp[kLptMax + 1] = tid;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(tmp[kLptMax + 1]);
 }
 
 // Segment j of nseg of a request's range: ceil(chunks / nseg) whole chunks of
@@ -279,14 +331,10 @@ prefill_kernel(const PrefillParams p) {
   const int pw = wave - 4;   // prep wave index
   const int ptid = tid - 256;
 
-  // Workgroups sharing a query/key head are consecutive; keep them on one XCD
-  // (workgroups are dealt to the 8 XCDs round-robin).
-  int blk = blockIdx.x;
-  const int nblk = gridDim.x;
-  if ((nblk & 31) == 0) blk = (blk & 7) * (nblk >> 3) + (blk >> 3);
+  const int blk = prefill_block_unit(blockIdx.x, gridDim.x, p.nsplit * max(p.hv / p.hq, 1), p.lpt);
   const int split = blk % p.nsplit;
   const int h = (blk / p.nsplit) % p.hv;
-  const int r = blk / (p.nsplit * p.hv);
+  const int r = prefill_request_of_rank(p, blk / (p.nsplit * p.hv), reinterpret_cast<int*>(&sm.raw[1].q[0][0]));
   const int qh = (int)(((int64_t)h * p.hq) / p.hv);
   const int v0 = split * DVS;
 

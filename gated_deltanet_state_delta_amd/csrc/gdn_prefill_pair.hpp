@@ -537,15 +537,15 @@ prefill_pair_kernel(const PrefillParams p) {
   const int x = lane & 15;
   const int g = lane >> 4;
 
-  int blk = blockIdx.x;
-  const int nblk = gridDim.x;
-  if ((nblk & 31) == 0) blk = (blk & 7) * (nblk >> 3) + (blk >> 3);
   // unit (request r, segment j, value head h, slice); without segments (SEG
   // false, an instantiation of its own) j = 0 and every slice is a value slice
+  const int blk = prefill_block_unit(blockIdx.x, gridDim.x, p.nsplit * max(p.hv / p.hq, 1), p.lpt);
   const int split = blk % p.nsplit;
   const int h = (blk / p.nsplit) % p.hv;
-  const int rj = blk / (p.nsplit * p.hv);
-  const int r = SEG ? rj / p.nseg : rj, j = SEG ? rj % p.nseg : 0;
+  const int kj = blk / (p.nsplit * p.hv);  // (rank, segment)
+  const int j = SEG ? kj % p.nseg : 0;
+  const int r = prefill_request_of_rank(p, SEG ? kj / p.nseg : kj, reinterpret_cast<int*>(&sm.buf[1].q[0][0]));
+  const int rj = SEG ? r * p.nseg + j : r;  // the unit's workspace index
   const int qh = (int)(((int64_t)h * p.hq) / p.hv);
   const bool trans = SEG && split >= p.nsv;  // transition slice of a local pass
   const int v0 = (trans ? split - p.nsv : split) * 64;

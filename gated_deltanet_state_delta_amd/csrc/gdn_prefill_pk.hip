@@ -214,13 +214,10 @@ prefill_pk_kernel(const PrefillParams p) {
   const int x = lane & 15;
   const int g = lane >> 4;
 
-  // Workgroups sharing a query/key head are consecutive; keep them on one XCD.
-  int blk = blockIdx.x;
-  const int nblk = gridDim.x;
-  if ((nblk & 31) == 0) blk = (blk & 7) * (nblk >> 3) + (blk >> 3);
+  const int blk = prefill_block_unit(blockIdx.x, gridDim.x, p.nsplit * max(p.hv / p.hq, 1), p.lpt);
   const int split = blk % p.nsplit;
   const int h = (blk / p.nsplit) % p.hv;
-  const int r = blk / (p.nsplit * p.hv);
+  const int r = prefill_request_of_rank(p, blk / (p.nsplit * p.hv), reinterpret_cast<int*>(&sm.xq[0][0]));
   const int qh = (int)(((int64_t)h * p.hq) / p.hv);
   const int v0 = split * DVS;
 
