@@ -113,6 +113,38 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
 
+// DPP moves: lanes whose row is not in ROWMASK (or whose source lane lies
+// outside the row for the shifts) receive `fill`.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_f(float fill, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(v), CTRL, ROWMASK, 0xF, false));
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int dpp_i(int fill, int v) {
+  return __builtin_amdgcn_update_dpp(fill, v, CTRL, ROWMASK, 0xF, false);
+}
+// Inclusive wave-wide scans (sum, max) in lane order: shifts within 16-lane
+// rows (row_shr 1, 2, 4, 8), then the row totals carried across rows
+// (row_bcast 15 into rows 1 and 3, row_bcast 31 into rows 2 and 3).
+__device__ __forceinline__ float wave_scan_add(float v) {
+  v += dpp_f<0x111, 0xF>(0.f, v);
+  v += dpp_f<0x112, 0xF>(0.f, v);
+  v += dpp_f<0x114, 0xF>(0.f, v);
+  v += dpp_f<0x118, 0xF>(0.f, v);
+  v += dpp_f<0x142, 0xA>(0.f, v);
+  v += dpp_f<0x143, 0xC>(0.f, v);
+  return v;
+}
+__device__ __forceinline__ int wave_scan_max(int v) {
+  v = max(v, dpp_i<0x111, 0xF>(-1, v));
+  v = max(v, dpp_i<0x112, 0xF>(-1, v));
+  v = max(v, dpp_i<0x114, 0xF>(-1, v));
+  v = max(v, dpp_i<0x118, 0xF>(-1, v));
+  v = max(v, dpp_i<0x142, 0xA>(-1, v));
+  v = max(v, dpp_i<0x143, 0xC>(-1, v));
+  return v;
+}
+
 // ----------------------------------------------------- DPP row reductions --
 // Sum over aligned groups of L lanes (L in {1, 2, 4, 8, 16}); every lane of
 // the group ends with the group's sum.  quad_perm swaps for 2 and 4,

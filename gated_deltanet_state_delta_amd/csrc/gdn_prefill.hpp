@@ -712,19 +712,10 @@ prefill_kernel(const PrefillParams p) {
         lg = reset ? 0.f : pg * 1.4426950408889634f;
       }
     }
-    float F = lg;
-    int z = reset ? lane : -1;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float Fo = __shfl_up(F, off);
-      const int zo = __shfl_up(z, off);
-      if (lane >= off) {
-        F += Fo;
-        z = max(z, zo);
-      }
-    }
-    const float Flast = __shfl(F, C - 1);
-    const int zlast = __shfl(z, C - 1);
+    const float F = wave_scan_add(lg);
+    const int z = wave_scan_max(reset ? lane : -1);
+    const float Flast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(F), C - 1));
+    const int zlast = __builtin_amdgcn_readlane(z, C - 1);
     if (lane < C) {
       const float gam = z < 0 ? exp2f(F) : 0.f;
       const float bt = pvalid ? pb : 0.f;
@@ -803,8 +794,10 @@ prefill_kernel(const PrefillParams p) {
       // columns t (query token) -- so that each lane (t = 16i + x) ends with
       // 4 consecutive s of row t and stores -A and M rows as vectors.  Prep
       // wave pw owns diagonal tile (pw, pw) (slot 0) and the off-diagonal
-      // tiles whose list index is pw mod 4 (slots 1..); all of a wave's tiles
-      // share one pass over the key blocks.
+      // tiles whose list index o has (NT + o) mod 4 == pw (slots 1..), so the
+      // off-diagonal tiles start on the waves without a diagonal one (each
+      // prep wave shares its SIMD with a state wave: the MFMA load is spread
+      // evenly); all of a wave's tiles share one pass over the key blocks.
       constexpr int MT = 1 + (NOFF + 3) / 4;
       int ti[MT], tm[MT];
       bool tv[MT];
@@ -812,7 +805,7 @@ prefill_kernel(const PrefillParams p) {
       tv[0] = pw < NT;
 #pragma unroll
       for (int k = 1; k < MT; ++k) {
-        const int o = pw + 4 * (k - 1);
+        const int o = (pw + 4 - NT % 4) % 4 + 4 * (k - 1);
         int i = 1, rem = o;
         while (rem >= i) { rem -= i; ++i; }
         ti[k] = i;

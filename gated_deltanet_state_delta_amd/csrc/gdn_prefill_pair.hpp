@@ -139,38 +139,6 @@ __device__ __forceinline__ bf8 cat8(bf4 lo, bf4 hi) {
   return bf8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// DPP moves: lanes whose row is not in ROWMASK (or whose source lane lies
-// outside the row for the shifts) receive `fill`.
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ float dpp_f(float fill, float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(v), CTRL, ROWMASK, 0xF, false));
-}
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ int dpp_i(int fill, int v) {
-  return __builtin_amdgcn_update_dpp(fill, v, CTRL, ROWMASK, 0xF, false);
-}
-// Inclusive wave-wide scans (sum, max) in lane order: shifts within 16-lane
-// rows (row_shr 1, 2, 4, 8), then the row totals carried across rows
-// (row_bcast 15 into rows 1 and 3, row_bcast 31 into rows 2 and 3).
-__device__ __forceinline__ float wave_scan_add(float v) {
-  v += dpp_f<0x111, 0xF>(0.f, v);
-  v += dpp_f<0x112, 0xF>(0.f, v);
-  v += dpp_f<0x114, 0xF>(0.f, v);
-  v += dpp_f<0x118, 0xF>(0.f, v);
-  v += dpp_f<0x142, 0xA>(0.f, v);
-  v += dpp_f<0x143, 0xC>(0.f, v);
-  return v;
-}
-__device__ __forceinline__ int wave_scan_max(int v) {
-  v = max(v, dpp_i<0x111, 0xF>(-1, v));
-  v = max(v, dpp_i<0x112, 0xF>(-1, v));
-  v = max(v, dpp_i<0x114, 0xF>(-1, v));
-  v = max(v, dpp_i<0x118, 0xF>(-1, v));
-  v = max(v, dpp_i<0x142, 0xA>(-1, v));
-  v = max(v, dpp_i<0x143, 0xC>(-1, v));
-  return v;
-}
-
 // One prep wave's half of a chunk, as loaded from global memory: Q and K rows
 // 32pw .. 32pw+31 as whole rows, DK/8 lanes per row (load u: row 32pw +
 // RPL u + lane / (DK/8), 16-byte slot lane % (DK/8), RPL = 512 / DK rows per
