@@ -56,7 +56,7 @@ METRIC = "GDN prefill tokens/s (B4×S4096,Hv32,d128) + decode state HBM GB/s % o
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_b4s4096_decode_b256_conv1d_b4s4096.json")
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_prefill_b4s4096.json")
 CALIB_BYTES = 2 * (1 << 30)   # the calibration copy reads 1 GiB and writes 1 GiB
-PREFILL_KERNEL = "prefill_pair_kernel<128,false,false>"
+PREFILL_KERNEL = "prefill_pair_kernel<128,false,false,false>"
 
 
 def kernel_source_hash() -> str:
@@ -75,8 +75,13 @@ def kernel_source_hash() -> str:
 # The kernels each traffic figure belongs to, by the instantiation the timed
 # workloads launch (demangled or mangled, as the profiler prints them).
 KERNEL_KEYS = (
-    ("prefill", ("prefill_pair_kernel<128, false, false>", "prefill_pair_kernelILi128ELb0ELb0E")),
+    ("prefill", ("prefill_pair_kernel<128, false, false, false>", "prefill_pair_kernelILi128ELb0ELb0ELb0E")),
     ("decode", ("decode_kernel<__bf16, 128, 128, 32>", "decode_kernelIDF16bLi128ELi128ELi32E")),
+    # extra workloads: the multi-token decode (B64 T4 n2, dv 64), the ragged
+    # fp32 prefill (general kernel, 32-token chunks), the per-key-decay prefill
+    ("decode_mtp", ("decode_kernel<__bf16, 128, 64, 32>", "decode_kernelIDF16bLi128ELi64ELi32E")),
+    ("prefill_f32", ("prefill_kernel<float, 128, 64, 32, false>", "prefill_kernelIfLi128ELi64ELi32ELb0E")),
+    ("prefill_pk", ("prefill_pk_kernel<__bf16, 128, 64, false>", "prefill_pk_kernelIDF16bLi128ELi64ELb0E")),
     ("gate", ("gate_kernel",)),
     ("conv1d_out", ("conv1d_out_kernel<__bf16, 4, 16>", "conv1d_out_kernelIDF16bLi4ELi16E")),
     ("conv1d_state", ("conv1d_state_kernel<__bf16, 4>", "conv1d_state_kernelIDF16bLi4E")),
@@ -107,20 +112,39 @@ def _counter_means(path, counter):
     return out
 
 
-def summarize_traffic(fetch_csv, write_csv):
-    f = _counter_means(fetch_csv, "FETCH_SIZE")
-    w = _counter_means(write_csv, "WRITE_SIZE")
-    # the copy reads and writes 1 GiB each: scale each counter separately
-    f_scale = (CALIB_BYTES / 2) / (f["copy"] * 1024.0)
-    w_scale = (CALIB_BYTES / 2) / (w["copy"] * 1024.0)
+# Instantiations that only the extra workloads launch: their counter means
+# come from a run of every workload; the headline kernels' from a run of the
+# headline step alone (extras reuse some headline instantiations on other
+# shapes, e.g. the long request's serial walk).
+EXTRA_KEYS = ("decode_mtp", "prefill_f32", "prefill_pk")
+
+
+def summarize_traffic(fetch_csv, write_csv, fetch_all_csv=None, write_all_csv=None):
+    """HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE (KiB) counter runs,
+    each scaled by what the same counter reads for the run's calibration copy
+    of known size."""
+    def run(fc, wc):
+        f = _counter_means(fc, "FETCH_SIZE")
+        w = _counter_means(wc, "WRITE_SIZE")
+        # the copy reads and writes 1 GiB each: scale each counter separately
+        return f, w, (CALIB_BYTES / 2) / (f["copy"] * 1024.0), (CALIB_BYTES / 2) / (w["copy"] * 1024.0)
+    f, w, f_scale, w_scale = run(fetch_csv, write_csv)
     res = {"source_hash": kernel_source_hash(), "calibration_copy_bytes": CALIB_BYTES,
            "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    def put(k, f, w, fs, ws):
+        rb = f[k] * 1024.0 * fs
+        wb = w[k] * 1024.0 * ws
+        res["kernels"][k] = {"fetch_kib_raw": f[k], "write_kib_raw": w[k],
+                             "read_bytes": rb, "write_bytes": wb, "bytes": rb + wb}
     for k in ("prefill", "decode", "gate", "conv1d_out", "conv1d_state"):
         if k in f and k in w:
-            rb = f[k] * 1024.0 * f_scale
-            wb = w[k] * 1024.0 * w_scale
-            res["kernels"][k] = {"fetch_kib_raw": f[k], "write_kib_raw": w[k],
-                                 "read_bytes": rb, "write_bytes": wb, "bytes": rb + wb}
+            put(k, f, w, f_scale, w_scale)
+    if fetch_all_csv and write_all_csv:
+        fa, wa, fa_scale, wa_scale = run(fetch_all_csv, write_all_csv)
+        res["all_workload_run"] = {"fetch_scale": fa_scale, "write_scale": wa_scale}
+        for k in EXTRA_KEYS:
+            if k in fa and k in wa:
+                put(k, fa, wa, fa_scale, wa_scale)
     if "conv1d_out" in res["kernels"]:
         # one conv1d call = the output launch + the write-back launch
         parts = [res["kernels"][k] for k in ("conv1d_out", "conv1d_state") if k in res["kernels"]]
@@ -129,25 +153,44 @@ def summarize_traffic(fetch_csv, write_csv):
     return res
 
 
-def summarize_mfma(csv_path):
+def summarize_mfma(csv_path, all_csv_path=None):
     """MfmaUtil (% of SIMD cycles the MFMA unit is busy) and MfmaFlopsBF16 of
-    the prefill kernel, averaged over its dispatches."""
-    vals = {}
-    for r in csv.DictReader(open(csv_path)):
-        if _kernel_key(r["Kernel_Name"]) == "prefill":
-            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-    return {"source_hash": kernel_source_hash(), "kernel": PREFILL_KERNEL,
-            "dispatches": len(vals.get("MfmaUtil", [])),
-            "mfma_util_pct": statistics.mean(vals["MfmaUtil"]),
-            "mfma_flops_bf16": statistics.mean(vals["MfmaFlopsBF16"])}
+    the headline prefill kernel (from a run of the headline step), averaged
+    over its dispatches; the same for the extra workloads' own prefill
+    kernels (under "others", from a run of every workload)."""
+    def read(path):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            key = _kernel_key(r["Kernel_Name"])
+            if key is not None:
+                vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+    vals = read(csv_path)
+    for k in EXTRA_KEYS:
+        vals.pop(k, None)
+    if all_csv_path:
+        va = read(all_csv_path)
+        for k in EXTRA_KEYS:
+            if k in va:
+                vals[k] = va[k]
+    def one(v):
+        return {"dispatches": len(v.get("MfmaUtil", [])),
+                "mfma_util_pct": statistics.mean(v["MfmaUtil"]) if "MfmaUtil" in v else None,
+                "mfma_flops_bf16": statistics.mean(v["MfmaFlopsBF16"]) if "MfmaFlopsBF16" in v else None}
+    res = {"source_hash": kernel_source_hash(), "kernel": PREFILL_KERNEL}
+    res.update(one(vals["prefill"]))
+    res["others"] = {k: one(v) for k, v in vals.items() if k in ("prefill_f32", "prefill_pk")}
+    return res
 
 
-def load_mfma():
+def load_mfma(kernel="prefill"):
     try:
         m = json.load(open(MFMA_FILE))
     except (OSError, ValueError):
         return None
-    return m if m.get("source_hash") == kernel_source_hash() else None
+    if m.get("source_hash") != kernel_source_hash():
+        return None
+    return m if kernel == "prefill" else m.get("others", {}).get(kernel)
 
 
 def load_traffic(kernel):
@@ -254,6 +297,11 @@ def _time_launches(torch, fn, warmup=3, runs=20, flush=None):
     return statistics.median(x.elapsed_time(y) for x, y in ts)
 
 
+def _progress(what):
+    """One progress line per workload on stderr (stdout carries only the JSON line)."""
+    print("[bench] %s" % what, file=sys.stderr, flush=True)
+
+
 def extra_workloads(torch, gdn, synth, dev):
     """The other workloads of the scope table, each timed on its own."""
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -263,6 +311,7 @@ def extra_workloads(torch, gdn, synth, dev):
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     cm = _time_launches(torch, lambda: dst.copy_(src), flush=flush)
+    _progress("copy_1gib")
     out["copy_1gib"] = {"ms": cm, "gbs": 2 * (1 << 30) / (cm * 1e-3) / 1e9}
     del src, dst
 
@@ -281,6 +330,7 @@ def extra_workloads(torch, gdn, synth, dev):
     fn = lambda: gdn.prefill(q, k, v, None, None, scale=px["scale"], out=o2, final_state=f2,
                              A_log=A_log, dt_bias=dt_bias, a=a, b=b, qk_l2norm=True)
     ms = _time_launches(torch, fn, flush=flush)
+    _progress("chunked_prefill_fused_gate_qk_l2norm")
     out["chunked_prefill_fused_gate_qk_l2norm"] = {"ms": ms, "tokens_per_s": px["T"] / (ms * 1e-3)}
     del q, k, v, o2, f2
 
@@ -294,6 +344,7 @@ def extra_workloads(torch, gdn, synth, dev):
     fn = lambda: gdn.prefill(q.view(B1, S1, 1, -1), k.view(B1, S1, 1, -1), v.view(B1, S1, 1, -1),
                              gam.view(B1, S1, 1), bet.view(B1, S1, 1), decay_kind="gamma",
                              scale=x["scale"], out=o1.view(B1, S1, 1, -1), final_state=f1)
+    _progress("single_head_scan_b2_s64_d16_f32")
     out["single_head_scan_b2_s64_d16_f32"] = {"ms": _time_launches(torch, fn, runs=50)}
 
     # ragged fp32 prefill: 8 requests, initial state, gamma gates
@@ -309,12 +360,16 @@ def extra_workloads(torch, gdn, synth, dev):
     T = x["T"]
     nb, nf = prefill_algorithmic(T, x["hq"], x["hv"], x["dk"], x["dv"], x["n_seqs"], 64, io_bytes=4)
     nb += x["n_seqs"] * x["hv"] * x["dv"] * x["dk"] * 4  # the initial state is read too
+    mf = load_mfma("prefill_f32")
+    _progress("ragged_prefill_8req_hv32_d128_f32")
     out["ragged_prefill_8req_hv32_d128_f32"] = {
         "ms": ms, "tokens": T, "tokens_per_s": T / (ms * 1e-3),
         "algorithmic_bytes": nb, "algorithmic_flops": nf,
         "gbs": nb / (ms * 1e-3) / 1e9, "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "fp32_matrix_tflops": nf / (ms * 1e-3) / 1e12,
-        "fp32_matrix_frac": nf / (ms * 1e-3) / 1e12 / FP32_MATRIX_PEAK_TFLOPS}
+        "fp32_matrix_frac": nf / (ms * 1e-3) / 1e12 / FP32_MATRIX_PEAK_TFLOPS,
+        "traffic": load_traffic("prefill_f32"),
+        "mfma_util_counter_pct": None if mf is None else mf["mfma_util_pct"]}
     del q, k, v, o3, f3, init
 
     # multi-token decode: pool [512, 16, 64, 128], B64, T4, n2, scatter
@@ -327,9 +382,10 @@ def extra_workloads(torch, gdn, synth, dev):
                             scale=x["scale"], out=o5)
     ms = _time_launches(torch, fn, flush=flush)
     by = decode_algorithmic(x)
+    _progress("mtp_decode_b64_t4_n2_h16_dv64_bf16")
     out["mtp_decode_b64_t4_n2_h16_dv64_bf16"] = {
         "ms": ms, "algorithmic_bytes": by, "gbs": by / (ms * 1e-3) / 1e9,
-        "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": load_traffic("decode_mtp")}
     del t, o5
 
     # multi-token decode batches (B64, n1) with 16 and 64 tokens per row: the
@@ -366,9 +422,13 @@ def extra_workloads(torch, gdn, synth, dev):
     ms = _time_launches(torch, fn, flush=flush, runs=5)
     nb, _ = prefill_algorithmic(T, px["hq"], hv, dk, px["dv"], px["n_seqs"], 16)
     nb += T * hv * dk * 4 - T * hv * 4  # the decay is per key
+    mf = load_mfma("prefill_pk")
+    _progress("chunked_prefill_per_key_decay_b4_s4096_bf16")
     out["chunked_prefill_per_key_decay_b4_s4096_bf16"] = {
         "ms": ms, "tokens_per_s": T / (ms * 1e-3), "algorithmic_bytes": nb,
-        "gbs": nb / (ms * 1e-3) / 1e9, "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        "gbs": nb / (ms * 1e-3) / 1e9, "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "traffic": load_traffic("prefill_pk"),
+        "mfma_util_counter_pct": None if mf is None else mf["mfma_util_pct"]}
     del q, k, v, dec, bet, o8, f8
 
     # one long request with few heads (1 x 65536 tokens, Hq 2, Hv 4, d 128):
@@ -388,6 +448,7 @@ def extra_workloads(torch, gdn, synth, dev):
     ms_scan = _time_launches(torch, fn_scan, flush=flush)
     ms_serial = _time_launches(torch, fn_serial, flush=flush, runs=5)
     T = x["T"]
+    _progress("long_request_b1_s65536_hq2_hv4_d128_bf16")
     out["long_request_b1_s65536_hq2_hv4_d128_bf16"] = {
         "ms_scan": ms_scan, "ms_serial": ms_serial, "speedup": ms_serial / ms_scan,
         "segments": need // (x["hv"] * x["dk"] * (2 * x["dv"] + x["dk"]) * 4),
@@ -407,6 +468,7 @@ def extra_workloads(torch, gdn, synth, dev):
         fn = lambda: gdn.conv1d(xd, wd, pool, sl, off, out=oc)
         ms = _time_launches(torch, fn, flush=flush)
         by = conv1d_algorithmic(x)
+        _progress(name)
         out[name] = {"ms": ms, "tokens": x["T"], "algorithmic_bytes": by,
                      "gbs": by / (ms * 1e-3) / 1e9, "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         del xd, wd, pool, oc
@@ -424,16 +486,22 @@ def main():
                          "the causal conv1d over the prefill batch's QKV rows")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
-    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
-    ap.add_argument("--summarize-mfma", metavar="MFMA_CSV")
+    ap.add_argument("--summarize-traffic", nargs="+", metavar="CSV",
+                    help="FETCH.csv WRITE.csv of the headline run [FETCH.csv WRITE.csv of an all-workload run]")
+    ap.add_argument("--summarize-mfma", nargs="+", metavar="CSV",
+                    help="MFMA.csv of the headline run [MFMA.csv of an all-workload run]")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the single-head, ragged-fp32 and multi-token-decode timings")
     args = ap.parse_args()
     if args.summarize_traffic:
+        if len(args.summarize_traffic) not in (2, 4):
+            ap.error("--summarize-traffic takes 2 or 4 CSV files")
         print(json.dumps(summarize_traffic(*args.summarize_traffic), indent=1))
         return
     if args.summarize_mfma:
-        print(json.dumps(summarize_mfma(args.summarize_mfma), indent=1))
+        if len(args.summarize_mfma) not in (1, 2):
+            ap.error("--summarize-mfma takes 1 or 2 CSV files")
+        print(json.dumps(summarize_mfma(*args.summarize_mfma), indent=1))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "

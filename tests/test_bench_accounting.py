@@ -55,13 +55,16 @@ def _write_counters(path, counter, rows):
 def test_traffic_summary_calibration_and_attribution(tmp_path):
     kib = bench.CALIB_BYTES / 2 / 1024.0          # the copy's read (and written) KiB
     fetch = [("void at::native::neg_kernel(...)", kib / 2),   # FETCH_SIZE reads half
-             ("void gdn::prefill_pair_kernel<128, false, false>(gdn::PrefillParams)", 1000.0),
-             ("void gdn::prefill_pair_kernel<128, false, false>(gdn::PrefillParams)", 1200.0),
+             ("void gdn::prefill_pair_kernel<128, false, false, false>(gdn::PrefillParams)", 1000.0),
+             ("void gdn::prefill_pair_kernel<128, false, false, false>(gdn::PrefillParams)", 1200.0),
              ("_ZN3gdn13decode_kernelIDF16bLi128ELi128ELi32EEEvNS_12DecodeParamsE", 500.0),
-             ("void gdn::prefill_pair_kernel<128, true, true>(gdn::PrefillParams)", 9999.0)]
+             ("void gdn::decode_kernel<__bf16, 128, 64, 32>(gdn::DecodeParams)", 700.0),
+             ("void gdn::prefill_pair_kernel<128, true, true, false>(gdn::PrefillParams)", 9999.0),
+             ("void gdn::prefill_pair_kernel<128, false, false, true>(gdn::PrefillParams)", 8888.0)]
     write = [("void at::native::neg_kernel(...)", kib),
-             ("void gdn::prefill_pair_kernel<128, false, false>(gdn::PrefillParams)", 300.0),
-             ("_ZN3gdn13decode_kernelIDF16bLi128ELi128ELi32EEEvNS_12DecodeParamsE", 400.0)]
+             ("void gdn::prefill_pair_kernel<128, false, false, false>(gdn::PrefillParams)", 300.0),
+             ("_ZN3gdn13decode_kernelIDF16bLi128ELi128ELi32EEEvNS_12DecodeParamsE", 400.0),
+             ("void gdn::decode_kernel<__bf16, 128, 64, 32>(gdn::DecodeParams)", 800.0)]
     fp, wp = tmp_path / "fetch.csv", tmp_path / "write.csv"
     _write_counters(fp, "FETCH_SIZE", fetch)
     _write_counters(wp, "WRITE_SIZE", write)
@@ -76,3 +79,15 @@ def test_traffic_summary_calibration_and_attribution(tmp_path):
     assert pre["write_bytes"] == pytest.approx(300.0 * 1024)
     dec = t["kernels"]["decode"]
     assert dec["bytes"] == pytest.approx(500.0 * 1024 * 2 + 400.0 * 1024)
+    # an extra workload's own kernel is taken from the all-workload run only,
+    # scaled by that run's own calibration copy
+    assert "decode_mtp" not in t["kernels"]
+    fa, wa = tmp_path / "fetch_all.csv", tmp_path / "write_all.csv"
+    _write_counters(fa, "FETCH_SIZE", [("void at::native::neg_kernel(...)", kib / 4),
+                                       ("void gdn::decode_kernel<__bf16, 128, 64, 32>(gdn::DecodeParams)", 350.0)])
+    _write_counters(wa, "WRITE_SIZE", [("void at::native::neg_kernel(...)", kib),
+                                       ("void gdn::decode_kernel<__bf16, 128, 64, 32>(gdn::DecodeParams)", 800.0)])
+    t = bench.summarize_traffic(str(fp), str(wp), str(fa), str(wa))
+    assert t["kernels"]["prefill"]["fetch_kib_raw"] == pytest.approx(1100.0)
+    assert t["all_workload_run"]["fetch_scale"] == pytest.approx(4.0)
+    assert t["kernels"]["decode_mtp"]["bytes"] == pytest.approx(350.0 * 1024 * 4 + 800.0 * 1024)
