@@ -160,11 +160,17 @@ struct PairPrepSet {
 // row K's value held by lane K of this lane's 16-lane row, broadcast with
 // DPP row_newbcast:K.  The entry step K-1 reads first is updated first.
 template <int K>
+__device__ __forceinline__ float row_bcast(float v) {
+  // row_newbcast writes every lane of the row, so no old value is needed
+  // (and none is materialised)
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + K, 0xF, 0xF, false));
+}
+template <int K>
 __device__ __forceinline__ void tri_inverse_steps(float (&acc)[16], const float (&arow)[16]) {
-  const float t = acc[K];
-  acc[K - 1] -= t * dpp_f<0x150 + K, 0xF>(0.f, arow[K - 1]);
+  const float nt = -acc[K];
+  acc[K - 1] = fmaf(row_bcast<K>(arow[K - 1]), nt, acc[K - 1]);
 #pragma unroll
-  for (int j = 0; j < K - 1; ++j) acc[j] -= t * dpp_f<0x150 + K, 0xF>(0.f, arow[j]);
+  for (int j = 0; j < K - 1; ++j) acc[j] = fmaf(row_bcast<K>(arow[j]), nt, acc[j]);
   if constexpr (K > 1) tri_inverse_steps<K - 1>(acc, arow);
 }
 
