@@ -155,22 +155,52 @@ struct PairPrepSet {
   __bf16 ga, gbr;    // or the fused gate's raw a and b
 };
 
+// acc[j] += row K's arow[j] * nt for the listed j, one fused DPP
+// multiply-add each (v_fmac_f32_dpp with row_newbcast:K, which reads the
+// operand from lane K of the lane's 16-lane row).  The compiler does not see
+// the DPP read inside the asm, so each group starts with the 2 wait states
+// a DPP read needs after a VALU write of its source.
+template <int K>
+__device__ __forceinline__ void fmac_bcast1(float& a0, float b0, float nt) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+      : "+v"(a0)
+      : "v"(b0), "v"(nt), "n"(K));
+}
+template <int K>
+__device__ __forceinline__ void fmac_bcast4(float& a0, float& a1, float& a2, float& a3, float b0, float b1, float b2,
+                                            float b3, float nt) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %4, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %5, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %6, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %7, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf"
+      : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3)
+      : "v"(b0), "v"(b1), "v"(b2), "v"(b3), "v"(nt), "n"(K));
+}
+
 // One right-looking step of pair_tri_inverse4 and the steps below it: with
 // t = T[r][K] final, T[r][j] -= t A[K][j] for every j < K, where A[K][j] is
-// row K's value held by lane K of this lane's 16-lane row, broadcast with
-// DPP row_newbcast:K.  The entry step K-1 reads first is updated first.
-template <int K>
-__device__ __forceinline__ float row_bcast(float v) {
-  // row_newbcast writes every lane of the row, so no old value is needed
-  // (and none is materialised)
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + K, 0xF, 0xF, false));
-}
+// row K's value held by lane K of this lane's 16-lane row.  The entry step
+// K-1 reads first is updated first.
 template <int K>
 __device__ __forceinline__ void tri_inverse_steps(float (&acc)[16], const float (&arow)[16]) {
   const float nt = -acc[K];
-  acc[K - 1] = fmaf(row_bcast<K>(arow[K - 1]), nt, acc[K - 1]);
+  // the order of updates: K-1, then 0 .. K-2
+  constexpr int NG = K / 4;  // full groups of four
 #pragma unroll
-  for (int j = 0; j < K - 1; ++j) acc[j] = fmaf(row_bcast<K>(arow[j]), nt, acc[j]);
+  for (int gi = 0; gi < NG; ++gi) {
+    auto jj = [](int i) { return i == 0 ? K - 1 : i - 1; };
+    const int j0 = jj(4 * gi), j1 = jj(4 * gi + 1), j2 = jj(4 * gi + 2), j3 = jj(4 * gi + 3);
+    fmac_bcast4<K>(acc[j0], acc[j1], acc[j2], acc[j3], arow[j0], arow[j1], arow[j2], arow[j3], nt);
+  }
+#pragma unroll
+  for (int i = 4 * NG; i < K; ++i) {
+    const int j = i == 0 ? K - 1 : i - 1;
+    fmac_bcast1<K>(acc[j], arow[j], nt);
+  }
   if constexpr (K > 1) tri_inverse_steps<K - 1>(acc, arow);
 }
 
