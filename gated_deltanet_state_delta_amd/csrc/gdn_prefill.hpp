@@ -184,6 +184,18 @@ __device__ __forceinline__ int prefill_request_of_rank(const PrefillParams& p, i
   return __builtin_amdgcn_readfirstlane(tmp[kLptMax + 1]);
 }
 
+// Polls an LDS counter until it reaches `target`, at most 2^22 times (far
+// beyond any wait of a working schedule); when the polls run out, lane 0
+// adds 1 to the call's wait-expiry word and the wave goes on, so a broken
+// schedule is reported instead of hanging the GPU.
+__device__ __forceinline__ void wait_lds_count(int* cnt, int target, unsigned int* wait_err) {
+  for (int spin = 0; spin < (1 << 22); ++spin) {
+    if (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (__lane_id() == 0) __hip_atomic_fetch_add(wait_err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Segment j of nseg of a request's range: ceil(chunks / nseg) whole chunks of
 // C tokens each (the last segments may be shorter or empty).
 __device__ __forceinline__ void prefill_segment_bounds(int nseg, int j, int C, int64_t& start, int64_t& end) {

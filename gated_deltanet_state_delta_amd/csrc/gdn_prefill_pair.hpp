@@ -94,18 +94,6 @@ struct PairSmem {
   int nrm_cnt;   // norm halves written by the prep waves so far (L2 norm only)
 };
 
-// Polls an LDS counter until it reaches `target`, at most 2^22 times (far
-// beyond any wait of a working schedule); when the polls run out, lane 0
-// adds 1 to the call's wait-expiry word and the wave goes on, so a broken
-// schedule is reported instead of hanging the GPU.
-__device__ __forceinline__ void pair_wait_count(int* cnt, int target, unsigned int* wait_err) {
-  for (int spin = 0; spin < (1 << 22); ++spin) {
-    if (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  if (__lane_id() == 0) __hip_atomic_fetch_add(wait_err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // 16-byte slot permutation of a Q/K row.
 __device__ __forceinline__ int pair_swz(int row, int slot) {
   return slot ^ (((row & 1) << 2) | ((row >> 1) & 3));
@@ -369,7 +357,7 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
         sc.Fx[lane] = __builtin_amdgcn_exp2f(Fb1 - F);
       }
       prefetch(c + 3, s, 1);
-      pair_wait_count(&sm.prep_cnt, 2 * staged, p.wait_err);
+      wait_lds_count(&sm.prep_cnt, 2 * staged, p.wait_err);
       const bool any_zero = zlast >= 0;  // wave-uniform
 
       // ---- per-token factors of the state waves (wave 2), after the norms
@@ -472,7 +460,7 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
         *reinterpret_cast<f2*>(&ad[20 * x + 8 + 2 * g]) = f2{arow[1], arow[3]};
       }
       if constexpr (NORM) {
-        pair_wait_count(&sm.nrm_cnt, 2 * staged, p.wait_err);
+        wait_lds_count(&sm.nrm_cnt, 2 * staged, p.wait_err);
         factors();
       }
       // ---- off-diagonal tiles: -A and M blocks.  D(t, s) = e_t c_im f_s for

@@ -100,6 +100,7 @@ struct PkSmem {
   alignas(16) float xk[C][DK];
   alignas(16) float xP[C][DK];
   alignas(16) float xn[C][DK];
+  int fin_cnt;  // chunks whose -A and M rows state wave 2 has formed (normal path)
 };
 
 // DPP move inside 16-lane rows; lanes without a source lane receive `fill`.
@@ -256,10 +257,16 @@ prefill_pk_kernel(const PrefillParams p) {
     return any != 0;
   };
 
+  if (tid == 0) sm.fin_cnt = 0;  // first read after the loops' first barrier
+
   // ------------------------------------------------------------ state waves
-  // Iteration j: the state pass of chunk j (state waves below NVT) and, on
-  // state wave 3, the finishing of chunk j+1: its partial tiles summed, the
-  // exceptional keys' terms added, -A and M formed, (I + A) inverted.
+  // Iteration j: the state pass of chunk j (state waves below NVT) and the
+  // finishing of chunk j+1 in two parts: state wave 2 sums its partial
+  // tiles, adds the exceptional keys' terms and forms -A and M before its
+  // state pass; state wave 3 inverts (I + A) after its own (an LDS counter
+  // says when the rows are there), so neither wave carries a state pass and
+  // a whole finishing.  A chunk with exceptional keys is finished whole by
+  // wave 3 before the state pass (see below).
   if (wave < 4) {
     const bool active = wave < NVT;  // waves beyond the slice only finish and keep the barriers
     const int vc = 16 * wave + x;    // value column inside the slice
@@ -356,8 +363,8 @@ prefill_pk_kernel(const PrefillParams p) {
           if (4 * g + e < nvalid) ob[(4 * g + e) * ost + x] = from_f32<E>(Y[e]);
       }
     };
-    // Finishing of chunk c (state wave 3, all 64 lanes).
-    auto finish = [&](int c) {
+    // Finishing of chunk c, first part (all 64 lanes of one wave): -A and M.
+    auto finish_rows = [&](int c) {
       const typename Sm::Part& Pa = sm.part[c & 1];
       const typename Sm::Raw& R = sm.raw[c % 3];
       typename Sm::Der& Dd = sm.der[c & 1];
@@ -422,8 +429,9 @@ prefill_pk_kernel(const PrefillParams p) {
         Dd.gs[t] = p.scale * rqt;
         Dd.dc[t] = rkt;
       }
-      pk_tri_inverse<E, Sm::LDC>(sm.ad, Dd.tinv, lane);
     };
+    // Second part: (I + A)^-1 from the rows the first part left in sm.ad.
+    auto finish_inverse = [&](int c) { pk_tri_inverse<E, Sm::LDC>(sm.ad, sm.der[c & 1].tinv, lane); };
 
     if (active) {
       if (ibase >= 0) {
@@ -433,17 +441,29 @@ prefill_pk_kernel(const PrefillParams p) {
       }
       if (nch > 0) load_v(0);
     }
+    int nsplit_fin = 0;  // chunks finished in two parts so far (the same in every wave)
     for (int j = -2; j < nch; ++j) {
-      const bool fin = wave == 3 && j + 1 >= 0 && j + 1 < nch;
+      const bool fj = j + 1 >= 0 && j + 1 < nch;  // a chunk to finish
       if (has_exc(j + 1)) {
         // the prep waves overwrite the exceptional keys' values only after
         // chunk j+1 has been finished
-        if (fin) finish(j + 1);
+        if (fj && wave == 3) {
+          finish_rows(j + 1);
+          finish_inverse(j + 1);
+        }
         lds_barrier();
         if (active && j >= 0) state_pass(j);
       } else {
+        if (fj) ++nsplit_fin;
+        if (fj && wave == 2) {
+          finish_rows(j + 1);
+          if (lane == 0) __hip_atomic_fetch_add(&sm.fin_cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
         if (active && j >= 0) state_pass(j);
-        if (fin) finish(j + 1);
+        if (fj && wave == 3) {
+          wait_lds_count(&sm.fin_cnt, nsplit_fin, p.wait_err);
+          finish_inverse(j + 1);
+        }
       }
       lds_barrier();
     }
