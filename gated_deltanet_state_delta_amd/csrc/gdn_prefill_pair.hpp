@@ -146,12 +146,13 @@ struct PairPrepSet {
 // acc[j] += row K's arow[j] * nt for the listed j, one fused DPP
 // multiply-add each (v_fmac_f32_dpp with row_newbcast:K, which reads the
 // operand from lane K of the lane's 16-lane row).  The compiler does not see
-// the DPP read inside the asm, so each group starts with the 2 wait states
-// a DPP read needs after a VALU write of its source.
+// the DPP read inside the asm, so it cannot insert the 2 wait states a DPP
+// read needs after a VALU write of its source.  None is needed: the DPP
+// sources are the rows of A as read from LDS, which no VALU instruction
+// writes (a test scans the kernels' assembly for such a write).
 template <int K>
 __device__ __forceinline__ void fmac_bcast1(float& a0, float b0, float nt) {
   asm volatile(
-      "s_nop 1\n\t"
       "v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
       : "+v"(a0)
       : "v"(b0), "v"(nt), "n"(K));
@@ -160,7 +161,6 @@ template <int K>
 __device__ __forceinline__ void fmac_bcast4(float& a0, float& a1, float& a2, float& a3, float b0, float b1, float b2,
                                             float b3, float nt) {
   asm volatile(
-      "s_nop 1\n\t"
       "v_fmac_f32_dpp %0, %4, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
       "v_fmac_f32_dpp %1, %5, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
       "v_fmac_f32_dpp %2, %6, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
