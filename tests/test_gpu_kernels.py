@@ -47,6 +47,29 @@ def test_gate_parity(dtype):
     assert torch.equal(ld2, ld)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gate_ragged_and_unaligned(dtype):
+    """The vector path (groups of eight elements, heads stepped across rows),
+    its ragged end (4 985 elements) and the element path of unaligned inputs
+    (views one element into their buffers) all match the oracle."""
+    import gated_deltanet_state_delta_amd as gdn
+    g = torch.Generator().manual_seed(102)
+    hv, n = 5, 997
+    A_log = torch.rand(hv, generator=g) * 4 - 1
+    dt_bias = torch.randn(hv, generator=g)
+    a = (torch.randn(n, hv, generator=g) * 8).to(synth.DTYPES[dtype])
+    b = (torch.randn(n, hv, generator=g) * 8).to(synth.DTYPES[dtype])
+    rg, rgam, rbeta = oracle.gate(A_log, dt_bias, a, b)
+    ld, gam, beta = gdn.gate(A_log.cuda(), dt_bias.cuda(), a.cuda(), b.cuda(), want_gamma=True)
+    assert rel_err(ld, rg) < 1e-5 and rel_err(gam, rgam) < 1e-5 and rel_err(beta, rbeta) < 1e-6
+    ua = torch.empty(n * hv + 1, dtype=a.dtype, device="cuda")[1:].view(n, hv)
+    ub = torch.empty(n * hv + 1, dtype=b.dtype, device="cuda")[1:].view(n, hv)
+    ua.copy_(a.cuda())
+    ub.copy_(b.cuda())
+    ld2, gam2, beta2 = gdn.gate(A_log.cuda(), dt_bias.cuda(), ua, ub, want_gamma=True)
+    assert torch.equal(ld2, ld) and torch.equal(gam2, gam) and torch.equal(beta2, beta)
+
+
 # ----------------------------------------------------------------- decode --
 
 def _gpu_decode(x, out=None, pool=None, **kw):
