@@ -314,8 +314,15 @@ __device__ __forceinline__ typename pack4<E>::type to_pack4(f4 v) {
 
 // EXT compiles the optional fused gate and in-kernel q/k L2 norm in (each
 // still switched by its argument); without it the code has neither.
+// 16-token chunks, and bf16 32-token chunks, are held to 128 VGPRs (four
+// waves per SIMD), so that two workgroups share a CU: their LDS fits twice,
+// and calls with many short requests (the chunked multi-token decode: one
+// or two chunks per workgroup, thousands of workgroups) hide one
+// workgroup's state loads and barriers behind the other's work.  The bf16
+// 32-token forms spill a few registers to do so and still gain; the fp32
+// 32-token form (the long ragged requests) keeps one workgroup per CU.
 template <typename E, int DK, int DVS, int C, bool EXT>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(512, (C == 16 || (C == 32 && sizeof(E) == 2)) ? 4 : 1)
 prefill_kernel(const PrefillParams p) {
   typedef typename frag_of<E>::type Fr;
   typedef PrefillSmem<E, DK, DVS, C> Sm;
