@@ -31,8 +31,13 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # B4 x S4096: about 18% faster than the default strategy; 1% faster than the
 # iterative ILP strategy (outputs bit-identical); the plain max-ILP strategy
 # is 6% slower.
+# The decode kernel at value width 128 (the single-step pool decode of
+# Hv32 x 128 x 128 states) takes the iterative ILP scheduler: 2.2% faster
+# there (three same-box A/B runs, bit-identical); the same flag made the
+# multi-token width-64 form 2.5% slower, so that one keeps the default.
 FILE_FLAGS = {"gdn_prefill_pair.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form",
-                                     "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
+                                     "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+              "gdn_decode_dv128.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Wno-unused-function", "-Wno-unused-variable", "-I", os.path.join(ROOT, "include")]
 
