@@ -27,16 +27,18 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # speed depends on latency hiding inside each wave: its MFMA accumulators stay
 # in VGPRs (its state is scaled and converted by VALU code every chunk, and
 # accumulators in AGPRs would cost a copy each way), and the machine
-# scheduler that groups memory operations into clauses is used.  On
-# B4 x S4096: about 18% faster than the default strategy; 1% faster than the
-# iterative ILP strategy (outputs bit-identical); the plain max-ILP strategy
+# scheduler that groups memory operations into clauses is used, with the
+# target's own register-pressure trackers.  On B4 x S4096: about 18% faster
+# than the default strategy; 1% faster than the iterative ILP strategy, and
+# the trackers 1.2% more (outputs bit-identical); the plain max-ILP strategy
 # is 6% slower.
 # The decode kernel at value width 128 (the single-step pool decode of
 # Hv32 x 128 x 128 states) takes the iterative ILP scheduler: 2.2% faster
 # there (three same-box A/B runs, bit-identical); the same flag made the
 # multi-token width-64 form 2.5% slower, so that one keeps the default.
 FILE_FLAGS = {"gdn_prefill_pair.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form",
-                                     "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+                                     "-mllvm", "-amdgpu-sched-strategy=max-memory-clause",
+                                     "-mllvm", "-amdgpu-use-amdgpu-trackers"],
               "gdn_decode_dv128.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Wno-unused-function", "-Wno-unused-variable", "-I", os.path.join(ROOT, "include")]
