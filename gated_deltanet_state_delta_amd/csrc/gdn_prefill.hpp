@@ -600,6 +600,11 @@ prefill_kernel(const PrefillParams p) {
   }
 
   // ------------------------------------------------------------- prep waves
+  // Each prep wave shares its SIMD with a state wave, and the state waves
+  // wait for the prep waves at the barriers: the prep waves issue first
+  // (the ragged fp32 workload 0.5-0.8% faster, the chunked decode at T = 16
+  // 2.5%, same-box A/B runs, bit-identical).
+  __builtin_amdgcn_s_setprio(2);
   u32x4 pq[NPT][4], pk[NPT][4];
   float pg = 0.f, pb = 0.f;     // prefetched decay/beta of token `lane`
   E pga = from_f32<E>(0.f), pgb = from_f32<E>(0.f);  // or the fused gate's raw a, b
