@@ -8,67 +8,57 @@
 
 namespace gdn {
 
-// Eight consecutive io elements of a or b at an element index that is a
-// multiple of 8, widened to fp32 (one 16-byte or two 16-byte loads).
-__device__ __forceinline__ void load8f(const __bf16* p, float* v) {
-  const bf8 x = *reinterpret_cast<const bf8*>(p);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
-}
-__device__ __forceinline__ void load8f(const float* p, float* v) {
-  const f4 x0 = reinterpret_cast<const f4*>(p)[0], x1 = reinterpret_cast<const f4*>(p)[1];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    v[e] = x0[e];
-    v[4 + e] = x1[e];
-  }
-}
-__device__ __forceinline__ void store8f(float* p, const float* v) {
-  reinterpret_cast<f4*>(p)[0] = f4{v[0], v[1], v[2], v[3]};
-  reinterpret_cast<f4*>(p)[1] = f4{v[4], v[5], v[6], v[7]};
+// Elements per thread.  The gate is latency-bound at the sizes it runs at
+// (expf / log1pf chains, a few MB of traffic), so threads are many and short.
+constexpr int kGateEPT = 4;
+
+__device__ __forceinline__ void store4f(float* p, const float* v) {
+  *reinterpret_cast<f4*>(p) = f4{v[0], v[1], v[2], v[3]};
 }
 
-// Each thread handles eight consecutive elements of the flattened
+// Each thread handles kGateEPT consecutive elements of the flattened
 // [n_tokens, hv] arrays.  VEC (every pointer 16-byte aligned): whole groups
-// of eight use vector loads and stores; the ragged end and unaligned calls
-// take the element loop.  The head of element i is i mod hv, found once per
-// thread and stepped from there.
+// use one vector load per input and one 16-byte store per output; the
+// ragged end and unaligned calls take the element loop.  The head of element
+// i is i mod hv, found once per thread and stepped from there.
 template <typename IN, bool VEC>
 __global__ void __launch_bounds__(256)
 gate_kernel(const float* __restrict__ A_log, const float* __restrict__ dt_bias,
             const IN* __restrict__ a, const IN* __restrict__ b, int64_t n_elems, int hv,
             float* __restrict__ log_decay, float* __restrict__ gamma, float* __restrict__ beta) {
-  const int64_t base = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  constexpr int N = kGateEPT;
+  static_assert(N == 4, "one f4 per input and output");
+  const int64_t base = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * N;
   if (base >= n_elems) return;
   int h0 = n_elems <= 0xffffffffLL ? (int)((uint32_t)base % (uint32_t)hv) : (int)(base % hv);
-  int hs[8];
+  int hs[N];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < N; ++e) {
     hs[e] = h0;
     h0 = h0 + 1 == hv ? 0 : h0 + 1;
   }
-  if (VEC && base + 8 <= n_elems) {
-    float v[8], o[8];
+  if (VEC && base + N <= n_elems) {
+    float o[N];
     if (a) {
-      load8f(a + base, v);
+      const f4 v = load4(a + base);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = gate_log_decay(A_log[hs[e]], dt_bias[hs[e]], v[e]);
-      if (log_decay) store8f(log_decay + base, o);
+      for (int e = 0; e < N; ++e) o[e] = gate_log_decay(A_log[hs[e]], dt_bias[hs[e]], v[e]);
+      if (log_decay) store4f(log_decay + base, o);
       if (gamma) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = expf(o[e]);
-        store8f(gamma + base, o);
+        for (int e = 0; e < N; ++e) o[e] = expf(o[e]);
+        store4f(gamma + base, o);
       }
     }
     if (b) {
-      load8f(b + base, v);
+      const f4 v = load4(b + base);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = sigmoidf(v[e]);
-      store8f(beta + base, o);
+      for (int e = 0; e < N; ++e) o[e] = sigmoidf(v[e]);
+      store4f(beta + base, o);
     }
     return;
   }
-  for (int e = 0; e < 8 && base + e < n_elems; ++e) {
+  for (int e = 0; e < N && base + e < n_elems; ++e) {
     const int64_t i = base + e;
     if (a) {
       const float g = gate_log_decay(A_log[hs[e]], dt_bias[hs[e]], to_f32(a[i]));
@@ -96,7 +86,7 @@ hipError_t launch_gate(const float* A_log, const float* dt_bias, const void* a, 
                        float* beta, hipStream_t stream) {
   const int64_t n = n_tokens * hv;
   if (n == 0) return hipSuccess;
-  const int64_t threads = (n + 7) / 8;
+  const int64_t threads = (n + kGateEPT - 1) / kGateEPT;
   const dim3 grid((unsigned)((threads + 255) / 256));
   auto al = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
   const bool vec = al(a) && al(b) && al(log_decay) && al(gamma) && al(beta);
