@@ -9,8 +9,16 @@
 namespace gdn {
 
 // Elements per thread.  The gate is latency-bound at the sizes it runs at
-// (expf / log1pf chains, a few MB of traffic), so threads are many and short.
+// (a few MB of traffic), so threads are many and short.
 constexpr int kGateEPT = 4;
+
+// The gates from the hardware exp2 / log2 / reciprocal (relative error about
+// 1e-6, the forms the fused-gate prefill uses), which shorten each thread's
+// dependent chain against the libm expf / log1pf forms.
+__device__ __forceinline__ float gate_ld(float A_log, float dt_bias, float a) {
+  return gate_log_decay_fast(__builtin_amdgcn_exp2f(A_log * 1.4426950408889634f), dt_bias, a);
+}
+__device__ __forceinline__ float exp_fast(float g) { return __builtin_amdgcn_exp2f(g * 1.4426950408889634f); }
 
 __device__ __forceinline__ void store4f(float* p, const float* v) {
   *reinterpret_cast<f4*>(p) = f4{v[0], v[1], v[2], v[3]};
@@ -42,18 +50,18 @@ gate_kernel(const float* __restrict__ A_log, const float* __restrict__ dt_bias,
     if (a) {
       const f4 v = load4(a + base);
 #pragma unroll
-      for (int e = 0; e < N; ++e) o[e] = gate_log_decay(A_log[hs[e]], dt_bias[hs[e]], v[e]);
+      for (int e = 0; e < N; ++e) o[e] = gate_ld(A_log[hs[e]], dt_bias[hs[e]], v[e]);
       if (log_decay) store4f(log_decay + base, o);
       if (gamma) {
 #pragma unroll
-        for (int e = 0; e < N; ++e) o[e] = expf(o[e]);
+        for (int e = 0; e < N; ++e) o[e] = exp_fast(o[e]);
         store4f(gamma + base, o);
       }
     }
     if (b) {
       const f4 v = load4(b + base);
 #pragma unroll
-      for (int e = 0; e < N; ++e) o[e] = sigmoidf(v[e]);
+      for (int e = 0; e < N; ++e) o[e] = sigmoid_fast(v[e]);
       store4f(beta + base, o);
     }
     return;
@@ -61,11 +69,11 @@ gate_kernel(const float* __restrict__ A_log, const float* __restrict__ dt_bias,
   for (int e = 0; e < N && base + e < n_elems; ++e) {
     const int64_t i = base + e;
     if (a) {
-      const float g = gate_log_decay(A_log[hs[e]], dt_bias[hs[e]], to_f32(a[i]));
+      const float g = gate_ld(A_log[hs[e]], dt_bias[hs[e]], to_f32(a[i]));
       if (log_decay) log_decay[i] = g;
-      if (gamma) gamma[i] = expf(g);
+      if (gamma) gamma[i] = exp_fast(g);
     }
-    if (b) beta[i] = sigmoidf(to_f32(b[i]));
+    if (b) beta[i] = sigmoid_fast(to_f32(b[i]));
   }
 }
 
