@@ -502,15 +502,17 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
     lds_barrier();
   };
 
-  // Two iterations per trip, both always run: (nch + 2) & ~1 barriers in all,
-  // matched by the state waves.
+  // Two iterations per trip, both always run; iteration c prepares chunk
+  // c + 1, so the trips end once chunk nch - 1 is prepared: nch + (nch & 1)
+  // barriers in all (one iteration on a chunk past the request when nch is
+  // odd), matched by the state waves.
   // The two first sets load in the loop's order (no instruction scheduled
   // across), so the loop head's wait for `sa` leaves `sb` in flight.
   PairPrepSet<DK> sa, sb;
   for (int part = 0; part < 3; ++part) prefetch(0, sa, part);
   __builtin_amdgcn_sched_barrier(0);
   for (int part = 0; part < 3; ++part) prefetch(1, sb, part);
-  for (int c = -1; c < nch; c += 2) {
+  for (int c = -1; c < nch - 1; c += 2) {
     iter(c, sa);
     iter(c + 1, sb);
   }
@@ -611,9 +613,10 @@ prefill_pair_kernel(const PrefillParams p) {
   const bool store_out = !SEG || p.seg_mode != 1;
   const int ost = (int)p.o_st;
 
-  // (nch + 2) & ~1 barriers, as the prep waves run them in pairs
-  const int nbar = (nch + 2) & ~1;
-  for (int c = -1; c < nbar - 1; ++c) {
+  // nch + (nch & 1) barriers, as the prep waves run them in pairs; the last
+  // chunk needs none after it (no buffer is written any more)
+  const int nbar = nch + (nch & 1);
+  for (int c = -1; c < nbar; ++c) {
     if (c >= 0 && c < nch) {
       const typename Sm::Buf& B = sm.buf[c & 1];
       // ---- (I + A_ii)^-1 of the four diagonal blocks, this wave's own copy
@@ -760,7 +763,7 @@ prefill_pair_kernel(const PrefillParams p) {
           }
       }
     }
-    lds_barrier();
+    if (c < nbar - 1) lds_barrier();
   }
   if (SEG && fbase >= 0 && trans) {
     // transition slice: element (key k, column i) of the K-major state is
