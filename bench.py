@@ -379,7 +379,7 @@ def extra_workloads(torch, gdn, synth, dev):
     o5 = torch.zeros(x["batch"], x["T"], x["hv"], x["dv"], dtype=torch.bfloat16, device=dev)
     fn = lambda: gdn.decode(t["q"], t["k"], t["v"], t["A_log"], t["dt_bias"], t["a"], t["b"],
                             t["pool"], t["read_idx"], scatter_idx=t["scatter_idx"],
-                            scale=x["scale"], out=o5)
+                            scale=x["scale"], out=o5, use_qk_l2norm=False)
     ms = _time_launches(torch, fn, flush=flush)
     by = decode_algorithmic(x)
     _progress("mtp_decode_b64_t4_n2_h16_dv64_bf16")
@@ -398,7 +398,7 @@ def extra_workloads(torch, gdn, synth, dev):
         o6 = torch.zeros(x["batch"], T16, x["hv"], x["dv"], dtype=torch.bfloat16, device=dev)
         fn = lambda: gdn.decode(t["q"], t["k"], t["v"], t["A_log"], t["dt_bias"], t["a"], t["b"],
                                 t["pool"], t["read_idx"], write_idx=t["write_idx"],
-                                scale=x["scale"], out=o6)
+                                scale=x["scale"], out=o6, use_qk_l2norm=False)
         ms = _time_launches(torch, fn, flush=flush)
         by = decode_algorithmic(x)
         out["mtp_decode_b64_t%d_h32_d128_bf16" % T16] = {
@@ -558,7 +558,7 @@ def main():
 
     def run_decode():
         gdn.decode(dq, dk_, dv_, dA, ddt, da, db, pool, rd, write_idx=wr, scale=dx["scale"],
-                   out=dout)
+                   out=dout, use_qk_l2norm=False)
 
     def run_conv():
         gdn.conv1d(c_x, c_w, c_pool, c_sl, c_off, out=c_out)

@@ -510,7 +510,7 @@ def state_update(q, k, v, gamma, beta):
 
 def decode_args(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None,
                 scatter_idx=None, disable_state_update=False, scale=None, out=None,
-                use_qk_l2norm=False, qk_l2norm_eps=1e-6, decay_per_key=None):
+                use_qk_l2norm=True, qk_l2norm_eps=1e-6, decay_per_key=None):
     """Validate shapes and build the gdn_decode_args struct (device-agnostic).
 
     Returns (args, keep, out)."""
@@ -572,7 +572,7 @@ def decode_args(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None
 
 
 def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None, scatter_idx=None,
-           disable_state_update=False, scale=None, out=None, stream=None, use_qk_l2norm=False,
+           disable_state_update=False, scale=None, out=None, stream=None, use_qk_l2norm=True,
            qk_l2norm_eps=1e-6, decay_per_key=None):
     """Slot-pool decode with Householder sub-steps (one fused launch).
 
@@ -581,7 +581,8 @@ def decode(q, k, v, A_log, dt_bias, a, b, pool, read_idx, *, write_idx=None, sca
     (updated in place); read_idx [B]; write_idx [B] or None; scatter_idx [B, T]
     or None.  scale None means 1/sqrt(dk).  use_qk_l2norm: use every q and k
     head vector as x / sqrt(sum x^2 + qk_l2norm_eps) (the FlashInfer page's
-    use_qk_l2norm; off by default here).  decay_per_key [B, T, hv, dk] float32
+    use_qk_l2norm, on by default as there; pass False for inputs already
+    normalised).  decay_per_key [B, T, hv, dk] float32
     log-decay per key dimension: replaces the gate's decay (a, A_log, dt_bias
     may then be None).  float16 q, k, v, a, b are converted to bfloat16 for
     the kernel and the output is copied into a float16 buffer (skipped rows

@@ -120,12 +120,24 @@ def _dec(B=8, T=2, n=2, hq=2, hv=4, dk=64, dv=32, P=20):
                 pool=torch.zeros(P, hv, dv, dk), read_idx=torch.zeros(B, dtype=torch.int64))
 
 
+def test_decode_l2norm_default_follows_flashinfer():
+    """use_qk_l2norm defaults to True (eps 1e-6) in the decode binding, as on
+    the FlashInfer page; False clears the struct's flag."""
+    x = _dec(B=2, T=1, n=1, hq=2, hv=4, dk=64, dv=64, P=4)
+    d, _, _ = gdn.decode_args(x["q"], x["k"], x["v"], x["A_log"], x["dt_bias"], x["a"], x["b"],
+                              x["pool"], x["read_idx"])
+    assert d.qk_l2norm == 1 and abs(d.qk_l2norm_eps - 1e-6) < 1e-12
+    d, _, _ = gdn.decode_args(x["q"], x["k"], x["v"], x["A_log"], x["dt_bias"], x["a"], x["b"],
+                              x["pool"], x["read_idx"], use_qk_l2norm=False)
+    assert d.qk_l2norm == 0
+
+
 def test_decode_struct_in_bounds_bench_shapes():
     x = _dec(B=256, T=1, n=1, hq=16, hv=32, dk=128, dv=128, P=8)
     out = torch.zeros(256, 1, 32, 128, dtype=torch.bfloat16)
     d, keep, o = gdn.decode_args(x["q"], x["k"], x["v"], x["A_log"], x["dt_bias"], x["a"],
                                  x["b"], x["pool"], x["read_idx"],
-                                 write_idx=torch.zeros(256, dtype=torch.int32), out=out)
+                                 write_idx=torch.zeros(256, dtype=torch.int32), out=out, use_qk_l2norm=False)
     assert o is out
     P = x["pool"]
     last = (d.pool_size - 1) * d.pool_slot_stride + (d.hv - 1) * d.pool_head_stride + d.dv * d.dk - 1
@@ -313,14 +325,14 @@ def test_int64_slot_and_offset_narrowing():
     rd = torch.tensor([2**32 + 3, 5, -2**33 + 1, 2**31, 2**31 - 1, -1], dtype=torch.int64)
     wr = torch.tensor([1, 2**40, 3, 4, 2**32, 0], dtype=torch.int64)
     d, keep, _ = gdn.decode_args(x["q"], x["k"], x["v"], x["A_log"], x["dt_bias"], x["a"],
-                                 x["b"], x["pool"], rd, write_idx=wr)
+                                 x["b"], x["pool"], rd, write_idx=wr, use_qk_l2norm=False)
     rd32, wr32 = keep[7], keep[8]
     assert rd32.dtype == torch.int32 and wr32.dtype == torch.int32
     assert rd32.tolist() == [-1, 5, -1, -1, 2**31 - 1, -1]
     assert wr32.tolist() == [1, -1, 3, 4, -1, 0]
     sc = torch.tensor([[2**32 + 1, 7]] * 6, dtype=torch.int64)
     _, keep, _ = gdn.decode_args(x["q"], x["k"], x["v"], x["A_log"], x["dt_bias"], x["a"],
-                                 x["b"], x["pool"], rd, scatter_idx=sc)
+                                 x["b"], x["pool"], rd, scatter_idx=sc, use_qk_l2norm=False)
     assert keep[9].tolist() == [[-1, 7]] * 6
     T, hq, hv, dk, dv = 96, 2, 4, 64, 32
     cu = torch.tensor([-2**40, 10, 2**35, 2**31 - 1], dtype=torch.int64)

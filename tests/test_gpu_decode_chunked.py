@@ -75,7 +75,7 @@ def test_chunked_and_token_loop_agree():
         sl = slice(t, t + 1)
         o, _ = gdn.decode(to_dev(x["q"][:, sl]), to_dev(x["k"][:, sl]), to_dev(x["v"][:, sl]),
                           to_dev(x["A_log"]), to_dev(x["dt_bias"]), to_dev(x["a"][:, sl]),
-                          to_dev(x["b"][:, sl]), pool_b, to_dev(x["read_idx"]), scale=x["scale"])
+                          to_dev(x["b"][:, sl]), pool_b, to_dev(x["read_idx"]), scale=x["scale"], use_qk_l2norm=False)
         outs.append(o)
     torch.cuda.synchronize()
     out_b = torch.cat(outs, dim=1)

@@ -159,6 +159,20 @@ def test_decode_use_qk_l2norm(T, n, dtype):
     assert np.abs(ro2 - ro).max() > 1e-2 * np.abs(ro).max()
 
 
+def test_decode_l2norm_on_by_default():
+    """The binding's use_qk_l2norm defaults to True with eps 1e-6, as the
+    FlashInfer page's decode: a call that names neither is bit-identical to
+    one that asks for the norm explicitly."""
+    x = _dec(870, 2, 2, "bf16", scatter=False)
+    args = [to_dev(x[kk]) for kk in ("q", "k", "v", "A_log", "dt_bias", "a", "b")]
+    p1, p2 = x["pool"].cuda(), x["pool"].cuda()
+    o1, _ = gdn.decode(*args, p1, to_dev(x["read_idx"]), write_idx=to_dev(x["write_idx"]), scale=x["scale"])
+    o2, _ = gdn.decode(*args, p2, to_dev(x["read_idx"]), write_idx=to_dev(x["write_idx"]), scale=x["scale"],
+                       use_qk_l2norm=True, qk_l2norm_eps=1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(p1, p2)
+
+
 @pytest.mark.parametrize("fused", [False, True])
 def test_prefill_float16_inputs(fused):
     """float16 q, k, v (the ONNX card's T includes f16): the float32 path on
@@ -196,7 +210,7 @@ def test_decode_float16_inputs_go_through_bfloat16():
     o, _ = gdn.decode(h["q"].cuda(), h["k"].cuda(), h["v"].cuda(), to_dev(x["A_log"]),
                       to_dev(x["dt_bias"]), h["a"].cuda(), h["b"].cuda(), pool,
                       to_dev(x["read_idx"]), write_idx=to_dev(x["write_idx"]), scale=x["scale"],
-                      out=out)
+                      out=out, use_qk_l2norm=False)
     # the oracle on the bfloat16 values the kernel saw
     bf = {n: t.to(torch.bfloat16) for n, t in h.items()}
     ro, rp = oracle.decode(bf["q"], bf["k"], bf["v"], x["A_log"], x["dt_bias"], bf["a"], bf["b"],

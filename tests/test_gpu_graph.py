@@ -86,14 +86,14 @@ def _calls(t, o, ps, fs):
     for n in ("d1", "d16"):
         gdn.decode(t[n + "q"], t[n + "k"], t[n + "v"], t[n + "A_log"], t[n + "dt_bias"], t[n + "a"],
                    t[n + "b"], t[n + "pool"], t[n + "read_idx"], write_idx=t[n + "write_idx"],
-                   scale=t[n + "scale"], out=o[n + "o"])
+                   scale=t[n + "scale"], out=o[n + "o"], use_qk_l2norm=False)
     gdn.conv1d(t["cx"], t["cweight"], t["cconv_state"], t["cslot"], t["coff"], out=o["co"])
     # per-key decay: prefill, and the chunked multi-token decode over a pool
     gdn.prefill(t["kq"], t["kk"], t["kv"], t["kdec"], t["kbeta"], cu_seqlens=t["kcu_seqlens"],
                 initial_state=t["kinitial_state"], scale=t["kscale"], out=o["ko"], final_state=o["kfin"],
                 decay_per_key=True)
     gdn.decode(t["eq"], t["ek"], t["ev"], None, None, None, t["eb"], t["epool"], t["eread_idx"],
-               write_idx=t["ewrite_idx"], scale=t["escale"], out=o["eo"], decay_per_key=t["edec"])
+               write_idx=t["ewrite_idx"], scale=t["escale"], out=o["eo"], decay_per_key=t["edec"], use_qk_l2norm=False)
 
 
 STATEFUL = ("d1pool", "d16pool", "cconv_state", "epool")

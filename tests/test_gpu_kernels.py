@@ -76,7 +76,7 @@ def _gpu_decode(x, out=None, pool=None, **kw):
     import gated_deltanet_state_delta_amd as gdn
     pool = to_dev(x["pool"]).clone() if pool is None else pool
     args = dict(write_idx=to_dev(x["write_idx"]), scatter_idx=to_dev(x["scatter_idx"]),
-                scale=x["scale"], out=out)
+                scale=x["scale"], out=out, use_qk_l2norm=False)
     args.update(kw)
     return gdn.decode(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(x["A_log"]),
                       to_dev(x["dt_bias"]), to_dev(x["a"]), to_dev(x["b"]), pool,
@@ -237,7 +237,7 @@ def test_decode_batch_zero_is_noop():
     pool = x["pool"].cuda()
     e = lambda t: t[:0].cuda()
     out, _ = gdn.decode(e(x["q"]), e(x["k"]), e(x["v"]), x["A_log"].cuda(), x["dt_bias"].cuda(),
-                        e(x["a"]), e(x["b"]), pool, e(x["read_idx"]))
+                        e(x["a"]), e(x["b"]), pool, e(x["read_idx"]), use_qk_l2norm=False)
     assert out.numel() == 0
     assert torch.equal(pool.cpu(), x["pool"])
 

@@ -183,7 +183,7 @@ def test_decode_per_key_matches_oracle(dtype, T, n, scatter):
     gdn.decode(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), None, None, None, to_dev(x["b"]),
                pool, to_dev(x["read_idx"]), write_idx=to_dev(x["write_idx"]),
                scatter_idx=to_dev(x["scatter_idx"]), scale=x["scale"], out=out,
-               decay_per_key=to_dev(dec))
+               decay_per_key=to_dev(dec), use_qk_l2norm=False)
     ro, rp = oracle.decode(x["q"], x["k"], x["v"], None, None, None, x["b"], x["pool"], x["read_idx"],
                            write_idx=x["write_idx"], scatter_idx=x["scatter_idx"], scale=x["scale"],
                            decay_per_key=dec)
@@ -200,7 +200,7 @@ def test_decode_per_key_chunked_modes(mode):
     """The multi-token decode with a per-key decay in its chunked form (T >= 16):
     no state write-back, and the in-kernel q/k L2 norm."""
     x, dec = _decode_pk(1500 + len(mode), "bf16", 24, 1, False)
-    kw = dict(disable_state_update=True) if mode == "disable" else dict(use_qk_l2norm=True, qk_l2norm_eps=1e-12)
+    kw = dict(disable_state_update=True, use_qk_l2norm=False) if mode == "disable" else dict(use_qk_l2norm=True, qk_l2norm_eps=1e-12)
     okw = dict(disable_state_update=True) if mode == "disable" else dict(qk_l2norm_eps=1e-12)
     if mode == "qk_l2norm":
         x["q"] = x["q"] * 2.5
@@ -227,7 +227,7 @@ def test_decode_per_key_equals_prefill_from_the_slot():
     pool_a = to_dev(x["pool"].clone())
     od, _ = gdn.decode(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), None, None, None,
                        to_dev(x["b"]), pool_a, to_dev(x["read_idx"]), scale=x["scale"],
-                       decay_per_key=to_dev(dec))
+                       decay_per_key=to_dev(dec), use_qk_l2norm=False)
     pool_b = to_dev(x["pool"].clone())
     beta = torch.sigmoid(x["b"].float()).reshape(B * T, 4)
     cu = torch.arange(B + 1, dtype=torch.int32) * T

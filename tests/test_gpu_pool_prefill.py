@@ -123,7 +123,7 @@ def test_multi_token_decode_as_pooled_prefill(T):
                                    "write_idx")}
     pool_a = to_dev(d["pool"].clone())
     od, _ = gdn.decode(t["q"], t["k"], t["v"], t["A_log"], t["dt_bias"], t["a"], t["b"], pool_a,
-                       t["read_idx"], write_idx=t["write_idx"], scale=d["scale"])
+                       t["read_idx"], write_idx=t["write_idx"], scale=d["scale"], use_qk_l2norm=False)
     pool_b = to_dev(d["pool"].clone())
     cu = torch.arange(B + 1, dtype=torch.int32, device="cuda") * T
     op, _ = gdn.prefill(t["q"].reshape(B * T, hq, dk), t["k"].reshape(B * T, hq, dk),

@@ -136,7 +136,7 @@ def _run_decode(x, pool_dev, out=None):
     return gdn.decode(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(x["A_log"]),
                       to_dev(x["dt_bias"]), to_dev(x["a"]), to_dev(x["b"]), pool_dev,
                       to_dev(x["read_idx"]), write_idx=to_dev(x["write_idx"]),
-                      scatter_idx=to_dev(x["scatter_idx"]), scale=x["scale"], out=out)
+                      scatter_idx=to_dev(x["scatter_idx"]), scale=x["scale"], out=out, use_qk_l2norm=False)
 
 
 def test_decode_pool1024_b256_bf16():
