@@ -32,10 +32,8 @@ static hipError_t dispatch_dk(const DecodeParams& p, int dk, int dv, hipStream_t
 // instead of one state pass per token.  Measured on B64 x Hv32 x 128x128 bf16
 // (token loop -> chunked): T = 16: 146 -> 112 us, T = 32: 256 -> 127 us,
 // T = 64: 470 -> 174 us (the token loop stays ahead below 16 tokens: 74 vs
-// 144 us at T = 4).  Chunks of 16 tokens below T = 32, else 32: the kernels
-// of both sizes run two workgroups per CU, which beat the 64-token pair
-// kernel's one at T = 64 (174 vs 185 us).  Every activation must be 16-byte
-// aligned, as the prefill kernels require.
+// 144 us at T = 4).  The chunk follows T (see launch_decode_chunked).  Every
+// activation must be 16-byte aligned, as the prefill kernels require.
 static bool decode_as_prefill(const gdn_decode_args& a) {
   if (a.T < 16 || a.n_householder != 1 || a.scatter_idx) return false;
   if ((int64_t)a.batch * a.T * a.hv >= (int64_t(1) << 31)) return false;
@@ -53,7 +51,14 @@ static hipError_t launch_decode_chunked(const gdn_decode_args& a, hipStream_t st
   pa.hq = a.hq; pa.hv = a.hv; pa.dk = a.dk; pa.dv = a.dv;
   pa.io_dtype = a.io_dtype;
   pa.decay_kind = GDN_DECAY_LOG;
-  pa.chunk_size = a.T < 32 ? 16 : 32;
+  // bf16 with the pair kernel's head sizes and T >= 32: its 64-token chunks
+  // with the multi-request walk (each workgroup runs a run of rows); B64 x
+  // Hv32 x 128x128: T = 32 125 -> 123 us, T = 64 177 -> 133 us against the
+  // general kernel at 32 tokens, which stays ahead at T = 16 (109 vs 123
+  // us).  Otherwise the general kernel at 16 or 32 tokens.
+  const bool pair = a.T >= 16 && a.io_dtype == GDN_BF16 && !a.decay_per_key && (a.dk == 64 || a.dk == 128) &&
+                    (a.dv == 64 || a.dv == 128);
+  pa.chunk_size = pair ? 0 : (a.T < 32 ? 16 : 32);
   pa.scale = a.scale;
   pa.q = a.q; pa.q_stride_token = (int64_t)a.hq * a.dk; pa.q_stride_head = a.dk;
   pa.k = a.k; pa.k_stride_token = (int64_t)a.hq * a.dk; pa.k_stride_head = a.dk;  // n = 1

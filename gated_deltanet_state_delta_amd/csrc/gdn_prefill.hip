@@ -93,6 +93,23 @@ static bool gates_mixed(const gdn_prefill_args& a) {
 // segment on average at least 16 chunks long, at most 64 segments, and at
 // least 4 (fewer cannot repay the three passes).  Only sizes decide, so a
 // call's result does not depend on the device.
+// Requests per workgroup of the pair kernel's multi-request walk: a call
+// with more (request, value head, slice) units than one round of the chip
+// takes (256 workgroups, one per CU) and short requests (four chunks or
+// fewer on average) runs each workgroup over a run of consecutive requests,
+// so that the kernel's start (the first chunks' loads and preparation) is
+// paid once per workgroup, not once per request.  Sizes only, so a call's
+// result never depends on the device.  0: one request per workgroup.
+static int pair_request_group(const gdn_prefill_args& a, int lpt) {
+  if (lpt || a.n_seqs < 2) return 0;
+  const int64_t per_req = (int64_t)a.hv * (a.dv / 64);
+  if ((int64_t)a.n_seqs * per_req <= 256) return 0;
+  if (a.total_tokens > (int64_t)a.n_seqs * 4 * 64) return 0;
+  const int64_t groups = std::max<int64_t>(1, 256 / per_req);
+  const int64_t g = std::min<int64_t>((a.n_seqs + groups - 1) / groups, kMultiMax);
+  return g >= 2 ? (int)g : 0;
+}
+
 int prefill_scan_segments(const gdn_prefill_args& a, int pool_flags) {
   if (pool_flags || a.decay_per_key || a.io_dtype != GDN_BF16 || gates_mixed(a) ||
       !prefill_pair_supported(a.dk, a.dv, a.chunk_size) || a.n_seqs <= 0 || a.total_tokens <= 0)
@@ -164,6 +181,7 @@ hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream, int poo
   p.nseg = 1; p.nsv = 1; p.seg_mode = 0; p.vzero = nullptr;
   p.lpt = a.cu_seqlens && a.n_seqs >= 2 && a.n_seqs <= kLptMax &&
           a.total_tokens >= (int64_t)kLptMinTokens * a.n_seqs;
+  p.rgroup = 0;
   p.decay_is_gamma = a.decay_kind == GDN_DECAY_GAMMA;
   p.scale = a.scale;
   p.qk_norm = a.qk_l2norm != 0;
@@ -195,7 +213,10 @@ hipError_t launch_prefill(const gdn_prefill_args& a, hipStream_t stream, int poo
   const int nseg = prefill_scan_segments(a, pool_flags);
   if (nseg > 1 && a.workspace && a.workspace_bytes >= prefill_workspace_bytes(a))
     return launch_prefill_scan(p, a, nseg, stream);
-  if (bf && !mixed && prefill_pair_supported(a.dk, a.dv, a.chunk_size)) return prefill_pair_bf16(p, a.dk, stream);
+  if (bf && !mixed && prefill_pair_supported(a.dk, a.dv, a.chunk_size)) {
+    p.rgroup = pair_request_group(a, p.lpt);
+    return prefill_pair_bf16(p, a.dk, stream);
+  }
   const int hint = a.chunk_size != 0 ? a.chunk_size : 64;
   const int c = bf ? prefill_chunk_for<__bf16>(a.dk, a.dv, hint)
                    : prefill_chunk_for<float>(a.dk, a.dv, hint);

@@ -117,6 +117,10 @@ struct PrefillParams {
   // count of in-kernel waits that ran out of polls (see gdn_wait_timeouts)
   unsigned int* wait_err;
   int lpt;  // take requests longest first (prefill_request_of_rank)
+  // Pair kernel: requests per workgroup of the multi-request walk (0 or 1:
+  // one request per workgroup).  Consecutive requests rgroup * i ..
+  // rgroup * (i + 1) - 1 share workgroup i of each (value head, slice).
+  int rgroup;
 };
 
 // Token range [start, end) of request r: cu_seqlens clamped to [0, T] (a

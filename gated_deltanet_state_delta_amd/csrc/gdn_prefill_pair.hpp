@@ -34,6 +34,10 @@
 //    diagonal blocks A_ii; wave 2 also writes the per-token factors;
 //  * one workgroup barrier per chunk: the state waves read buffer c & 1 while
 //    the prep waves fill buffer (c+1) & 1;
+//  * the multi-request walk (MULTI, its own instantiation): a workgroup runs
+//    a run of consecutive short requests of one (value head, slice) as one
+//    chunk stream, the state swapped at each request boundary, so the
+//    kernel's start is paid once per workgroup (see pair_multi_walk);
 //  * options, each its own instantiation: the fused gate (the prep waves gate
 //    a and b when they stage a chunk) and the in-kernel q/k L2 norm (1/|q_t|
 //    and 1/|k_t| from the diagonals of the diagonal Gram tiles, folded into
@@ -228,10 +232,43 @@ __device__ __forceinline__ void pair_tri_inverse4(const float (*ad)[16 * 20 + 4]
 // come from A_log, dt_bias, a, b (computed here); NORM: the in-kernel q/k L2
 // norm.  Each combination is its own instantiation, so none carries branches
 // for the options it does not use.
-template <int DK, int PW, bool FUSED, bool NORM>
+// Multi-request walk: a workgroup takes up to kMultiMax consecutive requests
+// for one (value head, slice) and runs their chunks as one stream, request
+// after request (each request's chunks start at its own first token).  The
+// group's token ranges sit in LDS (mt[i] start, mt[kMultiMax + i] end of the
+// group's request i); a cursor (request, chunk) walks the stream, skipping
+// empty requests.
+constexpr int kMultiMax = 64;
+struct PairCursor {
+  int r, c;
+};
+__device__ __forceinline__ int multi_nch(const int64_t* mt, int i) {
+  return (int)((mt[kMultiMax + i] - mt[i] + 63) / 64);
+}
+__device__ __forceinline__ int multi_next(const int64_t* mt, int nreq, int i) {
+  do ++i;
+  while (i < nreq && multi_nch(mt, i) == 0);
+  return i;
+}
+__device__ __forceinline__ void multi_advance(const int64_t* mt, int nreq, PairCursor& u) {
+  if (u.r >= nreq) return;
+  if (++u.c >= multi_nch(mt, u.r)) {
+    u.c = 0;
+    u.r = multi_next(mt, nreq, u.r);
+  }
+}
+// Chunk at the cursor: first token and row count (have false past the end).
+__device__ __forceinline__ void multi_chunk(const int64_t* mt, int nreq, const PairCursor& u, bool& have,
+                                            int64_t& t0, int& rem) {
+  have = u.r < nreq;
+  t0 = have ? mt[u.r] + (int64_t)u.c * 64 : 0;
+  rem = have ? (int)min((int64_t)64, mt[kMultiMax + u.r] - t0) : 0;
+}
+
+template <int DK, int PW, bool FUSED, bool NORM, bool MULTI>
 __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& sm, int64_t start,
                                           int64_t end, int nch, const __bf16* gq, const __bf16* gk,
-                                          const __bf16* gv, int v_st, int h) {
+                                          const __bf16* gv, int v_st, int h, const int64_t* mt, int nreq) {
   typedef PairSmem<DK> Sm;
   constexpr int C = 64, NPP = DK / 32;
   const int lane = threadIdx.x & 63, x = lane & 15, g = lane >> 4;
@@ -254,10 +291,8 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
   // (num_records 0), read zeros without touching memory.  The values are
   // kept exactly as loaded: nothing here may wait on these loads (padding
   // and the fused gate are applied when the set is staged).
-  auto prefetch = [&](int c, PairPrepSet<DK>& s, int part) {
-    const bool have = c < nch;
-    const int64_t t0 = start + (int64_t)(have ? c : 0) * C;
-    const int rem = have ? (int)min((int64_t)C, end - t0) : 1;  // rows of the chunk
+  auto prefetch_at = [&](bool have, int64_t t0, int rem, PairPrepSet<DK>& s, int part) {
+    rem = have ? rem : 1;  // rows of the chunk
     const int qst = (int)p.q_st, kst = (int)p.k_st, vst = v_st;
     auto rsrc = [&](const void* base, int bytes) { return buf_rsrc_n(base, have ? (uint32_t)bytes : 0u); };
     if (part == 0) {
@@ -284,6 +319,31 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
     for (int u = 0; u < 4; ++u)
       if (part == 0)
         s.v[u] = buf_load16(rv, (uint32_t)(((32 * PW + 8 * u + (lane >> 3)) * vst + 8 * (lane & 7)) * 2), 0);
+  };
+  // chunk c of the request (single-request walk), or the prefetch cursor's
+  // chunk (multi-request walk; the cursor moves on once per iteration)
+  PairCursor cp{0, 0}, cs{0, 0};
+  if constexpr (MULTI) {
+    cp.r = mt[0 + kMultiMax] > mt[0] ? 0 : multi_next(mt, nreq, 0);
+    cs = cp;
+  }
+  bool hp = false;
+  int64_t tp = 0;
+  int rp = 0;
+  auto prefetch = [&](int c, PairPrepSet<DK>& s, int part) {
+    if constexpr (MULTI) {
+      prefetch_at(hp, tp, rp, s, part);
+    } else {
+      const bool have = c < nch;
+      const int64_t t0 = start + (int64_t)(have ? c : 0) * C;
+      prefetch_at(have, t0, have ? (int)min((int64_t)C, end - t0) : 1, s, part);
+    }
+  };
+  auto next_prefetch_chunk = [&]() {
+    if constexpr (MULTI) {
+      multi_chunk(mt, nreq, cp, hp, tp, rp);
+      multi_advance(mt, nreq, cp);
+    }
   };
 
   auto frag_col = [&](int row, int pp) -> int { return 8 * pair_swz(row, 4 * pp + g); };
@@ -314,7 +374,16 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
         *reinterpret_cast<u32x4*>(&B.v[32 * PW + 8 * u + (lane >> 3)][8 * (lane & 7)]) = s.v[u];
       // gates of token `lane`; padded tokens: no decay (log-decay 0 / gamma
       // 1) and beta 0
-      const bool live = lane < (int)min((int64_t)C, end - (start + (int64_t)(c + 1) * C));
+      int srows;
+      if constexpr (MULTI) {
+        bool hs;
+        int64_t ts;
+        multi_chunk(mt, nreq, cs, hs, ts, srows);
+        multi_advance(mt, nreq, cs);
+      } else {
+        srows = (int)min((int64_t)C, end - (start + (int64_t)(c + 1) * C));
+      }
+      const bool live = lane < srows;
       if constexpr (FUSED) {  // an absent input: no decay, beta 1
         gd = live && p.dmask ? gate_log_decay_fast(ealog, dtb, (float)s.ga) : 0.f;
         btl = live ? (p.bmask ? sigmoid_fast((float)s.gbr) : 1.f) : 0.f;
@@ -329,6 +398,7 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
       ++staged;
       if (lane == 0) __hip_atomic_fetch_add(&sm.prep_cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
+    next_prefetch_chunk();
     prefetch(c + 3, s, 0);
     {
       typename Sm::Buf& B = sm.buf[(c + 1) & 1];
@@ -509,8 +579,10 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
   // The two first sets load in the loop's order (no instruction scheduled
   // across), so the loop head's wait for `sa` leaves `sb` in flight.
   PairPrepSet<DK> sa, sb;
+  next_prefetch_chunk();
   for (int part = 0; part < 3; ++part) prefetch(0, sa, part);
   __builtin_amdgcn_sched_barrier(0);
+  next_prefetch_chunk();
   for (int part = 0; part < 3; ++part) prefetch(1, sb, part);
   for (int c = -1; c < nch - 1; c += 2) {
     iter(c, sa);
@@ -518,12 +590,84 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
   }
 }
 
-template <int DK, bool FUSED, bool NORM, bool SEG>
+// The state waves' side of the multi-request walk.  Every request's chunks
+// run as in the single-request walk; at a request's first chunk the state
+// becomes its initial state, after its last chunk the state is stored to
+// its final slot.  The pool rules hold per request: a request whose read
+// slot is outside the pool is skipped under kPoolSkipUnread (no outputs, no
+// store; its chunks are still prepared), and an empty request's final state
+// is its initial state.
+// The next request's initial state is loaded into Sn during a request's
+// last chunk, before that chunk's outputs and final-state stores: the
+// vector-memory counter retires in issue order, so a state loaded after
+// the stores would wait for them.  Every chunk issues the same loads and
+// stores -- through buffer descriptors whose range is 0 when a chunk needs
+// none, so they move no data -- and takes the new state by a select, so
+// the compiler's count of memory operations in flight is exact on every
+// path and the wait for Sn leaves the stores in flight.
+template <int DK, typename Body>
+__device__ __forceinline__ void pair_multi_walk(const PrefillParams& p, const int64_t* mt, int nreq, int rg0,
+                                                int h, int v0, int nch, int w, int lane, f4 (&S)[DK / 16][2],
+                                                Body& chunk_body) {
+  constexpr int NKT = DK / 16;
+  constexpr uint32_t kSlice = 64u * DK * 4u;  // bytes of a 64-row state slice
+  const int x = lane & 15, g = lane >> 4;
+  auto off = [&](int jj, int ct) {
+    return (uint32_t)(((32 * w + 16 * ct + x) * DK + dk_of<NKT>(jj, 4 * g)) * 4);
+  };
+  auto load_state = [&](f4 (&D)[NKT][2], int64_t ib) {
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc_n(p.init + (ib >= 0 ? ib : 0), ib >= 0 ? kSlice : 0u);
+#pragma unroll
+    for (int jj = 0; jj < NKT; ++jj)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) D[jj][ct] = __builtin_bit_cast(f4, buf_load16(rs, off(jj, ct), 0));
+  };
+  auto store_state = [&](int64_t fb) {
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc_n(p.fin + (fb >= 0 ? fb : 0), fb >= 0 ? kSlice : 0u);
+#pragma unroll
+    for (int jj = 0; jj < NKT; ++jj)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, S[jj][ct]), rs, off(jj, ct), 0, 0);
+  };
+  auto skipped = [&](int64_t ib) { return (p.pool_flags & kPoolSkipUnread) && ib < 0; };
+  for (int i = 0; i < nreq; ++i) {
+    if (multi_nch(mt, i) != 0) continue;
+    int64_t ib, fb;
+    prefill_state_offsets(p, rg0 + i, h, v0, DK, ib, fb);
+    if (skipped(ib) || fb < 0) continue;
+    load_state(S, ib);
+    store_state(fb);
+  }
+  PairCursor u{0, 0};
+  u.r = multi_nch(mt, 0) > 0 ? 0 : multi_next(mt, nreq, 0);
+  int64_t ib_cur = -1, fb_cur = -1;
+  bool skip = false;
+  const int nbar = nch + (nch & 1);  // as the prep waves run them
+  for (int c = -1; c < nbar; ++c) {
+    if (c >= 0 && c < nch) {
+      const bool last = u.c == multi_nch(mt, u.r) - 1;
+      if (u.c == 0) {
+        prefill_state_offsets(p, rg0 + u.r, h, v0, DK, ib_cur, fb_cur);
+        skip = skipped(ib_cur);
+        load_state(S, ib_cur);
+      }
+      const int64_t tok0 = mt[u.r] + (int64_t)u.c * 64;
+      if (!skip) chunk_body(c, tok0, (int)min((int64_t)64, mt[kMultiMax + u.r] - tok0));
+      if (last && !skip && fb_cur >= 0) store_state(fb_cur);
+      multi_advance(mt, nreq, u);
+    }
+    if (c < nbar - 1) lds_barrier();
+  }
+}
+
+template <int DK, bool FUSED, bool NORM, bool SEG, bool MULTI>
 __global__ void __launch_bounds__(256, 1)
 prefill_pair_kernel(const PrefillParams p) {
   typedef PairSmem<DK> Sm;
   constexpr int C = 64, NKT = DK / 16, NPP = DK / 32;
   __shared__ Sm sm;
+  __shared__ int64_t mt[MULTI ? 2 * kMultiMax : 1];  // multi-request walk: the group's token ranges
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -536,9 +680,12 @@ prefill_pair_kernel(const PrefillParams p) {
   const int blk = prefill_block_unit(blockIdx.x, gridDim.x, p.nsplit * max(p.hv / p.hq, 1), p.lpt);
   const int split = blk % p.nsplit;
   const int h = (blk / p.nsplit) % p.hv;
-  const int kj = blk / (p.nsplit * p.hv);  // (rank, segment)
+  const int kj = blk / (p.nsplit * p.hv);  // (rank, segment), or the request group
   const int j = SEG ? kj % p.nseg : 0;
-  const int r = prefill_request_of_rank(p, SEG ? kj / p.nseg : kj, reinterpret_cast<int*>(&sm.buf[1].q[0][0]));
+  // multi-request walk: requests rg0 .. rg0 + nreq - 1
+  const int rg0 = MULTI ? kj * p.rgroup : 0;
+  const int nreq = MULTI ? min(p.rgroup, p.n_seqs - rg0) : 1;
+  const int r = MULTI ? rg0 : prefill_request_of_rank(p, SEG ? kj / p.nseg : kj, reinterpret_cast<int*>(&sm.buf[1].q[0][0]));
   const int rj = SEG ? r * p.nseg + j : r;  // the unit's workspace index
   const int qh = (int)(((int64_t)h * p.hq) / p.hv);
   const bool trans = SEG && split >= p.nsv;  // transition slice of a local pass
@@ -547,7 +694,15 @@ prefill_pair_kernel(const PrefillParams p) {
   int64_t start, end;
   prefill_request_bounds(p, r, start, end);
   if constexpr (SEG) prefill_segment_bounds(p.nseg, j, C, start, end);
-  const int nch = (int)((end - start + C - 1) / C);
+  int nch = (int)((end - start + C - 1) / C);
+  if constexpr (MULTI) {
+    if (tid < nreq) {
+      int64_t s0, s1;
+      prefill_request_bounds(p, rg0 + tid, s0, s1);
+      mt[tid] = s0;
+      mt[kMultiMax + tid] = s1;
+    }
+  }
 
   const __bf16* __restrict__ gq = (const __bf16*)p.q + (int64_t)qh * p.q_sh;
   const __bf16* __restrict__ gk = (const __bf16*)p.k + (int64_t)qh * p.k_sh;
@@ -567,7 +722,7 @@ prefill_pair_kernel(const PrefillParams p) {
   } else {
     prefill_state_offsets(p, r, h, v0, DK, ibase, fbase);
   }
-  if ((p.pool_flags & kPoolSkipUnread) && ibase < 0) return;  // uniform over the workgroup
+  if (!MULTI && (p.pool_flags & kPoolSkipUnread) && ibase < 0) return;  // uniform over the workgroup
 
   // The readout pairs each diagonal block of M with the block to its right,
   // which the prep waves never write: clear those two blocks once.
@@ -580,10 +735,15 @@ prefill_pair_kernel(const PrefillParams p) {
     sm.nrm_cnt = 0;
   }
   lds_barrier();
+  if constexpr (MULTI) {
+    // the stream's chunk count
+    nch = 0;
+    for (int i = 0; i < nreq; ++i) nch += multi_nch(mt, i);
+  }
 
   if (wave >= 2) {
-    if (wave == 2) pair_prep<DK, 0, FUSED, NORM>(p, sm, start, end, nch, gq, gk, gv, v_st, h);
-    else pair_prep<DK, 1, FUSED, NORM>(p, sm, start, end, nch, gq, gk, gv, v_st, h);
+    if (wave == 2) pair_prep<DK, 0, FUSED, NORM, MULTI>(p, sm, start, end, nch, gq, gk, gv, v_st, h, mt, nreq);
+    else pair_prep<DK, 1, FUSED, NORM, MULTI>(p, sm, start, end, nch, gq, gk, gv, v_st, h, mt, nreq);
     return;
   }
 
@@ -616,8 +776,9 @@ prefill_pair_kernel(const PrefillParams p) {
   // nch + (nch & 1) barriers, as the prep waves run them in pairs; the last
   // chunk needs none after it (no buffer is written any more)
   const int nbar = nch + (nch & 1);
-  for (int c = -1; c < nbar; ++c) {
-    if (c >= 0 && c < nch) {
+  // One chunk of the state waves: c is the chunk's place in the stream (its
+  // buffer parity), tok0 its first token, nvalid its rows to store.
+  auto chunk_body = [&](int c, int64_t tok0, int nvalid) {
       const typename Sm::Buf& B = sm.buf[c & 1];
       // ---- (I + A_ii)^-1 of the four diagonal blocks, this wave's own copy
       pair_tri_inverse4<Sm::LDT>(sm.adiag[c & 1], sm.tinv[w], lane);
@@ -734,8 +895,6 @@ prefill_pair_kernel(const PrefillParams p) {
         }
       }
       // ---- outputs (scale is folded into Gam and M)
-      const int64_t tok0 = start + (int64_t)c * C;
-      const int nvalid = store_out ? (int)min((int64_t)C, end - tok0) : 0;
       __bf16* ob = gout + tok0 * p.o_st + 32 * w;
       if (nvalid == C) {
         // Y^T tiles: lane (x, g) holds columns 16 ct + 4 g .. +3 of token
@@ -762,6 +921,23 @@ prefill_pair_kernel(const PrefillParams p) {
             if (t < nvalid) *reinterpret_cast<bf4*>(ob + (int64_t)t * ost + 16 * ct + 4 * g) = to_bf4(Y[i][ct]);
           }
       }
+  };
+  auto store_state = [&](int64_t fb) {
+#pragma unroll
+    for (int jj = 0; jj < NKT; ++jj)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        *reinterpret_cast<f4*>(p.fin + fb + (int64_t)(32 * w + 16 * ct + x) * DK + dk_of<NKT>(jj, 4 * g)) =
+            S[jj][ct];
+  };
+  if constexpr (MULTI) {
+    pair_multi_walk<DK>(p, mt, nreq, rg0, h, v0, nch, w, lane, S, chunk_body);
+    return;
+  }
+  for (int c = -1; c < nbar; ++c) {
+    if (c >= 0 && c < nch) {
+      const int64_t tok0 = start + (int64_t)c * C;
+      chunk_body(c, tok0, store_out ? (int)min((int64_t)C, end - tok0) : 0);
     }
     if (c < nbar - 1) lds_barrier();
   }
@@ -794,18 +970,22 @@ template <int DK>
 hipError_t launch_prefill_pair_t(PrefillParams p, hipStream_t stream) {
   p.nsv = p.dv / 64;
   p.nsplit = p.nsv + (p.seg_mode == 1 ? DK / 64 : 0);
-  const int64_t nblk = (int64_t)p.n_seqs * p.nseg * p.hv * p.nsplit;
+  const bool multi = !p.seg_mode && p.rgroup > 1;
+  const int64_t nunits = multi ? (p.n_seqs + p.rgroup - 1) / p.rgroup : (int64_t)p.n_seqs * p.nseg;
+  const int64_t nblk = nunits * p.hv * p.nsplit;
   const dim3 grid((unsigned)nblk), block(256);
   const bool fused = p.ga || p.gb;
-#define GDN_PAIR_LAUNCH(SEG)                                                                                   \
-  if (fused && p.qk_norm) hipLaunchKernelGGL((prefill_pair_kernel<DK, true, true, SEG>), grid, block, 0, stream, p); \
-  else if (fused) hipLaunchKernelGGL((prefill_pair_kernel<DK, true, false, SEG>), grid, block, 0, stream, p);       \
-  else if (p.qk_norm) hipLaunchKernelGGL((prefill_pair_kernel<DK, false, true, SEG>), grid, block, 0, stream, p);   \
-  else hipLaunchKernelGGL((prefill_pair_kernel<DK, false, false, SEG>), grid, block, 0, stream, p);
+#define GDN_PAIR_LAUNCH(SEG, MULTI)                                                                            \
+  if (fused && p.qk_norm) hipLaunchKernelGGL((prefill_pair_kernel<DK, true, true, SEG, MULTI>), grid, block, 0, stream, p); \
+  else if (fused) hipLaunchKernelGGL((prefill_pair_kernel<DK, true, false, SEG, MULTI>), grid, block, 0, stream, p);       \
+  else if (p.qk_norm) hipLaunchKernelGGL((prefill_pair_kernel<DK, false, true, SEG, MULTI>), grid, block, 0, stream, p);   \
+  else hipLaunchKernelGGL((prefill_pair_kernel<DK, false, false, SEG, MULTI>), grid, block, 0, stream, p);
   if (p.seg_mode) {
-    GDN_PAIR_LAUNCH(true)
+    GDN_PAIR_LAUNCH(true, false)
+  } else if (multi) {
+    GDN_PAIR_LAUNCH(false, true)
   } else {
-    GDN_PAIR_LAUNCH(false)
+    GDN_PAIR_LAUNCH(false, false)
   }
 #undef GDN_PAIR_LAUNCH
   return hipGetLastError();

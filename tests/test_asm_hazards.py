@@ -101,6 +101,8 @@ def test_pair_kernel_dpp_blocks_need_no_wait_states(tmp_path):
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
     n, bad = dpp_asm_hazards(open(out).read().split("\n"))
-    # 16 instantiations x 120 fused multiply-adds of the four-block inverse
-    assert n == 16 * 120, n
+    # 24 instantiations (dk 64/128 x fused gate x L2 norm x {one request,
+    # segments, multi-request walk}) x 120 fused multiply-adds of the
+    # four-block inverse
+    assert n == 24 * 120, n
     assert not bad, bad[:10]
