@@ -56,7 +56,7 @@ METRIC = "GDN prefill tokens/s (B4×S4096,Hv32,d128) + decode state HBM GB/s % o
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_b4s4096_decode_b256_conv1d_b4s4096.json")
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_prefill_b4s4096.json")
 CALIB_BYTES = 2 * (1 << 30)   # the calibration copy reads 1 GiB and writes 1 GiB
-PREFILL_KERNEL = "prefill_pair_kernel<128,false,false,false>"
+PREFILL_KERNEL = "prefill_pair_kernel<128,false,false,false,false>"
 
 
 def kernel_source_hash() -> str:
@@ -75,7 +75,7 @@ def kernel_source_hash() -> str:
 # The kernels each traffic figure belongs to, by the instantiation the timed
 # workloads launch (demangled or mangled, as the profiler prints them).
 KERNEL_KEYS = (
-    ("prefill", ("prefill_pair_kernel<128, false, false, false>", "prefill_pair_kernelILi128ELb0ELb0ELb0E")),
+    ("prefill", ("prefill_pair_kernel<128, false, false, false, false>", "prefill_pair_kernelILi128ELb0ELb0ELb0ELb0E")),
     ("decode", ("decode_kernel<__bf16, 128, 128, 32>", "decode_kernelIDF16bLi128ELi128ELi32E")),
     # extra workloads: the multi-token decode (B64 T4 n2, dv 64), the ragged
     # fp32 prefill (general kernel, 32-token chunks), the per-key-decay prefill

@@ -55,14 +55,14 @@ def _write_counters(path, counter, rows):
 def test_traffic_summary_calibration_and_attribution(tmp_path):
     kib = bench.CALIB_BYTES / 2 / 1024.0          # the copy's read (and written) KiB
     fetch = [("void at::native::neg_kernel(...)", kib / 2),   # FETCH_SIZE reads half
-             ("void gdn::prefill_pair_kernel<128, false, false, false>(gdn::PrefillParams)", 1000.0),
-             ("void gdn::prefill_pair_kernel<128, false, false, false>(gdn::PrefillParams)", 1200.0),
+             ("void gdn::prefill_pair_kernel<128, false, false, false, false>(gdn::PrefillParams)", 1000.0),
+             ("void gdn::prefill_pair_kernel<128, false, false, false, false>(gdn::PrefillParams)", 1200.0),
              ("_ZN3gdn13decode_kernelIDF16bLi128ELi128ELi32EEEvNS_12DecodeParamsE", 500.0),
              ("void gdn::decode_kernel<__bf16, 128, 64, 32>(gdn::DecodeParams)", 700.0),
-             ("void gdn::prefill_pair_kernel<128, true, true, false>(gdn::PrefillParams)", 9999.0),
-             ("void gdn::prefill_pair_kernel<128, false, false, true>(gdn::PrefillParams)", 8888.0)]
+             ("void gdn::prefill_pair_kernel<128, true, true, false, false>(gdn::PrefillParams)", 9999.0),
+             ("void gdn::prefill_pair_kernel<128, false, false, true, false>(gdn::PrefillParams)", 8888.0)]
     write = [("void at::native::neg_kernel(...)", kib),
-             ("void gdn::prefill_pair_kernel<128, false, false, false>(gdn::PrefillParams)", 300.0),
+             ("void gdn::prefill_pair_kernel<128, false, false, false, false>(gdn::PrefillParams)", 300.0),
              ("_ZN3gdn13decode_kernelIDF16bLi128ELi128ELi32EEEvNS_12DecodeParamsE", 400.0),
              ("void gdn::decode_kernel<__bf16, 128, 64, 32>(gdn::DecodeParams)", 800.0)]
     fp, wp = tmp_path / "fetch.csv", tmp_path / "write.csv"
