@@ -135,3 +135,22 @@ def test_multi_walk_decode_route(T, mode):
     _check_decode(x, out_g, pool_g, out_r, pool_r, "bf16")
     if mode == "disable":
         assert torch.equal(pool_g.cpu(), x["pool"])
+
+
+@pytest.mark.parametrize("hq,hv,dk,dv", [(4, 4, 128, 128), (2, 6, 64, 64), (1, 4, 64, 128)],
+                         ids=["no_gva", "gva3_d64", "gva4_dv128"])
+def test_multi_walk_head_maps(hq, hv, dk, dv):
+    """Value head h reads q/k head h * hq / hv inside the walk as outside it."""
+    n = 96
+    L = _lengths(1640 + hv + dk, n, 120)
+    x = synth.prefill_inputs(1641 + hq + hv, lengths=L, hq=hq, hv=hv, dk=dk, dv=dv, dtype="bf16",
+                             gate="gamma", init_std=0.05)
+    o, f = gdn.prefill(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(x["gamma"]),
+                       to_dev(x["beta"]), decay_kind="gamma", cu_seqlens=to_dev(x["cu_seqlens"]),
+                       initial_state=to_dev(x["initial_state"]), scale=x["scale"])
+    torch.cuda.synchronize()
+    ro, rf = oracle.prefill(x["q"], x["k"], x["v"], x["gamma"], x["beta"], decay_is_gamma=True,
+                            cu_seqlens=x["cu_seqlens"], initial_state=x["initial_state"],
+                            scale=x["scale"])
+    assert_close(o, ro, "bf16", "multi-walk out")
+    assert_close(f, rf, "bf16", "multi-walk final state")
