@@ -327,6 +327,14 @@ def extra_workloads(torch, gdn, synth, dev):
     b = px["b"].to(dev).view(B, S, -1)
     o2 = torch.empty_like(v)
     f2 = torch.empty(B, px["hv"], px["dv"], px["dk"], dtype=torch.float32, device=dev)
+    # the same gates computed inside the prefill kernel: one launch for the
+    # headline step's gate + prefill (the same arithmetic, g and beta never
+    # stored)
+    fn = lambda: gdn.prefill(q, k, v, None, None, scale=px["scale"], out=o2, final_state=f2,
+                             A_log=A_log, dt_bias=dt_bias, a=a, b=b)
+    ms = _time_launches(torch, fn, flush=flush)
+    _progress("chunked_prefill_fused_gate")
+    out["chunked_prefill_fused_gate"] = {"ms": ms, "tokens_per_s": px["T"] / (ms * 1e-3)}
     fn = lambda: gdn.prefill(q, k, v, None, None, scale=px["scale"], out=o2, final_state=f2,
                              A_log=A_log, dt_bias=dt_bias, a=a, b=b, qk_l2norm=True)
     ms = _time_launches(torch, fn, flush=flush)
