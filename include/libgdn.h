@@ -215,7 +215,9 @@ typedef struct {
    * a scan over the affine maps of request segments (three launches; see
    * gdn_prefill_workspace_size); otherwise, and whenever that size is 0, the
    * workspace is ignored and every (request, head) is one serial walk over
-   * its chunks.  Both compute the same result up to rounding order.  The
+   * its chunks (for many short bf16 requests one workgroup walks a run of
+   * consecutive requests, each from its own initial state).  All compute the
+   * same result up to rounding order.  The
    * library neither allocates nor keeps the workspace; calls that share one
    * workspace on overlapping streams race. */
   void* workspace;
