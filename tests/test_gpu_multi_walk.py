@@ -8,6 +8,8 @@ requests, uniform packing, initial states, both head sizes, the fused gate
 with the in-kernel L2 norm, pooled states with read and write slots, and the
 multi-token decode's chunked route (skipped rows, disable_state_update).
 """
+import random
+
 import numpy as np
 import pytest
 import torch
@@ -154,3 +156,101 @@ def test_multi_walk_head_maps(hq, hv, dk, dv):
                             scale=x["scale"])
     assert_close(o, ro, "bf16", "multi-walk out")
     assert_close(f, rf, "bf16", "multi-walk final state")
+
+
+USES = {"gated_delta": (True, True), "gated": (True, False), "delta": (False, True),
+        "linear": (False, False)}
+
+
+def _walk_config(i):
+    """A seeded draw of options inside the walk's regime: bf16 pair-kernel
+    head sizes, and more (request, value head, slice) units than 256 with
+    short requests."""
+    r = random.Random(17000 + i)
+    dk, dv = r.choice([(64, 64), (128, 128), (64, 128), (128, 64)])
+    hq = r.choice([1, 2])
+    hv = hq * r.choice([1, 2, 3])
+    units_per_req = hv * (dv // 64)
+    n = max(r.randint(40, 140), 256 // units_per_req + r.randint(1, 20))
+    lengths = [r.choice([0, 1, r.randint(2, 63), 64, r.randint(65, 200)]) for _ in range(n)]
+    if sum(lengths) == 0:
+        lengths[0] = 7
+    rule = r.choice(list(USES))
+    fused = rule != "linear" and r.random() < 0.5
+    return dict(dk=dk, dv=dv, hq=hq, hv=hv, lengths=lengths, rule=rule, fused=fused,
+                norm=r.random() < 0.4, pool=r.random() < 0.4, init=r.random() < 0.6)
+
+
+def run_walk_case(i):
+    c = _walk_config(i)
+    n, hq, hv, dk, dv = len(c["lengths"]), c["hq"], c["hv"], c["dk"], c["dv"]
+    x = synth.prefill_inputs(17100 + i, lengths=c["lengths"], hq=hq, hv=hv, dk=dk, dv=dv,
+                             dtype="bf16", gate="qwen", init_std=0.05 if c["init"] else None)
+    use_d, use_b = USES[c["rule"]]
+    if c["norm"]:
+        g = torch.Generator().manual_seed(17200 + i)
+        x["q"] = (x["q"].float() * (torch.rand(x["T"], hq, 1, generator=g) * 3 + 0.3)).to(torch.bfloat16)
+        x["k"] = (x["k"].float() * (torch.rand(x["T"], hq, 1, generator=g) * 3 + 0.3)).to(torch.bfloat16)
+    kw = dict(cu_seqlens=to_dev(x["cu_seqlens"]), scale=x["scale"], update_rule=c["rule"],
+              qk_l2norm=c["norm"])
+    okw = dict(cu_seqlens=x["cu_seqlens"], scale=x["scale"], update_rule=c["rule"],
+               qk_l2norm_eps=1e-12 if c["norm"] else None)
+    if c["fused"]:
+        gk = {}
+        if use_d:
+            gk.update(A_log=x["A_log"], dt_bias=x["dt_bias"], a=x["a"])
+        if use_b:
+            gk["b"] = x["b"]
+        kw.update({k: to_dev(v) for k, v in gk.items()})
+        okw.update(gk)
+        dec = bet = odec = obet = None
+    else:
+        gd, _, gb = oracle.gate(x["A_log"], x["dt_bias"], x["a"], x["b"])
+        odec = torch.from_numpy(gd).float() if use_d else None
+        obet = torch.from_numpy(gb).float() if use_b else None
+        dec, bet = to_dev(odec), to_dev(obet)
+    if c["pool"]:
+        P = n + 8
+        g = torch.Generator().manual_seed(17300 + i)
+        pool0 = torch.randn(P, hv, dv, dk, generator=g) * 0.05
+        perm = torch.randperm(P, generator=g)
+        read = perm[:n].clone().to(torch.int32)
+        read[::5] = -1                       # these start from zeros
+        write = perm[:n].clone().to(torch.int32)
+        write[2::7] = -1                     # these store nothing
+        pool = to_dev(pool0.clone())
+        out, _ = gdn.prefill(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), dec, bet, state_pool=pool,
+                             read_slot=to_dev(read), write_slot=to_dev(write), **kw)
+        oinit = np.zeros((n, hv, dv, dk))
+        for r_, s in enumerate(read.tolist()):
+            if s >= 0:
+                oinit[r_] = pool0[s].numpy()
+        ro, rf = oracle.prefill(x["q"], x["k"], x["v"], odec, obet, initial_state=oinit, **okw)
+        torch.cuda.synchronize()
+        assert_close(out, ro, "bf16", "out %s" % c)
+        want = pool0.double().numpy().copy()
+        for r_, s in enumerate(write.tolist()):
+            if s >= 0:
+                want[s] = rf[r_]
+        got = pool.cpu().double().numpy()
+        touched = set(s for s in write.tolist() if s >= 0)
+        for s in range(P):
+            if s in touched:
+                assert_close(got[s], want[s], "bf16", "slot %d %s" % (s, c))
+            else:
+                np.testing.assert_array_equal(got[s], want[s])
+    else:
+        out, fin = gdn.prefill(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), dec, bet,
+                               initial_state=to_dev(x["initial_state"]), **kw)
+        ro, rf = oracle.prefill(x["q"], x["k"], x["v"], odec, obet, initial_state=x["initial_state"], **okw)
+        torch.cuda.synchronize()
+        assert_close(out, ro, "bf16", "out %s" % c)
+        assert_close(fin, rf, "bf16", "final %s" % c)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_multi_walk_random_configuration(i):
+    """Seeded cross-feature draws inside the walk's regime: head sizes, GVA,
+    ragged lengths with empty, one-token and chunk-boundary requests, every
+    update rule, given or fused gates, the L2 norm, dense or pooled states."""
+    run_walk_case(i)
