@@ -596,15 +596,11 @@ __device__ __forceinline__ void pair_prep(const PrefillParams& p, PairSmem<DK>& 
 // its final slot.  The pool rules hold per request: a request whose read
 // slot is outside the pool is skipped under kPoolSkipUnread (no outputs, no
 // store; its chunks are still prepared), and an empty request's final state
-// is its initial state.
-// The next request's initial state is loaded into Sn during a request's
-// last chunk, before that chunk's outputs and final-state stores: the
-// vector-memory counter retires in issue order, so a state loaded after
-// the stores would wait for them.  Every chunk issues the same loads and
-// stores -- through buffer descriptors whose range is 0 when a chunk needs
-// none, so they move no data -- and takes the new state by a select, so
-// the compiler's count of memory operations in flight is exact on every
-// path and the wait for Sn leaves the stores in flight.
+// is its initial state.  States move through buffer descriptors whose
+// range is 0 for a slot outside the pool (such loads read zeros and move no
+// data).  The load is not hidden: holding the next request's state in a
+// second register set for a chunk made the chunks slower than the load it
+// hid.
 template <int DK, typename Body>
 __device__ __forceinline__ void pair_multi_walk(const PrefillParams& p, const int64_t* mt, int nreq, int rg0,
                                                 int h, int v0, int nch, int w, int lane, f4 (&S)[DK / 16][2],
@@ -921,14 +917,6 @@ prefill_pair_kernel(const PrefillParams p) {
             if (t < nvalid) *reinterpret_cast<bf4*>(ob + (int64_t)t * ost + 16 * ct + 4 * g) = to_bf4(Y[i][ct]);
           }
       }
-  };
-  auto store_state = [&](int64_t fb) {
-#pragma unroll
-    for (int jj = 0; jj < NKT; ++jj)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-        *reinterpret_cast<f4*>(p.fin + fb + (int64_t)(32 * w + 16 * ct + x) * DK + dk_of<NKT>(jj, 4 * g)) =
-            S[jj][ct];
   };
   if constexpr (MULTI) {
     pair_multi_walk<DK>(p, mt, nreq, rg0, h, v0, nch, w, lane, S, chunk_body);
