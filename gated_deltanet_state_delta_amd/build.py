@@ -33,13 +33,17 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # the trackers 1.2% more (outputs bit-identical); the plain max-ILP strategy
 # is 6% slower.
 # The decode kernel at value width 128 (the single-step pool decode of
-# Hv32 x 128 x 128 states) takes the iterative ILP scheduler: 2.2% faster
-# there (three same-box A/B runs, bit-identical); the same flag made the
-# multi-token width-64 form 2.5% slower, so that one keeps the default.
+# Hv32 x 128 x 128 states) takes the memory-clause scheduler with the
+# register-pressure trackers: 168.1-169.4 -> 165.9-167.0 us median over
+# three alternating same-box runs (the iterative ILP scheduler used before
+# had been 2.2% ahead of the default; the memory-clause scheduler without
+# the trackers is slower); a scheduler flag on the multi-token width-64
+# form made it 2.5% slower, so that one keeps the default.
 FILE_FLAGS = {"gdn_prefill_pair.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form",
                                      "-mllvm", "-amdgpu-sched-strategy=max-memory-clause",
                                      "-mllvm", "-amdgpu-use-amdgpu-trackers"],
-              "gdn_decode_dv128.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+              "gdn_decode_dv128.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause",
+                                       "-mllvm", "-amdgpu-use-amdgpu-trackers"]}
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Wno-unused-function", "-Wno-unused-variable", "-I", os.path.join(ROOT, "include")]
 
