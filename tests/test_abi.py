@@ -105,6 +105,9 @@ PREFILL_ERRORS = [
     (dict(update_rule=2, beta=None, decay=None), 1),   # delta needs a beta
     (dict(update_rule=3, beta=None), 2),               # linear takes no decay
     (dict(update_rule=3, decay=None), 2),              # ... and no beta
+    (dict(update_rule=3, decay=None, beta=None, gate_a=FAKE * 8, A_log=FAKE * 9,
+          dt_bias=FAKE * 10), 2),                      # linear takes no fused decay
+    (dict(update_rule=3, decay=None, beta=None, gate_b=FAKE * 11), 2),  # ... and no fused beta
     (dict(gate_a=FAKE * 8, A_log=FAKE * 9, dt_bias=FAKE * 10), 2),  # decay and gate_a
     (dict(gate_b=FAKE * 8), 2),                        # beta and gate_b
     (dict(decay=None, gate_a=FAKE * 8, A_log=None, dt_bias=FAKE * 10, beta=None,

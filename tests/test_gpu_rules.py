@@ -72,7 +72,17 @@ def _case(rule, cfg, source, seed):
 @pytest.mark.parametrize("rule", ["linear", "gated", "delta", "gated_delta"])
 def test_rule_matches_oracle(rule, cfg, source):
     if rule == "linear" and source == "fused":
-        pytest.skip("linear takes no gate inputs: nothing to fuse")
+        # linear takes no gate inputs: raw ones are refused, never ignored
+        name, dt, dk, dv, chunk = cfg
+        x = synth.prefill_inputs(300, lengths=LENGTHS, hq=2, hv=4, dk=dk, dv=dv, dtype=dt,
+                                 gate="qwen")
+        q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+        for raw in (dict(A_log=x["A_log"], dt_bias=x["dt_bias"], a=x["a"]), dict(b=x["b"])):
+            with pytest.raises(ValueError, match="linear takes no"):
+                gdn.prefill(q, k, v, None, None, cu_seqlens=to_dev(x["cu_seqlens"]),
+                            chunk_size=chunk, update_rule="linear",
+                            **{n: to_dev(t) for n, t in raw.items()})
+        return
     o, f, ro, rf, dt = _case(rule, cfg, source, seed=300 + CONFIGS.index(cfg))
     assert_close(o, ro, dt, "%s %s %s out" % (rule, cfg[0], source))
     assert_close(f, rf, dt, "%s %s %s final state" % (rule, cfg[0], source))
